@@ -1,0 +1,332 @@
+"""Plain fp64 definitions of one CP rank's share of causal THD attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing in the product
+library imports, links or runs this file.
+
+Pages cited (by title and section):
+  [AG]  "[PyTorch] Add no-load-balance THD all-gather CP"
+  [A2A] "[PyTorch] Extend no-load-balance CP to the a2a comm type"
+  [PAD] "[PyTorch][Attention] THD P2P context-parallel regression when padded
+         cu_seqlens are value-equal but not object-identical"
+
+Vocabulary follows the pages: ``cu_seqlens`` (cumulative actual lengths),
+``cu_seqlens_padded`` (cumulative physical offsets into the THD buffer),
+``cp_size``, ``rank``, ``s_local``, DUAL_CHUNK_SWAP and NO_LOAD_BALANCE.
+
+Readings of points the pages leave open (each is listed in the design notes):
+  * DUAL_CHUNK_SWAP gives rank r the chunks r and 2*cp_size-1-r of every
+    document ([AG] "Why" says only "2 * cp_size chunks" and "two attention
+    steps per rank"; the mirrored pair is the one that balances causal work,
+    which is the point of the load-balanced default).
+  * Local row order under DUAL_CHUNK_SWAP: document-major, chunk r before
+    chunk 2*cp_size-1-r, ascending token order inside a chunk.
+  * Padding of a document sits at its end: the first L_i rows of
+    [cu_seqlens_padded[i], cu_seqlens_padded[i+1]) are valid.
+  * Partitions cover the physical buffer, padding rows included ([AG]
+    "What changed": "one contiguous physical-token chunk"; "Why": "the
+    complete physical buffer").
+  * NO_LOAD_BALANCE: s_local = T / cp_size; rows at or past
+    cu_seqlens_padded[B] are a padding tail ([A2A] body: only the packed
+    total must divide).
+  * Causality is by position inside the document, diagonal included
+    (window_size = (-1, 0), [AG] "Scope and constraints"), and the mask is
+    identical to cp_size = 1 ([A2A] body).
+  * softmax scale 1/sqrt(D); LSE is the natural log; padding rows give
+    O = 0 and LSE = -inf; gradients of padding rows and of keys that no
+    local query attends are 0.
+
+Every function below is pinned by tests in ``tests/test_oracle_*.py`` against
+hand examples, closed forms, brute force, a library routine on special cases
+and finite differences; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+DUAL_CHUNK_SWAP = "dual_chunk_swap"
+NO_LOAD_BALANCE = "no_load_balance"
+
+# Row chunk size for the dense per-document score matrices (rows are
+# independent, so chunking rows changes no arithmetic).
+_MAX_SCORE_ELEMS = 1 << 24
+
+
+# --------------------------------------------------------------------------
+# Metadata
+# --------------------------------------------------------------------------
+
+def _as_list(a) -> list:
+    return [int(x) for x in np.asarray(a).reshape(-1)]
+
+
+def check_layout(cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, rank: int,
+                 strategy: str) -> None:
+    """Raise ValueError when the THD metadata breaks a rule the pages state.
+
+    [AG] "Why": DUAL_CHUNK_SWAP divides every sequence into 2*cp_size chunks,
+    so every padded document length must divide by 2*cp_size; NO_LOAD_BALANCE
+    only needs the packed total to divide by cp_size ([A2A] body).
+    """
+    cu = _as_list(cu_seqlens)
+    cup = _as_list(cu_seqlens_padded)
+    if len(cu) != len(cup) or len(cup) < 1:
+        raise ValueError("cu_seqlens and cu_seqlens_padded must have the same length B+1")
+    if cp_size < 1 or not (0 <= rank < cp_size):
+        raise ValueError("rank must lie in [0, cp_size)")
+    if cup[0] != 0 or cu[0] != 0:
+        raise ValueError("cumulative arrays must start at 0")
+    for i in range(len(cup) - 1):
+        p = cup[i + 1] - cup[i]
+        n = cu[i + 1] - cu[i]
+        if p < 0 or n < 0:
+            raise ValueError("cumulative arrays must be non-decreasing")
+        if n > p:
+            raise ValueError("a document's actual length exceeds its padded length")
+        if strategy == DUAL_CHUNK_SWAP and p % (2 * cp_size) != 0:
+            raise ValueError("DUAL_CHUNK_SWAP needs every padded length divisible by 2*cp_size")
+    if cup[-1] > T:
+        raise ValueError("cu_seqlens_padded[-1] exceeds T")
+    if strategy == DUAL_CHUNK_SWAP and cup[-1] != T:
+        raise ValueError("DUAL_CHUNK_SWAP needs T == cu_seqlens_padded[-1]")
+    if T % cp_size != 0:
+        raise ValueError("T must divide by cp_size")
+    if strategy not in (DUAL_CHUNK_SWAP, NO_LOAD_BALANCE):
+        raise ValueError("unknown strategy")
+
+
+def padding_present(cu_seqlens, cu_seqlens_padded, T: int) -> bool:
+    """Inter-sequence padding decided by value, never by object identity.
+
+    [PAD] "Expected behavior": equal values must mean "no padding" even when
+    the two arrays are separate objects.
+    """
+    cu = _as_list(cu_seqlens)
+    cup = _as_list(cu_seqlens_padded)
+    for i in range(len(cup) - 1):
+        if (cu[i + 1] - cu[i]) != (cup[i + 1] - cup[i]):
+            return True
+    return T > cup[-1]
+
+
+def token_table(cu_seqlens, cu_seqlens_padded, T: int):
+    """Per physical row t: document index (-1 in the tail), position inside
+    the document, and whether the row is a real (non-padding) token."""
+    cu = _as_list(cu_seqlens)
+    cup = _as_list(cu_seqlens_padded)
+    doc = np.full(T, -1, dtype=np.int64)
+    pos = np.zeros(T, dtype=np.int64)
+    valid = np.zeros(T, dtype=bool)
+    for i in range(len(cup) - 1):
+        start, end = cup[i], cup[i + 1]
+        length = cu[i + 1] - cu[i]
+        doc[start:end] = i
+        pos[start:end] = np.arange(end - start)
+        valid[start:end] = pos[start:end] < length
+    return doc, pos, valid
+
+
+def partition_index(cu_seqlens_padded, T: int, cp_size: int, rank: int,
+                    strategy: str) -> np.ndarray:
+    """Global physical row of each local row of ``rank`` (int64 [T/cp_size]).
+
+    NO_LOAD_BALANCE ([AG] "What changed"; [A2A] body): rank r owns the
+    contiguous range [r*s_local, (r+1)*s_local) with s_local = T/cp_size.
+
+    DUAL_CHUNK_SWAP ([AG] "Why"): every padded document is cut into
+    2*cp_size equal chunks; rank r takes chunk r and chunk 2*cp_size-1-r.
+    """
+    cup = _as_list(cu_seqlens_padded)
+    if strategy == NO_LOAD_BALANCE:
+        s_local = T // cp_size
+        return np.arange(rank * s_local, (rank + 1) * s_local, dtype=np.int64)
+    rows = []
+    for i in range(len(cup) - 1):
+        chunk = (cup[i + 1] - cup[i]) // (2 * cp_size)
+        for c in (rank, 2 * cp_size - 1 - rank):
+            first = cup[i] + c * chunk
+            rows.extend(range(first, first + chunk))
+    return np.asarray(rows, dtype=np.int64)
+
+
+def local_valid_lengths(cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, rank: int,
+                        strategy: str) -> np.ndarray:
+    """Number of real tokens of each document held by ``rank`` (int64 [B]).
+
+    The per-rank valid length the P2P path asks for ([PAD] "Describe the
+    bug", get_cu_seqlens_on_cp_rank), counted from the token table.
+    """
+    doc, _, valid = token_table(cu_seqlens, cu_seqlens_padded, T)
+    idx = partition_index(cu_seqlens_padded, T, cp_size, rank, strategy)
+    B = len(_as_list(cu_seqlens_padded)) - 1
+    out = np.zeros(B, dtype=np.int64)
+    for g in idx:
+        if valid[g]:
+            out[doc[g]] += 1
+    return out
+
+
+def causal_pairs(cu_seqlens, cu_seqlens_padded, T: int, idx) -> int:
+    """Number of (query, key) pairs the mask allows, summed over local rows
+    (per head): query g attends keys j of its own document with j <= g."""
+    doc, pos, valid = token_table(cu_seqlens, cu_seqlens_padded, T)
+    total = 0
+    for g in _as_list(idx):
+        if valid[g]:
+            total += int(pos[g]) + 1
+    return total
+
+
+def touched_keys(cu_seqlens, cu_seqlens_padded, T: int, idx) -> np.ndarray:
+    """bool [T]: key rows attended by at least one local query."""
+    doc, pos, valid = token_table(cu_seqlens, cu_seqlens_padded, T)
+    cup = _as_list(cu_seqlens_padded)
+    out = np.zeros(T, dtype=bool)
+    for g in _as_list(idx):
+        if valid[g]:
+            out[cup[doc[g]]:g + 1] = True
+    return out
+
+
+# --------------------------------------------------------------------------
+# Row movement
+# --------------------------------------------------------------------------
+
+def gather(src: np.ndarray, idx) -> np.ndarray:
+    """dst[m] = src[idx[m]] (the rank slicing of [AG] "How to use" and the
+    K/V restore of its sequence diagram)."""
+    return np.asarray(src)[np.asarray(idx, dtype=np.int64)]
+
+
+def scatter(src: np.ndarray, idx, n_dst: int, fill=0) -> np.ndarray:
+    """dst[idx[m]] = src[m]; rows not named keep ``fill``."""
+    src = np.asarray(src)
+    dst = np.full((n_dst,) + src.shape[1:], fill, dtype=src.dtype)
+    dst[np.asarray(idx, dtype=np.int64)] = src
+    return dst
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def _groups(idx, cu_seqlens, cu_seqlens_padded, T: int, rows: Optional[Sequence[int]]):
+    """Valid local rows grouped by document: (doc start, local rows, globals)."""
+    doc, _, valid = token_table(cu_seqlens, cu_seqlens_padded, T)
+    cup = _as_list(cu_seqlens_padded)
+    idx = np.asarray(idx, dtype=np.int64)
+    sel = np.arange(len(idx)) if rows is None else np.asarray(sorted(set(_as_list(rows))),
+                                                               dtype=np.int64)
+    by_doc = {}
+    for m in sel:
+        g = int(idx[m])
+        if valid[g]:
+            by_doc.setdefault(int(doc[g]), []).append(int(m))
+    out = []
+    for d in sorted(by_doc):
+        ms = np.asarray(by_doc[d], dtype=np.int64)
+        out.append((cup[d], ms, idx[ms]))
+    return out
+
+
+def _scores(q_rows, k_keys, g_rows, key0: int, scale: float):
+    """scale * q k^T with keys j > g (other rows of the future) set to -inf."""
+    s = (q_rows @ k_keys.T) * scale
+    keys = key0 + np.arange(k_keys.shape[0])
+    s[keys[None, :] > g_rows[:, None]] = -np.inf
+    return s
+
+
+def _chunks(n_rows: int, n_keys: int):
+    step = max(1, _MAX_SCORE_ELEMS // max(1, n_keys))
+    for r0 in range(0, n_rows, step):
+        yield r0, min(n_rows, r0 + step)
+
+
+def attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T: int,
+                  scale: Optional[float] = None, rows: Optional[Sequence[int]] = None):
+    """O [n, H, D] and LSE [H, n] of local queries against the full K/V.
+
+    A local row m with global row g = idx[m] that is a real token attends the
+    keys j of its own document with j <= g (all real, since padding sits at
+    the end of a document): s_j = scale * <Q_m, K_j>, LSE = log sum_j exp s_j,
+    O_m = sum_j exp(s_j - LSE) V_j. Padding rows: O = 0, LSE = -inf.
+    ``rows`` restricts the computation to those local rows (others stay 0/-inf).
+    """
+    q_local = np.asarray(q_local, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, H, D = q_local.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = np.zeros((n, H, v.shape[2]), dtype=np.float64)
+    lse = np.full((H, n), -np.inf, dtype=np.float64)
+    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, rows):
+        kend = int(gs.max()) + 1
+        for h in range(H):
+            kk = k[a:kend, h]
+            vv = v[a:kend, h]
+            for r0, r1 in _chunks(len(ms), kend - a):
+                s = _scores(q_local[ms[r0:r1], h], kk, gs[r0:r1], a, scale)
+                mx = s.max(axis=1)
+                e = np.exp(s - mx[:, None])
+                tot = e.sum(axis=1)
+                lse[h, ms[r0:r1]] = mx + np.log(tot)
+                out[ms[r0:r1], h] = (e / tot[:, None]) @ vv
+    return out, lse
+
+
+def attention_bwd(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded, T: int,
+                  scale: Optional[float] = None, rows: Optional[Sequence[int]] = None):
+    """Gradients of sum(dO * O) for ``attention_fwd``: dQ [n,H,D] (local rows)
+    and this rank's partial dK, dV [T,H,D] in global order.
+
+    With P the softmax rows and dP_j = <dO_m, V_j>, the softmax Jacobian gives
+    dS_j = P_j (dP_j - sum_i P_i dP_i); then dQ_m = scale sum_j dS_j K_j,
+    dK_j += scale dS_j Q_m, dV_j += P_j dO_m. These partials are what the
+    rank hands to the reduce-scatter ([AG] sequence diagram: dK/dV are
+    unrestored for reduce-scatter). Rows that are padding or that no local
+    query attends stay 0. ``rows`` restricts the query rows that contribute.
+    """
+    q_local = np.asarray(q_local, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do_local = np.asarray(do_local, dtype=np.float64)
+    n, H, D = q_local.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = np.zeros((n, H, D), dtype=np.float64)
+    dk = np.zeros((T, H, D), dtype=np.float64)
+    dv = np.zeros((T, H, D), dtype=np.float64)
+    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, rows):
+        kend = int(gs.max()) + 1
+        for h in range(H):
+            kk = k[a:kend, h]
+            vv = v[a:kend, h]
+            for r0, r1 in _chunks(len(ms), kend - a):
+                m_sel = ms[r0:r1]
+                qq = q_local[m_sel, h]
+                dd = do_local[m_sel, h]
+                s = _scores(qq, kk, gs[r0:r1], a, scale)
+                mx = s.max(axis=1)
+                e = np.exp(s - mx[:, None])
+                p = e / e.sum(axis=1)[:, None]
+                dp = dd @ vv.T
+                ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+                dq[m_sel, h] = scale * (ds @ kk)
+                dk[a:kend, h] += scale * (ds.T @ qq)
+                dv[a:kend, h] += p.T @ dd
+    return dq, dk, dv
+
+
+def rank_share(q, k, v, do, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int,
+               rank: int, strategy: str, scale: Optional[float] = None):
+    """Everything one rank computes, from global-order inputs: idx, O, LSE,
+    dQ (local rows) and the dK/dV partials (global rows)."""
+    idx = partition_index(cu_seqlens_padded, T, cp_size, rank, strategy)
+    q_local = gather(q, idx)
+    do_local = gather(do, idx)
+    o, lse = attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T, scale)
+    dq, dk, dv = attention_bwd(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded,
+                               T, scale)
+    return idx, o, lse, dq, dk, dv
