@@ -1,0 +1,256 @@
+"""Benchmark: one CP rank's share of causal THD attention on one MI355X.
+
+A step is one pass of the whole hot path for the measured rank over one batch:
+  validate + build the rank plan (host) and upload it,
+  partition index for every rank (the all-ranks permutation),
+  gather the rank's local Q and dO,
+  restore K and V from the rank-major all-gathered buffer to global order,
+  attention forward (O, LSE),
+  attention backward (preprocess, main kernel, gated zeroing of untouched rows),
+  unrestore dK and dV to rank-major order for the reduce-scatter.
+Inputs are synthetic and already resident in HBM when timing starts.
+
+value = 14 * D * H * causal_pairs / step time (TFLOP/s; causal-masked FLOPs
+only). The roofline object is for the attention backward main kernel, timed
+with HIP events on the stream it runs on; the gather roofline covers the two
+K/V restore launches.
+
+    python bench.py [--steps K] [--warmup W] [--workload dcs_8k] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal THD attn fwd+bwd TFLOP/s per CP-rank share; % bf16 MFMA peak; gather GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dcs_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 --pmc (optional)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build simulates every CP rank on a single "
+              f"device and has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import context_causal_attention_thd_amd as thd
+    import workloads as W
+
+    thd.lib()
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    t = W.bf16_tensors(w)
+    q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
+    cup_dev = torch.from_numpy(cup).to(dev)
+    T, H, D, cp, r = w.T, w.H, w.D, w.cp_size, w.rank
+    n_local = T // cp
+
+    # The all-gathered K/V as the rank receives it: every rank's share, rank-major.
+    perm0 = thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy)
+    k_rm = thd.gather(k, perm0)
+    v_rm = thd.gather(v, perm0)
+    torch.cuda.synchronize()
+
+    # Persistent buffers (allocation is outside the step).
+    perm = torch.empty(T, dtype=torch.int32, device=dev)
+    q_local = torch.empty((n_local, H, D), dtype=torch.bfloat16, device=dev)
+    do_local = torch.empty_like(q_local)
+    k_g = torch.empty_like(k)
+    v_g = torch.empty_like(v)
+    o = torch.empty_like(q_local)
+    lse = torch.empty((H, n_local), dtype=torch.float32, device=dev)
+    dq = torch.empty((n_local, H, D), dtype=torch.float32, device=dev)
+    dk = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    dk_rm = torch.empty_like(dk)
+    dv_rm = torch.empty_like(dk)
+    probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False)
+    ws = torch.empty(int(probe.info.workspace_bytes) + 4096, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(int(probe.info.bwd_scratch_bytes) + 256, dtype=torch.uint8, device=dev)
+    pairs = int(probe.info.causal_pairs)
+    probe.close()
+
+    ev = {}
+
+    def step(record: bool):
+        def mark(name):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev.setdefault(name, []).append(e)
+
+        plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False)
+        plan.upload_into(ws, stream)
+        thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
+        mine = perm[r * n_local:(r + 1) * n_local]
+        thd.gather(q, mine, out=q_local)
+        thd.gather(do, mine, out=do_local)
+        mark("restore0")
+        thd.scatter(k_rm, perm, k_g)
+        thd.scatter(v_rm, perm, v_g)
+        mark("restore1")
+        mark("fwd0")
+        thd.attn_fwd(plan, q_local, k_g, v_g, o=o, lse=lse)
+        mark("fwd1")
+        pair = None
+        if record:
+            pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev.setdefault("bwd", []).append(pair)
+        thd.attn_bwd_parts(plan, q_local, k_g, v_g, o, lse, do_local, dq, dk, dv, scratch,
+                           zero_untouched=True, events=pair)
+        thd.gather(dk, perm, out=dk_rm)
+        thd.gather(dv, perm, out=dv_rm)
+        return plan  # keep alive until the stream is synchronized
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    plans = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        plans.append(step(True))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    plans.clear()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    def avg(a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+
+    t_fwd = avg("fwd0", "fwd1")
+    t_bwd = float(np.mean([x.elapsed_time(y) for x, y in ev["bwd"]]))
+    t_restore = avg("restore0", "restore1")
+
+    flop_fwd = 4.0 * D * H * pairs
+    flop_bwd = 10.0 * D * H * pairs
+    tflops_step = (flop_fwd + flop_bwd) / (ms_step * 1e-3) / 1e12
+    tflops_bwd = flop_bwd / (t_bwd * 1e-3) / 1e12
+    tflops_fwd = flop_fwd / (t_fwd * 1e-3) / 1e12
+    row_bytes = H * D * 2
+    restore_bytes = 2 * (2 * T * row_bytes + 4 * T)    # K and V: read + write rows, read idx
+    gbs_restore = restore_bytes / (t_restore * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                tj = json.load(f)
+            entry = tj.get(args.workload, {}).get("attn_bwd_kernel")
+            if entry and entry.get("source_hash") == _kernel_hash():
+                traffic = entry["bytes_per_launch"]
+        except Exception:
+            traffic = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops_step, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "heads": H, "head_dim": D, "cp_size": cp,
+                   "rank": r, "strategy": w.strategy, "docs": w.B, "causal_pairs_per_head": pairs,
+                   "parallelism": "one simulated CP rank on one GPU"},
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd_kernel",
+                     "achieved": round(tflops_bwd, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_bwd / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "roofline_fwd": {"bound": "mfma", "kernel": "attn_fwd_kernel",
+                         "achieved": round(tflops_fwd, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops_fwd / PEAK_BF16_TFLOPS, 4)},
+        "roofline_gather": {"bound": "hbm", "kernel": "move_rows_kernel (K/V restore)",
+                            "achieved": round(gbs_restore, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs_restore / PEAK_HBM_GBS, 4),
+                            "bytes": restore_bytes},
+        "times_ms": {"step": round(ms_step, 4), "fwd": round(t_fwd, 4),
+                     "bwd_main": round(t_bwd, 4), "kv_restore": round(t_restore, 4),
+                     "attn_fwd_plus_bwd_main_tflops": round(
+                         (flop_fwd + flop_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
+                     "host_wall_per_step": round(wall / args.steps * 1e3, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, t)
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_hash() -> str:
+    import hashlib
+    p = os.path.join(ROOT, "context_causal_attention_thd_amd", "csrc", "attn_bwd.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(w, t):
+    """The fp64 oracle, as it stands, on the host cores: the same rank share's
+    forward + backward (every local row, every head), timed once."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    t64 = {n: x.double().numpy() for n, x in t.items()}
+    idx = O.partition_index(cup, w.T, w.cp_size, w.rank, w.strategy)
+    ql, dol = t64["q"][idx], t64["do"][idx]
+    t0 = time.perf_counter()
+    O.attention_fwd(ql, t64["k"], t64["v"], idx, cu, cup, w.T)
+    O.attention_bwd(ql, t64["k"], t64["v"], dol, idx, cu, cup, w.T)
+    dt = time.perf_counter() - t0
+    pairs = O.causal_pairs(cu, cup, w.T, idx)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(14.0 * w.D * w.H * pairs / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"full {w.name} rank-{w.rank} share (fwd+bwd, {len(idx)} local rows, "
+                      f"{w.H} heads), fp64 numpy, one run of {dt:.2f} s",
+            "seconds": round(dt, 3), "cpu_model": cpu,
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,388 @@
+"""Python binding of libthdcp (one CP rank's share of causal THD attention on
+MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP library through its C
+ABI (include/thdcp.h). PyTorch supplies device memory and the current HIP
+stream. There is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libthdcp.so")
+
+DUAL_CHUNK_SWAP = 0
+NO_LOAD_BALANCE = 1
+_STRATEGY_NAMES = {"dual_chunk_swap": DUAL_CHUNK_SWAP, "no_load_balance": NO_LOAD_BALANCE,
+                   DUAL_CHUNK_SWAP: DUAL_CHUNK_SWAP, NO_LOAD_BALANCE: NO_LOAD_BALANCE}
+
+EXPORTED_SYMBOLS = (
+    "thdcp_last_error", "thdcp_version", "thdcp_validate", "thd_partition_index", "thd_gather",
+    "thd_scatter", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
+    "thdcp_plan_upload", "thdcp_plan_destroy", "cp_attn_fwd", "cp_attn_bwd",
+    "cp_attn_bwd_preprocess", "cp_attn_bwd_main", "thdcp_zero_untouched",
+)
+
+
+class ThdcpError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libthdcp status {status}: {msg}")
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("cu_seqlens_padded_host", ctypes.POINTER(ctypes.c_int32)),
+        ("B", ctypes.c_int32),
+        ("T", ctypes.c_int64),
+        ("cp_size", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("strategy", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+        ("pad_between_seqs", ctypes.c_int32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("n_local", ctypes.c_int64),
+        ("causal_pairs", ctypes.c_int64),
+        ("touched_rows", ctypes.c_int64),
+        ("untouched_rows", ctypes.c_int64),
+        ("padding_present", ctypes.c_int32),
+        ("n_fwd_tiles", ctypes.c_int32),
+        ("n_bwd_tiles", ctypes.c_int32),
+        ("n_zero_ranges", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("bwd_scratch_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libthdcp.so (raises if it has not been built)."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libthdcp is not built ({LIB_PATH} missing); run "
+                          "`python -m context_causal_attention_thd_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    L.thdcp_last_error.restype = ctypes.c_char_p
+    L.thdcp_last_error.argtypes = []
+    L.thdcp_version.restype = i32
+    L.thdcp_validate.restype = i32
+    L.thdcp_validate.argtypes = [pi32, pi32, i32, i64, i32, i32, i32, i32, i32, i32, pi32]
+    L.thd_partition_index.restype = i32
+    L.thd_partition_index.argtypes = [pi32, vp, i32, i64, i32, i32, i32, vp, vp]
+    L.thd_gather.restype = i32
+    L.thd_gather.argtypes = [vp, i64, vp, i64, i64, vp, vp]
+    L.thd_scatter.restype = i32
+    L.thd_scatter.argtypes = [vp, i64, vp, i64, vp, i64, vp]
+    L.thdcp_plan_create.restype = i32
+    L.thdcp_plan_create.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(vp)]
+    L.thdcp_plan_get_info.restype = i32
+    L.thdcp_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    L.thdcp_plan_local_seqlens.restype = i32
+    L.thdcp_plan_local_seqlens.argtypes = [vp, pi32]
+    L.thdcp_plan_upload.restype = i32
+    L.thdcp_plan_upload.argtypes = [vp, vp, sz, vp]
+    L.thdcp_plan_destroy.restype = None
+    L.thdcp_plan_destroy.argtypes = [vp]
+    L.cp_attn_fwd.restype = i32
+    L.cp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    L.cp_attn_bwd.restype = i32
+    L.cp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+    L.cp_attn_bwd_preprocess.restype = i32
+    L.cp_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+    L.cp_attn_bwd_main.restype = i32
+    L.cp_attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.thdcp_zero_untouched.restype = i32
+    L.thdcp_zero_untouched.argtypes = [vp, vp, vp, vp]
+    _lib_handle = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise ThdcpError(status, lib().thdcp_last_error().decode(errors="replace"))
+
+
+def _i32_host(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _i32_ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _strategy(s) -> int:
+    try:
+        return _STRATEGY_NAMES[s]
+    except KeyError:
+        raise ValueError(f"unknown strategy {s!r}") from None
+
+
+def _stream(stream=None):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name: str, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# Metadata
+# ---------------------------------------------------------------------------
+
+def validate(cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, rank: int, strategy,
+             window=(-1, 0), pad_between_seqs: int = -1) -> bool:
+    """Check the THD layout rules; returns whether padding is present (by value)."""
+    cup = _i32_host(cu_seqlens_padded)
+    cu = None if cu_seqlens is None else _i32_host(cu_seqlens)
+    out = ctypes.c_int32(0)
+    _check(lib().thdcp_validate(_i32_ptr(cu), _i32_ptr(cup), len(cup) - 1, int(T), int(cp_size),
+                                int(rank), _strategy(strategy), int(window[0]), int(window[1]),
+                                int(pad_between_seqs), ctypes.byref(out)))
+    return bool(out.value)
+
+
+def partition_index(cu_seqlens_padded_host, cu_seqlens_padded_dev, T: int, cp_size: int,
+                    rank: int, strategy, out=None, stream=None, validate_host: bool = True):
+    """int32 device tensor [T/cp_size] (rank >= 0) or [T] (rank == -1, rank-major)."""
+    import torch
+    cup = _i32_host(cu_seqlens_padded_host)
+    n = int(T) if rank < 0 else int(T) // int(cp_size)
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=cu_seqlens_padded_dev.device)
+    _check(lib().thd_partition_index(_i32_ptr(cup) if validate_host else None,
+                                     _dev_ptr(cu_seqlens_padded_dev, "cu_seqlens_padded_dev",
+                                              torch.int32),
+                                     len(cup) - 1, int(T), int(cp_size), int(rank),
+                                     _strategy(strategy),
+                                     _dev_ptr(out, "out", torch.int32), _stream(stream)))
+    return out
+
+
+def _row_bytes(t) -> int:
+    return t[0].numel() * t.element_size() if t.shape[0] > 0 else (
+        int(np.prod(t.shape[1:])) * t.element_size())
+
+
+def gather(src, idx, out=None, stream=None):
+    """out[m] = src[idx[m]] over the leading dimension (any dtype)."""
+    import torch
+    if out is None:
+        out = torch.empty((idx.shape[0],) + tuple(src.shape[1:]), dtype=src.dtype,
+                          device=src.device)
+    rb = _row_bytes(src)
+    if _row_bytes(out) != rb:
+        raise ValueError("src and out rows differ in size")
+    _check(lib().thd_gather(_dev_ptr(src, "src"), src.shape[0], _dev_ptr(idx, "idx", torch.int32),
+                            idx.shape[0], rb, _dev_ptr(out, "out"), _stream(stream)))
+    return out
+
+
+def scatter(src, idx, out, stream=None):
+    """out[idx[m]] = src[m] over the leading dimension (any dtype)."""
+    import torch
+    rb = _row_bytes(src)
+    if _row_bytes(out) != rb:
+        raise ValueError("src and out rows differ in size")
+    _check(lib().thd_scatter(_dev_ptr(src, "src"), src.shape[0],
+                             _dev_ptr(idx, "idx", torch.int32), rb, _dev_ptr(out, "out"),
+                             out.shape[0], _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Plan + attention
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Host plan + its device workspace (a torch uint8 tensor)."""
+
+    def __init__(self, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, rank: int, strategy,
+                 H: int, D: int, softmax_scale: float = 0.0, window=(-1, 0),
+                 pad_between_seqs: int = -1, device=None, stream=None, upload: bool = True):
+        self._cup = _i32_host(cu_seqlens_padded)
+        self._cu = None if cu_seqlens is None else _i32_host(cu_seqlens)
+        d = _Desc()
+        d.cu_seqlens_host = _i32_ptr(self._cu)
+        d.cu_seqlens_padded_host = _i32_ptr(self._cup)
+        d.B = len(self._cup) - 1
+        d.T = int(T)
+        d.cp_size = int(cp_size)
+        d.rank = int(rank)
+        d.strategy = _strategy(strategy)
+        d.H = int(H)
+        d.D = int(D)
+        d.softmax_scale = float(softmax_scale)
+        d.window_left, d.window_right = int(window[0]), int(window[1])
+        d.pad_between_seqs = int(pad_between_seqs)
+        self._handle = ctypes.c_void_p()
+        _check(lib().thdcp_plan_create(ctypes.byref(d), ctypes.byref(self._handle)))
+        self.T, self.H, self.D, self.cp_size, self.rank = int(T), int(H), int(D), cp_size, rank
+        self.info = PlanInfo()
+        _check(lib().thdcp_plan_get_info(self._handle, ctypes.byref(self.info)))
+        self.n_local = int(self.info.n_local)
+        self.workspace = None
+        if upload:
+            self.upload(device=device, stream=stream)
+
+    def upload(self, device=None, stream=None):
+        import torch
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        nbytes = int(self.info.workspace_bytes)
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        base = self.workspace.data_ptr()
+        aligned = (base + 255) & ~255
+        _check(lib().thdcp_plan_upload(self._handle, ctypes.c_void_p(aligned), nbytes,
+                                       _stream(stream)))
+        return self
+
+    def upload_into(self, workspace, stream=None):
+        """Upload into a caller-owned uint8 device tensor (no allocation)."""
+        import torch
+        nbytes = int(self.info.workspace_bytes)
+        base = _dev_ptr(workspace, "workspace", torch.uint8).value
+        aligned = (base + 255) & ~255
+        if aligned + nbytes > base + workspace.numel():
+            raise ValueError("workspace too small")
+        self.workspace = workspace
+        _check(lib().thdcp_plan_upload(self._handle, ctypes.c_void_p(aligned), nbytes,
+                                       _stream(stream)))
+        return self
+
+    def local_seqlens(self) -> np.ndarray:
+        out = np.zeros(len(self._cup) - 1, dtype=np.int32)
+        _check(lib().thdcp_plan_local_seqlens(self._handle, _i32_ptr(out)))
+        return out
+
+    def close(self):
+        if self._handle is not None and self._handle.value:
+            lib().thdcp_plan_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._handle
+
+
+def attn_fwd(plan: Plan, q_local, k, v, o=None, lse=None, stream=None):
+    """O bf16 [n_local,H,D] and LSE fp32 [H,n_local]."""
+    import torch
+    n, H, D = plan.n_local, plan.H, plan.D
+    _shape(q_local, (n, H, D), "q_local")
+    _shape(k, (plan.T, H, D), "k")
+    _shape(v, (plan.T, H, D), "v")
+    if o is None:
+        o = torch.empty((n, H, D), dtype=torch.bfloat16, device=q_local.device)
+    if lse is None:
+        lse = torch.empty((H, n), dtype=torch.float32, device=q_local.device)
+    _check(lib().cp_attn_fwd(plan.handle, _dev_ptr(q_local, "q_local", torch.bfloat16),
+                             _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+                             _dev_ptr(o, "o", torch.bfloat16), _dev_ptr(lse, "lse", torch.float32),
+                             _stream(stream)))
+    return o, lse
+
+
+def attn_bwd(plan: Plan, q_local, k, v, o, lse, d_o, dq=None, dk=None, dv=None,
+             zero_untouched: bool = True, accumulate_dkv: bool = False, scratch=None,
+             stream=None):
+    """dQ fp32 [n_local,H,D]; dK, dV fp32 [T,H,D] (this rank's partials)."""
+    import torch
+    n, H, D, T = plan.n_local, plan.H, plan.D, plan.T
+    dev = q_local.device
+    _shape(d_o, (n, H, D), "d_o")
+    if dq is None:
+        dq = torch.empty((n, H, D), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = (torch.empty if zero_untouched else torch.zeros)((T, H, D), dtype=torch.float32,
+                                                              device=dev)
+    if dv is None:
+        dv = (torch.empty if zero_untouched else torch.zeros)((T, H, D), dtype=torch.float32,
+                                                              device=dev)
+    need = int(plan.info.bwd_scratch_bytes)
+    if scratch is None:
+        scratch = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib().cp_attn_bwd(plan.handle, _dev_ptr(q_local, "q_local", torch.bfloat16),
+                             _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+                             _dev_ptr(o, "o", torch.bfloat16),
+                             _dev_ptr(lse, "lse", torch.float32),
+                             _dev_ptr(d_o, "d_o", torch.bfloat16),
+                             _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
+                             _dev_ptr(dv, "dv", torch.float32), int(bool(zero_untouched)),
+                             int(bool(accumulate_dkv)), _dev_ptr(scratch, "scratch"),
+                             scratch.numel() * scratch.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_parts(plan: Plan, q_local, k, v, o, lse, d_o, dq, dk, dv, scratch,
+                   zero_untouched: bool = True, accumulate_dkv: bool = False, stream=None,
+                   events=None):
+    """cp_attn_bwd as its three launches. ``events`` (optional pair of
+    torch.cuda.Event) are recorded right before and after the main kernel."""
+    import torch
+    L = lib()
+    st = _stream(stream)
+    nbytes = scratch.numel() * scratch.element_size()
+    _check(L.cp_attn_bwd_preprocess(plan.handle, _dev_ptr(o, "o", torch.bfloat16),
+                                    _dev_ptr(lse, "lse", torch.float32),
+                                    _dev_ptr(d_o, "d_o", torch.bfloat16),
+                                    _dev_ptr(dq, "dq", torch.float32), _dev_ptr(scratch, "scratch"),
+                                    nbytes, st))
+    if events is not None:
+        events[0].record()
+    _check(L.cp_attn_bwd_main(plan.handle, _dev_ptr(q_local, "q_local", torch.bfloat16),
+                              _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+                              _dev_ptr(lse, "lse", torch.float32),
+                              _dev_ptr(d_o, "d_o", torch.bfloat16),
+                              _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
+                              _dev_ptr(dv, "dv", torch.float32), int(bool(accumulate_dkv)),
+                              _dev_ptr(scratch, "scratch"), nbytes, st))
+    if events is not None:
+        events[1].record()
+    if zero_untouched:
+        _check(L.thdcp_zero_untouched(plan.handle, _dev_ptr(dk, "dk", torch.float32),
+                                      _dev_ptr(dv, "dv", torch.float32), st))
+    return dq, dk, dv
+
+
+def _shape(t, shape: Sequence[int], name: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")

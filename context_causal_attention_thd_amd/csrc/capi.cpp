@@ -1,0 +1,529 @@
+// C ABI of libthdcp: argument checks, by-value padding detection, the rank
+// plan, and dispatch of the gfx950 kernels on the caller's stream.
+//
+// Pages cited (title and section):
+//   [AG]  "[PyTorch] Add no-load-balance THD all-gather CP"
+//   [A2A] "[PyTorch] Extend no-load-balance CP to the a2a comm type"
+//   [PAD] "[PyTorch][Attention] THD P2P context-parallel regression when padded
+//          cu_seqlens are value-equal but not object-identical"
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/thdcp.h"
+#include "internal.h"
+
+using namespace thdcp;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+thdcp_status_t fail(thdcp_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+thdcp_status_t ok() {
+  g_last_error.clear();
+  return THDCP_OK;
+}
+
+thdcp_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(THDCP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Layout rules ([AG] "Why", "Scope and constraints"; [A2A] body) and padding
+// by value ([PAD] "Expected behavior").
+thdcp_status_t check_layout(const int32_t* cu, const int32_t* cup, int32_t B, int64_t T,
+                            int32_t cp, int32_t rank, int32_t strategy, int32_t wl, int32_t wr,
+                            int32_t pad_flag, int32_t* padding_out) {
+  if (!cup) return fail(THDCP_ERR_ARG, "cu_seqlens_padded_host is NULL");
+  if (B < 0) return fail(THDCP_ERR_ARG, "B must be >= 0 (got %d)", B);
+  if (cp < 1) return fail(THDCP_ERR_ARG, "cp_size must be >= 1 (got %d)", cp);
+  if (rank < 0 || rank >= cp) return fail(THDCP_ERR_ARG, "rank %d outside [0, %d)", rank, cp);
+  if (strategy != THDCP_DUAL_CHUNK_SWAP && strategy != THDCP_NO_LOAD_BALANCE)
+    return fail(THDCP_ERR_ARG, "unknown strategy %d", strategy);
+  if (wl != -1 || wr != 0)
+    return fail(THDCP_ERR_UNSUPPORTED,
+                "only causal attention without a sliding window, window_size=(-1, 0), is "
+                "supported (got (%d, %d))", wl, wr);
+  if (T < 0 || T > INT32_MAX / 2) return fail(THDCP_ERR_ARG, "T=%lld out of range", (long long)T);
+  if (pad_flag < -1 || pad_flag > 1) return fail(THDCP_ERR_ARG, "pad_between_seqs must be -1, 0 or 1");
+  if (cup[0] != 0 || (cu && cu[0] != 0))
+    return fail(THDCP_ERR_LAYOUT, "cumulative sequence lengths must start at 0");
+  bool padding = false;
+  for (int32_t i = 0; i < B; ++i) {
+    const int64_t p = (int64_t)cup[i + 1] - cup[i];
+    const int64_t n = cu ? (int64_t)cu[i + 1] - cu[i] : p;
+    if (p < 0 || n < 0)
+      return fail(THDCP_ERR_LAYOUT, "cumulative sequence lengths decrease at doc %d", i);
+    if (n > p)
+      return fail(THDCP_ERR_LAYOUT, "doc %d: actual length %lld exceeds padded length %lld", i,
+                  (long long)n, (long long)p);
+    if (strategy == THDCP_DUAL_CHUNK_SWAP && p % (2 * (int64_t)cp) != 0)
+      return fail(THDCP_ERR_LAYOUT,
+                  "DUAL_CHUNK_SWAP: padded length %lld of doc %d is not divisible by "
+                  "2*cp_size=%d", (long long)p, i, 2 * cp);
+    if (n != p) padding = true;
+  }
+  if ((int64_t)cup[B] > T)
+    return fail(THDCP_ERR_LAYOUT, "cu_seqlens_padded[B]=%d exceeds T=%lld", cup[B], (long long)T);
+  if (strategy == THDCP_DUAL_CHUNK_SWAP && (int64_t)cup[B] != T)
+    return fail(THDCP_ERR_LAYOUT, "DUAL_CHUNK_SWAP needs T == cu_seqlens_padded[B]");
+  if (T % cp != 0)
+    return fail(THDCP_ERR_LAYOUT, "T=%lld is not divisible by cp_size=%d", (long long)T, cp);
+  if ((int64_t)cup[B] < T) padding = true;
+  if (pad_flag == 0 && padding)
+    return fail(THDCP_ERR_ARG,
+                "pad_between_seqs=0 but the sequence lengths show padding between sequences");
+  if (padding_out) *padding_out = padding ? 1 : 0;
+  return ok();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Plan
+// ---------------------------------------------------------------------------
+struct thdcp_plan {
+  thdcp_attn_desc desc;
+  std::vector<int32_t> cu, cup;
+  int64_t n_local = 0;
+  float scale = 0.f;
+  int32_t padding = 0;
+  int64_t pairs = 0, touched = 0;
+  std::vector<int32_t> local_seqlens;
+  std::vector<FwdTile> fwd;
+  std::vector<BwdTile> bwd;
+  std::vector<ZeroRange> zero;
+  std::vector<char> blob;  // host image of the device tables
+  size_t off_fwd = 0, off_bwd = 0, off_zero = 0, ws_bytes = 0;
+  char* ws_dev = nullptr;  // caller's workspace after upload
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Segment {  // consecutive local rows holding consecutive global rows of one document
+  int64_t m0, g0, len;
+  int64_t a, e;   // document start and end of its real tokens
+  int32_t doc;    // -1: buffer tail (no document)
+};
+
+std::vector<Segment> build_segments(const thdcp_plan& p) {
+  const auto& d = p.desc;
+  const int64_t cp = d.cp_size, r = d.rank;
+  std::vector<Segment> segs;
+  if (d.strategy == THDCP_DUAL_CHUNK_SWAP) {
+    // [AG] "Why": 2*cp_size chunks per document; rank r holds chunks r and
+    // 2*cp_size-1-r, document-major, local offset of doc i = cup[i]/cp_size.
+    for (int32_t i = 0; i < d.B; ++i) {
+      const int64_t P = p.cup[i + 1] - p.cup[i];
+      const int64_t c = P / (2 * cp);
+      if (c == 0) continue;
+      const int64_t a = p.cup[i], e = a + (p.cu[i + 1] - p.cu[i]);
+      const int64_t mdoc = a / cp;
+      segs.push_back({mdoc, a + r * c, c, a, e, i});
+      segs.push_back({mdoc + c, a + (2 * cp - 1 - r) * c, c, a, e, i});
+    }
+  } else {
+    // [AG] "What changed"; [A2A] body: rank r holds [r*s_local, (r+1)*s_local).
+    const int64_t s = d.T / cp, lo = r * s, hi = lo + s;
+    for (int32_t i = 0; i < d.B; ++i) {
+      const int64_t x0 = std::max<int64_t>(lo, p.cup[i]), x1 = std::min<int64_t>(hi, p.cup[i + 1]);
+      if (x1 <= x0) continue;
+      const int64_t a = p.cup[i], e = a + (p.cu[i + 1] - p.cu[i]);
+      segs.push_back({x0 - lo, x0, x1 - x0, a, e, i});
+    }
+    const int64_t t0 = std::max<int64_t>(lo, p.cup[d.B]);
+    if (t0 < hi) segs.push_back({t0 - lo, t0, hi - t0, t0, t0, -1});
+  }
+  return segs;
+}
+
+void build_plan(thdcp_plan& p) {
+  const auto& d = p.desc;
+  const std::vector<Segment> segs = build_segments(p);
+
+  p.local_seqlens.assign(d.B, 0);
+  p.pairs = 0;
+  for (const Segment& s : segs) {
+    if (s.doc < 0) continue;
+    const int64_t nvalid = std::max<int64_t>(0, std::min(s.g0 + s.len, s.e) - s.g0);
+    p.local_seqlens[s.doc] += (int32_t)nvalid;
+    // sum over real rows g in [g0, g0+nvalid) of (g - a + 1)
+    const int64_t f = s.g0 - s.a + 1;
+    p.pairs += nvalid * f + nvalid * (nvalid - 1) / 2;
+  }
+
+  // Forward tiles, longest first (LPT order over the workgroup queue).
+  p.fwd.clear();
+  std::vector<int64_t> fcost;
+  for (const Segment& s : segs) {
+    for (int64_t off = 0; off < s.len; off += kFwdBM) {
+      FwdTile t{};
+      t.m0 = (int32_t)(s.m0 + off);
+      t.n = (int32_t)std::min<int64_t>(kFwdBM, s.len - off);
+      t.g0 = (int32_t)(s.g0 + off);
+      t.a = (int32_t)s.a;
+      t.e = (int32_t)s.e;
+      const int64_t kend = std::min<int64_t>(t.g0 + t.n, s.e);
+      t.kend = kend > t.g0 ? (int32_t)kend : t.a;
+      p.fwd.push_back(t);
+      fcost.push_back((t.kend - t.a + kFwdBN - 1) / kFwdBN);
+    }
+  }
+  {
+    std::vector<size_t> order(p.fwd.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](size_t x, size_t y) { return fcost[x] > fcost[y]; });
+    std::vector<FwdTile> sorted;
+    sorted.reserve(order.size());
+    for (size_t i : order) sorted.push_back(p.fwd[i]);
+    p.fwd.swap(sorted);
+  }
+
+  // Backward tiles: per document, its local real rows (a prefix of the
+  // document's local rows, ascending in g) attend keys [a, g_max].
+  p.bwd.clear();
+  std::vector<int64_t> bcost;
+  std::vector<std::pair<int64_t, int64_t>> touched;  // [r0, r1) per document
+  for (size_t si = 0; si < segs.size();) {
+    const int32_t doc = segs[si].doc;
+    size_t sj = si;
+    while (sj < segs.size() && segs[sj].doc == doc && doc >= 0) ++sj;
+    if (doc < 0) { ++si; continue; }
+    // Real rows of each segment of this document.
+    struct Run { int64_t m0, g0, n; };
+    std::vector<Run> runs;
+    for (size_t k = si; k < sj; ++k) {
+      const Segment& s = segs[k];
+      const int64_t nv = std::max<int64_t>(0, std::min(s.g0 + s.len, s.e) - s.g0);
+      if (nv > 0) runs.push_back({s.m0, s.g0, nv});
+    }
+    si = sj;
+    if (runs.empty()) continue;
+    const int64_t a = segs[si - 1].a;
+    const Run& last = runs.back();
+    const int64_t gmax = last.g0 + last.n - 1;
+    const int64_t m_hi = last.m0 + last.n;
+    touched.push_back({a, gmax + 1});
+    const int64_t split = runs.size() > 1 ? runs[1].m0 : m_hi;
+    const int64_t dga = runs[0].g0 - runs[0].m0;
+    const int64_t dgb = runs.size() > 1 ? runs[1].g0 - runs[1].m0 : dga;
+    for (int64_t k0 = a; k0 <= gmax; k0 += kBwdBN) {
+      // first local row with g >= k0
+      int64_t m_lo = -1;
+      for (const Run& rn : runs) {
+        if (k0 <= rn.g0 + rn.n - 1) {
+          m_lo = rn.m0 + std::max<int64_t>(0, k0 - rn.g0);
+          break;
+        }
+      }
+      BwdTile t{};
+      t.k0 = (int32_t)k0;
+      t.k1 = (int32_t)std::min<int64_t>(k0 + kBwdBN, gmax + 1);
+      t.m_lo = (int32_t)m_lo;
+      t.m_hi = (int32_t)m_hi;
+      t.m_split = (int32_t)split;
+      t.dg_a = (int32_t)dga;
+      t.dg_b = (int32_t)dgb;
+      p.bwd.push_back(t);
+      bcost.push_back(m_hi - m_lo);
+    }
+  }
+  {
+    std::vector<size_t> order(p.bwd.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](size_t x, size_t y) { return bcost[x] > bcost[y]; });
+    std::vector<BwdTile> sorted;
+    sorted.reserve(order.size());
+    for (size_t i : order) sorted.push_back(p.bwd[i]);
+    p.bwd.swap(sorted);
+  }
+
+  // Untouched key rows: the complement of the touched ranges in [0, T).
+  std::sort(touched.begin(), touched.end());
+  p.zero.clear();
+  p.touched = 0;
+  int64_t cursor = 0, before = 0;
+  for (auto& tr : touched) {
+    if (tr.first > cursor) {
+      p.zero.push_back({(int32_t)cursor, (int32_t)tr.first, (int32_t)before, 0});
+      before += tr.first - cursor;
+    }
+    p.touched += tr.second - tr.first;
+    cursor = std::max(cursor, tr.second);
+  }
+  if (cursor < d.T) {
+    p.zero.push_back({(int32_t)cursor, (int32_t)d.T, (int32_t)before, 0});
+  }
+
+  // Host image of the device tables.
+  p.off_fwd = 0;
+  p.off_bwd = align256(p.off_fwd + p.fwd.size() * sizeof(FwdTile));
+  p.off_zero = align256(p.off_bwd + p.bwd.size() * sizeof(BwdTile));
+  p.ws_bytes = align256(p.off_zero + p.zero.size() * sizeof(ZeroRange));
+  if (p.ws_bytes == 0) p.ws_bytes = 256;
+  p.blob.assign(p.ws_bytes, 0);
+  if (!p.fwd.empty()) memcpy(p.blob.data() + p.off_fwd, p.fwd.data(), p.fwd.size() * sizeof(FwdTile));
+  if (!p.bwd.empty()) memcpy(p.blob.data() + p.off_bwd, p.bwd.data(), p.bwd.size() * sizeof(BwdTile));
+  if (!p.zero.empty())
+    memcpy(p.blob.data() + p.off_zero, p.zero.data(), p.zero.size() * sizeof(ZeroRange));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* thdcp_last_error(void) { return g_last_error.c_str(); }
+
+int32_t thdcp_version(void) { return 100; }
+
+thdcp_status_t thdcp_validate(const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_padded_host,
+                              int32_t B, int64_t T, int32_t cp_size, int32_t rank,
+                              thdcp_strategy_t strategy, int32_t window_left,
+                              int32_t window_right, int32_t pad_between_seqs,
+                              int32_t* padding_present_out) {
+  return check_layout(cu_seqlens_host, cu_seqlens_padded_host, B, T, cp_size, rank, strategy,
+                      window_left, window_right, pad_between_seqs, padding_present_out);
+}
+
+thdcp_status_t thd_partition_index(const int32_t* cup_host, const int32_t* cup_dev, int32_t B,
+                                   int64_t T, int32_t cp_size, int32_t rank,
+                                   thdcp_strategy_t strategy, int32_t* idx_out_dev,
+                                   void* stream) {
+  if (!cup_dev || !idx_out_dev) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (cp_size < 1 || rank < -1 || rank >= cp_size)
+    return fail(THDCP_ERR_ARG, "bad cp_size/rank (%d, %d)", cp_size, rank);
+  if (B < 0 || T < 0 || T > INT32_MAX / 2) return fail(THDCP_ERR_ARG, "bad B or T");
+  if (T % cp_size != 0) return fail(THDCP_ERR_LAYOUT, "T is not divisible by cp_size");
+  if (strategy != THDCP_DUAL_CHUNK_SWAP && strategy != THDCP_NO_LOAD_BALANCE)
+    return fail(THDCP_ERR_ARG, "unknown strategy %d", strategy);
+  if (cup_host) {
+    thdcp_status_t st = check_layout(nullptr, cup_host, B, T, cp_size, rank < 0 ? 0 : rank,
+                                     strategy, -1, 0, -1, nullptr);
+    if (st != THDCP_OK) return st;
+  }
+  const int64_t n_out = rank < 0 ? T : T / cp_size;
+  if (n_out == 0) return ok();
+  return hip_status(launch_partition(cup_dev, B, T, cp_size, rank, strategy, idx_out_dev, n_out,
+                                     (hipStream_t)stream),
+                    "thd_partition_index launch");
+}
+
+thdcp_status_t thd_gather(const void* src, int64_t n_src, const int32_t* idx, int64_t n,
+                          int64_t row_bytes, void* dst, void* stream) {
+  if (n < 0 || n_src < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
+  if (n == 0) return ok();
+  if (!src || !idx || !dst) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  return hip_status(launch_gather(src, n_src, idx, n, row_bytes, dst, (hipStream_t)stream),
+                    "thd_gather launch");
+}
+
+thdcp_status_t thd_scatter(const void* src, int64_t n, const int32_t* idx, int64_t row_bytes,
+                           void* dst, int64_t n_dst, void* stream) {
+  if (n < 0 || n_dst < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
+  if (n == 0) return ok();
+  if (!src || !idx || !dst) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  return hip_status(launch_scatter(src, n, idx, row_bytes, dst, n_dst, (hipStream_t)stream),
+                    "thd_scatter launch");
+}
+
+thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan_out) {
+  if (!desc || !plan_out) return fail(THDCP_ERR_ARG, "NULL argument");
+  *plan_out = nullptr;
+  const thdcp_attn_desc& d = *desc;
+  if (d.H < 1) return fail(THDCP_ERR_ARG, "H must be >= 1");
+  if (d.D != 64 && d.D != 128) return fail(THDCP_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d.D);
+  int32_t padding = 0;
+  thdcp_status_t st = check_layout(d.cu_seqlens_host, d.cu_seqlens_padded_host, d.B, d.T,
+                                   d.cp_size, d.rank, d.strategy, d.window_left, d.window_right,
+                                   d.pad_between_seqs, &padding);
+  if (st != THDCP_OK) return st;
+  const int64_t n_local = d.T / d.cp_size;
+  if (n_local * (int64_t)d.H * d.D > ((int64_t)1 << 40)) return fail(THDCP_ERR_ARG, "too large");
+  thdcp_plan* p = new (std::nothrow) thdcp_plan();
+  if (!p) return fail(THDCP_ERR_ARG, "out of host memory");
+  p->desc = d;
+  p->cup.assign(d.cu_seqlens_padded_host, d.cu_seqlens_padded_host + d.B + 1);
+  if (d.cu_seqlens_host)
+    p->cu.assign(d.cu_seqlens_host, d.cu_seqlens_host + d.B + 1);
+  else
+    p->cu = p->cup;
+  p->desc.cu_seqlens_host = nullptr;  // the plan keeps its own copies
+  p->desc.cu_seqlens_padded_host = nullptr;
+  p->n_local = n_local;
+  p->scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.0f / std::sqrt((float)d.D);
+  p->padding = padding;
+  build_plan(*p);
+  *plan_out = p;
+  return ok();
+}
+
+thdcp_status_t thdcp_plan_get_info(thdcp_plan_t p, thdcp_plan_info* info) {
+  if (!p || !info) return fail(THDCP_ERR_ARG, "NULL argument");
+  info->n_local = p->n_local;
+  info->causal_pairs = p->pairs;
+  info->touched_rows = p->touched;
+  info->untouched_rows = p->desc.T - p->touched;
+  info->padding_present = p->padding;
+  info->n_fwd_tiles = (int32_t)p->fwd.size();
+  info->n_bwd_tiles = (int32_t)p->bwd.size();
+  info->n_zero_ranges = (int32_t)p->zero.size();
+  info->workspace_bytes = p->ws_bytes;
+  info->bwd_scratch_bytes = align256((size_t)p->n_local * p->desc.H * sizeof(float));
+  return ok();
+}
+
+thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t p, int32_t* out) {
+  if (!p || !out) return fail(THDCP_ERR_ARG, "NULL argument");
+  std::copy(p->local_seqlens.begin(), p->local_seqlens.end(), out);
+  return ok();
+}
+
+thdcp_status_t thdcp_plan_upload(thdcp_plan_t p, void* ws, size_t bytes, void* stream) {
+  if (!p || !ws) return fail(THDCP_ERR_ARG, "NULL argument");
+  if (bytes < p->ws_bytes)
+    return fail(THDCP_ERR_ARG, "workspace of %zu bytes is below the %zu the plan needs", bytes,
+                p->ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(THDCP_ERR_ARG, "workspace must be 256-byte aligned");
+  hipError_t e = hipMemcpyAsync(ws, p->blob.data(), p->ws_bytes, hipMemcpyHostToDevice,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "plan upload");
+  p->ws_dev = static_cast<char*>(ws);
+  return ok();
+}
+
+void thdcp_plan_destroy(thdcp_plan_t p) { delete p; }
+
+thdcp_status_t cp_attn_fwd(thdcp_plan_t p, const void* q, const void* k, const void* v, void* o,
+                           float* lse, void* stream) {
+  if (!p) return fail(THDCP_ERR_ARG, "NULL plan");
+  if (!p->ws_dev) return fail(THDCP_ERR_ARG, "plan not uploaded (call thdcp_plan_upload)");
+  if (p->n_local == 0) return ok();
+  if (!q || !k || !v || !o || !lse) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(THDCP_ERR_ARG, "Q/K/V/O must be 16-byte aligned");
+  if (p->fwd.empty()) return ok();
+  return hip_status(
+      launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
+                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, o, lse, p->n_local,
+                      p->scale, (hipStream_t)stream),
+      "cp_attn_fwd launch");
+}
+
+namespace {
+
+thdcp_status_t check_plan(thdcp_plan_t p) {
+  if (!p) return fail(THDCP_ERR_ARG, "NULL plan");
+  if (!p->ws_dev) return fail(THDCP_ERR_ARG, "plan not uploaded (call thdcp_plan_upload)");
+  return ok();
+}
+
+size_t scratch_need(thdcp_plan_t p) {
+  return align256((size_t)p->n_local * p->desc.H * sizeof(float));
+}
+
+}  // namespace
+
+thdcp_status_t cp_attn_bwd_preprocess(thdcp_plan_t p, const void* o, const float* lse,
+                                      const void* d_o, float* dq, void* scratch,
+                                      size_t scratch_bytes, void* stream) {
+  thdcp_status_t st = check_plan(p);
+  if (st != THDCP_OK) return st;
+  if (!o || !lse || !d_o || !dq) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(o) || !aligned16(d_o) || !aligned16(dq))
+    return fail(THDCP_ERR_ARG, "O/dO/dQ must be 16-byte aligned");
+  if (!scratch || scratch_bytes < scratch_need(p))
+    return fail(THDCP_ERR_ARG, "scratch of %zu bytes is below the %zu needed", scratch_bytes,
+                scratch_need(p));
+  if (p->n_local == 0) return ok();
+  return hip_status(launch_bwd_prep(o, d_o, lse, static_cast<float*>(scratch), dq, p->n_local,
+                                    p->desc.H, p->desc.D, (hipStream_t)stream),
+                    "cp_attn_bwd_preprocess launch");
+}
+
+thdcp_status_t cp_attn_bwd_main(thdcp_plan_t p, const void* q, const void* k, const void* v,
+                                const float* lse, const void* d_o, float* dq, float* dk,
+                                float* dv, int32_t accumulate_dkv, const void* scratch,
+                                size_t scratch_bytes, void* stream) {
+  thdcp_status_t st = check_plan(p);
+  if (st != THDCP_OK) return st;
+  if (!q || !k || !v || !lse || !d_o || !dq || !dk || !dv)
+    return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(THDCP_ERR_ARG, "tensors must be 16-byte aligned");
+  if (!scratch || scratch_bytes < scratch_need(p))
+    return fail(THDCP_ERR_ARG, "scratch of %zu bytes is below the %zu needed", scratch_bytes,
+                scratch_need(p));
+  if (p->bwd.empty()) return ok();
+  return hip_status(
+      launch_attn_bwd(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
+                      (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, d_o, lse,
+                      static_cast<const float*>(scratch), dq, dk, dv, p->n_local, p->scale,
+                      accumulate_dkv, (hipStream_t)stream),
+      "cp_attn_bwd_main launch");
+}
+
+thdcp_status_t thdcp_zero_untouched(thdcp_plan_t p, float* dk, float* dv, void* stream) {
+  thdcp_status_t st = check_plan(p);
+  if (st != THDCP_OK) return st;
+  if (!dk || !dv) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(dk) || !aligned16(dv)) return fail(THDCP_ERR_ARG, "dK/dV must be 16-byte aligned");
+  // Gated: nothing is enqueued when every key row is attended by some local query.
+  if (p->zero.empty()) return ok();
+  const int64_t rows = p->desc.T - p->touched;
+  return hip_status(launch_zero_rows(reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_zero),
+                                     (int32_t)p->zero.size(), rows,
+                                     (int64_t)p->desc.H * p->desc.D, dk, dv, (hipStream_t)stream),
+                    "thdcp_zero_untouched launch");
+}
+
+thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* d_o, float* dq,
+                           float* dk, float* dv, int32_t zero_untouched, int32_t accumulate_dkv,
+                           void* scratch, size_t scratch_bytes, void* stream) {
+  thdcp_status_t st = check_plan(p);
+  if (st != THDCP_OK) return st;
+  if (zero_untouched && accumulate_dkv)
+    return fail(THDCP_ERR_ARG, "zero_untouched and accumulate_dkv are mutually exclusive");
+  if (!o) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  // Check every argument before enqueuing anything.
+  if (!q || !k || !v || !lse || !d_o || !dq || !dk || !dv)
+    return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(THDCP_ERR_ARG, "tensors must be 16-byte aligned");
+  if (!scratch || scratch_bytes < scratch_need(p))
+    return fail(THDCP_ERR_ARG, "scratch of %zu bytes is below the %zu needed", scratch_bytes,
+                scratch_need(p));
+  st = cp_attn_bwd_preprocess(p, o, lse, d_o, dq, scratch, scratch_bytes, stream);
+  if (st != THDCP_OK) return st;
+  st = cp_attn_bwd_main(p, q, k, v, lse, d_o, dq, dk, dv, accumulate_dkv, scratch, scratch_bytes,
+                        stream);
+  if (st != THDCP_OK) return st;
+  if (zero_untouched) return thdcp_zero_untouched(p, dk, dv, stream);
+  return ok();
+}
+
+}  // extern "C"

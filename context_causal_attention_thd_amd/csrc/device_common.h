@@ -1,0 +1,65 @@
+// Device-side helpers for the gfx950 kernels: bf16 vector types, MFMA
+// wrappers and small conversions. CDNA4 wave64 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace thdcp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
+// Lane l holds row l%32 of A and column l%32 of B, k-slots 8*(l/32)..+7;
+// accumulator element i of lane l is row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void store_bf16x8(bf16* p, const bf16x8& v) {
+  *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
+}
+
+__device__ __forceinline__ bf16x4 load_bf16x4(const bf16* p) {
+  return __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(p));
+}
+
+__device__ __forceinline__ bf16x8 concat4(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Round-to-nearest-even float -> bf16 for 8 consecutive accumulator values.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& v, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)v[base + j];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(bf16 lo, bf16 hi) {
+  uint16_t a = __builtin_bit_cast(uint16_t, lo);
+  uint16_t b = __builtin_bit_cast(uint16_t, hi);
+  return (uint32_t)a | ((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float shfl_xor32(float x) {
+  // exchange with the lane 32 away (the other half of the wave64)
+  return __shfl_xor(x, 32, 64);
+}
+
+}  // namespace thdcp

@@ -1,0 +1,73 @@
+// Internal definitions shared by the host planner and the gfx950 kernels.
+// Not part of the public ABI (include/thdcp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace thdcp {
+
+// Forward work item: up to kFwdBM consecutive local rows that lie in one
+// contiguous run of global rows of one document (a DUAL_CHUNK_SWAP chunk or a
+// NO_LOAD_BALANCE document piece), so row r of the tile is global row g0 + r.
+// Keys are walked from the document start `a` to `kend` (exclusive) in
+// doc-aligned blocks; kend == a marks a tile with no real rows.
+struct FwdTile {
+  int32_t m0;    // first local row
+  int32_t n;     // rows in the tile (<= kFwdBM)
+  int32_t g0;    // global row of m0
+  int32_t a;     // physical start of the document
+  int32_t e;     // end of the document's real tokens (a + actual length)
+  int32_t kend;  // min(g0 + n, e): one past the last key any row attends
+  int32_t pad0, pad1;
+};
+
+// Backward work item: key rows [k0, k1) of one document (all attended by at
+// least one local query) and the local query rows [m_lo, m_hi) that attend
+// them. Those rows are real tokens of the same document in ascending global
+// order; the global row of local row m is m + dg_a below m_split, m + dg_b
+// from m_split on (the two DUAL_CHUNK_SWAP chunks of the document).
+struct BwdTile {
+  int32_t k0, k1;
+  int32_t m_lo, m_hi;
+  int32_t m_split;
+  int32_t dg_a, dg_b;
+  int32_t pad0;
+};
+
+// Rows [r0, r1) of dK/dV that no local query attends; `before` is the number
+// of such rows in all earlier ranges (prefix sum for the zeroing kernel).
+struct ZeroRange {
+  int32_t r0, r1;
+  int32_t before;
+  int32_t pad0;
+};
+
+constexpr int kFwdBM = 128;  // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdBN = 64;   // keys per forward K/V tile
+constexpr int kBwdBN = 128;  // keys per backward workgroup (4 waves x 32)
+constexpr int kBwdBM = 32;   // query rows per backward inner step
+
+// Kernel launchers (defined in the .hip files). All enqueue on `stream`.
+hipError_t launch_partition(const int32_t* cup, int32_t B, int64_t T, int32_t cp,
+                            int32_t rank, int32_t strategy, int32_t* out, int64_t n_out,
+                            hipStream_t stream);
+hipError_t launch_gather(const void* src, int64_t n_src, const int32_t* idx, int64_t n,
+                         int64_t row_bytes, void* dst, hipStream_t stream);
+hipError_t launch_scatter(const void* src, int64_t n, const int32_t* idx, int64_t row_bytes,
+                          void* dst, int64_t n_dst, hipStream_t stream);
+hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
+                            int64_t row_floats, float* a, float* b, hipStream_t stream);
+hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
+                           float* dq, int64_t n_local, int32_t H, int32_t D,
+                           hipStream_t stream);
+hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
+                           const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t n_local, float scale, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
+                           const void* q, const void* k, const void* v, const void* d_o,
+                           const float* lse, const float* delta, float* dq, float* dk,
+                           float* dv, int64_t n_local, float scale, int32_t accumulate,
+                           hipStream_t stream);
+
+}  // namespace thdcp

@@ -1,0 +1,250 @@
+// Row-movement and small bandwidth-bound kernels for gfx950:
+//   partition index ("[PyTorch] Add no-load-balance THD all-gather CP",
+//   "What changed" and "Why"), row gather / scatter (the rank slicing of its
+//   "How to use" and the K/V restore / dK-dV unrestore of its sequence
+//   diagram), the gated zeroing of untouched gradient rows ("THD P2P
+//   context-parallel regression ...", "Expected behavior") and the backward
+//   preprocess delta = rowsum(dO * O).
+//
+// All of these are HBM-bound: each maps (row, 16-byte chunk) pairs onto
+// consecutive lanes so that every wave issues contiguous 16-byte accesses.
+#include "device_common.h"
+#include "internal.h"
+
+namespace thdcp {
+
+// ---------------------------------------------------------------------------
+// Partition index
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) partition_kernel(const int32_t* __restrict__ cup,
+                                                        int32_t B, int64_t T, int32_t cp,
+                                                        int32_t rank, int32_t strategy,
+                                                        int32_t* __restrict__ out,
+                                                        int64_t n_out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_out) return;
+  const int64_t s_local = T / cp;
+  const int64_t r = rank >= 0 ? rank : i / s_local;
+  const int64_t m = rank >= 0 ? i : i - r * s_local;
+  if (strategy == 1) {  // NO_LOAD_BALANCE: contiguous physical range
+    out[i] = (int32_t)(r * s_local + m);
+    return;
+  }
+  // DUAL_CHUNK_SWAP: document j occupies local rows [cup[j]/cp, cup[j+1]/cp);
+  // find the last j in [0, B) with cup[j] <= m*cp (cup[j] is a multiple of cp).
+  int32_t lo = 0, hi = B - 1;
+  const int64_t key = m * cp;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cup[mid] <= key) lo = mid; else hi = mid - 1;
+  }
+  const int64_t a = cup[lo];
+  const int64_t c = ((int64_t)cup[lo + 1] - a) / (2 * cp);
+  const int64_t j = m - a / cp;
+  const int64_t g = j < c ? a + r * c + j : a + (2 * cp - 1 - r) * c + (j - c);
+  out[i] = (int32_t)g;
+}
+
+hipError_t launch_partition(const int32_t* cup, int32_t B, int64_t T, int32_t cp, int32_t rank,
+                            int32_t strategy, int32_t* out, int64_t n_out, hipStream_t stream) {
+  if (B == 0 && strategy == 0) {
+    // no documents: nothing to index (T must then be 0 under DUAL_CHUNK_SWAP)
+    return hipSuccess;
+  }
+  const int threads = 256;
+  const int64_t blocks = (n_out + threads - 1) / threads;
+  hipLaunchKernelGGL(partition_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, cup, B, T,
+                     cp, rank, strategy, out, n_out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gather / scatter of rows of arbitrary byte size
+// ---------------------------------------------------------------------------
+template <int VB>
+struct Vec;
+template <> struct Vec<16> { typedef u32x4 T; };
+template <> struct Vec<8> { typedef u32x2 T; };
+template <> struct Vec<4> { typedef uint32_t T; };
+template <> struct Vec<2> { typedef uint16_t T; };
+template <> struct Vec<1> { typedef uint8_t T; };
+
+constexpr int kRowThreads = 256;
+constexpr int kRowUnroll = 4;
+
+// SCATTER = false: dst[m] = src[idx[m]]; true: dst[idx[m]] = src[m].
+template <int VB, bool SCATTER>
+__global__ void __launch_bounds__(kRowThreads) move_rows_kernel(
+    const char* __restrict__ src, const int32_t* __restrict__ idx, char* __restrict__ dst,
+    uint32_t chunks_per_row, uint64_t total_chunks, int64_t n_other, int64_t row_bytes) {
+  typedef typename Vec<VB>::T V;
+  const uint64_t stride = (uint64_t)gridDim.x * kRowThreads * kRowUnroll;
+  for (uint64_t base = (uint64_t)blockIdx.x * kRowThreads * kRowUnroll + threadIdx.x;
+       base < total_chunks; base += stride) {
+    V val[kRowUnroll];
+    int64_t drow[kRowUnroll];
+    uint32_t dchunk[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const uint64_t t = base + (uint64_t)u * kRowThreads;
+      drow[u] = -1;
+      if (t < total_chunks) {
+        const uint64_t row = t / chunks_per_row;
+        const uint32_t c = (uint32_t)(t - row * chunks_per_row);
+        const int64_t other = idx[row];
+        const bool in = other >= 0 && other < n_other;
+        const int64_t srow = SCATTER ? (int64_t)row : other;
+        drow[u] = SCATTER ? (in ? other : -1) : (int64_t)row;
+        dchunk[u] = c;
+        if (SCATTER || in) {
+          val[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const V*>(src + srow * row_bytes + (int64_t)c * VB));
+        } else {
+          val[u] = V{};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      if (drow[u] >= 0) {
+        __builtin_nontemporal_store(
+            val[u], reinterpret_cast<V*>(dst + drow[u] * row_bytes + (int64_t)dchunk[u] * VB));
+      }
+    }
+  }
+}
+
+template <bool SCATTER>
+hipError_t launch_move(const void* src, const int32_t* idx, void* dst, int64_t n, int64_t n_other,
+                       int64_t row_bytes, hipStream_t stream) {
+  int vb = 1;
+  const uintptr_t addr_bits = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
+  for (int cand : {16, 8, 4, 2}) {
+    if (row_bytes % cand == 0 && (addr_bits % cand) == 0) { vb = cand; break; }
+  }
+  const uint64_t cpr = (uint64_t)(row_bytes / vb);
+  const uint64_t total = cpr * (uint64_t)n;
+  if (cpr > 0xffffffffull) return hipErrorInvalidValue;
+  uint64_t blocks = (total + kRowThreads * kRowUnroll - 1) / (kRowThreads * kRowUnroll);
+  if (blocks > 65536) blocks = 65536;
+  const dim3 grid((unsigned)blocks), block(kRowThreads);
+  const char* s = static_cast<const char*>(src);
+  char* d = static_cast<char*>(dst);
+  switch (vb) {
+    case 16: hipLaunchKernelGGL((move_rows_kernel<16, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 8:  hipLaunchKernelGGL((move_rows_kernel<8, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 4:  hipLaunchKernelGGL((move_rows_kernel<4, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 2:  hipLaunchKernelGGL((move_rows_kernel<2, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
+    default: hipLaunchKernelGGL((move_rows_kernel<1, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* src, int64_t n_src, const int32_t* idx, int64_t n,
+                         int64_t row_bytes, void* dst, hipStream_t stream) {
+  return launch_move<false>(src, idx, dst, n, n_src, row_bytes, stream);
+}
+
+hipError_t launch_scatter(const void* src, int64_t n, const int32_t* idx, int64_t row_bytes,
+                          void* dst, int64_t n_dst, hipStream_t stream) {
+  return launch_move<true>(src, idx, dst, n, n_dst, row_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Zero the dK/dV rows no local query attends (only launched when some exist)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) zero_rows_kernel(const ZeroRange* __restrict__ ranges,
+                                                        int32_t n_ranges, uint64_t total_vec,
+                                                        uint32_t vec_per_row,
+                                                        float* __restrict__ a,
+                                                        float* __restrict__ b) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total_vec;
+       t += (uint64_t)gridDim.x * blockDim.x) {
+    const uint64_t lin = t / vec_per_row;  // index among all untouched rows
+    const uint32_t c = (uint32_t)(t - lin * vec_per_row);
+    int32_t lo = 0, hi = n_ranges - 1;     // last range with before <= lin
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if ((uint64_t)ranges[mid].before <= lin) lo = mid; else hi = mid - 1;
+    }
+    const int64_t row = ranges[lo].r0 + (int64_t)(lin - ranges[lo].before);
+    const int64_t off = row * vec_per_row + c;
+    reinterpret_cast<f32x4*>(a)[off] = z;
+    reinterpret_cast<f32x4*>(b)[off] = z;
+  }
+}
+
+hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
+                            int64_t row_floats, float* a, float* b, hipStream_t stream) {
+  if (row_floats % 4 != 0) return hipErrorInvalidValue;
+  const uint64_t vpr = (uint64_t)row_floats / 4;
+  const uint64_t total = vpr * (uint64_t)total_rows;
+  if (total == 0) return hipSuccess;
+  uint64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ranges,
+                     n_ranges, total, (uint32_t)vpr, a, b);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Backward preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32), and
+// dQ := 0 (the main backward kernel accumulates dQ with atomics).
+// One group of D/8 lanes per (row, head); each lane reads 16 bytes of O and dO.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const bf16* __restrict__ o,
+                                                       const bf16* __restrict__ d_o,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ delta,
+                                                       float* __restrict__ dq, int64_t n_local,
+                                                       int32_t H) {
+  constexpr int G = D / 8;  // lanes per (row, head)
+  const int64_t pairs = n_local * H;
+  const int64_t groups_per_grid = (int64_t)gridDim.x * (blockDim.x / G);
+  const int sub = threadIdx.x % G;
+  for (int64_t pr = (int64_t)blockIdx.x * (blockDim.x / G) + threadIdx.x / G; pr < pairs;
+       pr += groups_per_grid) {
+    // pr enumerates (m, h) row-major over [n_local, H], matching the memory order
+    const int64_t m = pr / H;
+    const int32_t h = (int32_t)(pr - m * H);
+    const int64_t off = pr * D + sub * 8;
+    const bf16x8 ov = load_bf16x8(o + off);
+    const bf16x8 dv = load_bf16x8(d_o + off);
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += (float)ov[j] * (float)dv[j];
+#pragma unroll
+    for (int w = G / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 64);
+    if (sub == 0) {
+      const float l = lse[(int64_t)h * n_local + m];
+      delta[(int64_t)h * n_local + m] = (l == -INFINITY) ? 0.f : acc;
+    }
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    reinterpret_cast<f32x4*>(dq + off)[0] = z;
+    reinterpret_cast<f32x4*>(dq + off)[1] = z;
+  }
+}
+
+hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
+                           float* dq, int64_t n_local, int32_t H, int32_t D, hipStream_t stream) {
+  const int64_t pairs = n_local * H;
+  const int per_block = 256 / (D / 8);
+  int64_t blocks = (pairs + per_block - 1) / per_block;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks == 0) return hipSuccess;
+  const bf16* ob = static_cast<const bf16*>(o);
+  const bf16* db = static_cast<const bf16*>(d_o);
+  if (D == 128)
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, ob, db,
+                       lse, delta, dq, n_local, H);
+  else if (D == 64)
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, ob, db,
+                       lse, delta, dq, n_local, H);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace thdcp

@@ -1,0 +1,233 @@
+/*
+ * thdcp.h -- C ABI of libthdcp: one context-parallel (CP) rank's share of
+ * causal self-attention over THD-packed variable-length documents, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [AG]  "[PyTorch] Add no-load-balance THD all-gather CP"
+ *   [A2A] "[PyTorch] Extend no-load-balance CP to the a2a comm type"
+ *   [PAD] "[PyTorch][Attention] THD P2P context-parallel regression when padded
+ *          cu_seqlens are value-equal but not object-identical"
+ *
+ * Conventions for every entry point
+ *   - Device buffers are owned by the caller. The library never allocates,
+ *     frees or keeps device memory; the plan's device tables and the backward
+ *     scratch live in caller-provided workspaces whose sizes the plan reports.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the default stream).
+ *     Device work is only enqueued on it; no call synchronizes with the
+ *     device or copies device memory back to the host.
+ *   - Tensors are row-major THD [rows, H, D] with D contiguous (bshd with
+ *     batch 1 is the same memory as THD with one document). Q/K/V/O/dO are
+ *     bfloat16; LSE, the backward scratch and dQ/dK/dV are float32.
+ *   - cu_seqlens / cu_seqlens_padded are int32 [B+1]: cumulative actual and
+ *     cumulative physical (padded) lengths. Padding of a document sits at its
+ *     end. A NULL cu_seqlens means "equal to cu_seqlens_padded".
+ *   - Errors: every call returns a thdcp_status_t; on a non-OK status nothing
+ *     was enqueued and thdcp_last_error() gives a message (thread-local).
+ *     Invalid metadata is reported, never trapped on the device.
+ */
+#ifndef THDCP_H
+#define THDCP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Token partition strategy ([AG] "How to use", "What changed"). */
+typedef enum {
+  THDCP_DUAL_CHUNK_SWAP = 0, /* every padded doc cut into 2*cp_size chunks;
+                                rank r holds chunks r and 2*cp_size-1-r */
+  THDCP_NO_LOAD_BALANCE = 1  /* rank r holds physical rows
+                                [r*s_local, (r+1)*s_local), s_local = T/cp_size */
+} thdcp_strategy_t;
+
+typedef enum {
+  THDCP_OK = 0,
+  THDCP_ERR_ARG = 1,         /* bad pointer, size or flag combination */
+  THDCP_ERR_LAYOUT = 2,      /* cu_seqlens / divisibility rules broken */
+  THDCP_ERR_UNSUPPORTED = 3, /* window, head_dim or other unsupported setting */
+  THDCP_ERR_HIP = 4          /* a HIP launch or copy failed */
+} thdcp_status_t;
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* thdcp_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t thdcp_version(void);
+
+/*
+ * Validate THD metadata and detect inter-sequence padding by value.
+ * [AG] "Why" / "Scope and constraints": DUAL_CHUNK_SWAP needs every padded
+ * length divisible by 2*cp_size and T == cu_seqlens_padded[B];
+ * NO_LOAD_BALANCE needs only T divisible by cp_size ([A2A] body);
+ * window must be (-1, 0). [PAD] "Expected behavior": padding is present iff
+ * some document's actual length is below its padded length or
+ * T > cu_seqlens_padded[B] -- decided from the values, never from whether the
+ * two arrays are the same object.
+ *   pad_between_seqs: -1 = detect, 0 = caller asserts none (an error if the
+ *   values show padding), 1 = caller asserts padding (accepted either way).
+ *   padding_present_out (nullable): 1 if padding exists, else 0.
+ * Host pointers only; no device work.
+ */
+thdcp_status_t thdcp_validate(const int32_t* cu_seqlens_host,
+                              const int32_t* cu_seqlens_padded_host, int32_t B,
+                              int64_t T, int32_t cp_size, int32_t rank,
+                              thdcp_strategy_t strategy, int32_t window_left,
+                              int32_t window_right, int32_t pad_between_seqs,
+                              int32_t* padding_present_out);
+
+/*
+ * Partition index ([AG] "What changed", "Why"; [A2A] body): for local row m of
+ * `rank`, idx_out[m] is the global physical row it holds (int32 [T/cp_size]).
+ * rank == -1 writes every rank's indices rank-major (int32 [T]): the
+ * permutation that restores an all-gathered buffer to global order.
+ * cu_seqlens_padded_host (nullable) is used only to validate; the kernel reads
+ * cu_seqlens_padded_dev (int32 [B+1], device). Without the host copy the
+ * caller guarantees the layout rules of thdcp_validate; the kernel then still
+ * stays inside its buffers.
+ */
+thdcp_status_t thd_partition_index(const int32_t* cu_seqlens_padded_host,
+                                   const int32_t* cu_seqlens_padded_dev, int32_t B,
+                                   int64_t T, int32_t cp_size, int32_t rank,
+                                   thdcp_strategy_t strategy, int32_t* idx_out_dev,
+                                   void* stream);
+
+/*
+ * Row gather: dst[m, :] = src[idx[m], :] for m in [0, n), rows of row_bytes
+ * bytes (any dtype: bf16 Q/K/V rows, fp32 gradient rows, int64 token ids).
+ * This is the per-rank slicing of [AG] "How to use" and the K/V restore /
+ * dK-dV unrestore of the [AG] sequence diagram. idx values outside
+ * [0, n_src) give an all-zero dst row. src and dst must not overlap.
+ * row_bytes % 16 == 0 takes a 16-byte vector path.
+ */
+thdcp_status_t thd_gather(const void* src_dev, int64_t n_src, const int32_t* idx_dev,
+                          int64_t n, int64_t row_bytes, void* dst_dev, void* stream);
+
+/*
+ * Row scatter: dst[idx[m], :] = src[m, :] for m in [0, n). idx values outside
+ * [0, n_dst) are skipped. Duplicate idx values race (last writer unspecified).
+ */
+thdcp_status_t thd_scatter(const void* src_dev, int64_t n, const int32_t* idx_dev,
+                           int64_t row_bytes, void* dst_dev, int64_t n_dst, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Rank plan: the THD metadata of one rank ([AG] sequence diagram "partition
+ * and build THD metadata"), built once per batch on the host and shared by
+ * forward and backward so both use the same token layout ([AG] "What changed":
+ * the strategy is captured for backward). It holds the per-rank valid lengths
+ * ([PAD] get_cu_seqlens_on_cp_rank), the forward query-tile and backward
+ * key-tile work lists (tiles wholly outside the document / causal mask are
+ * never listed) and the key-row ranges that no local query attends.
+ * ---------------------------------------------------------------------- */
+typedef struct thdcp_plan* thdcp_plan_t;
+
+typedef struct {
+  const int32_t* cu_seqlens_host;        /* [B+1] host; NULL = cu_seqlens_padded */
+  const int32_t* cu_seqlens_padded_host; /* [B+1] host */
+  int32_t B;
+  int64_t T;                 /* physical THD rows of the full (gathered) K/V */
+  int32_t cp_size;
+  int32_t rank;
+  thdcp_strategy_t strategy;
+  int32_t H;                 /* heads of Q, K and V (self-attention, equal) */
+  int32_t D;                 /* head dim: 64 or 128 */
+  float softmax_scale;       /* <= 0 selects 1/sqrt(D) */
+  int32_t window_left;       /* must be -1 */
+  int32_t window_right;      /* must be 0  */
+  int32_t pad_between_seqs;  /* -1 detect by value, 0 none, 1 present */
+} thdcp_attn_desc;
+
+typedef struct {
+  int64_t n_local;           /* T / cp_size local rows */
+  int64_t causal_pairs;      /* allowed (query,key) pairs per head */
+  int64_t touched_rows;      /* key rows attended by >= 1 local query */
+  int64_t untouched_rows;    /* T - touched_rows */
+  int32_t padding_present;   /* by value, see thdcp_validate */
+  int32_t n_fwd_tiles;
+  int32_t n_bwd_tiles;
+  int32_t n_zero_ranges;     /* untouched key-row ranges */
+  size_t workspace_bytes;    /* device bytes thdcp_plan_upload needs */
+  size_t bwd_scratch_bytes;  /* device bytes cp_attn_bwd needs as scratch */
+} thdcp_plan_info;
+
+/* Build a plan on the host. *plan_out receives a host object the caller
+ * releases with thdcp_plan_destroy. No device work. */
+thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan_out);
+thdcp_status_t thdcp_plan_get_info(thdcp_plan_t plan, thdcp_plan_info* info_out);
+/* Per-document count of real tokens this rank holds (int32 [B], host). */
+thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
+/* Copy the plan's device tables into the caller's workspace (device,
+ * >= workspace_bytes, 256-byte aligned) with one async host-to-device copy on
+ * `stream`. The plan keeps the pointer; the workspace must stay alive and
+ * unmodified while forward/backward calls using the plan are in flight. The
+ * host source stays owned by the plan, which must outlive the copy. */
+thdcp_status_t thdcp_plan_upload(thdcp_plan_t plan, void* workspace_dev, size_t bytes,
+                                 void* stream);
+void thdcp_plan_destroy(thdcp_plan_t plan);
+
+/*
+ * Forward ([AG] "Why": DUAL_CHUNK_SWAP's two attention steps and
+ * NO_LOAD_BALANCE's one are all query tiles of this single launch; the mask is
+ * the cp_size = 1 mask, [A2A] body). Each real local query g attends the keys
+ * j of its own document with j <= g:
+ *   O = softmax(scale * q K^T) V,   LSE = log sum exp(scale * q K^T).
+ *   q_local  bf16 [n_local, H, D]   local queries in local row order
+ *   k, v     bf16 [T, H, D]         full K/V in global order (after restore)
+ *   o_local  bf16 [n_local, H, D]   written for every local row
+ *   lse      fp32 [H, n_local]      natural log; -inf on padding rows
+ * Padding rows get O = 0. Padding key rows are never read into a product.
+ */
+thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k,
+                           const void* v, void* o_local, float* lse, void* stream);
+
+/*
+ * Backward of cp_attn_fwd for loss gradient dO ([AG] sequence diagram: the
+ * dK/dV produced here are the partials that are unrestored for the
+ * reduce-scatter).
+ *   o_local, lse  outputs of cp_attn_fwd;  d_o bf16 [n_local, H, D]
+ *   dq      fp32 [n_local, H, D]   fully written (padding rows 0)
+ *   dk, dv  fp32 [T, H, D]         this rank's partial: rows attended by at
+ *                                  least one local query are written
+ *                                  (accumulate_dkv = 1: added to dk/dv)
+ *   zero_untouched = 1: also write 0 to every other row of dk/dv -- padding
+ *   rows, the buffer tail and keys no local query attends. The zeroing runs
+ *   only when the plan has such rows, so a layout with no tail costs nothing
+ *   ([PAD] "Expected behavior": gate tail zeroing on the metadata).
+ *   zero_untouched and accumulate_dkv are mutually exclusive.
+ *   scratch  device, >= bwd_scratch_bytes, 256-byte aligned.
+ * dQ is accumulated with float atomics, so its low bits may vary run to run;
+ * dK and dV are deterministic.
+ */
+thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k,
+                           const void* v, const void* o_local, const float* lse,
+                           const void* d_o, float* dq, float* dk, float* dv,
+                           int32_t zero_untouched, int32_t accumulate_dkv, void* scratch,
+                           size_t scratch_bytes, void* stream);
+
+/*
+ * The three launches cp_attn_bwd makes, exposed for callers that schedule or
+ * time them separately. Calling them in this order on one stream is exactly
+ * cp_attn_bwd.
+ *   cp_attn_bwd_preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32,
+ *     into scratch) and dq := 0.
+ *   cp_attn_bwd_main: dQ (atomic adds into dq), dK/dV partials.
+ *   thdcp_zero_untouched: writes 0 to every dk/dv row no local query attends;
+ *     enqueues nothing when the plan has no such row.
+ */
+thdcp_status_t cp_attn_bwd_preprocess(thdcp_plan_t plan, const void* o_local, const float* lse,
+                                      const void* d_o, float* dq, void* scratch,
+                                      size_t scratch_bytes, void* stream);
+thdcp_status_t cp_attn_bwd_main(thdcp_plan_t plan, const void* q_local, const void* k,
+                                const void* v, const float* lse, const void* d_o, float* dq,
+                                float* dk, float* dv, int32_t accumulate_dkv,
+                                const void* scratch, size_t scratch_bytes, void* stream);
+thdcp_status_t thdcp_zero_untouched(thdcp_plan_t plan, float* dk, float* dv, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THDCP_H */

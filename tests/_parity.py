@@ -1,0 +1,109 @@
+"""Shared helpers for the GPU parity tests: run one rank's share through the
+HIP library (via the C ABI binding) and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+# Bar for floating-point outputs (bf16 inputs, fp32 accumulation).
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+
+
+def err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = got - ref
+    max_abs = float(np.abs(d).max()) if d.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d)) / nref if nref > 0 else float(np.linalg.norm(d))
+    return max_abs, rel
+
+
+def assert_close(got, ref, name, max_abs=MAX_ABS, rel_l2=REL_L2):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    a, r = err(got, ref)
+    assert a <= max_abs and r <= rel_l2, f"{name}: max_abs={a:.3e} rel_l2={r:.3e}"
+    return a, r
+
+
+def assert_lse(got, ref, name="lse"):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    pad = np.isneginf(ref)
+    assert np.all(np.isneginf(got[pad])), f"{name}: padding rows must be -inf"
+    return assert_close(got[~pad], ref[~pad], name)
+
+
+def device():
+    import torch
+    return torch.device("cuda", 0)
+
+
+def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
+              accumulate=False):
+    """Product path on cuda:0 for one rank: partition index -> gather local Q
+    and dO -> plan -> forward -> backward. Returns numpy arrays."""
+    import torch
+    import context_causal_attention_thd_amd as thd
+    dev = device()
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    cup_dev = torch.from_numpy(cup).to(dev)
+    q, k, v, do = (tensors[n].to(dev) for n in ("q", "k", "v", "do"))
+    idx = thd.partition_index(cup, cup_dev, w.T, w.cp_size, rank, w.strategy)
+    q_local = thd.gather(q, idx)
+    do_local = thd.gather(do, idx)
+    plan = thd.Plan(cu, cup, w.T, w.cp_size, rank, w.strategy, w.H, w.D)
+    o, lse = thd.attn_fwd(plan, q_local, k, v)
+    dk = None if dk_init is None else dk_init.to(dev).clone()
+    dv = None if dv_init is None else dv_init.to(dev).clone()
+    dq, dk, dv = thd.attn_bwd(plan, q_local, k, v, o, lse, do_local, dk=dk, dv=dv,
+                              zero_untouched=zero_untouched, accumulate_dkv=accumulate)
+    torch.cuda.synchronize()
+    out = dict(idx=idx.cpu().numpy(), o=o.float().cpu().numpy(), lse=lse.cpu().numpy(),
+               dq=dq.cpu().numpy(), dk=dk.cpu().numpy(), dv=dv.cpu().numpy(), plan=plan)
+    return out
+
+
+def f64(tensors):
+    return {n: t.double().numpy() for n, t in tensors.items()}
+
+
+def oracle_share(w, rank, t64, rows=None):
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    idx = O.partition_index(cup, w.T, w.cp_size, rank, w.strategy)
+    ql = t64["q"][idx]
+    dol = t64["do"][idx]
+    o, lse = O.attention_fwd(ql, t64["k"], t64["v"], idx, cu, cup, w.T, rows=rows)
+    dq, dk, dv = O.attention_bwd(ql, t64["k"], t64["v"], dol, idx, cu, cup, w.T, rows=rows)
+    return dict(idx=idx, o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+
+
+def sample_plan(w, rank, rng, n_rows=96, max_attending=400):
+    """Pick local query rows and key rows whose oracle values are cheap to get
+    one by one at full size: keys attended by few local queries (near the last
+    attended key of a document), and the local rows attending them."""
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    idx = O.partition_index(cup, w.T, w.cp_size, rank, w.strategy)
+    doc, pos, valid = O.token_table(cu, cup, w.T)
+    gl = idx
+    vl = valid[gl]
+    rows = set(rng.choice(len(idx), size=min(n_rows, len(idx)), replace=False).tolist())
+    rows |= {0, len(idx) - 1}
+    keys = []
+    docs = sorted(set(doc[gl[vl]].tolist()))
+    for d in rng.permutation(docs)[:6]:
+        local = np.nonzero(vl & (doc[gl] == d))[0]
+        gmax = int(gl[local].max())
+        a = cup[d]
+        cand = [gmax, gmax - 1, gmax - 7, gmax - 33, gmax - 100, a]
+        for j in cand:
+            if j < a:
+                continue
+            attending = local[gl[local] >= j]
+            if 0 < len(attending) <= max_attending:
+                keys.append(j)
+                rows |= set(attending.tolist())
+    return sorted(rows), sorted(set(keys))

@@ -1,0 +1,125 @@
+"""Host-side checks of libthdcp (no GPU needed): the library loads, exports
+every entry point include/thdcp.h declares, and its host logic -- layout
+validation, padding detection by value, and the rank plan's metadata -- agrees
+with the oracle. No device compute is called here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "thdcp.h")
+
+thd = pytest.importorskip("context_causal_attention_thd_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(thd.LIB_PATH):
+        pytest.skip("libthdcp not built")
+    return thd.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keywords = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in keywords and (n.startswith("thd") or n.startswith("cp_"))})
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = _declared_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in thdcp.h but not exported"
+    assert set(declared) == set(thd.EXPORTED_SYMBOLS)
+    assert L.thdcp_version() >= 100
+
+
+STRAT = {O.DUAL_CHUNK_SWAP: thd.DUAL_CHUNK_SWAP, O.NO_LOAD_BALANCE: thd.NO_LOAD_BALANCE}
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_validate_and_padding_by_value(L, name):
+    w = W.WORKLOADS[name]
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    pad = thd.validate(cu, cup, w.T, w.cp_size, w.rank, w.strategy)
+    assert pad == O.padding_present(cu, cup, w.T)
+
+
+def test_value_equal_clone_is_not_padding(L):
+    cu = np.array([0, 4096], np.int32)
+    cup = cu.copy()
+    assert not thd.validate(cu, cup, 4096, 4, 1, "no_load_balance")
+    # caller asserting "no padding" is accepted when true, rejected when false
+    assert not thd.validate(cu, cup, 4096, 4, 1, "no_load_balance", pad_between_seqs=0)
+    with pytest.raises(thd.ThdcpError):
+        thd.validate([0, 30, 60], [0, 32, 64], 64, 2, 0, "no_load_balance", pad_between_seqs=0)
+
+
+@pytest.mark.parametrize("args,status", [
+    (([0, 6], [0, 6], 6, 2, 0, "dual_chunk_swap"), 2),       # 6 % (2*2) != 0
+    (([0, 8], [0, 8], 8, 2, 2, "dual_chunk_swap"), 1),       # rank >= cp_size
+    (([0, 9], [0, 8], 8, 2, 0, "no_load_balance"), 2),       # actual > padded
+    (([0, 7], [0, 7], 7, 2, 0, "no_load_balance"), 2),       # T % cp_size
+    (([0, 8], [0, 8], 12, 2, 0, "dual_chunk_swap"), 2),      # buffer tail under DCS
+])
+def test_validate_rejects_bad_layouts(L, args, status):
+    with pytest.raises(thd.ThdcpError) as ei:
+        thd.validate(*args)
+    assert ei.value.status == status
+    # the oracle rejects the same layouts
+    with pytest.raises(ValueError):
+        O.check_layout(*args)
+
+
+def test_window_other_than_causal_is_unsupported(L):
+    with pytest.raises(thd.ThdcpError) as ei:
+        thd.validate([0, 8], [0, 8], 8, 2, 0, "no_load_balance", window=(128, 0))
+    assert ei.value.status == 3
+
+
+def _plan(w, rank=None, **kw):
+    return thd.Plan(w.cu_seqlens(), w.cu_seqlens_padded(), w.T, w.cp_size,
+                    w.rank if rank is None else rank, w.strategy, w.H, w.D, upload=False, **kw)
+
+
+def _small_layouts():
+    yield W.custom("dcs_pad", [5, 0, 11], [8, 0, 16], None, 2, 64, 2, 0, "dual_chunk_swap")
+    yield W.custom("nlb_tail", [5, 8], [7, 8], 18, 2, 64, 3, 0, "no_load_balance")
+    yield W.custom("dcs_big_pad", [3, 13, 40], [16, 16, 48], None, 1, 128, 2, 0, "dual_chunk_swap")
+    for name in W.ORDER:
+        yield W.WORKLOADS[name]
+
+
+@pytest.mark.parametrize("w", list(_small_layouts()), ids=lambda w: w.name)
+def test_plan_metadata_matches_oracle(L, w):
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    ranks = range(w.cp_size) if w.T <= 40000 else [w.rank]
+    for r in ranks:
+        p = _plan(w, rank=r)
+        idx = O.partition_index(cup, w.T, w.cp_size, r, w.strategy)
+        assert p.n_local == len(idx)
+        assert p.info.causal_pairs == O.causal_pairs(cu, cup, w.T, idx)
+        assert p.local_seqlens().tolist() == O.local_valid_lengths(cu, cup, w.T, w.cp_size, r,
+                                                                   w.strategy).tolist()
+        touched = O.touched_keys(cu, cup, w.T, idx)
+        assert p.info.touched_rows == int(touched.sum())
+        assert p.info.untouched_rows == w.T - int(touched.sum())
+        assert p.info.padding_present == int(O.padding_present(cu, cup, w.T))
+        assert p.info.bwd_scratch_bytes >= p.n_local * w.H * 4
+        p.close()
+
+
+def test_plan_rejects_unsupported(L):
+    w = W.WORKLOADS["tiny_nlb"]
+    with pytest.raises(thd.ThdcpError) as ei:
+        thd.Plan(w.cu_seqlens(), w.cu_seqlens_padded(), w.T, 2, 0, w.strategy, 2, 96, upload=False)
+    assert ei.value.status == 3
