@@ -2,6 +2,9 @@
 HIP library (via the C ABI binding) and compare with the fp64 oracle."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 import oracle as O
@@ -21,10 +24,19 @@ def err(got, ref):
     return max_abs, rel
 
 
+def _log(name, a, r):
+    """Append measured errors to $THDCP_PARITY_LOG (JSON lines) when set."""
+    path = os.environ.get("THDCP_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"check": name, "max_abs": a, "rel_l2": r}) + "\n")
+
+
 def assert_close(got, ref, name, max_abs=MAX_ABS, rel_l2=REL_L2):
     got = np.asarray(got, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     a, r = err(got, ref)
+    _log(name, a, r)
     assert a <= max_abs and r <= rel_l2, f"{name}: max_abs={a:.3e} rel_l2={r:.3e}"
     return a, r
 

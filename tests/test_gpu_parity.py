@@ -136,7 +136,7 @@ SMALL = [
              "dual_chunk_swap"),
     W.custom("nlb_tail_d128", [250, 5, 900, 333], [256, 5, 900, 340], 1548, 2, 128, 3, 0,
              "no_load_balance"),
-    W.custom("nlb_nopad_d64", [37, 91, 200, 1], [37, 91, 200, 1], None, 2, 64, 3, 0,
+    W.custom("nlb_nopad_d64", [37, 91, 200, 2], [37, 91, 200, 2], None, 2, 64, 3, 0,
              "no_load_balance"),
 ]
 
