@@ -11,9 +11,10 @@ A step is one pass of the whole hot path for the measured rank over one batch:
 Inputs are synthetic and already resident in HBM when timing starts.
 
 value = 14 * D * H * causal_pairs / step time (TFLOP/s; causal-masked FLOPs
-only). The roofline object is for the attention backward main kernel, timed
-with HIP events on the stream it runs on; the gather roofline covers the two
-K/V restore launches.
+only). The roofline object is for the dominant kernel, the backward dK/dV
+kernel (8 * D * H * pairs algorithmic FLOPs: S, dP, dV, dK), timed with HIP
+events on the stream it runs on; the dQ kernel, the forward and the K/V
+restore (gather roofline) are reported beside it.
 
     python bench.py [--steps K] [--warmup W] [--workload dcs_8k] [--no-cpu-baseline]
 """
@@ -120,12 +121,14 @@ def main():
         mark("fwd0")
         thd.attn_fwd(plan, q_local, k_g, v_g, o=o, lse=lse)
         mark("fwd1")
-        pair = None
+        pairs_ev = None
         if record:
-            pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            ev.setdefault("bwd", []).append(pair)
+            pairs_ev = {n: (torch.cuda.Event(enable_timing=True),
+                            torch.cuda.Event(enable_timing=True)) for n in ("dkdv", "dq")}
+            for n, pr in pairs_ev.items():
+                ev.setdefault(n, []).append(pr)
         thd.attn_bwd_parts(plan, q_local, k_g, v_g, o, lse, do_local, dq, dk, dv, scratch,
-                           zero_untouched=True, events=pair)
+                           zero_untouched=True, events=pairs_ev)
         thd.gather(dk, perm, out=dk_rm)
         thd.gather(dv, perm, out=dv_rm)
         return plan  # keep alive until the stream is synchronized
@@ -150,13 +153,19 @@ def main():
         return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
 
     t_fwd = avg("fwd0", "fwd1")
-    t_bwd = float(np.mean([x.elapsed_time(y) for x, y in ev["bwd"]]))
+    t_dkdv = float(np.mean([x.elapsed_time(y) for x, y in ev["dkdv"]]))
+    t_dq = float(np.mean([x.elapsed_time(y) for x, y in ev["dq"]]))
+    t_bwd = t_dkdv + t_dq
     t_restore = avg("restore0", "restore1")
 
-    flop_fwd = 4.0 * D * H * pairs
-    flop_bwd = 10.0 * D * H * pairs
+    flop_fwd = 4.0 * D * H * pairs      # QK^T, PV
+    flop_bwd = 10.0 * D * H * pairs     # S, dP, dV, dK, dQ
+    flop_dkdv = 8.0 * D * H * pairs     # S, dP, dV, dK
+    flop_dq_exec = 6.0 * D * H * pairs  # S, dP recomputed, dQ
     tflops_step = (flop_fwd + flop_bwd) / (ms_step * 1e-3) / 1e12
     tflops_bwd = flop_bwd / (t_bwd * 1e-3) / 1e12
+    tflops_dkdv = flop_dkdv / (t_dkdv * 1e-3) / 1e12
+    tflops_dq = flop_dq_exec / (t_dq * 1e-3) / 1e12
     tflops_fwd = flop_fwd / (t_fwd * 1e-3) / 1e12
     row_bytes = H * D * 2
     restore_bytes = 2 * (2 * T * row_bytes + 4 * T)    # K and V: read + write rows, read idx
@@ -167,7 +176,7 @@ def main():
         try:
             with open(args.traffic_json) as f:
                 tj = json.load(f)
-            entry = tj.get(args.workload, {}).get("attn_bwd_kernel")
+            entry = tj.get(args.workload, {}).get("attn_bwd_dkdv_kernel")
             if entry and entry.get("source_hash") == _kernel_hash():
                 traffic = entry["bytes_per_launch"]
         except Exception:
@@ -189,10 +198,16 @@ def main():
         "config": {"workload": w.name, "T": T, "heads": H, "head_dim": D, "cp_size": cp,
                    "rank": r, "strategy": w.strategy, "docs": w.B, "causal_pairs_per_head": pairs,
                    "parallelism": "one simulated CP rank on one GPU"},
-        "roofline": {"bound": "mfma", "kernel": "attn_bwd_kernel",
-                     "achieved": round(tflops_bwd, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops_bwd / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd_dkdv_kernel",
+                     "achieved": round(tflops_dkdv, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_dkdv / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        "roofline_bwd_dq": {"bound": "mfma", "kernel": "attn_bwd_dq_kernel",
+                            "achieved": round(tflops_dq, 2), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tflops_dq / PEAK_BF16_TFLOPS, 4),
+                            "note": "executed FLOPs: S and dP recomputed, then dQ"},
+        "bwd_algorithmic": {"achieved": round(tflops_bwd, 2), "unit": "TFLOP/s",
+                            "frac": round(tflops_bwd / PEAK_BF16_TFLOPS, 4)},
         "roofline_fwd": {"bound": "mfma", "kernel": "attn_fwd_kernel",
                          "achieved": round(tflops_fwd, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops_fwd / PEAK_BF16_TFLOPS, 4)},
@@ -201,8 +216,9 @@ def main():
                             "unit": "GB/s", "frac": round(gbs_restore / PEAK_HBM_GBS, 4),
                             "bytes": restore_bytes},
         "times_ms": {"step": round(ms_step, 4), "fwd": round(t_fwd, 4),
-                     "bwd_main": round(t_bwd, 4), "kv_restore": round(t_restore, 4),
-                     "attn_fwd_plus_bwd_main_tflops": round(
+                     "bwd_dkdv": round(t_dkdv, 4), "bwd_dq": round(t_dq, 4),
+                     "kv_restore": round(t_restore, 4),
+                     "attn_kernels_tflops": round(
                          (flop_fwd + flop_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
                      "host_wall_per_step": round(wall / args.steps * 1e3, 4)},
     }

@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "thdcp_last_error", "thdcp_version", "thdcp_validate", "thd_partition_index", "thd_gather",
     "thd_scatter", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
     "thdcp_plan_upload", "thdcp_plan_destroy", "cp_attn_fwd", "cp_attn_bwd",
-    "cp_attn_bwd_preprocess", "cp_attn_bwd_main", "thdcp_zero_untouched",
+    "cp_attn_bwd_preprocess", "cp_attn_bwd_dkdv", "cp_attn_bwd_dq", "thdcp_zero_untouched",
 )
 
 
@@ -108,9 +108,11 @@ def lib() -> ctypes.CDLL:
     L.cp_attn_bwd.restype = i32
     L.cp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
     L.cp_attn_bwd_preprocess.restype = i32
-    L.cp_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
-    L.cp_attn_bwd_main.restype = i32
-    L.cp_attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.cp_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, sz, vp]
+    L.cp_attn_bwd_dkdv.restype = i32
+    L.cp_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.cp_attn_bwd_dq.restype = i32
+    L.cp_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.thdcp_zero_untouched.restype = i32
     L.thdcp_zero_untouched.argtypes = [vp, vp, vp, vp]
     _lib_handle = L
@@ -355,28 +357,34 @@ def attn_bwd(plan: Plan, q_local, k, v, o, lse, d_o, dq=None, dk=None, dv=None,
 def attn_bwd_parts(plan: Plan, q_local, k, v, o, lse, d_o, dq, dk, dv, scratch,
                    zero_untouched: bool = True, accumulate_dkv: bool = False, stream=None,
                    events=None):
-    """cp_attn_bwd as its three launches. ``events`` (optional pair of
-    torch.cuda.Event) are recorded right before and after the main kernel."""
+    """cp_attn_bwd as its separate launches. ``events`` (optional dict of
+    torch.cuda.Event pairs, keys "dkdv" and "dq") are recorded around those
+    two kernels."""
     import torch
     L = lib()
     st = _stream(stream)
     nbytes = scratch.numel() * scratch.element_size()
+    sp = _dev_ptr(scratch, "scratch")
     _check(L.cp_attn_bwd_preprocess(plan.handle, _dev_ptr(o, "o", torch.bfloat16),
                                     _dev_ptr(lse, "lse", torch.float32),
-                                    _dev_ptr(d_o, "d_o", torch.bfloat16),
-                                    _dev_ptr(dq, "dq", torch.float32), _dev_ptr(scratch, "scratch"),
-                                    nbytes, st))
-    if events is not None:
-        events[0].record()
-    _check(L.cp_attn_bwd_main(plan.handle, _dev_ptr(q_local, "q_local", torch.bfloat16),
-                              _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
-                              _dev_ptr(lse, "lse", torch.float32),
-                              _dev_ptr(d_o, "d_o", torch.bfloat16),
-                              _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
-                              _dev_ptr(dv, "dv", torch.float32), int(bool(accumulate_dkv)),
-                              _dev_ptr(scratch, "scratch"), nbytes, st))
-    if events is not None:
-        events[1].record()
+                                    _dev_ptr(d_o, "d_o", torch.bfloat16), sp, nbytes, st))
+    args = (_dev_ptr(q_local, "q_local", torch.bfloat16), _dev_ptr(k, "k", torch.bfloat16),
+            _dev_ptr(v, "v", torch.bfloat16), _dev_ptr(lse, "lse", torch.float32),
+            _dev_ptr(d_o, "d_o", torch.bfloat16))
+    ev = events or {}
+    if "dkdv" in ev:
+        ev["dkdv"][0].record()
+    _check(L.cp_attn_bwd_dkdv(plan.handle, *args, _dev_ptr(dk, "dk", torch.float32),
+                              _dev_ptr(dv, "dv", torch.float32), int(bool(accumulate_dkv)), sp,
+                              nbytes, st))
+    if "dkdv" in ev:
+        ev["dkdv"][1].record()
+    if "dq" in ev:
+        ev["dq"][0].record()
+    _check(L.cp_attn_bwd_dq(plan.handle, *args, _dev_ptr(dq, "dq", torch.float32), sp, nbytes,
+                            st))
+    if "dq" in ev:
+        ev["dq"][1].record()
     if zero_untouched:
         _check(L.thdcp_zero_untouched(plan.handle, _dev_ptr(dk, "dk", torch.float32),
                                       _dev_ptr(dv, "dv", torch.float32), st))

@@ -1,20 +1,23 @@
-// Backward attention of one CP rank's share: dQ for the local rows and this
-// rank's partial dK/dV over the full K/V ("[PyTorch] Add no-load-balance THD
-// all-gather CP", sequence diagram: the dK/dV partials are unrestored for the
-// reduce-scatter). Padding never enters a product: query rows that are not
-// real tokens are not listed, key rows past the tile end are zeroed, and
-// masked probabilities are selected to 0 (NaN-safe).
+// Backward, key side: this rank's partial dK/dV over the full K/V ("[PyTorch]
+// Add no-load-balance THD all-gather CP", sequence diagram: the dK/dV partials
+// are unrestored for the reduce-scatter). dQ is computed by the query-major
+// kernel in attn_bwd_dq.hip, so this kernel needs no atomics and every key row
+// it owns is written by exactly one workgroup. Padding never enters a product:
+// query rows that are not real tokens are not listed, key rows past the tile
+// end are zeroed, and masked probabilities are selected to 0 (NaN-safe).
 //
 // gfx950 design: a workgroup of 4 waves owns 128 consecutive keys of one
-// document (32 per wave) and walks the local query rows that attend them in
-// blocks of 32. Per block, each wave computes with v_mfma_f32_32x32x16_bf16
-//   S = Q K^T, dP = dO V^T   (queries x its keys; K, V fragments in registers)
+// document (32 per wave, K and V fragments in registers) and walks the local
+// query rows that attend them in blocks of 64. Query blocks (Q, dO, LSE,
+// delta) are double-buffered in LDS and the next block's global loads are in
+// flight while the current one is computed; one barrier per block. Per block
+// each wave computes with v_mfma_f32_32x32x16_bf16
+//   S = Q K^T, dP = dO V^T          (A = Q / dO rows from LDS, B = K / V regs)
 //   P = exp(S - LSE), dS = P (dP - delta)
-//   dV += P^T dO, dK += dS^T Q   (accumulators stay in registers)
-// P and dS are already in the A-operand layout of the last two products, so
-// only dO^T and Q^T are staged transposed in LDS. dS is written to LDS once
-// and wave w then forms dQ for head dims [32w, 32w+32) over all 128 keys and
-// adds it to global dQ with float atomics (coalesced 128-byte rows).
+//   dV += P^T dO, dK += dS^T Q       (accumulators stay in registers)
+// P and dS come out of the first products already in the A-operand layout of
+// the last two; their B operands (dO and Q, sliced by column) are transposing
+// LDS reads of the row-major tiles.
 #include <atomic>
 
 #include "device_common.h"
@@ -26,36 +29,33 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+constexpr int kBM = 64;  // query rows per block
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct BwdSmem {
-  static constexpr int QP = D + 8;         // Q / dO row-major pitch (bf16)
-  static constexpr int TP = kBwdBM + 4;    // Q^T / dO^T pitch (bf16)
-  static constexpr int SP = kBwdBN + 8;    // dS pitch (bf16)
-  static constexpr int KTP = kBwdBN + 8;   // K^T pitch (bf16)
-  bf16 q[kBwdBM * QP];
-  bf16 qt[D * TP];
-  bf16 dO[kBwdBM * QP];
-  bf16 dOt[D * TP];
-  bf16 ds[kBwdBM * SP];
-  bf16 kt[D * KTP];
-  float lse2[kBwdBM];
-  float dlt[kBwdBM];
-  int32_t gq[kBwdBM];
+  static constexpr int P = D + 16;     // Q / dO row pitch (bf16)
+  bf16 q[2][kBM * P];
+  bf16 dO[2][kBM * P];
+  float lse2[2][kBM];
+  float dlt[2][kBM];
+  int32_t gq[2][kBM];
 };
 
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1)
-attn_bwd_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
-                const bf16* __restrict__ k, const bf16* __restrict__ v,
-                const bf16* __restrict__ d_o, const float* __restrict__ lse,
-                const float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dk,
-                float* __restrict__ dv, int64_t n_local, float scale, float scale_log2,
-                int32_t accumulate) {
+attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
+                     const bf16* __restrict__ k, const bf16* __restrict__ v,
+                     const bf16* __restrict__ d_o, const float* __restrict__ lse,
+                     const float* __restrict__ delta, float* __restrict__ dk,
+                     float* __restrict__ dv, int64_t n_local, float scale, float scale_log2,
+                     int32_t accumulate) {
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int CH = kBM * CPR / kThreads;    // chunks per thread per block and tensor
   typedef BwdSmem<D> S;
+  constexpr int P = S::P;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   S& sm = *reinterpret_cast<S*>(smem_raw);
 
@@ -66,27 +66,23 @@ attn_bwd_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int lane = threadIdx.x & 63;
   const int li = lane & 31;
   const int hh = lane >> 5;
+  const int sl = lane & 15;
+  const int g16 = lane >> 4;
   const int64_t rs = (int64_t)H * D;
+  const int64_t head_off = (int64_t)h * D;
 
   // This lane's key (column of S and dP; row of the dK/dV A operands).
   const int my_key = t.k0 + w * 32 + li;
   const bool key_ok = my_key < t.k1;
-  const bool wave_live = t.k0 + w * 32 < t.k1;
   bf16x8 kf[KSTEPS], vf[KSTEPS];
   {
-    const int64_t off = (int64_t)my_key * rs + (int64_t)h * D + hh * 8;
+    const int64_t off = (int64_t)my_key * rs + head_off + hh * 8;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       kf[kk] = key_ok ? load_bf16x8(k + off + kk * 16) : zero_bf16x8();
       vf[kk] = key_ok ? load_bf16x8(v + off + kk * 16) : zero_bf16x8();
     }
   }
-  // K^T for the dQ product: kt[d][key in tile]
-#pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sm.kt[(kk * 16 + hh * 8 + j) * S::KTP + w * 32 + li] = kf[kk][j];
-
   f32x16 dka[DB], dva[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -96,109 +92,112 @@ attn_bwd_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       dva[db][i] = 0.f;
     }
 
-  for (int mb = t.m_lo; mb < t.m_hi; mb += kBwdBM) {
-    __syncthreads();  // previous block fully consumed (and K^T staged)
-    for (int c = threadIdx.x; c < kBwdBM * (D / 8); c += kThreads) {
-      const int rr = c % kBwdBM, dc = c / kBwdBM;
-      const int m = mb + rr;
-      const bool ok = m < t.m_hi;
-      const int64_t off = (int64_t)m * rs + (int64_t)h * D + dc * 8;
-      const bf16x8 qv = ok ? load_bf16x8(q + off) : zero_bf16x8();
-      const bf16x8 dv8 = ok ? load_bf16x8(d_o + off) : zero_bf16x8();
-      store_bf16x8(&sm.q[rr * S::QP + dc * 8], qv);
-      store_bf16x8(&sm.dO[rr * S::QP + dc * 8], dv8);
+  // Query-block staging: chunk c = threadIdx.x + j*kThreads of the block.
+  bf16x8 qreg[CH], dreg[CH];
+  float lreg = 0.f, dlreg = 0.f;
+  int greg = -1;
+  auto load_block = [&](int mb) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        sm.qt[(dc * 8 + j) * S::TP + rr] = qv[j];
-        sm.dOt[(dc * 8 + j) * S::TP + rr] = dv8[j];
-      }
-    }
-    if (threadIdx.x < kBwdBM) {
-      const int rr = threadIdx.x;
+    for (int j = 0; j < CH; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      const int rr = c / CPR, dc = c - rr * CPR;
       const int m = mb + rr;
-      const bool ok = m < t.m_hi;
-      sm.lse2[rr] = ok ? lse[(int64_t)h * n_local + m] * kLog2e : 0.f;
-      sm.dlt[rr] = ok ? delta[(int64_t)h * n_local + m] : 0.f;
-      sm.gq[rr] = ok ? m + (m < t.m_split ? t.dg_a : t.dg_b) : -1;
+      const int64_t off = (int64_t)m * rs + head_off + dc * 8;
+      qreg[j] = m < t.m_hi ? load_bf16x8(q + off) : zero_bf16x8();
+      dreg[j] = m < t.m_hi ? load_bf16x8(d_o + off) : zero_bf16x8();
     }
-    __syncthreads();
+    if (threadIdx.x < kBM) {
+      const int m = mb + threadIdx.x;
+      const bool ok = m < t.m_hi;
+      lreg = ok ? lse[(int64_t)h * n_local + m] * kLog2e : 0.f;
+      dlreg = ok ? delta[(int64_t)h * n_local + m] : 0.f;
+      greg = ok ? m + (m < t.m_split ? t.dg_a : t.dg_b) : -1;
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      const int rr = c / CPR, dc = c - rr * CPR;
+      store_bf16x8(&sm.q[buf][rr * P + dc * 8], qreg[j]);
+      store_bf16x8(&sm.dO[buf][rr * P + dc * 8], dreg[j]);
+    }
+    if (threadIdx.x < kBM) {
+      sm.lse2[buf][threadIdx.x] = lreg;
+      sm.dlt[buf][threadIdx.x] = dlreg;
+      sm.gq[buf][threadIdx.x] = greg;
+    }
+  };
 
-    if (wave_live) {
-      f32x16 s, dp;
+  const int nblocks = (t.m_hi - t.m_lo + kBM - 1) / kBM;
+  load_block(t.m_lo);
+  store_block(0);
+  __syncthreads();
+
+  for (int it = 0; it < nblocks; ++it) {
+    const int mb = t.m_lo + it * kBM;
+    const int cur = it & 1;
+    const bool has_next = it + 1 < nblocks;
+    if (has_next) load_block(mb + kBM);  // in flight during this block's compute
+
+    // S and dP for the two 32-query halves (rows = queries, column = my_key).
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
+        s[qb][i] = 0.f;
+        dp[qb][i] = 0.f;
       }
-      const bf16* qa = &sm.q[li * S::QP + hh * 8];
-      const bf16* da = &sm.dO[li * S::QP + hh * 8];
+      const bf16* qa = &sm.q[cur][(qb * 32 + li) * P + hh * 8];
+      const bf16* da = &sm.dO[cur][(qb * 32 + li) * P + hh * 8];
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        s = mfma32(load_bf16x8(qa + kk * 16), kf[kk], s);
-        dp = mfma32(load_bf16x8(da + kk * 16), vf[kk], dp);
+        s[qb] = mfma32(load_bf16x8(qa + kk * 16), kf[kk], s[qb]);
+        dp[qb] = mfma32(load_bf16x8(da + kk * 16), vf[kk], dp[qb]);
       }
-      // Element i of this lane: query row 8*(i/4) + 4*hh + i%4, key my_key.
+    }
+    // Element i of s[qb]: query row qb*32 + 8*(i/4) + 4*hh + i%4, key my_key.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int qr0 = i4 * 8 + hh * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[qr0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[qr0]);
+        const int qr0 = qb * 32 + i4 * 8 + hh * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = i4 * 4 + j;
-          const bool ok = key_ok && my_key <= sm.gq[qr0 + j];
-          const float p = ok ? exp2f(fmaf(s[i], scale_log2, -l4[j])) : 0.f;
-          const float dsv = ok ? p * (dp[i] - d4[j]) : 0.f;
-          s[i] = p;
-          dp[i] = dsv;
+          const bool ok = key_ok && my_key <= sm.gq[cur][qr0 + j];
+          const float p = ok ? fast_exp2(fmaf(s[qb][i], scale_log2, -l4[j])) : 0.f;
+          const float dsv = ok ? p * (dp[qb][i] - d4[j]) : 0.f;
+          s[qb][i] = p;
+          dp[qb][i] = dsv;
         }
       }
-      // dV += P^T dO and dK += dS^T Q. k-step u covers query rows
-      // 16u + (j/4)*8 + hh*4 + j%4 for slot j: accumulator entries u*8..u*8+7.
+    // dV += P^T dO and dK += dS^T Q. k-step (qb, u) covers query rows
+    // qb*32 + 16u + (j/4)*8 + hh*4 + j%4 for slot j: accumulator entries
+    // u*8..u*8+7 of s[qb] / dp[qb]. The B operands (lane = head dim, slots =
+    // those rows) are two transposing reads each of the row-major dO and Q.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 pa = to_bf16x8(s, u * 8);
-        const bf16x8 dsa = to_bf16x8(dp, u * 8);
-        const int qcol = 16 * u + hh * 4;
+        const bf16x8 pa = to_bf16x8(s[qb], u * 8);
+        const bf16x8 dsa = to_bf16x8(dp[qb], u * 8);
+        const int roff = (qb * 32 + 16 * u + hh * 4 + (sl >> 2)) * P + 16 * (g16 & 1) + 4 * (sl & 3);
+        const bf16* dob = &sm.dO[cur][roff];
+        const bf16* qbp = &sm.q[cur][roff];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16* dop = &sm.dOt[(db * 32 + li) * S::TP + qcol];
-          dva[db] = mfma32(pa, concat4(load_bf16x4(dop), load_bf16x4(dop + 8)), dva[db]);
-          const bf16* qp = &sm.qt[(db * 32 + li) * S::TP + qcol];
-          dka[db] = mfma32(dsa, concat4(load_bf16x4(qp), load_bf16x4(qp + 8)), dka[db]);
+          const bf16x8 bdo = concat4(lds_read_tr4(dob + db * 32), lds_read_tr4(dob + db * 32 + 8 * P));
+          dva[db] = mfma32(pa, bdo, dva[db]);
+          const bf16x8 bq = concat4(lds_read_tr4(qbp + db * 32), lds_read_tr4(qbp + db * 32 + 8 * P));
+          dka[db] = mfma32(dsa, bq, dka[db]);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = (i >> 2) * 8 + hh * 4 + (i & 3);
-        sm.ds[qr * S::SP + w * 32 + li] = (bf16)dp[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = (i >> 2) * 8 + hh * 4 + (i & 3);
-        sm.ds[qr * S::SP + w * 32 + li] = (bf16)0.f;
-      }
-    }
+    if (has_next) store_block(cur ^ 1);
     __syncthreads();
-
-    // dQ[queries, 32w .. 32w+31] += scale * dS (32 x 128 keys) K (128 keys x 32 dims)
-    if (w < DB) {
-      f32x16 dqa;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dqa[i] = 0.f;
-      const bf16* dsa = &sm.ds[li * S::SP + hh * 8];
-      const bf16* kta = &sm.kt[(w * 32 + li) * S::KTP + hh * 8];
-#pragma unroll
-      for (int kt = 0; kt < kBwdBN / 16; ++kt)
-        dqa = mfma32(load_bf16x8(dsa + kt * 16), load_bf16x8(kta + kt * 16), dqa);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = (i >> 2) * 8 + hh * 4 + (i & 3);
-        const int m = mb + qr;
-        if (m < t.m_hi) unsafeAtomicAdd(dq + (int64_t)m * rs + (int64_t)h * D + w * 32 + li, dqa[i] * scale);
-      }
-    }
   }
 
   // dK (scaled) and dV rows of this wave's keys; lane li holds head dim db*32 + li.
@@ -208,7 +207,7 @@ attn_bwd_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     for (int i = 0; i < 16; ++i) {
       const int key = t.k0 + w * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
       if (key < t.k1) {
-        const int64_t off = (int64_t)key * rs + (int64_t)h * D + db * 32 + li;
+        const int64_t off = (int64_t)key * rs + head_off + db * 32 + li;
         const float kval = dka[db][i] * scale;
         const float vval = dva[db][i];
         if (accumulate) {
@@ -225,7 +224,7 @@ attn_bwd_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 template <int D>
 hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const void* q,
                         const void* k, const void* v, const void* d_o, const float* lse,
-                        const float* delta, float* dq, float* dk, float* dv, int64_t n_local,
+                        const float* delta, float* dk, float* dv, int64_t n_local,
                         float scale, int32_t accumulate, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
@@ -238,30 +237,30 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_set.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_kernel<D>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  hipLaunchKernelGGL(attn_bwd_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), smem, stream,
-                     tiles, H, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(d_o), lse, delta, dq,
-                     dk, dv, n_local, scale, scale * kLog2e, accumulate);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), smem,
+                     stream, tiles, H, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(d_o), lse, delta, dk,
+                     dv, n_local, scale, scale * kLog2e, accumulate);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, const void* d_o,
-                           const float* lse, const float* delta, float* dq, float* dk,
-                           float* dv, int64_t n_local, float scale, int32_t accumulate,
-                           hipStream_t stream) {
+hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
+                                const void* q, const void* k, const void* v, const void* d_o,
+                                const float* lse, const float* delta, float* dk, float* dv,
+                                int64_t n_local, float scale, int32_t accumulate,
+                                hipStream_t stream) {
   if (D == 128)
-    return launch_bwd_d<128>(tiles, n_tiles, H, q, k, v, d_o, lse, delta, dq, dk, dv, n_local,
+    return launch_bwd_d<128>(tiles, n_tiles, H, q, k, v, d_o, lse, delta, dk, dv, n_local,
                              scale, accumulate, stream);
   if (D == 64)
-    return launch_bwd_d<64>(tiles, n_tiles, H, q, k, v, d_o, lse, delta, dq, dk, dv, n_local,
+    return launch_bwd_d<64>(tiles, n_tiles, H, q, k, v, d_o, lse, delta, dk, dv, n_local,
                             scale, accumulate, stream);
   return hipErrorInvalidValue;
 }

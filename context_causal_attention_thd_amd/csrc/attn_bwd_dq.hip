@@ -1,0 +1,215 @@
+// Backward, query side: dQ for the local rows of one CP rank's share
+// ("[PyTorch] Add no-load-balance THD all-gather CP", sequence diagram: the
+// backward of the rank's attention steps). Each query row's gradient only
+// needs that row's LSE and delta, so dQ is computed query-tile-major, exactly
+// like the forward pass: no atomics, every local row written once (padding
+// rows 0), bit-identical from run to run.
+//
+// gfx950 design (mirrors the forward kernel): a workgroup of 4 waves owns up
+// to 128 consecutive query rows of one (document piece, head), 32 per wave,
+// and walks the keys from the document start in 64-key tiles, double-buffered
+// in LDS with the next tile's loads in flight. Per tile, with
+// v_mfma_f32_32x32x16_bf16:
+//   S^T = K Q^T, dP^T = V dO^T   (A = K / V rows from LDS, B = Q / dO regs)
+//   P^T = exp(S^T - LSE), dS^T = P^T (dP^T - delta)   (lane-local per query)
+//   dQ^T += K^T dS^T             (A = K^T by transposing LDS reads)
+// dS^T leaves the first products in exactly the B-operand layout of the
+// third, so it never touches LDS.
+#include "device_common.h"
+#include "internal.h"
+
+namespace thdcp {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct DqSmem {
+  static constexpr int P = D + 16;  // row pitch (bf16), as in the forward kernel
+  bf16 k[2][kFwdBN * P];
+  bf16 v[2][kFwdBN * P];
+};
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2)
+attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
+                   const bf16* __restrict__ k, const bf16* __restrict__ v,
+                   const bf16* __restrict__ d_o, const float* __restrict__ lse,
+                   const float* __restrict__ delta, float* __restrict__ dq, int64_t n_local,
+                   float scale, float scale_log2) {
+  constexpr int BN = kFwdBN;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int P = DqSmem<D>::P;
+  constexpr int CPR = D / 8;
+  constexpr int CH = BN * CPR / kThreads;
+  __shared__ DqSmem<D> sm;
+
+  const int tile_id = blockIdx.x / H;
+  const int h = blockIdx.x - tile_id * H;
+  const FwdTile t = tiles[tile_id];
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 31;
+  const int hh = lane >> 5;
+  const int sl = lane & 15;
+  const int g16 = lane >> 4;
+  const int64_t rs = (int64_t)H * D;
+  const int64_t head_off = (int64_t)h * D;
+
+  const int r = w * 32 + li;
+  const bool in_tile = r < t.n;
+  const int g = t.g0 + r;
+  const bool valid = in_tile && g < t.e;
+  const int64_t m = (int64_t)t.m0 + r;
+  const int my_g = valid ? g : -1;
+
+  // Q and dO fragments (B operands): query li, head dims kk*16 + hh*8 .. +7
+  bf16x8 qf[KSTEPS], dof[KSTEPS];
+  {
+    const int64_t off = m * rs + head_off + hh * 8;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      qf[kk] = valid ? load_bf16x8(q + off + kk * 16) : zero_bf16x8();
+      dof[kk] = valid ? load_bf16x8(d_o + off + kk * 16) : zero_bf16x8();
+    }
+  }
+  const float lse2 = valid ? lse[(int64_t)h * n_local + m] * kLog2e : 0.f;
+  const float dlt = valid ? delta[(int64_t)h * n_local + m] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  const int wrow_last = min(w * 32 + 31, t.n - 1);
+  const bool wave_has_rows = (w * 32 < t.n) && (t.g0 + w * 32 < t.e);
+  const int wave_kmax = wave_has_rows ? min(t.g0 + wrow_last, t.e - 1) : -1;
+  const int wave_gmin = t.g0 + w * 32;
+  const bool wave_all_valid = (w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e);
+
+  bf16x8 kreg[CH], vreg[CH];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      const int kr = c / CPR, dc = c - kr * CPR;
+      const int key = k0 + kr;
+      const int64_t off = (int64_t)key * rs + head_off + dc * 8;
+      kreg[j] = key < t.kend ? load_bf16x8(k + off) : zero_bf16x8();
+      vreg[j] = key < t.kend ? load_bf16x8(v + off) : zero_bf16x8();
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      const int kr = c / CPR, dc = c - kr * CPR;
+      store_bf16x8(&sm.k[buf][kr * P + dc * 8], kreg[j]);
+      store_bf16x8(&sm.v[buf][kr * P + dc * 8], vreg[j]);
+    }
+  };
+
+  const int ntiles = t.kend > t.a ? (t.kend - t.a + BN - 1) / BN : 0;
+  if (ntiles > 0) {
+    load_tile(t.a);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = t.a + it * BN;
+    const int cur = it & 1;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(k0 + BN);
+
+    if (k0 <= wave_kmax) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[kb][i] = 0.f;
+          dp[kb][i] = 0.f;
+        }
+        const bf16* kp = &sm.k[cur][(kb * 32 + li) * P + hh * 8];
+        const bf16* vp = &sm.v[cur][(kb * 32 + li) * P + hh * 8];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          s[kb] = mfma32(load_bf16x8(kp + kk * 16), qf[kk], s[kb]);
+          dp[kb] = mfma32(load_bf16x8(vp + kk * 16), dof[kk], dp[kb]);
+        }
+      }
+      const bool diag = !wave_all_valid || k0 + BN - 1 > wave_gmin;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+          const bool ok = !diag || key <= my_g;
+          const float p = ok ? fast_exp2(fmaf(s[kb][i], scale_log2, -lse2)) : 0.f;
+          dp[kb][i] = ok ? p * (dp[kb][i] - dlt) : 0.f;
+        }
+      // dQ^T += K^T dS^T; k-step (kb, u): slot j = key kb*32 + 16u +
+      // (j/4)*8 + hh*4 + j%4 (accumulator entries u*8..u*8+7 of dp[kb]).
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 dsb = to_bf16x8(dp[kb], u * 8);
+          const bf16* kb_p = &sm.k[cur][(kb * 32 + 16 * u + hh * 4 + (sl >> 2)) * P +
+                                        16 * (g16 & 1) + 4 * (sl & 3)];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 a = concat4(lds_read_tr4(kb_p + db * 32), lds_read_tr4(kb_p + db * 32 + 8 * P));
+            acc[db] = mfma32(a, dsb, acc[db]);
+          }
+        }
+    }
+
+    if (has_next) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (!in_tile) return;
+  float* qp = dq + m * rs + head_off;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 out;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = acc[db][i4 * 4 + j] * scale;
+      *reinterpret_cast<f32x4*>(qp + db * 32 + i4 * 8 + hh * 4) = out;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
+                              const void* q, const void* k, const void* v, const void* d_o,
+                              const float* lse, const float* delta, float* dq, int64_t n_local,
+                              float scale, hipStream_t stream) {
+  const int64_t blocks = (int64_t)n_tiles * H;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const bf16* qb = static_cast<const bf16*>(q);
+  const bf16* kb = static_cast<const bf16*>(k);
+  const bf16* vb = static_cast<const bf16*>(v);
+  const bf16* db = static_cast<const bf16*>(d_o);
+  if (D == 128)
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       tiles, H, qb, kb, vb, db, lse, delta, dq, n_local, scale, scale * kLog2e);
+  else if (D == 64)
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       tiles, H, qb, kb, vb, db, lse, delta, dq, n_local, scale, scale * kLog2e);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace thdcp

@@ -9,14 +9,18 @@
 //
 // gfx950 design: a workgroup of 4 waves owns up to 128 consecutive query rows
 // of one (document piece, head); each wave owns 32 query rows. Keys are walked
-// from the document start in 64-key tiles staged in LDS (K row-major, V
-// transposed). Everything is computed in the transposed form
+// from the document start in 64-key tiles, double-buffered in LDS (row-major
+// K and V); the next tile's global loads are issued before the current tile's
+// MFMAs so their latency hides behind compute, and one barrier per tile
+// suffices. Everything is computed in the transposed form
 //   S^T = K Q^T  and  O^T = V^T P^T
 // with v_mfma_f32_32x32x16_bf16, so every lane owns one query column of the
 // accumulators: the online-softmax max/sum/rescale are lane-local apart from
-// one exchange with the lane 32 away. Only tiles on the causal diagonal apply
-// a per-element mask; key rows beyond the last attended key are zeroed when
-// staged, so padding rows never enter a product (NaN-safe).
+// one exchange with the lane 32 away, and P feeds the second product with no
+// data movement. V^T operands come from the row-major V tile through the
+// transposing LDS read. Only tiles on the causal diagonal apply a per-element
+// mask; key rows past the last attended key are zeroed when staged, so padding
+// rows never enter a product (NaN-safe).
 #include "device_common.h"
 #include "internal.h"
 
@@ -31,10 +35,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int KP = D + 8;        // K tile pitch (bf16): conflict-free 16-byte reads
-  static constexpr int VP = kFwdBN + 4;   // V^T tile pitch (bf16): conflict-free 8-byte reads
-  bf16 k[kFwdBN * KP];
-  bf16 vt[D * VP];
+  // Row pitch (bf16) = D + 16: 16-byte row reads of 8 consecutive rows and
+  // transposing reads of 4 consecutive rows both hit distinct banks.
+  static constexpr int P = D + 16;
+  bf16 k[2][kFwdBN * P];
+  bf16 v[2][kFwdBN * P];
 };
 
 template <int D>
@@ -45,6 +50,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   constexpr int BN = kFwdBN;
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DB = D / 32;      // 32-wide blocks of the head dim
+  constexpr int P = FwdSmem<D>::P;
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int CH = BN * CPR / kThreads;       // chunks per thread per tile and tensor
   __shared__ FwdSmem<D> sm;
 
   const int tile_id = blockIdx.x / H;
@@ -54,6 +62,8 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int lane = threadIdx.x & 63;
   const int li = lane & 31;   // query column of this lane (and row index of A operands)
   const int hh = lane >> 5;   // which half of the wave
+  const int sl = lane & 15;   // lane within its 16-lane group (transposing reads)
+  const int g16 = lane >> 4;  // 16-lane group
   const int64_t rs = (int64_t)H * D;  // row stride in elements
 
   const int r = w * 32 + li;
@@ -86,103 +96,122 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int wave_gmin = t.g0 + w * 32;
   const bool wave_all_valid = (w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e);
 
-  for (int k0 = t.a; k0 < t.kend; k0 += BN) {
-    __syncthreads();  // previous tile fully consumed
-    // Stage K rows [k0, k0+BN) row-major; rows at or past kend are zero.
-    for (int c = threadIdx.x; c < BN * (D / 8); c += kThreads) {
-      const int kr = c / (D / 8), dc = c - kr * (D / 8);
+  // Staging: thread handles chunks c = threadIdx.x + j*kThreads of the tile.
+  const int64_t head_off = (int64_t)h * D;
+  bf16x8 kreg[CH], vreg[CH];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      const int kr = c / CPR, dc = c - kr * CPR;
       const int key = k0 + kr;
-      const bf16x8 val = key < t.kend ? load_bf16x8(k + (int64_t)key * rs + (int64_t)h * D + dc * 8)
-                                      : zero_bf16x8();
-      store_bf16x8(&sm.k[kr * FwdSmem<D>::KP + dc * 8], val);
+      const int64_t off = (int64_t)key * rs + head_off + dc * 8;
+      kreg[j] = key < t.kend ? load_bf16x8(k + off) : zero_bf16x8();
+      vreg[j] = key < t.kend ? load_bf16x8(v + off) : zero_bf16x8();
     }
-    // Stage V transposed: a lane takes two adjacent keys and one 8-dim chunk
-    // and writes eight 32-bit (key, key+1) pairs into V^T[d][key].
-    for (int c = threadIdx.x; c < (BN / 2) * (D / 8); c += kThreads) {
-      const int kp = c % (BN / 2), dc = c / (BN / 2);
-      const int key = k0 + 2 * kp;
-      const bf16* vp = v + (int64_t)key * rs + (int64_t)h * D + dc * 8;
-      const bf16x8 v0 = key < t.kend ? load_bf16x8(vp) : zero_bf16x8();
-      const bf16x8 v1 = key + 1 < t.kend ? load_bf16x8(vp + rs) : zero_bf16x8();
+  };
+  auto store_tile = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        *reinterpret_cast<uint32_t*>(&sm.vt[(dc * 8 + j) * FwdSmem<D>::VP + 2 * kp]) =
-            pack_bf16x2(v0[j], v1[j]);
+    for (int j = 0; j < CH; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      const int kr = c / CPR, dc = c - kr * CPR;
+      store_bf16x8(&sm.k[buf][kr * P + dc * 8], kreg[j]);
+      store_bf16x8(&sm.v[buf][kr * P + dc * 8], vreg[j]);
+    }
+  };
+
+  const int ntiles = t.kend > t.a ? (t.kend - t.a + BN - 1) / BN : 0;
+  if (ntiles > 0) {
+    load_tile(t.a);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = t.a + it * BN;
+    const int cur = it & 1;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) load_tile(k0 + BN);  // in flight during this tile's compute
+
+    if (k0 <= wave_kmax) {
+      // S^T (keys x queries) for the two 32-key halves of the tile.
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+        const bf16* kp = &sm.k[cur][(kb * 32 + li) * P + hh * 8];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) s[kb] = mfma32(load_bf16x8(kp + kk * 16), qf[kk], s[kb]);
       }
-    }
-    __syncthreads();
-    if (k0 > wave_kmax) continue;  // no row of this wave attends these keys
 
-    // S^T (keys x queries) for the two 32-key halves of the tile.
-    f32x16 s[2];
+      // Causal / padding mask, only where some key may exceed some row's g.
+      if (!wave_all_valid || k0 + BN - 1 > wave_gmin) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      const bf16* kp = &sm.k[(kb * 32 + li) * FwdSmem<D>::KP + hh * 8];
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) s[kb] = mfma32(load_bf16x8(kp + kk * 16), qf[kk], s[kb]);
-    }
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+            if (key > my_g) s[kb][i] = -INFINITY;
+          }
+      }
 
-    // Causal / padding mask, only where some key may exceed some row's g.
-    if (!wave_all_valid || k0 + BN - 1 > wave_gmin) {
+      // Online softmax in the log2 domain (scale * log2(e) folded in).
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = fmaxf(mx, shfl_xor32(mx));
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (key > my_g) s[kb][i] = -INFINITY;
+          const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
+          s[kb][i] = p;
+          psum += p;
+        }
+      psum += shfl_xor32(psum);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      if (!__all(alpha == 1.f)) {  // rescale only when some row's max moved
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
+
+      // O^T += V^T P^T. k-step (kb, u) covers 16 keys; slot j of this lane is
+      // key kb*32 + 16u + (j/4)*8 + hh*4 + j%4 -- exactly accumulator entries
+      // u*8 .. u*8+7 of s[kb], so P needs no data movement. The V^T operand
+      // (lane = head dim, slots = those keys) is two transposing reads of the
+      // row-major V tile: rows kb*32+16u+hh*4+{0..3} and the same +8.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pb = to_bf16x8(s[kb], u * 8);
+          const bf16* vb = &sm.v[cur][(kb * 32 + 16 * u + hh * 4 + (sl >> 2)) * P +
+                                      16 * (g16 & 1) + 4 * (sl & 3)];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 a = concat4(lds_read_tr4(vb + db * 32), lds_read_tr4(vb + db * 32 + 8 * P));
+            oacc[db] = mfma32(a, pb, oacc[db]);
+          }
         }
     }
 
-    // Online softmax in the log2 domain (scale * log2(e) folded in).
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, shfl_xor32(mx));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(fmaf(s[kb][i], scale_log2, -m_use));
-        s[kb][i] = p;
-        psum += p;
-      }
-    psum += shfl_xor32(psum);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-
-    // O^T += V^T P^T. k-step (kb, u) covers 16 keys; slot j of this lane is
-    // key kb*32 + 16u + (j/4)*8 + hh*4 + j%4 -- exactly accumulator entries
-    // u*8 .. u*8+7 of s[kb], so P needs no data movement.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 pb = to_bf16x8(s[kb], u * 8);
-        const int kcol = kb * 32 + 16 * u + hh * 4;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16* vp = &sm.vt[(db * 32 + li) * FwdSmem<D>::VP + kcol];
-          const bf16x8 a = concat4(load_bf16x4(vp), load_bf16x4(vp + 8));
-          oacc[db] = mfma32(a, pb, oacc[db]);
-        }
-      }
+    if (has_next) store_tile(cur ^ 1);
+    __syncthreads();
   }
 
   if (!in_tile) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  bf16* op = o + m * rs + (int64_t)h * D;
+  bf16* op = o + m * rs + head_off;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -191,7 +220,7 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       bf16x4 out;
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = (bf16)(oacc[db][i4 * 4 + j] * inv);
-      *reinterpret_cast<u32x2*>(op + db * 32 + i4 * 8 + hh * 4) = __builtin_bit_cast(u32x2, out);
+      store_bf16x4(op + db * 32 + i4 * 8 + hh * 4, out);
     }
   if (hh == 0) {
     lse[(int64_t)h * n_local + m] =

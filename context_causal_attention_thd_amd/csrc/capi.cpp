@@ -446,43 +446,72 @@ size_t scratch_need(thdcp_plan_t p) {
 }  // namespace
 
 thdcp_status_t cp_attn_bwd_preprocess(thdcp_plan_t p, const void* o, const float* lse,
-                                      const void* d_o, float* dq, void* scratch,
-                                      size_t scratch_bytes, void* stream) {
+                                      const void* d_o, void* scratch, size_t scratch_bytes,
+                                      void* stream) {
   thdcp_status_t st = check_plan(p);
   if (st != THDCP_OK) return st;
-  if (!o || !lse || !d_o || !dq) return fail(THDCP_ERR_ARG, "NULL device pointer");
-  if (!aligned16(o) || !aligned16(d_o) || !aligned16(dq))
-    return fail(THDCP_ERR_ARG, "O/dO/dQ must be 16-byte aligned");
+  if (!o || !lse || !d_o) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(o) || !aligned16(d_o)) return fail(THDCP_ERR_ARG, "O/dO must be 16-byte aligned");
   if (!scratch || scratch_bytes < scratch_need(p))
     return fail(THDCP_ERR_ARG, "scratch of %zu bytes is below the %zu needed", scratch_bytes,
                 scratch_need(p));
   if (p->n_local == 0) return ok();
-  return hip_status(launch_bwd_prep(o, d_o, lse, static_cast<float*>(scratch), dq, p->n_local,
+  return hip_status(launch_bwd_prep(o, d_o, lse, static_cast<float*>(scratch), p->n_local,
                                     p->desc.H, p->desc.D, (hipStream_t)stream),
                     "cp_attn_bwd_preprocess launch");
 }
 
-thdcp_status_t cp_attn_bwd_main(thdcp_plan_t p, const void* q, const void* k, const void* v,
-                                const float* lse, const void* d_o, float* dq, float* dk,
-                                float* dv, int32_t accumulate_dkv, const void* scratch,
-                                size_t scratch_bytes, void* stream) {
-  thdcp_status_t st = check_plan(p);
-  if (st != THDCP_OK) return st;
-  if (!q || !k || !v || !lse || !d_o || !dq || !dk || !dv)
-    return fail(THDCP_ERR_ARG, "NULL device pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv))
+namespace {
+
+thdcp_status_t check_bwd_inputs(thdcp_plan_t p, const void* q, const void* k, const void* v,
+                                const float* lse, const void* d_o, const void* scratch,
+                                size_t scratch_bytes) {
+  if (!q || !k || !v || !lse || !d_o) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o))
     return fail(THDCP_ERR_ARG, "tensors must be 16-byte aligned");
   if (!scratch || scratch_bytes < scratch_need(p))
     return fail(THDCP_ERR_ARG, "scratch of %zu bytes is below the %zu needed", scratch_bytes,
                 scratch_need(p));
+  return ok();
+}
+
+}  // namespace
+
+thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t p, const void* q, const void* k, const void* v,
+                                const float* lse, const void* d_o, float* dk, float* dv,
+                                int32_t accumulate_dkv, const void* scratch, size_t scratch_bytes,
+                                void* stream) {
+  thdcp_status_t st = check_plan(p);
+  if (st != THDCP_OK) return st;
+  st = check_bwd_inputs(p, q, k, v, lse, d_o, scratch, scratch_bytes);
+  if (st != THDCP_OK) return st;
+  if (!dk || !dv) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(dk) || !aligned16(dv)) return fail(THDCP_ERR_ARG, "dK/dV must be 16-byte aligned");
   if (p->bwd.empty()) return ok();
   return hip_status(
-      launch_attn_bwd(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
-                      (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, d_o, lse,
-                      static_cast<const float*>(scratch), dq, dk, dv, p->n_local, p->scale,
-                      accumulate_dkv, (hipStream_t)stream),
-      "cp_attn_bwd_main launch");
+      launch_attn_bwd_dkdv(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
+                           (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, d_o, lse,
+                           static_cast<const float*>(scratch), dk, dv, p->n_local, p->scale,
+                           accumulate_dkv, (hipStream_t)stream),
+      "cp_attn_bwd_dkdv launch");
+}
+
+thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, const void* v,
+                              const float* lse, const void* d_o, float* dq, const void* scratch,
+                              size_t scratch_bytes, void* stream) {
+  thdcp_status_t st = check_plan(p);
+  if (st != THDCP_OK) return st;
+  st = check_bwd_inputs(p, q, k, v, lse, d_o, scratch, scratch_bytes);
+  if (st != THDCP_OK) return st;
+  if (!dq) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(dq)) return fail(THDCP_ERR_ARG, "dQ must be 16-byte aligned");
+  if (p->fwd.empty()) return ok();
+  return hip_status(
+      launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
+                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, d_o, lse,
+                         static_cast<const float*>(scratch), dq, p->n_local, p->scale,
+                         (hipStream_t)stream),
+      "cp_attn_bwd_dq launch");
 }
 
 thdcp_status_t thdcp_zero_untouched(thdcp_plan_t p, float* dk, float* dv, void* stream) {
@@ -517,10 +546,12 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (!scratch || scratch_bytes < scratch_need(p))
     return fail(THDCP_ERR_ARG, "scratch of %zu bytes is below the %zu needed", scratch_bytes,
                 scratch_need(p));
-  st = cp_attn_bwd_preprocess(p, o, lse, d_o, dq, scratch, scratch_bytes, stream);
+  st = cp_attn_bwd_preprocess(p, o, lse, d_o, scratch, scratch_bytes, stream);
   if (st != THDCP_OK) return st;
-  st = cp_attn_bwd_main(p, q, k, v, lse, d_o, dq, dk, dv, accumulate_dkv, scratch, scratch_bytes,
+  st = cp_attn_bwd_dkdv(p, q, k, v, lse, d_o, dk, dv, accumulate_dkv, scratch, scratch_bytes,
                         stream);
+  if (st != THDCP_OK) return st;
+  st = cp_attn_bwd_dq(p, q, k, v, lse, d_o, dq, scratch, scratch_bytes, stream);
   if (st != THDCP_OK) return st;
   if (zero_untouched) return thdcp_zero_untouched(p, dk, dv, stream);
   return ok();

@@ -57,6 +57,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(bf16 lo, bf16 hi) {
   return (uint32_t)a | ((uint32_t)b << 16);
 }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i receives element i%4 of the 8 bytes that lane 4j + i/4 of the
+// group addressed, as its element j. So if source lane s of the group points
+// at row R[s/4], columns c0 + 4*(s%4) .. +3 of a row-major b16 matrix, lane i
+// receives column c0 + i of rows R[0..3]: a column slice, as MFMA operands
+// want, read straight from row-major tiles. All 64 lanes must be active.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void store_bf16x4(bf16* p, const bf16x4& v) {
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ float shfl_xor32(float x) {
   // exchange with the lane 32 away (the other half of the wave64)
   return __shfl_xor(x, 32, 64);

@@ -46,7 +46,6 @@ struct ZeroRange {
 constexpr int kFwdBM = 128;  // query rows per forward workgroup (4 waves x 32)
 constexpr int kFwdBN = 64;   // keys per forward K/V tile
 constexpr int kBwdBN = 128;  // keys per backward workgroup (4 waves x 32)
-constexpr int kBwdBM = 32;   // query rows per backward inner step
 
 // Kernel launchers (defined in the .hip files). All enqueue on `stream`.
 hipError_t launch_partition(const int32_t* cup, int32_t B, int64_t T, int32_t cp,
@@ -59,15 +58,18 @@ hipError_t launch_scatter(const void* src, int64_t n, const int32_t* idx, int64_
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
                             int64_t row_floats, float* a, float* b, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
-                           float* dq, int64_t n_local, int32_t H, int32_t D,
-                           hipStream_t stream);
+                           int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                            const void* q, const void* k, const void* v, void* o, float* lse,
                            int64_t n_local, float scale, hipStream_t stream);
-hipError_t launch_attn_bwd(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, const void* d_o,
-                           const float* lse, const float* delta, float* dq, float* dk,
-                           float* dv, int64_t n_local, float scale, int32_t accumulate,
-                           hipStream_t stream);
+hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
+                                const void* q, const void* k, const void* v, const void* d_o,
+                                const float* lse, const float* delta, float* dk, float* dv,
+                                int64_t n_local, float scale, int32_t accumulate,
+                                hipStream_t stream);
+hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
+                              const void* q, const void* k, const void* v, const void* d_o,
+                              const float* lse, const float* delta, float* dq, int64_t n_local,
+                              float scale, hipStream_t stream);
 
 }  // namespace thdcp

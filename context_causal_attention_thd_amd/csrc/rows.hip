@@ -189,8 +189,7 @@ hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t t
 }
 
 // ---------------------------------------------------------------------------
-// Backward preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32), and
-// dQ := 0 (the main backward kernel accumulates dQ with atomics).
+// Backward preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32).
 // One group of D/8 lanes per (row, head); each lane reads 16 bytes of O and dO.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -198,8 +197,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const bf16* __restrict__ 
                                                        const bf16* __restrict__ d_o,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ delta,
-                                                       float* __restrict__ dq, int64_t n_local,
-                                                       int32_t H) {
+                                                       int64_t n_local, int32_t H) {
   constexpr int G = D / 8;  // lanes per (row, head)
   const int64_t pairs = n_local * H;
   const int64_t groups_per_grid = (int64_t)gridDim.x * (blockDim.x / G);
@@ -221,14 +219,11 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const bf16* __restrict__ 
       const float l = lse[(int64_t)h * n_local + m];
       delta[(int64_t)h * n_local + m] = (l == -INFINITY) ? 0.f : acc;
     }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    reinterpret_cast<f32x4*>(dq + off)[0] = z;
-    reinterpret_cast<f32x4*>(dq + off)[1] = z;
   }
 }
 
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
-                           float* dq, int64_t n_local, int32_t H, int32_t D, hipStream_t stream) {
+                           int64_t n_local, int32_t H, int32_t D, hipStream_t stream) {
   const int64_t pairs = n_local * H;
   const int per_block = 256 / (D / 8);
   int64_t blocks = (pairs + per_block - 1) / per_block;
@@ -238,10 +233,10 @@ hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, flo
   const bf16* db = static_cast<const bf16*>(d_o);
   if (D == 128)
     hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, ob, db,
-                       lse, delta, dq, n_local, H);
+                       lse, delta, n_local, H);
   else if (D == 64)
     hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, ob, db,
-                       lse, delta, dq, n_local, H);
+                       lse, delta, n_local, H);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

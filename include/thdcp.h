@@ -198,8 +198,8 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k
  *   ([PAD] "Expected behavior": gate tail zeroing on the metadata).
  *   zero_untouched and accumulate_dkv are mutually exclusive.
  *   scratch  device, >= bwd_scratch_bytes, 256-byte aligned.
- * dQ is accumulated with float atomics, so its low bits may vary run to run;
- * dK and dV are deterministic.
+ * No atomics are used: every output row is written by exactly one workgroup,
+ * so dQ, dK and dV are bit-identical from run to run.
  */
 thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k,
                            const void* v, const void* o_local, const float* lse,
@@ -208,22 +208,28 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k
                            size_t scratch_bytes, void* stream);
 
 /*
- * The three launches cp_attn_bwd makes, exposed for callers that schedule or
- * time them separately. Calling them in this order on one stream is exactly
+ * The launches cp_attn_bwd makes, exposed for callers that schedule or time
+ * them separately. Calling them in this order on one stream is exactly
  * cp_attn_bwd.
  *   cp_attn_bwd_preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32,
- *     into scratch) and dq := 0.
- *   cp_attn_bwd_main: dQ (atomic adds into dq), dK/dV partials.
+ *     [H, n_local], into scratch).
+ *   cp_attn_bwd_dkdv: the dK/dV partials (key-tile-major; written, or added
+ *     when accumulate_dkv = 1, for every attended key row).
+ *   cp_attn_bwd_dq: dQ for every local row (query-tile-major; padding rows 0).
+ *     dkdv and dq only read delta, so they may run in either order.
  *   thdcp_zero_untouched: writes 0 to every dk/dv row no local query attends;
  *     enqueues nothing when the plan has no such row.
  */
 thdcp_status_t cp_attn_bwd_preprocess(thdcp_plan_t plan, const void* o_local, const float* lse,
-                                      const void* d_o, float* dq, void* scratch,
-                                      size_t scratch_bytes, void* stream);
-thdcp_status_t cp_attn_bwd_main(thdcp_plan_t plan, const void* q_local, const void* k,
-                                const void* v, const float* lse, const void* d_o, float* dq,
-                                float* dk, float* dv, int32_t accumulate_dkv,
-                                const void* scratch, size_t scratch_bytes, void* stream);
+                                      const void* d_o, void* scratch, size_t scratch_bytes,
+                                      void* stream);
+thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t plan, const void* q_local, const void* k,
+                                const void* v, const float* lse, const void* d_o, float* dk,
+                                float* dv, int32_t accumulate_dkv, const void* scratch,
+                                size_t scratch_bytes, void* stream);
+thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t plan, const void* q_local, const void* k,
+                              const void* v, const float* lse, const void* d_o, float* dq,
+                              const void* scratch, size_t scratch_bytes, void* stream);
 thdcp_status_t thdcp_zero_untouched(thdcp_plan_t plan, float* dk, float* dv, void* stream);
 
 #ifdef __cplusplus

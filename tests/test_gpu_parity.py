@@ -189,20 +189,18 @@ def test_padding_poison():
         _say("poison rank", r)
         clean = run_share(w, r, t)
         dirty = run_share(w, r, bad)
-        for n in ("o", "lse", "dk", "dv"):
+        for n in ("o", "lse", "dq", "dk", "dv"):
             assert np.array_equal(clean[n], dirty[n]), n
-        assert np.all(np.isfinite(dirty["dq"]))
-        assert_close(dirty["dq"], clean["dq"], "dq poison", max_abs=1e-5, rel_l2=1e-6)
 
 
-def test_determinism_of_o_dk_dv():
+def test_determinism_run_to_run():
+    # No atomics anywhere: every output is bit-identical across runs.
     w = SMALL[2]
     t = W.bf16_tensors(w)
     a = run_share(w, 1, t)
     b = run_share(w, 1, t)
-    for n in ("o", "lse", "dk", "dv"):
+    for n in ("o", "lse", "dq", "dk", "dv"):
         assert np.array_equal(a[n], b[n]), n
-    assert_close(a["dq"], b["dq"], "dq rerun", max_abs=1e-5, rel_l2=1e-6)
 
 
 def test_zero_untouched_gate_and_accumulate():
