@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 --pmc (optional)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 512 MiB device copy (a known-size reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -66,6 +69,13 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.int16, device=dev)   # 512 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
     t = W.bf16_tensors(w)
