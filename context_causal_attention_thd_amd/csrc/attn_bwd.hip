@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 64;  // query rows per block
+constexpr int kBM = 64;  // query rows per block (two 32-query halves)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -165,10 +165,12 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
         const int qr0 = qb * 32 + i4 * 8 + hh * 4;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
+        const i32x4 g4 = *reinterpret_cast<const i32x4*>(&sm.gq[cur][qr0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = i4 * 4 + j;
-          const bool ok = key_ok && my_key <= sm.gq[cur][qr0 + j];
+          // bitwise & keeps the LDS read unconditional (no divergent branch)
+          const bool ok = key_ok & (my_key <= g4[j]);
           const float p = ok ? fast_exp2(fmaf(s[qb][i], scale_log2, -l4[j])) : 0.f;
           const float dsv = ok ? p * (dp[qb][i] - d4[j]) : 0.f;
           s[qb][i] = p;

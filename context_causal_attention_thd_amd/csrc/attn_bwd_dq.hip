@@ -88,9 +88,10 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
 
   const int wrow_last = min(w * 32 + 31, t.n - 1);
   const bool wave_has_rows = (w * 32 < t.n) && (t.g0 + w * 32 < t.e);
-  const int wave_kmax = wave_has_rows ? min(t.g0 + wrow_last, t.e - 1) : -1;
-  const int wave_gmin = t.g0 + w * 32;
-  const bool wave_all_valid = (w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e);
+  const int wave_kmax = wave_uniform(wave_has_rows ? min(t.g0 + wrow_last, t.e - 1) : -1);
+  const int wave_gmin = wave_uniform(t.g0 + w * 32);
+  const bool wave_all_valid =
+      wave_uniform((w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e)) != 0;
 
   bf16x8 kreg[CH], vreg[CH];
   auto load_tile = [&](int k0) {

@@ -15,7 +15,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/thdcp.h"
+#include "thdcp.h"
 #include "internal.h"
 
 using namespace thdcp;

@@ -14,6 +14,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
 // Lane l holds row l%32 of A and column l%32 of B, k-slots 8*(l/32)..+7;
@@ -71,6 +72,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value known to be the same in every lane of the wave, moved to a scalar
+// register so that branches on it are scalar (no exec-mask divergence).
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 
 __device__ __forceinline__ void store_bf16x4(bf16* p, const bf16x4& v) {
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
