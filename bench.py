@@ -122,11 +122,9 @@ def main():
         plan.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
-        thd.gather(q, mine, out=q_local)
-        thd.gather(do, mine, out=do_local)
+        thd.gather_many([q, do], mine, [q_local, do_local])
         mark("restore0")
-        thd.scatter(k_rm, perm, k_g)
-        thd.scatter(v_rm, perm, v_g)
+        thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g])
         mark("restore1")
         mark("fwd0")
         thd.attn_fwd(plan, q_local, k_g, v_g, o=o, lse=lse)
@@ -139,8 +137,7 @@ def main():
                 ev.setdefault(n, []).append(pr)
         thd.attn_bwd_parts(plan, q_local, k_g, v_g, o, lse, do_local, dq, dk, dv, scratch,
                            zero_untouched=True, events=pairs_ev)
-        thd.gather(dk, perm, out=dk_rm)
-        thd.gather(dv, perm, out=dv_rm)
+        thd.gather_many([dk, dv], perm, [dk_rm, dv_rm])
         return plan  # keep alive until the stream is synchronized
 
     for _ in range(args.warmup):
@@ -221,7 +218,7 @@ def main():
         "roofline_fwd": {"bound": "mfma", "kernel": "attn_fwd_kernel",
                          "achieved": round(tflops_fwd, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops_fwd / PEAK_BF16_TFLOPS, 4)},
-        "roofline_gather": {"bound": "hbm", "kernel": "move_rows_kernel (K/V restore)",
+        "roofline_gather": {"bound": "hbm", "kernel": "move_rows_kernel (K and V restore, one launch)",
                             "achieved": round(gbs_restore, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs_restore / PEAK_HBM_GBS, 4),
                             "bytes": restore_bytes},

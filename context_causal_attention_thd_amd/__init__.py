@@ -23,7 +23,7 @@ _STRATEGY_NAMES = {"dual_chunk_swap": DUAL_CHUNK_SWAP, "no_load_balance": NO_LOA
 
 EXPORTED_SYMBOLS = (
     "thdcp_last_error", "thdcp_version", "thdcp_validate", "thd_partition_index", "thd_gather",
-    "thd_scatter", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
+    "thd_scatter", "thd_gather_batched", "thd_scatter_batched", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
     "thdcp_plan_upload", "thdcp_plan_destroy", "cp_attn_fwd", "cp_attn_bwd",
     "cp_attn_bwd_preprocess", "cp_attn_bwd_dkdv", "cp_attn_bwd_dq", "thdcp_zero_untouched",
 )
@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
     L.thd_gather.argtypes = [vp, i64, vp, i64, i64, vp, vp]
     L.thd_scatter.restype = i32
     L.thd_scatter.argtypes = [vp, i64, vp, i64, vp, i64, vp]
+    pvp = ctypes.POINTER(vp)
+    L.thd_gather_batched.restype = i32
+    L.thd_gather_batched.argtypes = [i32, pvp, i64, vp, i64, i64, pvp, vp]
+    L.thd_scatter_batched.restype = i32
+    L.thd_scatter_batched.argtypes = [i32, pvp, i64, vp, i64, pvp, i64, vp]
     L.thdcp_plan_create.restype = i32
     L.thdcp_plan_create.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(vp)]
     L.thdcp_plan_get_info.restype = i32
@@ -223,6 +228,44 @@ def scatter(src, idx, out, stream=None):
                              _dev_ptr(idx, "idx", torch.int32), rb, _dev_ptr(out, "out"),
                              out.shape[0], _stream(stream)))
     return out
+
+
+def _ptr_list(ts, name):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _dev_ptr(t, f"{name}[{i}]").value
+    return arr
+
+
+def gather_many(srcs, idx, outs=None, stream=None):
+    """outs[i][m] = srcs[i][idx[m]] for 1..4 same-shaped tensors, one launch."""
+    import torch
+    if outs is None:
+        outs = [torch.empty((idx.shape[0],) + tuple(s.shape[1:]), dtype=s.dtype,
+                            device=s.device) for s in srcs]
+    rb = _row_bytes(srcs[0])
+    if any(_row_bytes(x) != rb for x in list(srcs) + list(outs)):
+        raise ValueError("all rows must have the same size")
+    if any(x.shape[0] != srcs[0].shape[0] for x in srcs):
+        raise ValueError("all sources must have the same number of rows")
+    _check(lib().thd_gather_batched(len(srcs), _ptr_list(srcs, "src"), srcs[0].shape[0],
+                                    _dev_ptr(idx, "idx", torch.int32), idx.shape[0], rb,
+                                    _ptr_list(outs, "out"), _stream(stream)))
+    return outs
+
+
+def scatter_many(srcs, idx, outs, stream=None):
+    """outs[i][idx[m]] = srcs[i][m] for 1..4 same-shaped tensors, one launch."""
+    import torch
+    rb = _row_bytes(srcs[0])
+    if any(_row_bytes(x) != rb for x in list(srcs) + list(outs)):
+        raise ValueError("all rows must have the same size")
+    if any(x.shape[0] != outs[0].shape[0] for x in outs):
+        raise ValueError("all destinations must have the same number of rows")
+    _check(lib().thd_scatter_batched(len(srcs), _ptr_list(srcs, "src"), srcs[0].shape[0],
+                                     _dev_ptr(idx, "idx", torch.int32), rb,
+                                     _ptr_list(outs, "out"), outs[0].shape[0], _stream(stream)))
+    return outs
 
 
 # ---------------------------------------------------------------------------

@@ -331,19 +331,48 @@ thdcp_status_t thd_partition_index(const int32_t* cup_host, const int32_t* cup_d
 
 thdcp_status_t thd_gather(const void* src, int64_t n_src, const int32_t* idx, int64_t n,
                           int64_t row_bytes, void* dst, void* stream) {
-  if (n < 0 || n_src < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
-  if (n == 0) return ok();
-  if (!src || !idx || !dst) return fail(THDCP_ERR_ARG, "NULL device pointer");
-  return hip_status(launch_gather(src, n_src, idx, n, row_bytes, dst, (hipStream_t)stream),
-                    "thd_gather launch");
+  return thd_gather_batched(1, &src, n_src, idx, n, row_bytes, &dst, stream);
 }
 
 thdcp_status_t thd_scatter(const void* src, int64_t n, const int32_t* idx, int64_t row_bytes,
                            void* dst, int64_t n_dst, void* stream) {
-  if (n < 0 || n_dst < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
+  return thd_scatter_batched(1, &src, n, idx, row_bytes, &dst, n_dst, stream);
+}
+
+namespace {
+thdcp_status_t check_batch(int32_t n_tensors, const void* const* srcs, void* const* dsts) {
+  if (n_tensors < 1 || n_tensors > kMaxMoveTensors)
+    return fail(THDCP_ERR_ARG, "n_tensors must be in [1, %d]", kMaxMoveTensors);
+  if (!srcs || !dsts) return fail(THDCP_ERR_ARG, "NULL pointer list");
+  for (int32_t i = 0; i < n_tensors; ++i)
+    if (!srcs[i] || !dsts[i]) return fail(THDCP_ERR_ARG, "NULL device pointer in list");
+  return ok();
+}
+}  // namespace
+
+thdcp_status_t thd_gather_batched(int32_t n_tensors, const void* const* srcs, int64_t n_src,
+                                  const int32_t* idx, int64_t n, int64_t row_bytes,
+                                  void* const* dsts, void* stream) {
+  if (n < 0 || n_src < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
+  thdcp_status_t st = check_batch(n_tensors, srcs, dsts);
+  if (st != THDCP_OK) return st;
   if (n == 0) return ok();
-  if (!src || !idx || !dst) return fail(THDCP_ERR_ARG, "NULL device pointer");
-  return hip_status(launch_scatter(src, n, idx, row_bytes, dst, n_dst, (hipStream_t)stream),
+  if (!idx) return fail(THDCP_ERR_ARG, "NULL index pointer");
+  return hip_status(launch_gather(n_tensors, srcs, n_src, idx, n, row_bytes, dsts,
+                                  (hipStream_t)stream),
+                    "thd_gather launch");
+}
+
+thdcp_status_t thd_scatter_batched(int32_t n_tensors, const void* const* srcs, int64_t n,
+                                   const int32_t* idx, int64_t row_bytes, void* const* dsts,
+                                   int64_t n_dst, void* stream) {
+  if (n < 0 || n_dst < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
+  thdcp_status_t st = check_batch(n_tensors, srcs, dsts);
+  if (st != THDCP_OK) return st;
+  if (n == 0) return ok();
+  if (!idx) return fail(THDCP_ERR_ARG, "NULL index pointer");
+  return hip_status(launch_scatter(n_tensors, srcs, n, idx, row_bytes, dsts, n_dst,
+                                   (hipStream_t)stream),
                     "thd_scatter launch");
 }
 

@@ -51,10 +51,13 @@ constexpr int kBwdBN = 128;  // keys per backward workgroup (4 waves x 32)
 hipError_t launch_partition(const int32_t* cup, int32_t B, int64_t T, int32_t cp,
                             int32_t rank, int32_t strategy, int32_t* out, int64_t n_out,
                             hipStream_t stream);
-hipError_t launch_gather(const void* src, int64_t n_src, const int32_t* idx, int64_t n,
-                         int64_t row_bytes, void* dst, hipStream_t stream);
-hipError_t launch_scatter(const void* src, int64_t n, const int32_t* idx, int64_t row_bytes,
-                          void* dst, int64_t n_dst, hipStream_t stream);
+constexpr int kMaxMoveTensors = 4;  // tensors one gather/scatter launch can move
+hipError_t launch_gather(int32_t n_tensors, const void* const* srcs, int64_t n_src,
+                         const int32_t* idx, int64_t n, int64_t row_bytes, void* const* dsts,
+                         hipStream_t stream);
+hipError_t launch_scatter(int32_t n_tensors, const void* const* srcs, int64_t n,
+                          const int32_t* idx, int64_t row_bytes, void* const* dsts,
+                          int64_t n_dst, hipStream_t stream);
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
                             int64_t row_floats, float* a, float* b, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,

@@ -72,12 +72,20 @@ template <> struct Vec<1> { typedef uint8_t T; };
 constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 4;
 
+// Up to kMaxTensors tensors moved by one launch (blockIdx.y picks the tensor).
+struct RowPtrs {
+  const char* src[kMaxMoveTensors];
+  char* dst[kMaxMoveTensors];
+};
+
 // SCATTER = false: dst[m] = src[idx[m]]; true: dst[idx[m]] = src[m].
 template <int VB, bool SCATTER>
 __global__ void __launch_bounds__(kRowThreads) move_rows_kernel(
-    const char* __restrict__ src, const int32_t* __restrict__ idx, char* __restrict__ dst,
-    uint32_t chunks_per_row, uint64_t total_chunks, int64_t n_other, int64_t row_bytes) {
+    const RowPtrs ptrs, const int32_t* __restrict__ idx, uint32_t chunks_per_row,
+    uint64_t total_chunks, int64_t n_other, int64_t row_bytes) {
   typedef typename Vec<VB>::T V;
+  const char* __restrict__ src = ptrs.src[blockIdx.y];
+  char* __restrict__ dst = ptrs.dst[blockIdx.y];
   const uint64_t stride = (uint64_t)gridDim.x * kRowThreads * kRowUnroll;
   for (uint64_t base = (uint64_t)blockIdx.x * kRowThreads * kRowUnroll + threadIdx.x;
        base < total_chunks; base += stride) {
@@ -115,10 +123,18 @@ __global__ void __launch_bounds__(kRowThreads) move_rows_kernel(
 }
 
 template <bool SCATTER>
-hipError_t launch_move(const void* src, const int32_t* idx, void* dst, int64_t n, int64_t n_other,
-                       int64_t row_bytes, hipStream_t stream) {
+hipError_t launch_move(int32_t n_tensors, const void* const* srcs, const int32_t* idx,
+                       void* const* dsts, int64_t n, int64_t n_other, int64_t row_bytes,
+                       hipStream_t stream) {
+  if (n_tensors < 1 || n_tensors > kMaxMoveTensors) return hipErrorInvalidValue;
+  RowPtrs ptrs{};
+  uintptr_t addr_bits = 0;
+  for (int i = 0; i < n_tensors; ++i) {
+    ptrs.src[i] = static_cast<const char*>(srcs[i]);
+    ptrs.dst[i] = static_cast<char*>(dsts[i]);
+    addr_bits |= reinterpret_cast<uintptr_t>(srcs[i]) | reinterpret_cast<uintptr_t>(dsts[i]);
+  }
   int vb = 1;
-  const uintptr_t addr_bits = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst);
   for (int cand : {16, 8, 4, 2}) {
     if (row_bytes % cand == 0 && (addr_bits % cand) == 0) { vb = cand; break; }
   }
@@ -127,27 +143,27 @@ hipError_t launch_move(const void* src, const int32_t* idx, void* dst, int64_t n
   if (cpr > 0xffffffffull) return hipErrorInvalidValue;
   uint64_t blocks = (total + kRowThreads * kRowUnroll - 1) / (kRowThreads * kRowUnroll);
   if (blocks > 65536) blocks = 65536;
-  const dim3 grid((unsigned)blocks), block(kRowThreads);
-  const char* s = static_cast<const char*>(src);
-  char* d = static_cast<char*>(dst);
+  const dim3 grid((unsigned)blocks, (unsigned)n_tensors), block(kRowThreads);
   switch (vb) {
-    case 16: hipLaunchKernelGGL((move_rows_kernel<16, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
-    case 8:  hipLaunchKernelGGL((move_rows_kernel<8, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
-    case 4:  hipLaunchKernelGGL((move_rows_kernel<4, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
-    case 2:  hipLaunchKernelGGL((move_rows_kernel<2, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
-    default: hipLaunchKernelGGL((move_rows_kernel<1, SCATTER>), grid, block, 0, stream, s, idx, d, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 16: hipLaunchKernelGGL((move_rows_kernel<16, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 8:  hipLaunchKernelGGL((move_rows_kernel<8, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 4:  hipLaunchKernelGGL((move_rows_kernel<4, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 2:  hipLaunchKernelGGL((move_rows_kernel<2, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
+    default: hipLaunchKernelGGL((move_rows_kernel<1, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const void* src, int64_t n_src, const int32_t* idx, int64_t n,
-                         int64_t row_bytes, void* dst, hipStream_t stream) {
-  return launch_move<false>(src, idx, dst, n, n_src, row_bytes, stream);
+hipError_t launch_gather(int32_t n_tensors, const void* const* srcs, int64_t n_src,
+                         const int32_t* idx, int64_t n, int64_t row_bytes, void* const* dsts,
+                         hipStream_t stream) {
+  return launch_move<false>(n_tensors, srcs, idx, dsts, n, n_src, row_bytes, stream);
 }
 
-hipError_t launch_scatter(const void* src, int64_t n, const int32_t* idx, int64_t row_bytes,
-                          void* dst, int64_t n_dst, hipStream_t stream) {
-  return launch_move<true>(src, idx, dst, n, n_dst, row_bytes, stream);
+hipError_t launch_scatter(int32_t n_tensors, const void* const* srcs, int64_t n,
+                          const int32_t* idx, int64_t row_bytes, void* const* dsts,
+                          int64_t n_dst, hipStream_t stream) {
+  return launch_move<true>(n_tensors, srcs, idx, dsts, n, n_dst, row_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

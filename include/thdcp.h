@@ -113,6 +113,20 @@ thdcp_status_t thd_gather(const void* src_dev, int64_t n_src, const int32_t* idx
 thdcp_status_t thd_scatter(const void* src_dev, int64_t n, const int32_t* idx_dev,
                            int64_t row_bytes, void* dst_dev, int64_t n_dst, void* stream);
 
+/*
+ * The same gather / scatter applied to 1..4 tensors that share the index, the
+ * row count and the row size, in one launch (e.g. the K and V restore, the
+ * local Q and dO slices, the dK and dV unrestore). src_list and dst_list are
+ * host arrays of n_tensors device pointers; per tensor the behaviour is that
+ * of thd_gather / thd_scatter.
+ */
+thdcp_status_t thd_gather_batched(int32_t n_tensors, const void* const* src_list, int64_t n_src,
+                                  const int32_t* idx_dev, int64_t n, int64_t row_bytes,
+                                  void* const* dst_list, void* stream);
+thdcp_status_t thd_scatter_batched(int32_t n_tensors, const void* const* src_list, int64_t n,
+                                   const int32_t* idx_dev, int64_t row_bytes,
+                                   void* const* dst_list, int64_t n_dst, void* stream);
+
 /* ------------------------------------------------------------------------
  * Rank plan: the THD metadata of one rank ([AG] sequence diagram "partition
  * and build THD metadata"), built once per batch on the host and shared by

@@ -123,3 +123,16 @@ def test_plan_rejects_unsupported(L):
     with pytest.raises(thd.ThdcpError) as ei:
         thd.Plan(w.cu_seqlens(), w.cu_seqlens_padded(), w.T, 2, 0, w.strategy, 2, 96, upload=False)
     assert ei.value.status == 3
+
+
+def test_batched_moves_reject_bad_tensor_counts(L):
+    import ctypes
+    pv = ctypes.c_void_p
+    arr = (pv * 5)(*([pv(16)] * 5))
+    for n in (0, 5):
+        st = L.thd_gather_batched(n, arr, 10, pv(16), 10, 16, arr, None)
+        assert st == 1
+        st = L.thd_scatter_batched(n, arr, 10, pv(16), 16, arr, 10, None)
+        assert st == 1
+    # zero rows enqueue nothing and succeed
+    assert L.thd_gather_batched(2, arr, 10, pv(16), 0, 16, arr, None) == 0

@@ -107,6 +107,27 @@ def test_gather_scatter_byte_exact(row_shape, dtype):
     assert np.array_equal(dv, expd)
 
 
+@pytest.mark.parametrize("n_tensors", [1, 2, 4])
+def test_batched_gather_scatter_byte_exact(n_tensors):
+    g = torch.Generator().manual_seed(7)
+    n_src = 2053
+    srcs = [torch.randn((n_src, 5, 128), generator=g).to(torch.bfloat16) for _ in range(n_tensors)]
+    idx = torch.randint(0, n_src, (1500,), generator=g, dtype=torch.int32)
+    idx[3] = -7
+    dev_srcs = [x.to(device()) for x in srcs]
+    outs = thd.gather_many(dev_srcs, idx.to(device()))
+    for x, o in zip(srcs, outs):
+        exp = np.array(O.gather(x.view(torch.int16).numpy(), np.clip(idx.numpy(), 0, n_src - 1)))
+        exp[3] = 0
+        assert np.array_equal(o.cpu().view(torch.int16).numpy(), exp)
+    perm = torch.randperm(n_src, generator=g).to(torch.int32)
+    dsts = [torch.zeros_like(x) for x in dev_srcs]
+    thd.scatter_many(dev_srcs, perm.to(device()), dsts)
+    for x, d in zip(srcs, dsts):
+        exp = O.scatter(x.view(torch.int16).numpy(), perm.numpy(), n_src)
+        assert np.array_equal(d.cpu().view(torch.int16).numpy(), exp)
+
+
 @pytest.mark.parametrize("name", ["dcs_8k", "nlb_32k", "pad_131k"])
 def test_kv_restore_round_trip(name):
     """Simulated all-gather: rank-major buffer of every rank's share, restored
@@ -116,12 +137,18 @@ def test_kv_restore_round_trip(name):
     cup = w.cu_seqlens_padded()
     dev = device()
     cup_dev = torch.from_numpy(cup).to(dev)
-    k = W.bf16_tensors(w, ("k",))["k"].to(dev)
+    t = W.bf16_tensors(w, ("k", "v"))
+    k, v = t["k"].to(dev), t["v"].to(dev)
     perm = thd.partition_index(cup, cup_dev, w.T, w.cp_size, -1, w.strategy)
     k_rm = thd.gather(k, perm)                  # all-gather output, rank-major
     k_glob = torch.empty_like(k)
     thd.scatter(k_rm, perm, k_glob)             # restore
     assert torch.equal(k_glob, k)
+    # K and V together in one launch
+    k_rm2, v_rm2 = thd.gather_many([k, v], perm)
+    k_g2, v_g2 = torch.empty_like(k), torch.empty_like(v)
+    thd.scatter_many([k_rm2, v_rm2], perm, [k_g2, v_g2])
+    assert torch.equal(k_g2, k) and torch.equal(v_g2, v) and torch.equal(k_rm2, k_rm)
     exp = O.gather(k.view(torch.int16).cpu().numpy(),
                    O.partition_index(cup, w.T, w.cp_size, 0, w.strategy))
     assert np.array_equal(k_rm[: w.T // w.cp_size].view(torch.int16).cpu().numpy(), exp)
