@@ -6,18 +6,21 @@
 // query rows that are not real tokens are not listed, key rows past the tile
 // end are zeroed, and masked probabilities are selected to 0 (NaN-safe).
 //
-// gfx950 design: a workgroup of 4 waves owns 128 consecutive keys of one
-// document (32 per wave, K and V fragments in registers) and walks the local
-// query rows that attend them in blocks of 64. Query blocks (Q, dO, LSE,
-// delta) are double-buffered in LDS and the next block's global loads are in
-// flight while the current one is computed; one barrier per block. Per block
-// each wave computes with v_mfma_f32_32x32x16_bf16
+// gfx950 design: a workgroup of 8 waves (two per SIMD) owns 128 consecutive
+// keys of one document, 16 per wave, with K and V fragments in registers, and
+// walks the local query rows that attend them in blocks of 64. Query blocks
+// (Q, dO, LSE, delta) are double-buffered in LDS and the next block's global
+// loads are in flight while the current one is computed; one barrier per
+// block. Per block each wave computes with v_mfma_f32_16x16x32_bf16
 //   S = Q K^T, dP = dO V^T          (A = Q / dO rows from LDS, B = K / V regs)
 //   P = exp(S - LSE), dS = P (dP - delta)
 //   dV += P^T dO, dK += dS^T Q       (accumulators stay in registers)
 // P and dS come out of the first products already in the A-operand layout of
 // the last two; their B operands (dO and Q, sliced by column) are transposing
-// LDS reads of the row-major tiles.
+// LDS reads of the row-major tiles. 16-key waves keep the per-wave state at
+// ~230 registers, so two waves share each SIMD and hide each other's LDS and
+// exp latency (a 32-key, 4-wave variant needed ~400 registers and ran at one
+// wave per SIMD, 25-35% slower).
 #include <atomic>
 
 #include "device_common.h"
@@ -27,10 +30,27 @@ namespace thdcp {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 64;  // query rows per block (two 32-query halves)
+constexpr int kBM = 64;  // query rows per block (four 16-query M-blocks)
 constexpr float kLog2e = 1.4426950408889634f;
+
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate. Lane l holds
+// row l%16 of A and column l%16 of B, k-slots 8*(l/16)..+7; accumulator
+// element i of lane l is row 4*(l/16) + i, column l%16.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = (bf16)x[j];
+    r[4 + j] = (bf16)y[j];
+  }
+  return r;
+}
 
 template <int D>
 struct BwdSmem {
@@ -50,8 +70,8 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
                      const float* __restrict__ delta, float* __restrict__ dk,
                      float* __restrict__ dv, int64_t n_local, float scale, float scale_log2,
                      int32_t accumulate) {
-  constexpr int KSTEPS = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int KS = D / 32;                  // 16x16x32 k-steps over the head dim
+  constexpr int NB = D / 16;                  // 16-wide blocks of the head dim
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int CH = kBM * CPR / kThreads;    // chunks per thread per block and tensor
   typedef BwdSmem<D> S;
@@ -64,35 +84,31 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   const BwdTile t = tiles[tile_id];
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int li = lane & 31;
-  const int hh = lane >> 5;
-  const int sl = lane & 15;
-  const int g16 = lane >> 4;
+  const int l16 = lane & 15;   // key column of S / dP; row of the dV / dK A operand
+  const int G = lane >> 4;     // 16-lane group: k-slot block and accumulator row block
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = (int64_t)h * D;
 
-  // This lane's key (column of S and dP; row of the dK/dV A operands).
-  const int my_key = t.k0 + w * 32 + li;
+  const int my_key = t.k0 + w * 16 + l16;
   const bool key_ok = my_key < t.k1;
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  bf16x8 kf[KS], vf[KS];
   {
-    const int64_t off = (int64_t)my_key * rs + head_off + hh * 8;
+    const int64_t off = (int64_t)my_key * rs + head_off + G * 8;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      kf[kk] = key_ok ? load_bf16x8(k + off + kk * 16) : zero_bf16x8();
-      vf[kk] = key_ok ? load_bf16x8(v + off + kk * 16) : zero_bf16x8();
+    for (int kk = 0; kk < KS; ++kk) {
+      kf[kk] = key_ok ? load_bf16x8(k + off + kk * 32) : zero_bf16x8();
+      vf[kk] = key_ok ? load_bf16x8(v + off + kk * 32) : zero_bf16x8();
     }
   }
-  f32x16 dka[DB], dva[DB];
+  f32x4 dka[NB], dva[NB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dka[db][i] = 0.f;
-      dva[db][i] = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      dka[nb][i] = 0.f;
+      dva[nb][i] = 0.f;
     }
 
-  // Query-block staging: chunk c = threadIdx.x + j*kThreads of the block.
   bf16x8 qreg[CH], dreg[CH];
   float lreg = 0.f, dlreg = 0.f;
   int greg = -1;
@@ -138,80 +154,76 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     const int mb = t.m_lo + it * kBM;
     const int cur = it & 1;
     const bool has_next = it + 1 < nblocks;
-    if (has_next) load_block(mb + kBM);  // in flight during this block's compute
+    if (has_next) load_block(mb + kBM);
 
-    // S and dP for the two 32-query halves (rows = queries, column = my_key).
-    f32x16 s[2], dp[2];
+    // S and dP for four 16-query M-blocks (rows = queries, column = my_key).
+    f32x4 s[4], dp[4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qm = 0; qm < 4; ++qm) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[qb][i] = 0.f;
-        dp[qb][i] = 0.f;
-      }
-      const bf16* qa = &sm.q[cur][(qb * 32 + li) * P + hh * 8];
-      const bf16* da = &sm.dO[cur][(qb * 32 + li) * P + hh * 8];
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        s[qb] = mfma32(load_bf16x8(qa + kk * 16), kf[kk], s[qb]);
-        dp[qb] = mfma32(load_bf16x8(da + kk * 16), vf[kk], dp[qb]);
+      for (int i = 0; i < 4; ++i) {
+        s[qm][i] = 0.f;
+        dp[qm][i] = 0.f;
       }
     }
-    // Element i of s[qb]: query row qb*32 + 8*(i/4) + 4*hh + i%4, key my_key.
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int qr0 = qb * 32 + i4 * 8 + hh * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
-        const i32x4 g4 = *reinterpret_cast<const i32x4*>(&sm.gq[cur][qr0]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i4 * 4 + j;
-          // bitwise & keeps the LDS read unconditional (no divergent branch)
-          const bool ok = key_ok & (my_key <= g4[j]);
-          const float p = ok ? fast_exp2(fmaf(s[qb][i], scale_log2, -l4[j])) : 0.f;
-          const float dsv = ok ? p * (dp[qb][i] - d4[j]) : 0.f;
-          s[qb][i] = p;
-          dp[qb][i] = dsv;
-        }
+      for (int qm = 0; qm < 4; ++qm) {
+        const int o = (qm * 16 + l16) * P + kk * 32 + G * 8;
+        s[qm] = mfma16(load_bf16x8(&sm.q[cur][o]), kf[kk], s[qm]);
+        dp[qm] = mfma16(load_bf16x8(&sm.dO[cur][o]), vf[kk], dp[qm]);
       }
-    // dV += P^T dO and dK += dS^T Q. k-step (qb, u) covers query rows
-    // qb*32 + 16u + (j/4)*8 + hh*4 + j%4 for slot j: accumulator entries
-    // u*8..u*8+7 of s[qb] / dp[qb]. The B operands (lane = head dim, slots =
-    // those rows) are two transposing reads each of the row-major dO and Q.
+    // Element i of s[qm]: query row qm*16 + 4*G + i, key my_key.
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qm = 0; qm < 4; ++qm) {
+      const int qr0 = qm * 16 + G * 4;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
+      const i32x4 g4 = *reinterpret_cast<const i32x4*>(&sm.gq[cur][qr0]);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 pa = to_bf16x8(s[qb], u * 8);
-        const bf16x8 dsa = to_bf16x8(dp[qb], u * 8);
-        const int roff = (qb * 32 + 16 * u + hh * 4 + (sl >> 2)) * P + 16 * (g16 & 1) + 4 * (sl & 3);
-        const bf16* dob = &sm.dO[cur][roff];
-        const bf16* qbp = &sm.q[cur][roff];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 bdo = concat4(lds_read_tr4(dob + db * 32), lds_read_tr4(dob + db * 32 + 8 * P));
-          dva[db] = mfma32(pa, bdo, dva[db]);
-          const bf16x8 bq = concat4(lds_read_tr4(qbp + db * 32), lds_read_tr4(qbp + db * 32 + 8 * P));
-          dka[db] = mfma32(dsa, bq, dka[db]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = key_ok & (my_key <= g4[i]);
+        const float p = ok ? fast_exp2(fmaf(s[qm][i], scale_log2, -l4[i])) : 0.f;
+        const float dsv = ok ? p * (dp[qm][i] - d4[i]) : 0.f;
+        s[qm][i] = p;
+        dp[qm][i] = dsv;
       }
+    }
+    // dV += P^T dO and dK += dS^T Q. k-step ks covers the M-blocks 2ks and
+    // 2ks+1: slot j of this lane is query (2ks + j/4)*16 + 4*G + j%4, i.e.
+    // accumulator entries of s[2ks], s[2ks+1] (P needs no data movement).
+    // B operands (lane = head dim, slots = those queries) are two
+    // transposing reads each of the row-major dO and Q tiles.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pa = pack8(s[2 * ks], s[2 * ks + 1]);
+      const bf16x8 dsa = pack8(dp[2 * ks], dp[2 * ks + 1]);
+      const int o1 = (2 * ks * 16 + G * 4 + (l16 >> 2)) * P + 4 * (l16 & 3);
+      const int o2 = o1 + 16 * P;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8 bdo = concat4(lds_read_tr4(&sm.dO[cur][o1 + nb * 16]), lds_read_tr4(&sm.dO[cur][o2 + nb * 16]));
+        dva[nb] = mfma16(pa, bdo, dva[nb]);
+        const bf16x8 bq = concat4(lds_read_tr4(&sm.q[cur][o1 + nb * 16]), lds_read_tr4(&sm.q[cur][o2 + nb * 16]));
+        dka[nb] = mfma16(dsa, bq, dka[nb]);
+      }
+    }
     if (has_next) store_block(cur ^ 1);
     __syncthreads();
   }
 
-  // dK (scaled) and dV rows of this wave's keys; lane li holds head dim db*32 + li.
+  // dK (scaled) and dV rows of this wave's keys; lane holds head dim nb*16 + l16
+  // for keys 4*G + i of the wave's 16.
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = t.k0 + w * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+    for (int i = 0; i < 4; ++i) {
+      const int key = t.k0 + w * 16 + G * 4 + i;
       if (key < t.k1) {
-        const int64_t off = (int64_t)key * rs + head_off + db * 32 + li;
-        const float kval = dka[db][i] * scale;
-        const float vval = dva[db][i];
+        const int64_t off = (int64_t)key * rs + head_off + nb * 16 + l16;
+        const float kval = dka[nb][i] * scale;
+        const float vval = dva[nb][i];
         if (accumulate) {
           dk[off] += kval;
           dv[off] += vval;
