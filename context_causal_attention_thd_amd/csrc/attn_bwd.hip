@@ -35,23 +35,6 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBM = 64;  // query rows per block (four 16-query M-blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 
-// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate. Lane l holds
-// row l%16 of A and column l%16 of B, k-slots 8*(l/16)..+7; accumulator
-// element i of lane l is row 4*(l/16) + i, column l%16.
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[j] = (bf16)x[j];
-    r[4 + j] = (bf16)y[j];
-  }
-  return r;
-}
-
 template <int D>
 struct BwdSmem {
   static constexpr int P = D + 16;     // Q / dO row pitch (bf16)

@@ -7,20 +7,21 @@
 // comm type" (body: the mask is the cp_size = 1 mask). Both DUAL_CHUNK_SWAP
 // chunks of a document are separate query tiles of this one launch.
 //
-// gfx950 design: a workgroup of 4 waves owns up to 128 consecutive query rows
-// of one (document piece, head); each wave owns 32 query rows. Keys are walked
+// gfx950 design: a workgroup of 8 waves owns up to 128 consecutive query rows
+// of one (document piece, head); each wave owns 16 query rows. Keys are walked
 // from the document start in 64-key tiles, double-buffered in LDS (row-major
 // K and V); the next tile's global loads are issued before the current tile's
 // MFMAs so their latency hides behind compute, and one barrier per tile
 // suffices. Everything is computed in the transposed form
 //   S^T = K Q^T  and  O^T = V^T P^T
-// with v_mfma_f32_32x32x16_bf16, so every lane owns one query column of the
-// accumulators: the online-softmax max/sum/rescale are lane-local apart from
-// one exchange with the lane 32 away, and P feeds the second product with no
-// data movement. V^T operands come from the row-major V tile through the
-// transposing LDS read. Only tiles on the causal diagonal apply a per-element
-// mask; key rows past the last attended key are zeroed when staged, so padding
-// rows never enter a product (NaN-safe).
+// with v_mfma_f32_16x16x32_bf16: lane l owns query column l%16 and keys
+// 4*(l/16) + i of each 16-key block, so the online-softmax max/sum need two
+// exchanges across the four 16-lane groups and the rescale is lane-local; P
+// feeds the second product with no data movement. V^T operands come from the
+// row-major V tile through the transposing LDS read. 16-query waves keep the
+// state near 100 registers, so up to four waves share a SIMD. Only tiles on
+// the causal diagonal apply a per-element mask; key rows past the last
+// attended key are zeroed when staged, so padding never enters a product.
 #include "device_common.h"
 #include "internal.h"
 
@@ -28,7 +29,7 @@ namespace thdcp {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -48,11 +49,12 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
                 const bf16* __restrict__ k, const bf16* __restrict__ v, bf16* __restrict__ o,
                 float* __restrict__ lse, int64_t n_local, float scale_log2) {
   constexpr int BN = kFwdBN;
-  constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;      // 32-wide blocks of the head dim
+  constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
+  constexpr int NB = D / 16;   // 16-wide blocks of the head dim
+  constexpr int KB = BN / 16;  // 16-key blocks per tile
   constexpr int P = FwdSmem<D>::P;
-  constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  constexpr int CH = BN * CPR / kThreads;       // chunks per thread per tile and tensor
+  constexpr int CPR = D / 8;
+  constexpr int CH = BN * CPR / kThreads;
   __shared__ FwdSmem<D> sm;
 
   const int tile_id = blockIdx.x / H;
@@ -60,45 +62,40 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const FwdTile t = tiles[tile_id];
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int li = lane & 31;   // query column of this lane (and row index of A operands)
-  const int hh = lane >> 5;   // which half of the wave
-  const int sl = lane & 15;   // lane within its 16-lane group (transposing reads)
-  const int g16 = lane >> 4;  // 16-lane group
-  const int64_t rs = (int64_t)H * D;  // row stride in elements
+  const int l16 = lane & 15;  // query column of this lane (and row of A operands)
+  const int G = lane >> 4;    // 16-lane group
+  const int64_t rs = (int64_t)H * D;
+  const int64_t head_off = (int64_t)h * D;
 
-  const int r = w * 32 + li;
+  const int r = w * 16 + l16;
   const bool in_tile = r < t.n;
   const int g = t.g0 + r;
   const bool valid = in_tile && g < t.e;
   const int64_t m = (int64_t)t.m0 + r;
-  const int my_g = valid ? g : -1;   // key j is allowed iff j <= my_g (keys start at t.a >= 0)
+  const int my_g = valid ? g : -1;   // key j is allowed iff j <= my_g
 
-  // Q fragment (B operand of S^T): query li, head dims kk*16 + hh*8 .. +7
-  bf16x8 qf[KSTEPS];
+  // Q fragment (B operand of S^T): query l16, head dims kk*32 + G*8 .. +7
+  bf16x8 qf[KS];
   {
-    const bf16* qp = q + m * rs + (int64_t)h * D + hh * 8;
+    const bf16* qp = q + m * rs + head_off + G * 8;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = valid ? load_bf16x8(qp + kk * 16) : zero_bf16x8();
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = valid ? load_bf16x8(qp + kk * 32) : zero_bf16x8();
   }
 
-  f32x16 oacc[DB];
+  f32x4 oacc[NB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    for (int i = 0; i < 4; ++i) oacc[nb][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Wave-level bounds: the last key any row of this wave attends, and the
-  // first row's global index (every key <= it is visible to all real rows).
-  const int wrow_last = min(w * 32 + 31, t.n - 1);
-  const bool wave_has_rows = (w * 32 < t.n) && (t.g0 + w * 32 < t.e);
+  const int wrow_last = min(w * 16 + 15, t.n - 1);
+  const bool wave_has_rows = (w * 16 < t.n) && (t.g0 + w * 16 < t.e);
   const int wave_kmax = wave_uniform(wave_has_rows ? min(t.g0 + wrow_last, t.e - 1) : -1);
-  const int wave_gmin = wave_uniform(t.g0 + w * 32);
+  const int wave_gmin = wave_uniform(t.g0 + w * 16);
   const bool wave_all_valid =
-      wave_uniform((w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e)) != 0;
+      wave_uniform((w * 16 + 15 < t.n) && (t.g0 + w * 16 + 15 < t.e)) != 0;
 
-  // Staging: thread handles chunks c = threadIdx.x + j*kThreads of the tile.
-  const int64_t head_off = (int64_t)h * D;
   bf16x8 kreg[CH], vreg[CH];
   auto load_tile = [&](int k0) {
 #pragma unroll
@@ -135,75 +132,76 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     if (has_next) load_tile(k0 + BN);  // in flight during this tile's compute
 
     if (k0 <= wave_kmax) {
-      // S^T (keys x queries) for the two 32-key halves of the tile.
-      f32x16 s[2];
+      // S^T (keys x queries), one 16x16 accumulator per 16-key block.
+      f32x4 s[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-        const bf16* kp = &sm.k[cur][(kb * 32 + li) * P + hh * 8];
+        for (int i = 0; i < 4; ++i) s[kb][i] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) s[kb] = mfma32(load_bf16x8(kp + kk * 16), qf[kk], s[kb]);
-      }
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          s[kb] = mfma16(load_bf16x8(&sm.k[cur][(kb * 16 + l16) * P + kk * 32 + G * 8]), qf[kk], s[kb]);
 
       // Causal / padding mask, only where some key may exceed some row's g.
       if (!wave_all_valid || k0 + BN - 1 > wave_gmin) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + kb * 16 + G * 4 + i;
             if (key > my_g) s[kb][i] = -INFINITY;
           }
       }
 
-      // Online softmax in the log2 domain (scale * log2(e) folded in).
+      // Online softmax in the log2 domain; the four 16-lane groups hold
+      // different keys of the same queries.
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, shfl_xor32(mx));
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx * scale_log2);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
       float psum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
           s[kb][i] = p;
           psum += p;
         }
-      psum += shfl_xor32(psum);
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
       l_run = l_run * alpha + psum;
       m_run = m_new;
       if (!__all(alpha == 1.f)) {  // rescale only when some row's max moved
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+          for (int i = 0; i < 4; ++i) oacc[nb][i] *= alpha;
       }
 
-      // O^T += V^T P^T. k-step (kb, u) covers 16 keys; slot j of this lane is
-      // key kb*32 + 16u + (j/4)*8 + hh*4 + j%4 -- exactly accumulator entries
-      // u*8 .. u*8+7 of s[kb], so P needs no data movement. The V^T operand
-      // (lane = head dim, slots = those keys) is two transposing reads of the
-      // row-major V tile: rows kb*32+16u+hh*4+{0..3} and the same +8.
+      // O^T += V^T P^T. k-step ks covers key blocks 2ks, 2ks+1: slot j of this
+      // lane is key (2ks + j/4)*16 + 4*G + j%4 -- accumulator entries of
+      // s[2ks], s[2ks+1]. The V^T operand (lane = head dim, slots = those
+      // keys) is two transposing reads of the row-major V tile.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < KB / 2; ++ks) {
+        const bf16x8 pb = pack8(s[2 * ks], s[2 * ks + 1]);
+        const int o1 = (2 * ks * 16 + G * 4 + (l16 >> 2)) * P + 4 * (l16 & 3);
+        const int o2 = o1 + 16 * P;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 pb = to_bf16x8(s[kb], u * 8);
-          const bf16* vb = &sm.v[cur][(kb * 32 + 16 * u + hh * 4 + (sl >> 2)) * P +
-                                      16 * (g16 & 1) + 4 * (sl & 3)];
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 a = concat4(lds_read_tr4(vb + db * 32), lds_read_tr4(vb + db * 32 + 8 * P));
-            oacc[db] = mfma32(a, pb, oacc[db]);
-          }
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 a = concat4(lds_read_tr4(&sm.v[cur][o1 + nb * 16]), lds_read_tr4(&sm.v[cur][o2 + nb * 16]));
+          oacc[nb] = mfma16(a, pb, oacc[nb]);
         }
+      }
     }
 
     if (has_next) store_tile(cur ^ 1);
@@ -214,16 +212,14 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   bf16* op = o + m * rs + head_off;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int nb = 0; nb < NB; ++nb) {
+    // accumulator rows (head dims) nb*16 + 4*G + 0..3 of query l16
+    bf16x4 out;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      // accumulator rows (head dims) db*32 + i4*8 + hh*4 + 0..3 of query li
-      bf16x4 out;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) out[j] = (bf16)(oacc[db][i4 * 4 + j] * inv);
-      store_bf16x4(op + db * 32 + i4 * 8 + hh * 4, out);
-    }
-  if (hh == 0) {
+    for (int j = 0; j < 4; ++j) out[j] = (bf16)(oacc[nb][j] * inv);
+    store_bf16x4(op + nb * 16 + G * 4, out);
+  }
+  if (G == 0) {
     lse[(int64_t)h * n_local + m] =
         (valid && l_run > 0.f) ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
   }

@@ -23,6 +23,24 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate. Lane l holds
+// row l%16 of A and column l%16 of B, k-slots 8*(l/16)..+7; accumulator
+// element i of lane l is row 4*(l/16) + i, column l%16.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Round two 16x16 accumulators' entries (4 each) to one bf16x8 operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = (bf16)x[j];
+    r[4 + j] = (bf16)y[j];
+  }
+  return r;
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return __builtin_bit_cast(bf16x8, z);
