@@ -11,10 +11,12 @@ A step is one pass of the whole hot path for the measured rank over one batch:
 Inputs are synthetic and already resident in HBM when timing starts.
 
 value = 14 * D * H * causal_pairs / step time (TFLOP/s; causal-masked FLOPs
-only). The roofline object is for the dominant kernel, the backward dK/dV
-kernel (8 * D * H * pairs algorithmic FLOPs: S, dP, dV, dK), timed with HIP
-events on the stream it runs on; the dQ kernel, the forward and the K/V
-restore (gather roofline) are reported beside it.
+only), the steps timed with no events inside. The roofline object is for the
+dominant kernel, the backward dK/dV kernel (8 * D * H * pairs algorithmic
+FLOPs: S, dP, dV, dK); its duration is measured live with HIP events on the
+stream it runs on, around back-to-back launches on the same inputs right after
+the timed steps. The dQ kernel, the forward and the K/V restore (gather
+roofline) are reported beside it.
 
     python bench.py [--steps K] [--warmup W] [--workload dcs_8k] [--no-cpu-baseline]
 """
@@ -109,39 +111,22 @@ def main():
     pairs = int(probe.info.causal_pairs)
     probe.close()
 
-    ev = {}
-
-    def step(record: bool):
-        def mark(name):
-            if record:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record(stream)
-                ev.setdefault(name, []).append(e)
-
+    def step():
         plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False)
         plan.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
         thd.gather_many([q, do], mine, [q_local, do_local])
-        mark("restore0")
         thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g])
-        mark("restore1")
-        mark("fwd0")
         thd.attn_fwd(plan, q_local, k_g, v_g, o=o, lse=lse)
-        mark("fwd1")
-        pairs_ev = None
-        if record:
-            pairs_ev = {n: (torch.cuda.Event(enable_timing=True),
-                            torch.cuda.Event(enable_timing=True)) for n in ("dkdv", "dq")}
-            for n, pr in pairs_ev.items():
-                ev.setdefault(n, []).append(pr)
         thd.attn_bwd_parts(plan, q_local, k_g, v_g, o, lse, do_local, dq, dk, dv, scratch,
-                           zero_untouched=True, events=pairs_ev)
+                           zero_untouched=True)
         thd.gather_many([dk, dv], perm, [dk_rm, dv_rm])
         return plan  # keep alive until the stream is synchronized
 
+    # Whole steps: no events inside the timed region.
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     plans = []
     t_start = torch.cuda.Event(enable_timing=True)
@@ -149,21 +134,42 @@ def main():
     t_start.record(stream)
     wall0 = time.perf_counter()
     for _ in range(args.steps):
-        plans.append(step(True))
+        plans.append(step())
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     plans.clear()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    def avg(a, b):
-        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+    # Per-kernel durations, live on the same stream and inputs: events around
+    # REPS back-to-back launches of one kernel, so the events' own cost is
+    # amortized. Each launch recomputes the same outputs.
+    plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False)
+    plan.upload_into(ws, stream)
+    reps = max(5, min(50, int(20.0 / max(ms_step, 1e-3))))
 
-    t_fwd = avg("fwd0", "fwd1")
-    t_dkdv = float(np.mean([x.elapsed_time(y) for x, y in ev["dkdv"]]))
-    t_dq = float(np.mean([x.elapsed_time(y) for x, y in ev["dq"]]))
+    def timed(fn):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    L = thd.lib()
+    pargs = (thd._dev_ptr(q_local, "q"), thd._dev_ptr(k_g, "k"), thd._dev_ptr(v_g, "v"),
+             thd._dev_ptr(lse, "lse"), thd._dev_ptr(do_local, "do"))
+    sp, sn, st = thd._dev_ptr(scratch, "scratch"), scratch.numel(), thd._stream(stream)
+    t_restore = timed(lambda: thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g]))
+    t_fwd = timed(lambda: thd.attn_fwd(plan, q_local, k_g, v_g, o=o, lse=lse))
+    t_dkdv = timed(lambda: thd._check(L.cp_attn_bwd_dkdv(
+        plan.handle, *pargs, thd._dev_ptr(dk, "dk"), thd._dev_ptr(dv, "dv"), 0, sp, sn, st)))
+    t_dq = timed(lambda: thd._check(L.cp_attn_bwd_dq(
+        plan.handle, *pargs, thd._dev_ptr(dq, "dq"), sp, sn, st)))
     t_bwd = t_dkdv + t_dq
-    t_restore = avg("restore0", "restore1")
 
     flop_fwd = 4.0 * D * H * pairs      # QK^T, PV
     flop_bwd = 10.0 * D * H * pairs     # S, dP, dV, dK, dQ
@@ -227,7 +233,8 @@ def main():
                      "kv_restore": round(t_restore, 4),
                      "attn_kernels_tflops": round(
                          (flop_fwd + flop_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
-                     "host_wall_per_step": round(wall / args.steps * 1e3, 4)},
+                     "host_wall_per_step": round(wall / args.steps * 1e3, 4),
+                     "kernel_reps": reps},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, t)
