@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dcs_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-a2a", action="store_true",
+                    help="skip the all-to-all layout measurement (flat vs dual-chunk)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 --pmc (optional)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -236,9 +238,97 @@ def main():
                      "host_wall_per_step": round(wall / args.steps * 1e3, 4),
                      "kernel_reps": reps},
     }
+    if not args.no_a2a:
+        result["a2a_layout"] = a2a_layout(stream)
+        if w.name == "flat_75k":
+            # the gather this workload is quoted on: the dual-chunk reorder of
+            # q, k and v that flat sharding removes (s = 75600, cp = 8)
+            row = result["a2a_layout"]["s75600"]
+            result["roofline_gather"] = {
+                "bound": "hbm", "kernel": "move_rows_kernel (q, k, v dual-chunk reorder, one launch)",
+                "achieved": row["reorder_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(row["reorder_gbs"] / PEAK_HBM_GBS, 4), "bytes": row["reorder_bytes"]}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, t)
     print(json.dumps(result), flush=True)
+
+
+def a2a_layout(stream, seqlens=(8192, 32768, 75600), cp=8, heads=40, head_dim=128):
+    """Local layout work of one before-attention all-to-all of q, k and v and
+    of the return exchange of O, for bshd with batch 1 (one document), cp=8,
+    h=40, d=128: the head-group pack every rank does before sending, and the
+    dual-chunk reorder of the received sequence that flat sharding removes.
+    The exchange itself (RCCL over xGMI) is not part of a one-GPU run.
+
+    Every launch is timed cold: launches rotate over enough independent
+    buffer sets that the 256 MB last-level cache holds none of them."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import context_causal_attention_thd_amd as thd
+    dev = torch.device("cuda", 0)
+    hl = heads // cp
+    out = {"config": {"layout": "bshd, batch 1", "cp_size": cp, "heads": heads,
+                      "head_dim": head_dim, "tensors_before_attn": "q, k, v",
+                      "tensors_after_attn": "o", "timing": "cold, rotated buffer sets"}}
+    for s in seqlens:
+        s_local = s // cp
+        per_tensor = s_local * heads * head_dim * 2          # == s * hl * head_dim * 2
+        sets = max(1, math.ceil((1536 << 20) / (12 * per_tensor)))
+        cup = np.array([0, s], dtype=np.int32)
+        cup_dev = torch.from_numpy(cup).to(dev)
+        perm = thd.partition_index(cup, cup_dev, s, cp, -1, "dual_chunk_swap")
+        bufs = []
+        for _ in range(sets):
+            shard = [torch.randn((s_local, heads, head_dim), device=dev).to(torch.bfloat16)
+                     for _ in range(3)]
+            packed = [torch.empty((cp, s_local, hl, head_dim), dtype=torch.bfloat16, device=dev)
+                      for _ in range(3)]
+            recv = [torch.randn((s, hl, head_dim), device=dev).to(torch.bfloat16)
+                    for _ in range(3)]
+            glob = [torch.empty_like(x) for x in recv]
+            bufs.append((shard, packed, recv, glob))
+        torch.cuda.synchronize()
+        reps = max(2 * sets, 20)
+
+        def timed(fn):
+            for i in range(sets):
+                fn(bufs[i])
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                fn(bufs[i % sets])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        t_pack = timed(lambda b: thd.a2a_pack(b[0], cp, outs=b[1]))
+        t_reorder = timed(lambda b: thd.scatter_many(b[2], perm, b[3]))
+        # return direction, O only: rank-major gather (dual-chunk only), unpack
+        t_unorder = timed(lambda b: thd.gather_many(b[3][:1], perm, b[2][:1]))
+        t_unpack = timed(lambda b: thd.a2a_unpack(
+            [b[1][0]], outs=[b[0][0]]))
+        pack_bytes = 3 * 2 * per_tensor
+        reorder_bytes = 3 * (2 * per_tensor + 4 * s)
+        out[f"s{s}"] = {
+            "pack_ms": round(t_pack, 4),
+            "pack_gbs": round(pack_bytes / (t_pack * 1e-3) / 1e9, 1),
+            "reorder_ms": round(t_reorder, 4),
+            "reorder_gbs": round(reorder_bytes / (t_reorder * 1e-3) / 1e9, 1),
+            "reorder_bytes": reorder_bytes,
+            "before_attn_flat_ms": round(t_pack, 4),
+            "before_attn_dual_chunk_ms": round(t_pack + t_reorder, 4),
+            "before_attn_local_saving": round(t_reorder / (t_pack + t_reorder), 4),
+            "after_attn_flat_ms": round(t_unpack, 4),
+            "after_attn_dual_chunk_ms": round(t_unpack + t_unorder, 4),
+            "buffer_sets": sets,
+        }
+        del bufs
+        torch.cuda.empty_cache()
+    return out
 
 
 def _kernel_hash() -> str:

@@ -23,7 +23,8 @@ _STRATEGY_NAMES = {"dual_chunk_swap": DUAL_CHUNK_SWAP, "no_load_balance": NO_LOA
 
 EXPORTED_SYMBOLS = (
     "thdcp_last_error", "thdcp_version", "thdcp_validate", "thd_partition_index", "thd_gather",
-    "thd_scatter", "thd_gather_batched", "thd_scatter_batched", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
+    "thd_scatter", "thd_gather_batched", "thd_scatter_batched", "thd_a2a_pack",
+    "thd_a2a_unpack", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
     "thdcp_plan_upload", "thdcp_plan_destroy", "cp_attn_fwd", "cp_attn_bwd",
     "cp_attn_bwd_preprocess", "cp_attn_bwd_dkdv", "cp_attn_bwd_dq", "thdcp_zero_untouched",
 )
@@ -98,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.thd_gather_batched.argtypes = [i32, pvp, i64, vp, i64, i64, pvp, vp]
     L.thd_scatter_batched.restype = i32
     L.thd_scatter_batched.argtypes = [i32, pvp, i64, vp, i64, pvp, i64, vp]
+    for name in ("thd_a2a_pack", "thd_a2a_unpack"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = [i32, pvp, i64, i32, i64, pvp, vp]
     L.thdcp_plan_create.restype = i32
     L.thdcp_plan_create.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(vp)]
     L.thdcp_plan_get_info.restype = i32
@@ -265,6 +269,45 @@ def scatter_many(srcs, idx, outs, stream=None):
     _check(lib().thd_scatter_batched(len(srcs), _ptr_list(srcs, "src"), srcs[0].shape[0],
                                      _dev_ptr(idx, "idx", torch.int32), rb,
                                      _ptr_list(outs, "out"), outs[0].shape[0], _stream(stream)))
+    return outs
+
+
+def a2a_pack(srcs, cp_size: int, outs=None, stream=None):
+    """Head-group pack before the all-to-all: each src [n, H, ...] becomes
+    [cp_size, n, H // cp_size, ...] with block c = head group c of every token
+    (the send buffer for rank c). 1..4 same-shaped tensors, one launch."""
+    import torch
+    n, H = srcs[0].shape[0], srcs[0].shape[1]
+    if H % cp_size != 0:
+        raise ValueError(f"heads ({H}) not divisible by cp_size ({cp_size})")
+    shape = (cp_size, n, H // cp_size) + tuple(srcs[0].shape[2:])
+    if any(tuple(x.shape) != tuple(srcs[0].shape) or x.dtype != srcs[0].dtype for x in srcs):
+        raise ValueError("all sources must have the same shape and dtype")
+    if outs is None:
+        outs = [torch.empty(shape, dtype=x.dtype, device=x.device) for x in srcs]
+    if any(tuple(o.shape) != shape or o.dtype != srcs[0].dtype for o in outs):
+        raise ValueError(f"outputs must be {shape}")
+    gb = (_row_bytes(srcs[0]) // cp_size) if n > 0 else 1
+    _check(lib().thd_a2a_pack(len(srcs), _ptr_list(srcs, "src"), n, cp_size, gb,
+                              _ptr_list(outs, "out"), _stream(stream)))
+    return outs
+
+
+def a2a_unpack(srcs, outs=None, stream=None):
+    """Inverse of a2a_pack: each src [cp, n, Hl, ...] (block c = head group c
+    received from rank c) becomes [n, cp * Hl, ...]."""
+    import torch
+    cp, n, Hl = srcs[0].shape[0], srcs[0].shape[1], srcs[0].shape[2]
+    shape = (n, cp * Hl) + tuple(srcs[0].shape[3:])
+    if any(tuple(x.shape) != tuple(srcs[0].shape) or x.dtype != srcs[0].dtype for x in srcs):
+        raise ValueError("all sources must have the same shape and dtype")
+    if outs is None:
+        outs = [torch.empty(shape, dtype=x.dtype, device=x.device) for x in srcs]
+    if any(tuple(o.shape) != shape or o.dtype != srcs[0].dtype for o in outs):
+        raise ValueError(f"outputs must be {shape}")
+    gb = int(np.prod(srcs[0].shape[2:])) * srcs[0].element_size()
+    _check(lib().thd_a2a_unpack(len(srcs), _ptr_list(srcs, "src"), n, cp, max(gb, 1),
+                                _ptr_list(outs, "out"), _stream(stream)))
     return outs
 
 

@@ -340,9 +340,16 @@ thdcp_status_t thd_scatter(const void* src, int64_t n, const int32_t* idx, int64
 }
 
 namespace {
-thdcp_status_t check_batch(int32_t n_tensors, const void* const* srcs, void* const* dsts) {
+// Pointer lists are only checked when there is something to move: an empty
+// move (no rows) succeeds whatever the pointers are.
+thdcp_status_t check_count(int32_t n_tensors) {
   if (n_tensors < 1 || n_tensors > kMaxMoveTensors)
     return fail(THDCP_ERR_ARG, "n_tensors must be in [1, %d]", kMaxMoveTensors);
+  return ok();
+}
+
+thdcp_status_t check_batch(int32_t n_tensors, const void* const* srcs, void* const* dsts) {
+  if (check_count(n_tensors) != THDCP_OK) return THDCP_ERR_ARG;
   if (!srcs || !dsts) return fail(THDCP_ERR_ARG, "NULL pointer list");
   for (int32_t i = 0; i < n_tensors; ++i)
     if (!srcs[i] || !dsts[i]) return fail(THDCP_ERR_ARG, "NULL device pointer in list");
@@ -354,9 +361,10 @@ thdcp_status_t thd_gather_batched(int32_t n_tensors, const void* const* srcs, in
                                   const int32_t* idx, int64_t n, int64_t row_bytes,
                                   void* const* dsts, void* stream) {
   if (n < 0 || n_src < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
+  if (check_count(n_tensors) != THDCP_OK) return THDCP_ERR_ARG;
+  if (n == 0) return ok();
   thdcp_status_t st = check_batch(n_tensors, srcs, dsts);
   if (st != THDCP_OK) return st;
-  if (n == 0) return ok();
   if (!idx) return fail(THDCP_ERR_ARG, "NULL index pointer");
   return hip_status(launch_gather(n_tensors, srcs, n_src, idx, n, row_bytes, dsts,
                                   (hipStream_t)stream),
@@ -367,13 +375,45 @@ thdcp_status_t thd_scatter_batched(int32_t n_tensors, const void* const* srcs, i
                                    const int32_t* idx, int64_t row_bytes, void* const* dsts,
                                    int64_t n_dst, void* stream) {
   if (n < 0 || n_dst < 0 || row_bytes <= 0) return fail(THDCP_ERR_ARG, "bad sizes");
+  if (check_count(n_tensors) != THDCP_OK) return THDCP_ERR_ARG;
+  if (n == 0) return ok();
   thdcp_status_t st = check_batch(n_tensors, srcs, dsts);
   if (st != THDCP_OK) return st;
-  if (n == 0) return ok();
   if (!idx) return fail(THDCP_ERR_ARG, "NULL index pointer");
   return hip_status(launch_scatter(n_tensors, srcs, n, idx, row_bytes, dsts, n_dst,
                                    (hipStream_t)stream),
                     "thd_scatter launch");
+}
+
+namespace {
+thdcp_status_t a2a_move(int32_t n_tensors, const void* const* srcs, int64_t n_tokens,
+                        int32_t cp_size, int64_t group_bytes, void* const* dsts, bool unpack,
+                        void* stream) {
+  if (n_tokens < 0 || cp_size < 1 || group_bytes <= 0)
+    return fail(THDCP_ERR_ARG, "bad sizes (n_tokens %lld, cp_size %d, group_bytes %lld)",
+                (long long)n_tokens, cp_size, (long long)group_bytes);
+  if (n_tokens * (int64_t)cp_size > INT32_MAX)
+    return fail(THDCP_ERR_ARG, "n_tokens * cp_size exceeds int32");
+  if (check_count(n_tensors) != THDCP_OK) return THDCP_ERR_ARG;
+  if (n_tokens == 0) return ok();
+  thdcp_status_t st = check_batch(n_tensors, srcs, dsts);
+  if (st != THDCP_OK) return st;
+  return hip_status(launch_a2a(n_tensors, srcs, n_tokens, cp_size, group_bytes, dsts, unpack,
+                               (hipStream_t)stream),
+                    unpack ? "thd_a2a_unpack launch" : "thd_a2a_pack launch");
+}
+}  // namespace
+
+thdcp_status_t thd_a2a_pack(int32_t n_tensors, const void* const* srcs, int64_t n_tokens,
+                            int32_t cp_size, int64_t group_bytes, void* const* dsts,
+                            void* stream) {
+  return a2a_move(n_tensors, srcs, n_tokens, cp_size, group_bytes, dsts, false, stream);
+}
+
+thdcp_status_t thd_a2a_unpack(int32_t n_tensors, const void* const* srcs, int64_t n_tokens,
+                              int32_t cp_size, int64_t group_bytes, void* const* dsts,
+                              void* stream) {
+  return a2a_move(n_tensors, srcs, n_tokens, cp_size, group_bytes, dsts, true, stream);
 }
 
 thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan_out) {

@@ -58,6 +58,9 @@ hipError_t launch_gather(int32_t n_tensors, const void* const* srcs, int64_t n_s
 hipError_t launch_scatter(int32_t n_tensors, const void* const* srcs, int64_t n,
                           const int32_t* idx, int64_t row_bytes, void* const* dsts,
                           int64_t n_dst, hipStream_t stream);
+// Head-group pack ([n, cp, G] -> [cp, n, G]) or its inverse, G = group_bytes.
+hipError_t launch_a2a(int32_t n_tensors, const void* const* srcs, int64_t n_tokens, int32_t cp,
+                      int64_t group_bytes, void* const* dsts, bool unpack, hipStream_t stream);
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
                             int64_t row_floats, float* a, float* b, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,

@@ -2,6 +2,8 @@
 //   partition index ("[PyTorch] Add no-load-balance THD all-gather CP",
 //   "What changed" and "Why"), row gather / scatter (the rank slicing of its
 //   "How to use" and the K/V restore / dK-dV unrestore of its sequence
+//   diagram), the head-group pack / unpack around the all-to-all exchange
+//   ("[PyTorch] Extend no-load-balance CP to the a2a comm type", body and
 //   diagram), the gated zeroing of untouched gradient rows ("THD P2P
 //   context-parallel regression ...", "Expected behavior") and the backward
 //   preprocess delta = rowsum(dO * O).
@@ -78,11 +80,26 @@ struct RowPtrs {
   char* dst[kMaxMoveTensors];
 };
 
-// SCATTER = false: dst[m] = src[idx[m]]; true: dst[idx[m]] = src[m].
-template <int VB, bool SCATTER>
+// Which row of src feeds which row of dst. The index modes read an int32
+// table; the a2a modes compute the row from (n, cp) and read no table.
+enum MoveMode : int {
+  kGather = 0,   // dst[m] = src[idx[m]]; idx outside [0, n_other) gives a zero row
+  kScatter = 1,  // dst[idx[m]] = src[m]; idx outside [0, n_other) is skipped
+  kPack = 2,     // dst[c*n + m] = src[m*cp + c]  ([n, cp, G] -> [cp, n, G])
+  kUnpack = 3,   // dst[m*cp + c] = src[c*n + m]  ([cp, n, G] -> [n, cp, G])
+};
+
+struct RowMap {
+  const int32_t* idx;
+  int64_t n_other;  // index modes: rows of the indexed tensor
+  int64_t n;        // a2a modes: tokens per group
+  int64_t cp;       // a2a modes: groups
+};
+
+template <int VB, int MODE>
 __global__ void __launch_bounds__(kRowThreads) move_rows_kernel(
-    const RowPtrs ptrs, const int32_t* __restrict__ idx, uint32_t chunks_per_row,
-    uint64_t total_chunks, int64_t n_other, int64_t row_bytes) {
+    const RowPtrs ptrs, const RowMap map, uint32_t chunks_per_row, uint64_t total_chunks,
+    int64_t row_bytes) {
   typedef typename Vec<VB>::T V;
   const char* __restrict__ src = ptrs.src[blockIdx.y];
   char* __restrict__ dst = ptrs.dst[blockIdx.y];
@@ -99,12 +116,25 @@ __global__ void __launch_bounds__(kRowThreads) move_rows_kernel(
       if (t < total_chunks) {
         const uint64_t row = t / chunks_per_row;
         const uint32_t c = (uint32_t)(t - row * chunks_per_row);
-        const int64_t other = idx[row];
-        const bool in = other >= 0 && other < n_other;
-        const int64_t srow = SCATTER ? (int64_t)row : other;
-        drow[u] = SCATTER ? (in ? other : -1) : (int64_t)row;
+        int64_t srow;
+        bool load = true;
+        if (MODE == kGather || MODE == kScatter) {
+          const int64_t other = map.idx[row];
+          const bool in = other >= 0 && other < map.n_other;
+          srow = MODE == kScatter ? (int64_t)row : other;
+          drow[u] = MODE == kScatter ? (in ? other : -1) : (int64_t)row;
+          load = MODE == kScatter || in;
+        } else if (MODE == kPack) {
+          const int64_t grp = (int64_t)row / map.n;
+          srow = ((int64_t)row - grp * map.n) * map.cp + grp;
+          drow[u] = (int64_t)row;
+        } else {
+          const int64_t tok = (int64_t)row / map.cp;
+          srow = ((int64_t)row - tok * map.cp) * map.n + tok;
+          drow[u] = (int64_t)row;
+        }
         dchunk[u] = c;
-        if (SCATTER || in) {
+        if (load) {
           val[u] = __builtin_nontemporal_load(
               reinterpret_cast<const V*>(src + srow * row_bytes + (int64_t)c * VB));
         } else {
@@ -122,10 +152,11 @@ __global__ void __launch_bounds__(kRowThreads) move_rows_kernel(
   }
 }
 
-template <bool SCATTER>
-hipError_t launch_move(int32_t n_tensors, const void* const* srcs, const int32_t* idx,
-                       void* const* dsts, int64_t n, int64_t n_other, int64_t row_bytes,
-                       hipStream_t stream) {
+// n: rows the launch walks (dst rows for gather / pack / unpack, src rows for
+// scatter).
+template <int MODE>
+hipError_t launch_move(int32_t n_tensors, const void* const* srcs, void* const* dsts,
+                       const RowMap& map, int64_t n, int64_t row_bytes, hipStream_t stream) {
   if (n_tensors < 1 || n_tensors > kMaxMoveTensors) return hipErrorInvalidValue;
   RowPtrs ptrs{};
   uintptr_t addr_bits = 0;
@@ -141,15 +172,16 @@ hipError_t launch_move(int32_t n_tensors, const void* const* srcs, const int32_t
   const uint64_t cpr = (uint64_t)(row_bytes / vb);
   const uint64_t total = cpr * (uint64_t)n;
   if (cpr > 0xffffffffull) return hipErrorInvalidValue;
+  if (total == 0) return hipSuccess;
   uint64_t blocks = (total + kRowThreads * kRowUnroll - 1) / (kRowThreads * kRowUnroll);
   if (blocks > 65536) blocks = 65536;
   const dim3 grid((unsigned)blocks, (unsigned)n_tensors), block(kRowThreads);
   switch (vb) {
-    case 16: hipLaunchKernelGGL((move_rows_kernel<16, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
-    case 8:  hipLaunchKernelGGL((move_rows_kernel<8, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
-    case 4:  hipLaunchKernelGGL((move_rows_kernel<4, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
-    case 2:  hipLaunchKernelGGL((move_rows_kernel<2, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
-    default: hipLaunchKernelGGL((move_rows_kernel<1, SCATTER>), grid, block, 0, stream, ptrs, idx, (uint32_t)cpr, total, n_other, row_bytes); break;
+    case 16: hipLaunchKernelGGL((move_rows_kernel<16, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
+    case 8:  hipLaunchKernelGGL((move_rows_kernel<8, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
+    case 4:  hipLaunchKernelGGL((move_rows_kernel<4, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
+    case 2:  hipLaunchKernelGGL((move_rows_kernel<2, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
+    default: hipLaunchKernelGGL((move_rows_kernel<1, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
   }
   return hipGetLastError();
 }
@@ -157,13 +189,23 @@ hipError_t launch_move(int32_t n_tensors, const void* const* srcs, const int32_t
 hipError_t launch_gather(int32_t n_tensors, const void* const* srcs, int64_t n_src,
                          const int32_t* idx, int64_t n, int64_t row_bytes, void* const* dsts,
                          hipStream_t stream) {
-  return launch_move<false>(n_tensors, srcs, idx, dsts, n, n_src, row_bytes, stream);
+  const RowMap map{idx, n_src, 0, 1};
+  return launch_move<kGather>(n_tensors, srcs, dsts, map, n, row_bytes, stream);
 }
 
 hipError_t launch_scatter(int32_t n_tensors, const void* const* srcs, int64_t n,
                           const int32_t* idx, int64_t row_bytes, void* const* dsts,
                           int64_t n_dst, hipStream_t stream) {
-  return launch_move<true>(n_tensors, srcs, idx, dsts, n, n_dst, row_bytes, stream);
+  const RowMap map{idx, n_dst, 0, 1};
+  return launch_move<kScatter>(n_tensors, srcs, dsts, map, n, row_bytes, stream);
+}
+
+hipError_t launch_a2a(int32_t n_tensors, const void* const* srcs, int64_t n_tokens, int32_t cp,
+                      int64_t group_bytes, void* const* dsts, bool unpack, hipStream_t stream) {
+  const RowMap map{nullptr, 0, n_tokens, cp};
+  const int64_t rows = n_tokens * cp;
+  return unpack ? launch_move<kUnpack>(n_tensors, srcs, dsts, map, rows, group_bytes, stream)
+                : launch_move<kPack>(n_tensors, srcs, dsts, map, rows, group_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

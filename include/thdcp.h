@@ -118,7 +118,8 @@ thdcp_status_t thd_scatter(const void* src_dev, int64_t n, const int32_t* idx_de
  * row count and the row size, in one launch (e.g. the K and V restore, the
  * local Q and dO slices, the dK and dV unrestore). src_list and dst_list are
  * host arrays of n_tensors device pointers; per tensor the behaviour is that
- * of thd_gather / thd_scatter.
+ * of thd_gather / thd_scatter. A move of zero rows (n == 0) succeeds without
+ * looking at the pointers and enqueues nothing.
  */
 thdcp_status_t thd_gather_batched(int32_t n_tensors, const void* const* src_list, int64_t n_src,
                                   const int32_t* idx_dev, int64_t n, int64_t row_bytes,
@@ -126,6 +127,36 @@ thdcp_status_t thd_gather_batched(int32_t n_tensors, const void* const* src_list
 thdcp_status_t thd_scatter_batched(int32_t n_tensors, const void* const* src_list, int64_t n,
                                    const int32_t* idx_dev, int64_t row_bytes,
                                    void* const* dst_list, int64_t n_dst, void* stream);
+
+/*
+ * Local layout work around the all-to-all exchange ([A2A] body and diagram).
+ * Before attention every rank sends head group c of each of its n_tokens
+ * local tokens to rank c; after attention the exchange runs the other way.
+ * Each token row is cp_size equal head groups of group_bytes bytes
+ * (group_bytes = H / cp_size * D * sizeof(element)).
+ *
+ * thd_a2a_pack:   src [n_tokens, cp_size, G] -> dst [cp_size, n_tokens, G],
+ *                 dst[c, m, :] = src[m, c, :]; dst block c is the contiguous
+ *                 send buffer for rank c.
+ * thd_a2a_unpack: src [cp_size, n_tokens, G] -> dst [n_tokens, cp_size, G],
+ *                 dst[m, c, :] = src[c, m, :]; the inverse of the pack (after
+ *                 the return exchange, block c holds head group c).
+ *
+ * Rank-major order after the forward exchange equals global order under
+ * NO_LOAD_BALANCE; under DUAL_CHUNK_SWAP it is restored with
+ * thd_scatter_batched by the all-ranks permutation of thd_partition_index
+ * (rank = -1), and undone after attention with thd_gather_batched by the same
+ * permutation. 1..4 tensors of the same shape move in one launch; src_list and
+ * dst_list are host arrays of device pointers; src and dst must not overlap.
+ * n_tokens * cp_size must be below 2^31; n_tokens == 0 succeeds without
+ * looking at the pointers and enqueues nothing.
+ */
+thdcp_status_t thd_a2a_pack(int32_t n_tensors, const void* const* src_list, int64_t n_tokens,
+                            int32_t cp_size, int64_t group_bytes, void* const* dst_list,
+                            void* stream);
+thdcp_status_t thd_a2a_unpack(int32_t n_tensors, const void* const* src_list, int64_t n_tokens,
+                              int32_t cp_size, int64_t group_bytes, void* const* dst_list,
+                              void* stream);
 
 /* ------------------------------------------------------------------------
  * Rank plan: the THD metadata of one rank ([AG] sequence diagram "partition

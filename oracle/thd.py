@@ -137,8 +137,10 @@ def partition_index(cu_seqlens_padded, T: int, cp_size: int, rank: int,
 
     DUAL_CHUNK_SWAP ([AG] "Why"): every padded document is cut into
     2*cp_size equal chunks; rank r takes chunk r and chunk 2*cp_size-1-r.
+    A layout that breaks the strategy's divisibility rules raises ValueError.
     """
     cup = _as_list(cu_seqlens_padded)
+    check_layout(cup, cup, T, cp_size, rank, strategy)
     if strategy == NO_LOAD_BALANCE:
         s_local = T // cp_size
         return np.arange(rank * s_local, (rank + 1) * s_local, dtype=np.int64)
@@ -206,6 +208,81 @@ def scatter(src: np.ndarray, idx, n_dst: int, fill=0) -> np.ndarray:
     dst = np.full((n_dst,) + src.shape[1:], fill, dtype=src.dtype)
     dst[np.asarray(idx, dtype=np.int64)] = src
     return dst
+
+
+def a2a_pack(x: np.ndarray, cp_size: int) -> np.ndarray:
+    """Split every token's heads into cp_size equal groups and make group c one
+    contiguous block: [n, H, ...] -> [cp_size, n, H / cp_size, ...]. Block c
+    is what this rank sends to rank c in the all-to-all before attention
+    ([A2A] body: after the exchange each rank holds only its own head slice)."""
+    x = np.asarray(x)
+    n, H = x.shape[0], x.shape[1]
+    if H % cp_size != 0:
+        raise ValueError("heads not divisible by cp_size")
+    hl = H // cp_size
+    out = np.empty((cp_size, n, hl) + x.shape[2:], dtype=x.dtype)
+    for c in range(cp_size):
+        for m in range(n):
+            out[c, m] = x[m, c * hl:(c + 1) * hl]
+    return out
+
+
+def a2a_unpack(y: np.ndarray) -> np.ndarray:
+    """Inverse of a2a_pack: block c of [cp, n, Hl, ...] becomes heads
+    c*Hl .. c*Hl+Hl-1 of every token of [n, cp*Hl, ...] (the last step of
+    the [A2A] diagram: local token shard, full heads)."""
+    y = np.asarray(y)
+    cp, n, hl = y.shape[0], y.shape[1], y.shape[2]
+    out = np.empty((n, cp * hl) + y.shape[3:], dtype=y.dtype)
+    for c in range(cp):
+        for m in range(n):
+            out[m, c * hl:(c + 1) * hl] = y[c, m]
+    return out
+
+
+def _all_ranks_index(cu_seqlens_padded, T: int, cp_size: int, strategy: str) -> np.ndarray:
+    return np.concatenate([partition_index(cu_seqlens_padded, T, cp_size, r, strategy)
+                           for r in range(cp_size)]).astype(np.int64)
+
+
+def a2a_before_attn(local_shards, cu_seqlens_padded, T: int, cp_size: int,
+                    strategy: str = DUAL_CHUNK_SWAP):
+    """The forward exchange of [A2A], simulated for all ranks at once.
+
+    local_shards[r] is rank r's [T/cp, H, ...] token shard (its partition, all
+    heads). Each rank packs, the all-to-all hands block c of rank r to rank c
+    (placed at position r of rank c's receive buffer), and the receive buffer
+    is read as one sequence in rank-major order. Under NO_LOAD_BALANCE that is
+    already global order; under DUAL_CHUNK_SWAP the rank-major rows are put
+    back into global order (the reorder that flat sharding removes, [A2A]
+    body). Returns, per rank, the full sequence [T, H/cp, ...] of its head
+    group."""
+    send = [a2a_pack(x, cp_size) for x in local_shards]
+    out = []
+    for r in range(cp_size):
+        rank_major = np.concatenate([send[c][r] for c in range(cp_size)], axis=0)
+        if strategy == NO_LOAD_BALANCE:
+            out.append(rank_major)
+        else:
+            perm = _all_ranks_index(cu_seqlens_padded, T, cp_size, strategy)
+            out.append(scatter(rank_major, perm, T))
+    return out
+
+
+def a2a_after_attn(full_outputs, cu_seqlens_padded, T: int, cp_size: int,
+                   strategy: str = DUAL_CHUNK_SWAP):
+    """The return exchange of [A2A] (diagram: split the sequence by CP rank,
+    exchange, local token shard with full heads), simulated for all ranks.
+    full_outputs[r] is rank r's [T, H/cp, ...] result for head group r in
+    global order; returns every rank's [T/cp, H, ...] shard."""
+    s_local = T // cp_size
+    send = []
+    for r in range(cp_size):
+        x = np.asarray(full_outputs[r])
+        if strategy != NO_LOAD_BALANCE:
+            x = gather(x, _all_ranks_index(cu_seqlens_padded, T, cp_size, strategy))
+        send.append([x[c * s_local:(c + 1) * s_local] for c in range(cp_size)])
+    return [a2a_unpack(np.stack([send[c][r] for c in range(cp_size)])) for r in range(cp_size)]
 
 
 # --------------------------------------------------------------------------

@@ -136,3 +136,31 @@ def test_batched_moves_reject_bad_tensor_counts(L):
         assert st == 1
     # zero rows enqueue nothing and succeed
     assert L.thd_gather_batched(2, arr, 10, pv(16), 0, 16, arr, None) == 0
+
+
+def test_a2a_moves_reject_bad_arguments(L):
+    import ctypes
+    pv = ctypes.c_void_p
+    arr = (pv * 5)(*([pv(16)] * 5))
+    for fn in (L.thd_a2a_pack, L.thd_a2a_unpack):
+        assert fn(0, arr, 10, 2, 16, arr, None) == 1          # no tensors
+        assert fn(5, arr, 10, 2, 16, arr, None) == 1          # too many tensors
+        assert fn(1, arr, -1, 2, 16, arr, None) == 1          # negative tokens
+        assert fn(1, arr, 10, 0, 16, arr, None) == 1          # cp_size < 1
+        assert fn(1, arr, 10, 2, 0, arr, None) == 1           # empty groups
+        assert fn(1, arr, 1 << 30, 4, 16, arr, None) == 1     # rows exceed int32
+        nul = (pv * 1)(None)
+        assert fn(1, nul, 10, 2, 16, arr, None) == 1          # NULL device pointer
+        assert fn(2, arr, 0, 2, 16, arr, None) == 0           # nothing to move
+
+
+def test_empty_moves_ignore_pointers(L):
+    import ctypes
+    pv = ctypes.c_void_p
+    nul = (pv * 2)(None, None)
+    assert L.thd_gather_batched(2, nul, 0, None, 0, 16, nul, None) == 0
+    assert L.thd_scatter_batched(2, nul, 0, None, 16, nul, 0, None) == 0
+    assert L.thd_a2a_pack(2, nul, 0, 4, 16, nul, None) == 0
+    assert L.thd_a2a_unpack(2, nul, 0, 4, 16, nul, None) == 0
+    # the tensor count is still checked
+    assert L.thd_gather_batched(0, nul, 0, None, 0, 16, nul, None) == 1

@@ -154,6 +154,100 @@ def test_kv_restore_round_trip(name):
     assert np.array_equal(k_rm[: w.T // w.cp_size].view(torch.int16).cpu().numpy(), exp)
 
 
+# ---------------------------------------------------------------- a2a layout kernels
+
+@pytest.mark.parametrize("n,cp,hl,tail,dtype,n_tensors", [
+    (1037, 8, 5, (128,), torch.bfloat16, 3),   # the bshd cp=8, h=40, d=128 shape
+    (37, 3, 2, (7,), torch.bfloat16, 1),       # 28-byte groups: 4-byte vectors
+    (50, 4, 1, (3,), torch.uint8, 2),          # 3-byte groups: byte path
+    (129, 1, 4, (64,), torch.float32, 1),      # cp_size = 1: pack is a copy
+    (0, 4, 2, (16,), torch.bfloat16, 1),       # no tokens
+])
+def test_a2a_pack_unpack_byte_exact(n, cp, hl, tail, dtype, n_tensors):
+    _say("a2a pack/unpack", n, cp, hl, tail, dtype, n_tensors)
+    g = torch.Generator().manual_seed(n + cp)
+    shape = (n, cp * hl) + tail
+    if dtype.is_floating_point:
+        xs = [torch.randn(shape, generator=g).to(dtype) for _ in range(n_tensors)]
+    else:
+        xs = [torch.randint(0, 255, shape, generator=g).to(dtype) for _ in range(n_tensors)]
+    bits = (lambda t: t.view(torch.int16).numpy()) if dtype == torch.bfloat16 else (
+        lambda t: t.numpy())
+    packed = thd.a2a_pack([x.to(device()) for x in xs], cp)
+    for x, pk in zip(xs, packed):
+        assert tuple(pk.shape) == (cp, n, hl) + tail
+        assert np.array_equal(bits(pk.cpu()), O.a2a_pack(bits(x), cp))
+    back = thd.a2a_unpack(packed)
+    for x, b in zip(xs, back):
+        assert np.array_equal(bits(b.cpu()), bits(x))
+
+
+def _exchange(send):
+    """The all-to-all itself (communication, simulated with device copies):
+    rank r receives block r of every rank's send buffer, rank-major."""
+    cp = len(send)
+    return [torch.cat([send[c][r] for c in range(cp)], dim=0) for r in range(cp)]
+
+
+def _a2a_round_trip(cup, T, cp, H, strategy, tensors):
+    """Forward exchange of every rank, checked against the global head
+    slices, then the return exchange, checked against the local shards."""
+    dev = device()
+    cup_dev = torch.from_numpy(np.asarray(cup, dtype=np.int32)).to(dev)
+    perm = thd.partition_index(np.asarray(cup, dtype=np.int32), cup_dev, T, cp, -1, strategy)
+    s_local, hl = T // cp, H // cp
+    shards = [thd.gather_many(tensors, perm[r * s_local:(r + 1) * s_local]) for r in range(cp)]
+    send = [thd.a2a_pack(sh, cp) for sh in shards]           # per rank: list over tensors
+    full = []
+    for i in range(len(tensors)):
+        recv = _exchange([send[r][i] for r in range(cp)])     # [T, hl, D], rank-major
+        if strategy == "dual_chunk_swap":
+            glob = [torch.empty_like(x) for x in recv]
+            for r in range(cp):
+                thd.scatter(recv[r], perm, glob[r])
+            recv = glob
+        full.append(recv)
+    for i, x in enumerate(tensors):
+        for r in range(cp):
+            assert torch.equal(full[i][r], x[:, r * hl:(r + 1) * hl]), (i, r)
+    # return exchange of the (unchanged) full-sequence head slices
+    for i, x in enumerate(tensors):
+        outs = full[i]
+        if strategy == "dual_chunk_swap":
+            outs = [thd.gather(o, perm) for o in outs]        # global -> rank-major
+        send_back = [[o[c * s_local:(c + 1) * s_local] for c in range(cp)] for o in outs]
+        recv = [torch.stack([send_back[c][r] for c in range(cp)]) for r in range(cp)]
+        for r in range(cp):
+            (local,) = thd.a2a_unpack([recv[r]])
+            assert torch.equal(local, shards[r][i]), (i, r)
+    return full
+
+
+@pytest.mark.parametrize("strategy", ["dual_chunk_swap", "no_load_balance"])
+def test_a2a_exchange_small_vs_oracle(strategy):
+    cup, T, cp, H, D = [0, 48, 176, 192, 320], 320, 4, 8, 64
+    _say("a2a exchange small", strategy)
+    x = torch.randn((T, H, D), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    full = _a2a_round_trip(cup, T, cp, H, strategy, [x.to(device())])
+    shards = [x.view(torch.int16).numpy()[O.partition_index(cup, T, cp, r, strategy)]
+              for r in range(cp)]
+    exp = O.a2a_before_attn(shards, cup, T, cp, strategy)
+    for r in range(cp):
+        assert np.array_equal(full[0][r].cpu().view(torch.int16).numpy(), exp[r])
+
+
+@pytest.mark.parametrize("s", [8192, 75600])
+@pytest.mark.parametrize("strategy", ["dual_chunk_swap", "no_load_balance"])
+def test_a2a_exchange_bshd_full_size(s, strategy):
+    """bshd, cp=8, h=40, d=128 (batch 1 = one document) at the benchmarked
+    sequence lengths: q, k and v through pack, exchange, (reorder), return."""
+    _say("a2a exchange full", s, strategy)
+    g = torch.Generator(device=device()).manual_seed(s)
+    qkv = [torch.randn((s, 40, 128), generator=g, device=device()).to(torch.bfloat16)
+           for _ in range(3)]
+    _a2a_round_trip([0, s], s, 8, 40, strategy, qkv)
+
+
 # ---------------------------------------------------------------- attention, element by element
 
 SMALL = [
