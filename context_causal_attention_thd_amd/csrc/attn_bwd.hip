@@ -92,45 +92,59 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
       dva[nb][i] = 0.f;
     }
 
-  bf16x8 qreg[CH], dreg[CH];
+  // Per-thread staging slots: chunk c = threadIdx + j*kThreads is row c/CPR,
+  // 16-byte column c%CPR of the query block.
+  uint32_t goff[CH];
+  int soff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    const int rr = c / CPR, dc = c - rr * CPR;
+    goff[j] = (uint32_t)(rr * rs * 2 + dc * 16);
+    soff[j] = rr * P + dc * 8;
+  }
+  // Loads are buffer loads whose descriptors end at row m_hi (later rows read
+  // 0), so they need no branch; nothing is computed from them until they are
+  // written to LDS after the current block's MFMAs, so they stay in flight.
+  u32x4 qreg[CH], dreg[CH];
   float lreg = 0.f, dlreg = 0.f;
   int greg = -1;
   auto load_block = [&](int mb) {
+    const int64_t base = (int64_t)mb * rs + head_off;
+    const uint32_t bytes = (uint32_t)((int64_t)(t.m_hi - mb) * rs * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(d_o + base, bytes);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      const int rr = c / CPR, dc = c - rr * CPR;
-      const int m = mb + rr;
-      const int64_t off = (int64_t)m * rs + head_off + dc * 8;
-      qreg[j] = m < t.m_hi ? load_bf16x8(q + off) : zero_bf16x8();
-      dreg[j] = m < t.m_hi ? load_bf16x8(d_o + off) : zero_bf16x8();
+      qreg[j] = buffer_load16(rq, goff[j]);
+      dreg[j] = buffer_load16(rd, goff[j]);
     }
-    if (threadIdx.x < kBM) {
-      const int m = mb + threadIdx.x;
-      const bool ok = m < t.m_hi;
-      lreg = ok ? lse[(int64_t)h * n_local + m] * kLog2e : 0.f;
-      dlreg = ok ? delta[(int64_t)h * n_local + m] : 0.f;
-      greg = ok ? m + (m < t.m_split ? t.dg_a : t.dg_b) : -1;
+    if (wave_uniform(w) == 0) {  // wave 0 fetches the block's per-row scalars
+      const int64_t row = (int64_t)h * n_local + mb;
+      const uint32_t rbytes = (uint32_t)(t.m_hi - mb) * 4u;
+      lreg = buffer_load_f32(make_rsrc(lse + row, rbytes), (uint32_t)lane * 4u);
+      dlreg = buffer_load_f32(make_rsrc(delta + row, rbytes), (uint32_t)lane * 4u);
+      const int m = mb + lane;
+      greg = m < t.m_hi ? m + (m < t.m_split ? t.dg_a : t.dg_b) : -1;
     }
   };
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      const int rr = c / CPR, dc = c - rr * CPR;
-      store_bf16x8(&sm.q[buf][rr * P + dc * 8], qreg[j]);
-      store_bf16x8(&sm.dO[buf][rr * P + dc * 8], dreg[j]);
+      *reinterpret_cast<u32x4*>(&sm.q[buf][soff[j]]) = qreg[j];
+      *reinterpret_cast<u32x4*>(&sm.dO[buf][soff[j]]) = dreg[j];
     }
-    if (threadIdx.x < kBM) {
-      sm.lse2[buf][threadIdx.x] = lreg;
-      sm.dlt[buf][threadIdx.x] = dlreg;
-      sm.gq[buf][threadIdx.x] = greg;
+    if (wave_uniform(w) == 0) {
+      sm.lse2[buf][lane] = lreg * kLog2e;
+      sm.dlt[buf][lane] = dlreg;
+      sm.gq[buf][lane] = greg;
     }
   };
 
   const int nblocks = (t.m_hi - t.m_lo + kBM - 1) / kBM;
   load_block(t.m_lo);
   store_block(0);
+  wait_vmem();  // K/V fragments have landed: the loop's MFMAs never wait on loads
   __syncthreads();
 
   for (int it = 0; it < nblocks; ++it) {

@@ -8,7 +8,7 @@
 // gfx950 design (mirrors the forward kernel): a workgroup of 4 waves owns up
 // to 128 consecutive query rows of one (document piece, head), 32 per wave,
 // and walks the keys from the document start in 64-key tiles, double-buffered
-// in LDS with the next tile's loads in flight. Per tile, with
+// in LDS with the next tile's loads (branch-free buffer loads) in flight. Per tile, with
 // v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T, dP^T = V dO^T   (A = K / V rows from LDS, B = Q / dO regs)
 //   P^T = exp(S^T - LSE), dS^T = P^T (dP^T - delta)   (lane-local per query)
@@ -93,25 +93,37 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   const bool wave_all_valid =
       wave_uniform((w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e)) != 0;
 
-  bf16x8 kreg[CH], vreg[CH];
+  // Per-thread staging slots: chunk c = threadIdx + j*kThreads is row c/CPR,
+  // 16-byte column c%CPR of the tile. The loads are buffer loads whose
+  // descriptor ends at the last attended key (later rows read 0): no branch,
+  // and nothing uses them before they are written to LDS after the current
+  // tile's MFMAs, so they stay in flight.
+  uint32_t goff[CH];
+  int soff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    const int kr = c / CPR, dc = c - kr * CPR;
+    goff[j] = (uint32_t)(kr * rs * 2 + dc * 16);
+    soff[j] = kr * P + dc * 8;
+  }
+  u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int k0) {
+    const int64_t base = (int64_t)k0 * rs + head_off;
+    const uint32_t bytes = (uint32_t)((int64_t)(t.kend - k0) * rs * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base, bytes);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      const int kr = c / CPR, dc = c - kr * CPR;
-      const int key = k0 + kr;
-      const int64_t off = (int64_t)key * rs + head_off + dc * 8;
-      kreg[j] = key < t.kend ? load_bf16x8(k + off) : zero_bf16x8();
-      vreg[j] = key < t.kend ? load_bf16x8(v + off) : zero_bf16x8();
+      kreg[j] = buffer_load16(rk, goff[j]);
+      vreg[j] = buffer_load16(rv, goff[j]);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      const int kr = c / CPR, dc = c - kr * CPR;
-      store_bf16x8(&sm.k[buf][kr * P + dc * 8], kreg[j]);
-      store_bf16x8(&sm.v[buf][kr * P + dc * 8], vreg[j]);
+      *reinterpret_cast<u32x4*>(&sm.k[buf][soff[j]]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][soff[j]]) = vreg[j];
     }
   };
 
@@ -120,6 +132,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
     load_tile(t.a);
     store_tile(0);
   }
+  wait_vmem();  // Q/dO fragments have landed: the loop's MFMAs never wait on loads
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {

@@ -7,21 +7,33 @@
 // comm type" (body: the mask is the cp_size = 1 mask). Both DUAL_CHUNK_SWAP
 // chunks of a document are separate query tiles of this one launch.
 //
-// gfx950 design: a workgroup of 8 waves owns up to 128 consecutive query rows
-// of one (document piece, head); each wave owns 16 query rows. Keys are walked
-// from the document start in 64-key tiles, double-buffered in LDS (row-major
-// K and V); the next tile's global loads are issued before the current tile's
-// MFMAs so their latency hides behind compute, and one barrier per tile
-// suffices. Everything is computed in the transposed form
+// gfx950 design: a workgroup of 4 waves owns up to 128 consecutive query rows
+// of one (document piece, head); each wave owns 32 query rows as two 16-row
+// blocks. Keys are walked from the document start in 64-key tiles,
+// double-buffered in LDS (row-major K and V). Everything is computed in the
+// transposed form
 //   S^T = K Q^T  and  O^T = V^T P^T
-// with v_mfma_f32_16x16x32_bf16: lane l owns query column l%16 and keys
-// 4*(l/16) + i of each 16-key block, so the online-softmax max/sum need two
-// exchanges across the four 16-lane groups and the rescale is lane-local; P
-// feeds the second product with no data movement. V^T operands come from the
-// row-major V tile through the transposing LDS read. 16-query waves keep the
-// state near 100 registers, so up to four waves share a SIMD. Only tiles on
-// the causal diagonal apply a per-element mask; key rows past the last
-// attended key are zeroed when staged, so padding never enters a product.
+// with v_mfma_f32_16x16x32_bf16: lane l owns query column l%16 of each block
+// and keys 4*(l/16) + i of every 16-key block. Each K fragment (one 16-byte
+// LDS read) and each V^T fragment (two transposing LDS reads) feeds the MFMAs
+// of both query blocks, which halves the LDS bytes per MFMA against 16-row
+// waves; the transposing reads run at half the LDS rate of 16-byte reads, so
+// this is what keeps the kernel MFMA-bound. P feeds the second product with no
+// data movement.
+//
+// The next tile's K/V rows are fetched with buffer loads whose descriptor ends
+// at the last attended key: rows past it read as zero with no branch, so the
+// loads are unconditional, stay in flight during the current tile's MFMAs and
+// are only waited for when they are written to LDS. Padding never enters a
+// product.
+//
+// Online softmax in the log2 domain with lazy rescaling: the running max of a
+// query only moves when a tile's scores exceed it by more than kRescaleLog2,
+// so probabilities stay below 2^kRescaleLog2 (exact in fp32, representable in
+// bf16) and the accumulator rescale, with its cross-lane max, runs only on the
+// rare tiles where some lane of the wave crosses that bound (a wave vote). The
+// row sum is kept per lane and reduced across the four 16-lane groups once, at
+// the end. Only tiles on the causal diagonal apply a per-element mask.
 #include "device_common.h"
 #include "internal.h"
 
@@ -29,10 +41,13 @@ namespace thdcp {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.f;
+static_assert(kWaves * kRowsPerWave == kFwdBM, "query tile = waves x rows per wave");
 
 template <int D>
 struct FwdSmem {
@@ -53,7 +68,7 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   constexpr int NB = D / 16;   // 16-wide blocks of the head dim
   constexpr int KB = BN / 16;  // 16-key blocks per tile
   constexpr int P = FwdSmem<D>::P;
-  constexpr int CPR = D / 8;
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
   constexpr int CH = BN * CPR / kThreads;
   __shared__ FwdSmem<D> sm;
 
@@ -67,54 +82,72 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = (int64_t)h * D;
 
-  const int r = w * 16 + l16;
-  const bool in_tile = r < t.n;
-  const int g = t.g0 + r;
-  const bool valid = in_tile && g < t.e;
-  const int64_t m = (int64_t)t.m0 + r;
-  const int my_g = valid ? g : -1;   // key j is allowed iff j <= my_g
-
-  // Q fragment (B operand of S^T): query l16, head dims kk*32 + G*8 .. +7
-  bf16x8 qf[KS];
-  {
-    const bf16* qp = q + m * rs + head_off + G * 8;
+  // Query rows of this lane: block qb holds tile row w*32 + qb*16 + l16.
+  int my_g[2];
+  bool in_tile[2];
+  int64_t m_row[2];
+  bf16x8 qf[2][KS];  // B operand of S^T: query l16, head dims kk*32 + G*8 .. +7
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = valid ? load_bf16x8(qp + kk * 32) : zero_bf16x8();
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = w * kRowsPerWave + qb * 16 + l16;
+    in_tile[qb] = r < t.n;
+    const int g = t.g0 + r;
+    const bool valid = in_tile[qb] && g < t.e;
+    m_row[qb] = (int64_t)t.m0 + r;
+    my_g[qb] = valid ? g : -1;  // key j is allowed iff j <= my_g
+    const bf16* qp = q + m_row[qb] * rs + head_off + G * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      qf[qb][kk] = valid ? load_bf16x8(qp + kk * 32) : zero_bf16x8();
   }
 
-  f32x4 oacc[NB];
+  f32x4 oacc[2][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) oacc[nb][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[qb][nb][i] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_part[2] = {0.f, 0.f};  // this lane's share of the row sum
 
-  const int wrow_last = min(w * 16 + 15, t.n - 1);
-  const bool wave_has_rows = (w * 16 < t.n) && (t.g0 + w * 16 < t.e);
+  const int row0 = w * kRowsPerWave;
+  const bool wave_has_rows = (row0 < t.n) && (t.g0 + row0 < t.e);
+  const int wrow_last = min(row0 + kRowsPerWave - 1, t.n - 1);
   const int wave_kmax = wave_uniform(wave_has_rows ? min(t.g0 + wrow_last, t.e - 1) : -1);
-  const int wave_gmin = wave_uniform(t.g0 + w * 16);
-  const bool wave_all_valid =
-      wave_uniform((w * 16 + 15 < t.n) && (t.g0 + w * 16 + 15 < t.e)) != 0;
+  const int wave_gmin = wave_uniform(t.g0 + row0);
+  const bool wave_all_valid = wave_uniform((row0 + kRowsPerWave - 1 < t.n) &&
+                                           (t.g0 + row0 + kRowsPerWave - 1 < t.e)) != 0;
 
-  bf16x8 kreg[CH], vreg[CH];
+  // Per-thread staging slots: chunk c = threadIdx + j*kThreads is row c/CPR,
+  // 16-byte column c%CPR of the tile.
+  uint32_t goff[CH];
+  int soff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    const int kr = c / CPR, dc = c - kr * CPR;
+    goff[j] = (uint32_t)(kr * rs * 2 + dc * 16);
+    soff[j] = kr * P + dc * 8;
+  }
+  u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int k0) {
+    // Descriptor from key k0 to the last attended key: later rows read 0.
+    const int64_t base = (int64_t)k0 * rs + head_off;
+    const uint32_t bytes = (uint32_t)((int64_t)(t.kend - k0) * rs * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base, bytes);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      const int kr = c / CPR, dc = c - kr * CPR;
-      const int key = k0 + kr;
-      const int64_t off = (int64_t)key * rs + head_off + dc * 8;
-      kreg[j] = key < t.kend ? load_bf16x8(k + off) : zero_bf16x8();
-      vreg[j] = key < t.kend ? load_bf16x8(v + off) : zero_bf16x8();
+      kreg[j] = buffer_load16(rk, goff[j]);
+      vreg[j] = buffer_load16(rv, goff[j]);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      const int kr = c / CPR, dc = c - kr * CPR;
-      store_bf16x8(&sm.k[buf][kr * P + dc * 8], kreg[j]);
-      store_bf16x8(&sm.v[buf][kr * P + dc * 8], vreg[j]);
+      *reinterpret_cast<u32x4*>(&sm.k[buf][soff[j]]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][soff[j]]) = vreg[j];
     }
   };
 
@@ -123,6 +156,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     load_tile(t.a);
     store_tile(0);
   }
+  // The Q fragments (and the first tile) have landed before the loop, so the
+  // loop's MFMAs never wait on the prefetch loads issued inside it.
+  wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
@@ -132,74 +168,96 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     if (has_next) load_tile(k0 + BN);  // in flight during this tile's compute
 
     if (k0 <= wave_kmax) {
-      // S^T (keys x queries), one 16x16 accumulator per 16-key block.
-      f32x4 s[KB];
+      // S^T (keys x queries): one 16x16 accumulator per (query block, key block).
+      f32x4 s[2][KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kb][i] = 0.f;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[qb][kb][i] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          s[kb] = mfma16(load_bf16x8(&sm.k[cur][(kb * 16 + l16) * P + kk * 32 + G * 8]), qf[kk], s[kb]);
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 a = load_bf16x8(&sm.k[cur][(kb * 16 + l16) * P + kk * 32 + G * 8]);
+          s[0][kb] = mfma16(a, qf[0][kk], s[0][kb]);
+          s[1][kb] = mfma16(a, qf[1][kk], s[1][kb]);
+        }
 
       // Causal / padding mask, only where some key may exceed some row's g.
       if (!wave_all_valid || k0 + BN - 1 > wave_gmin) {
 #pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + kb * 16 + G * 4 + i;
+              if (key > my_g[qb]) s[qb][kb][i] = -INFINITY;
+            }
+      }
+
+      // Lazy rescale: does any score of this lane exceed its running max by
+      // more than the bound?
+      float lm[2];
+      bool need = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float mx = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][kb][i]);
+        lm[qb] = mx * scale_log2;
+        need |= lm[qb] > m_run[qb] + kRescaleLog2;
+      }
+      if (__any(need)) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float rm = group_max4(lm[qb]);  // the row's tile max (uniform per query)
+          const float m_new = rm > m_run[qb] + kRescaleLog2 ? rm : m_run[qb];
+          const float alpha = m_new == m_run[qb] ? 1.f : fast_exp2(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_part[qb] *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[qb][nb][i] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        float ps = 0.f;
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = k0 + kb * 16 + G * 4 + i;
-            if (key > my_g) s[kb][i] = -INFINITY;
+            const float p = fast_exp2(fmaf(s[qb][kb][i], scale_log2, -m_use));
+            s[qb][kb][i] = p;
+            ps += p;
           }
-      }
-
-      // Online softmax in the log2 domain; the four 16-lane groups hold
-      // different keys of the same queries.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
-          s[kb][i] = p;
-          psum += p;
-        }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (!__all(alpha == 1.f)) {  // rescale only when some row's max moved
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[nb][i] *= alpha;
+        l_part[qb] += ps;
       }
 
       // O^T += V^T P^T. k-step ks covers key blocks 2ks, 2ks+1: slot j of this
       // lane is key (2ks + j/4)*16 + 4*G + j%4 -- accumulator entries of
-      // s[2ks], s[2ks+1]. The V^T operand (lane = head dim, slots = those
-      // keys) is two transposing reads of the row-major V tile.
+      // s[.][2ks], s[.][2ks+1]. The V^T operand (lane = head dim, slots = those
+      // keys) is two transposing reads of the row-major V tile, shared by both
+      // query blocks.
 #pragma unroll
       for (int ks = 0; ks < KB / 2; ++ks) {
-        const bf16x8 pb = pack8(s[2 * ks], s[2 * ks + 1]);
+        const bf16x8 pb0 = pack8(s[0][2 * ks], s[0][2 * ks + 1]);
+        const bf16x8 pb1 = pack8(s[1][2 * ks], s[1][2 * ks + 1]);
         const int o1 = (2 * ks * 16 + G * 4 + (l16 >> 2)) * P + 4 * (l16 & 3);
         const int o2 = o1 + 16 * P;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 a = concat4(lds_read_tr4(&sm.v[cur][o1 + nb * 16]), lds_read_tr4(&sm.v[cur][o2 + nb * 16]));
-          oacc[nb] = mfma16(a, pb, oacc[nb]);
+          const bf16x8 a = concat4(lds_read_tr4(&sm.v[cur][o1 + nb * 16]),
+                                   lds_read_tr4(&sm.v[cur][o2 + nb * 16]));
+          oacc[0][nb] = mfma16(a, pb0, oacc[0][nb]);
+          oacc[1][nb] = mfma16(a, pb1, oacc[1][nb]);
         }
       }
     }
@@ -208,20 +266,24 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     __syncthreads();
   }
 
-  if (!in_tile) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  bf16* op = o + m * rs + head_off;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    // accumulator rows (head dims) nb*16 + 4*G + 0..3 of query l16
-    bf16x4 out;
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = group_sum4(l_part[qb]);
+    if (!in_tile[qb]) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16* op = o + m_row[qb] * rs + head_off;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = (bf16)(oacc[nb][j] * inv);
-    store_bf16x4(op + nb * 16 + G * 4, out);
-  }
-  if (G == 0) {
-    lse[(int64_t)h * n_local + m] =
-        (valid && l_run > 0.f) ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    for (int nb = 0; nb < NB; ++nb) {
+      // accumulator rows (head dims) nb*16 + 4*G + 0..3 of query l16
+      bf16x4 out;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = (bf16)(oacc[qb][nb][j] * inv);
+      store_bf16x4(op + nb * 16 + G * 4, out);
+    }
+    if (G == 0) {
+      lse[(int64_t)h * n_local + m_row[qb]] =
+          (my_g[qb] >= 0 && l > 0.f) ? (m_run[qb] + __log2f(l)) * kLn2 : -INFINITY;
+    }
   }
 }
 

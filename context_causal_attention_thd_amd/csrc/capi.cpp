@@ -429,6 +429,20 @@ thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan
   if (st != THDCP_OK) return st;
   const int64_t n_local = d.T / d.cp_size;
   if (n_local * (int64_t)d.H * d.D > ((int64_t)1 << 40)) return fail(THDCP_ERR_ARG, "too large");
+  {
+    // The attention kernels reach one document's K/V rows, and the local
+    // Q/dO rows, through 32-bit buffer offsets.
+    const int64_t row_bytes = (int64_t)d.H * d.D * 2;
+    int64_t max_doc = 0;
+    for (int32_t i = 0; i < d.B; ++i)
+      max_doc = std::max<int64_t>(max_doc, (int64_t)d.cu_seqlens_padded_host[i + 1] -
+                                               d.cu_seqlens_padded_host[i]);
+    if (max_doc * row_bytes >= ((int64_t)1 << 32) || n_local * row_bytes >= ((int64_t)1 << 32))
+      return fail(THDCP_ERR_UNSUPPORTED,
+                  "a document (%lld rows) or the local share (%lld rows) exceeds 4 GiB of "
+                  "bf16 rows of %lld bytes",
+                  (long long)max_doc, (long long)n_local, (long long)row_bytes);
+  }
   thdcp_plan* p = new (std::nothrow) thdcp_plan();
   if (!p) return fail(THDCP_ERR_ARG, "out of host memory");
   p->desc = d;

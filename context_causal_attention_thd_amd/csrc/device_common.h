@@ -105,4 +105,46 @@ __device__ __forceinline__ float shfl_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3):
+// loads at offsets past the end return 0 without touching memory, so a tile
+// whose last rows fall outside the data needs no branch around its loads.
+// `bytes` must be below 2^32; callers check that on the host.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Maximum (or sum) over the four 16-lane groups of a wave with the gfx950
+// lane-swap instructions (VALU, no LDS traffic): permlane16_swap exchanges
+// 16-lane rows 0<->1 and 2<->3, permlane32_swap the two halves of the wave.
+__device__ __forceinline__ float group_max4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t u2 = __float_as_uint(x);
+  auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float group_sum4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t u2 = __float_as_uint(x);
+  auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace thdcp

@@ -199,7 +199,10 @@ typedef struct {
 } thdcp_plan_info;
 
 /* Build a plan on the host. *plan_out receives a host object the caller
- * releases with thdcp_plan_destroy. No device work. */
+ * releases with thdcp_plan_destroy. No device work. Returns
+ * THDCP_ERR_UNSUPPORTED when one document's rows, or the local share's rows,
+ * of bf16 [H, D] exceed 4 GiB (the kernels address them with 32-bit buffer
+ * offsets). */
 thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan_out);
 thdcp_status_t thdcp_plan_get_info(thdcp_plan_t plan, thdcp_plan_info* info_out);
 /* Per-document count of real tokens this rank holds (int32 [B], host). */
