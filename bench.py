@@ -4,11 +4,15 @@ A step is one pass of the whole hot path for the measured rank over one batch:
   validate + build the rank plan (host) and upload it,
   partition index for every rank (the all-ranks permutation),
   gather the rank's local Q and dO,
-  restore K and V from the rank-major all-gathered buffer to global order,
-  attention forward (O, LSE),
-  attention backward (preprocess, main kernel, gated zeroing of untouched rows),
-  unrestore dK and dV to rank-major order for the reduce-scatter.
-Inputs are synthetic and already resident in HBM when timing starts.
+  attention forward (O, LSE) on K and V as the all-gather delivers them
+    (rank-major): the restore to global order is fused into the kernels'
+    K/V loads through the plan's row map,
+  attention backward (preprocess, dK/dV, dQ, gated zeroing of untouched rows),
+    whose dK/dV stores go straight to rank-major order for the reduce-scatter
+    (the unrestore fused the same way).
+Inputs are synthetic and already resident in HBM when timing starts. The
+standalone K+V restore (one batched gather launch over all T rows) is timed
+separately for the gather roofline.
 
 value = 14 * D * H * causal_pairs / step time (TFLOP/s; causal-masked FLOPs
 only), the steps timed with no events inside. The roofline object is for the
@@ -98,32 +102,29 @@ def main():
     perm = torch.empty(T, dtype=torch.int32, device=dev)
     q_local = torch.empty((n_local, H, D), dtype=torch.bfloat16, device=dev)
     do_local = torch.empty_like(q_local)
-    k_g = torch.empty_like(k)
+    k_g = torch.empty_like(k)     # global order (standalone restore timing only)
     v_g = torch.empty_like(v)
     o = torch.empty_like(q_local)
     lse = torch.empty((H, n_local), dtype=torch.float32, device=dev)
     dq = torch.empty((n_local, H, D), dtype=torch.float32, device=dev)
-    dk = torch.empty((T, H, D), dtype=torch.float32, device=dev)
-    dv = torch.empty_like(dk)
-    dk_rm = torch.empty_like(dk)
-    dv_rm = torch.empty_like(dk)
-    probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False)
+    dk_rm = torch.empty((T, H, D), dtype=torch.float32, device=dev)   # rank-major partials
+    dv_rm = torch.empty_like(dk_rm)
+    probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major")
     ws = torch.empty(int(probe.info.workspace_bytes) + 4096, dtype=torch.uint8, device=dev)
     scratch = torch.empty(int(probe.info.bwd_scratch_bytes) + 256, dtype=torch.uint8, device=dev)
     pairs = int(probe.info.causal_pairs)
     probe.close()
 
     def step():
-        plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False)
+        plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
+                        kv_layout="rank_major")
         plan.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
         thd.gather_many([q, do], mine, [q_local, do_local])
-        thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g])
-        thd.attn_fwd(plan, q_local, k_g, v_g, o=o, lse=lse)
-        thd.attn_bwd_parts(plan, q_local, k_g, v_g, o, lse, do_local, dq, dk, dv, scratch,
-                           zero_untouched=True)
-        thd.gather_many([dk, dv], perm, [dk_rm, dv_rm])
+        thd.attn_fwd(plan, q_local, k_rm, v_rm, o=o, lse=lse)
+        thd.attn_bwd_parts(plan, q_local, k_rm, v_rm, o, lse, do_local, dq, dk_rm, dv_rm,
+                           scratch, zero_untouched=True)
         return plan  # keep alive until the stream is synchronized
 
     # Whole steps: no events inside the timed region.
@@ -146,7 +147,7 @@ def main():
     # Per-kernel durations, live on the same stream and inputs: events around
     # REPS back-to-back launches of one kernel, so the events' own cost is
     # amortized. Each launch recomputes the same outputs.
-    plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False)
+    plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major")
     plan.upload_into(ws, stream)
     reps = max(5, min(50, int(20.0 / max(ms_step, 1e-3))))
 
@@ -162,13 +163,14 @@ def main():
         return e0.elapsed_time(e1) / reps
 
     L = thd.lib()
-    pargs = (thd._dev_ptr(q_local, "q"), thd._dev_ptr(k_g, "k"), thd._dev_ptr(v_g, "v"),
+    pargs = (thd._dev_ptr(q_local, "q"), thd._dev_ptr(k_rm, "k"), thd._dev_ptr(v_rm, "v"),
              thd._dev_ptr(lse, "lse"), thd._dev_ptr(do_local, "do"))
     sp, sn, st = thd._dev_ptr(scratch, "scratch"), scratch.numel(), thd._stream(stream)
     t_restore = timed(lambda: thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g]))
-    t_fwd = timed(lambda: thd.attn_fwd(plan, q_local, k_g, v_g, o=o, lse=lse))
+    t_fwd = timed(lambda: thd.attn_fwd(plan, q_local, k_rm, v_rm, o=o, lse=lse))
     t_dkdv = timed(lambda: thd._check(L.cp_attn_bwd_dkdv(
-        plan.handle, *pargs, thd._dev_ptr(dk, "dk"), thd._dev_ptr(dv, "dv"), 0, sp, sn, st)))
+        plan.handle, *pargs, thd._dev_ptr(dk_rm, "dk"), thd._dev_ptr(dv_rm, "dv"), 0, sp, sn,
+        st)))
     t_dq = timed(lambda: thd._check(L.cp_attn_bwd_dq(
         plan.handle, *pargs, thd._dev_ptr(dq, "dq"), sp, sn, st)))
     t_bwd = t_dkdv + t_dq

@@ -51,6 +51,7 @@ class _Desc(ctypes.Structure):
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
         ("pad_between_seqs", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
     ]
 
 
@@ -150,6 +151,10 @@ def _strategy(s) -> int:
         return _STRATEGY_NAMES[s]
     except KeyError:
         raise ValueError(f"unknown strategy {s!r}") from None
+
+
+# Row order of K/V in and dK/dV out of the attention calls (thdcp_kv_layout_t).
+KV_LAYOUTS = {"global": 0, "rank_major": 1}
 
 
 def _stream(stream=None):
@@ -320,7 +325,8 @@ class Plan:
 
     def __init__(self, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, rank: int, strategy,
                  H: int, D: int, softmax_scale: float = 0.0, window=(-1, 0),
-                 pad_between_seqs: int = -1, device=None, stream=None, upload: bool = True):
+                 pad_between_seqs: int = -1, device=None, stream=None, upload: bool = True,
+                 kv_layout: str = "global"):
         self._cup = _i32_host(cu_seqlens_padded)
         self._cu = None if cu_seqlens is None else _i32_host(cu_seqlens)
         d = _Desc()
@@ -336,6 +342,10 @@ class Plan:
         d.softmax_scale = float(softmax_scale)
         d.window_left, d.window_right = int(window[0]), int(window[1])
         d.pad_between_seqs = int(pad_between_seqs)
+        if kv_layout not in KV_LAYOUTS:
+            raise ValueError(f"unknown kv_layout {kv_layout!r} (one of {sorted(KV_LAYOUTS)})")
+        d.kv_layout = KV_LAYOUTS[kv_layout]
+        self.kv_layout = kv_layout
         self._handle = ctypes.c_void_p()
         _check(lib().thdcp_plan_create(ctypes.byref(d), ctypes.byref(self._handle)))
         self.T, self.H, self.D, self.cp_size, self.rank = int(T), int(H), int(D), cp_size, rank

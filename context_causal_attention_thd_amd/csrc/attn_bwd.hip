@@ -49,7 +49,8 @@ template <int D>
 __global__ void __launch_bounds__(kThreads, 1)
 attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                      const bf16* __restrict__ k, const bf16* __restrict__ v,
-                     const bf16* __restrict__ d_o, const float* __restrict__ lse,
+                     const int32_t* __restrict__ kv_row, const bf16* __restrict__ d_o,
+                     const float* __restrict__ lse,
                      const float* __restrict__ delta, float* __restrict__ dk,
                      float* __restrict__ dv, int64_t n_local, float scale, float scale_log2,
                      int32_t accumulate) {
@@ -72,11 +73,15 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = (int64_t)h * D;
 
+  // Key j sits at row j of K/V and dK/dV (global order) or at row kv_row[j]
+  // (rank-major: the restore and the unrestore fused into these loads and
+  // stores).
+  auto key_row = [&](int key) -> int64_t { return kv_row ? kv_row[key] : key; };
   const int my_key = t.k0 + w * 16 + l16;
   const bool key_ok = my_key < t.k1;
   bf16x8 kf[KS], vf[KS];
   {
-    const int64_t off = (int64_t)my_key * rs + head_off + G * 8;
+    const int64_t off = key_row(min(my_key, t.k1 - 1)) * rs + head_off + G * 8;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       kf[kk] = key_ok ? load_bf16x8(k + off + kk * 32) : zero_bf16x8();
@@ -212,13 +217,18 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
 
   // dK (scaled) and dV rows of this wave's keys; lane holds head dim nb*16 + l16
   // for keys 4*G + i of the wave's 16.
+  int64_t out_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = t.k0 + w * 16 + G * 4 + i;
+    out_row[i] = key < t.k1 ? key_row(key) : -1;
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = t.k0 + w * 16 + G * 4 + i;
-      if (key < t.k1) {
-        const int64_t off = (int64_t)key * rs + head_off + nb * 16 + l16;
+      if (out_row[i] >= 0) {
+        const int64_t off = out_row[i] * rs + head_off + nb * 16 + l16;
         const float kval = dka[nb][i] * scale;
         const float vval = dva[nb][i];
         if (accumulate) {
@@ -234,7 +244,8 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
 
 template <int D>
 hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const void* q,
-                        const void* k, const void* v, const void* d_o, const float* lse,
+                        const void* k, const void* v, const int32_t* kv_row, const void* d_o,
+                        const float* lse,
                         const float* delta, float* dk, float* dv, int64_t n_local,
                         float scale, int32_t accumulate, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
@@ -255,7 +266,8 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
   }
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), smem,
                      stream, tiles, H, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(d_o), lse, delta, dk,
+                     static_cast<const bf16*>(v), kv_row, static_cast<const bf16*>(d_o), lse,
+                     delta, dk,
                      dv, n_local, scale, scale * kLog2e, accumulate);
   return hipGetLastError();
 }
@@ -263,15 +275,16 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
 }  // namespace
 
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                                const void* q, const void* k, const void* v, const void* d_o,
+                                const void* q, const void* k, const void* v,
+                                const int32_t* kv_row, const void* d_o,
                                 const float* lse, const float* delta, float* dk, float* dv,
                                 int64_t n_local, float scale, int32_t accumulate,
                                 hipStream_t stream) {
   if (D == 128)
-    return launch_bwd_d<128>(tiles, n_tiles, H, q, k, v, d_o, lse, delta, dk, dv, n_local,
+    return launch_bwd_d<128>(tiles, n_tiles, H, q, k, v, kv_row, d_o, lse, delta, dk, dv, n_local,
                              scale, accumulate, stream);
   if (D == 64)
-    return launch_bwd_d<64>(tiles, n_tiles, H, q, k, v, d_o, lse, delta, dk, dv, n_local,
+    return launch_bwd_d<64>(tiles, n_tiles, H, q, k, v, kv_row, d_o, lse, delta, dk, dv, n_local,
                             scale, accumulate, stream);
   return hipErrorInvalidValue;
 }

@@ -28,15 +28,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct DqSmem {
-  static constexpr int P = D + 16;  // row pitch (bf16), as in the forward kernel
+  // Row pitch (bf16) = D + 24, a row stride of 4 (mod 8) dwords: the 32-row
+  // fragment reads of K and V (lane = row l%32, 16-byte column (l/32)) are
+  // free of LDS bank conflicts (measured: the forward's D + 16 halves their
+  // rate). The transposing K^T reads keep a 2-way conflict at this pitch.
+  static constexpr int P = D + 24;
   bf16 k[2][kFwdBN * P];
   bf16 v[2][kFwdBN * P];
 };
 
-template <int D>
+// MAPPED: K/V rows are found through kv_row (rank-major K/V) instead of by key.
+template <int D, bool MAPPED>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                    const bf16* __restrict__ k, const bf16* __restrict__ v,
+                   const int32_t* __restrict__ kv_row, uint32_t kv_bytes,
                    const bf16* __restrict__ d_o, const float* __restrict__ lse,
                    const float* __restrict__ delta, float* __restrict__ dq, int64_t n_local,
                    float scale, float scale_log2) {
@@ -94,43 +100,72 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       wave_uniform((w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e)) != 0;
 
   // Per-thread staging slots: chunk c = threadIdx + j*kThreads is row c/CPR,
-  // 16-byte column c%CPR of the tile. The loads are buffer loads whose
-  // descriptor ends at the last attended key (later rows read 0): no branch,
-  // and nothing uses them before they are written to LDS after the current
-  // tile's MFMAs, so they stay in flight.
-  uint32_t goff[CH];
-  int soff[CH];
+  // 16-byte column c%CPR of the tile; kThreads is a multiple of CPR, so every
+  // chunk of a thread is in the same column and its rows are RSTEP apart.
+  constexpr int RSTEP = kThreads / CPR;
+  static_assert(RSTEP * CPR == kThreads, "threads cover whole rows");
+  const int krow0 = threadIdx.x / CPR;
+  const uint32_t coff = (uint32_t)(threadIdx.x % CPR) * 16u;
+  const int soff0 = krow0 * P + (threadIdx.x % CPR) * 8;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t goff0 = (uint32_t)krow0 * row_bytes + coff;  // from the tile's first row
+  // Tile rows are fetched with buffer loads; a row past the last attended key
+  // reads 0 with no branch, and nothing uses the loads before they are written
+  // to LDS after the current tile's MFMAs, so they stay in flight.
+  //  - Global order: the descriptor runs from row k0 to the last attended
+  //    key, so the constant chunk offsets land past its end for those rows.
+  //  - Rank-major (MAPPED): key j sits at row kv_row[j] (the restore fused
+  //    into these loads); pos[] holds this thread's rows of a tile, looked up
+  //    one tile ahead of the loads that use them, and a skipped row gets an
+  //    offset past the descriptor, which spans all rows (below 2 GiB).
+  auto rows_pos = [&](int k0, int (&pos)[CH]) {
+    if constexpr (MAPPED) {
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const int c = threadIdx.x + j * kThreads;
-    const int kr = c / CPR, dc = c - kr * CPR;
-    goff[j] = (uint32_t)(kr * rs * 2 + dc * 16);
-    soff[j] = kr * P + dc * 8;
-  }
+      for (int j = 0; j < CH; ++j) {
+        const int key = k0 + krow0 + j * RSTEP;
+        const int r = kv_row[min(key, t.kend - 1)];
+        pos[j] = key < t.kend ? r : -1;
+      }
+    }
+  };
   u32x4 kreg[CH], vreg[CH];
-  auto load_tile = [&](int k0) {
-    const int64_t base = (int64_t)k0 * rs + head_off;
-    const uint32_t bytes = (uint32_t)((int64_t)(t.kend - k0) * rs * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base, bytes);
+  auto load_tile = [&](int k0, const int (&pos)[CH]) {
+    if constexpr (MAPPED) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, kv_bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, kv_bytes);
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      kreg[j] = buffer_load16(rk, goff[j]);
-      vreg[j] = buffer_load16(rv, goff[j]);
+      for (int j = 0; j < CH; ++j) {
+        const uint32_t off = pos[j] >= 0 ? (uint32_t)pos[j] * row_bytes + coff : 0xFFFFFFF0u;
+        kreg[j] = buffer_load16(rk, off);
+        vreg[j] = buffer_load16(rv, off);
+      }
+    } else {
+      const int64_t n = (int64_t)t.kend - k0;
+      const uint32_t bytes = n > 0 ? (uint32_t)(n * rs * 2) : 0u;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (int64_t)k0 * rs + head_off, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (int64_t)k0 * rs + head_off, bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        kreg[j] = buffer_load16(rk, goff0 + j * RSTEP * row_bytes);
+        vreg[j] = buffer_load16(rv, goff0 + j * RSTEP * row_bytes);
+      }
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      *reinterpret_cast<u32x4*>(&sm.k[buf][soff[j]]) = kreg[j];
-      *reinterpret_cast<u32x4*>(&sm.v[buf][soff[j]]) = vreg[j];
+      *reinterpret_cast<u32x4*>(&sm.k[buf][soff0 + j * RSTEP * P]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][soff0 + j * RSTEP * P]) = vreg[j];
     }
   };
 
   const int ntiles = t.kend > t.a ? (t.kend - t.a + BN - 1) / BN : 0;
+  int pos[CH];
   if (ntiles > 0) {
-    load_tile(t.a);
+    rows_pos(t.a, pos);
+    load_tile(t.a, pos);
     store_tile(0);
+    rows_pos(t.a + BN, pos);
   }
   wait_vmem();  // Q/dO fragments have landed: the loop's MFMAs never wait on loads
   __syncthreads();
@@ -139,7 +174,10 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
     const int k0 = t.a + it * BN;
     const int cur = it & 1;
     const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(k0 + BN);
+    if (has_next) {
+      load_tile(k0 + BN, pos);
+      rows_pos(k0 + 2 * BN, pos);
+    }
 
     if (k0 <= wave_kmax) {
       f32x16 s[2], dp[2];
@@ -205,7 +243,8 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
 }  // namespace
 
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                              const void* q, const void* k, const void* v, const void* d_o,
+                              const void* q, const void* k, const void* v, const int32_t* kv_row,
+                              int64_t T, const void* d_o,
                               const float* lse, const float* delta, float* dq, int64_t n_local,
                               float scale, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
@@ -215,14 +254,19 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
   const bf16* db = static_cast<const bf16*>(d_o);
-  if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       tiles, H, qb, kb, vb, db, lse, delta, dq, n_local, scale, scale * kLog2e);
-  else if (D == 64)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       tiles, H, qb, kb, vb, db, lse, delta, dq, n_local, scale, scale * kLog2e);
-  else
-    return hipErrorInvalidValue;
+  const int64_t kv_bytes = T * H * D * 2;
+  if (kv_row && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const uint32_t kvb = kv_row ? (uint32_t)kv_bytes : 0u;
+#define THDCP_DQ_LAUNCH(DD, M)                                                               \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD, M>), dim3((unsigned)blocks), dim3(kThreads), 0,   \
+                     stream, tiles, H, qb, kb, vb, kv_row, kvb, db, lse, delta, dq, n_local,   \
+                     scale, scale * kLog2e)
+  if (D == 128 && kv_row) THDCP_DQ_LAUNCH(128, true);
+  else if (D == 128) THDCP_DQ_LAUNCH(128, false);
+  else if (D == 64 && kv_row) THDCP_DQ_LAUNCH(64, true);
+  else if (D == 64) THDCP_DQ_LAUNCH(64, false);
+  else return hipErrorInvalidValue;
+#undef THDCP_DQ_LAUNCH
   return hipGetLastError();
 }
 

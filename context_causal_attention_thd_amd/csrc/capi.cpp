@@ -110,8 +110,12 @@ struct thdcp_plan {
   std::vector<FwdTile> fwd;
   std::vector<BwdTile> bwd;
   std::vector<ZeroRange> zero;
+  // THDCP_KV_RANK_MAJOR with a layout whose rank-major order differs from
+  // global order: kv_row[g] = rank-major position of global row g.
+  bool kv_mapped = false;
+  std::vector<int32_t> kv_row;
   std::vector<char> blob;  // host image of the device tables
-  size_t off_fwd = 0, off_bwd = 0, off_zero = 0, ws_bytes = 0;
+  size_t off_fwd = 0, off_bwd = 0, off_zero = 0, off_kvrow = 0, ws_bytes = 0;
   char* ws_dev = nullptr;  // caller's workspace after upload
 };
 
@@ -125,9 +129,9 @@ struct Segment {  // consecutive local rows holding consecutive global rows of o
   int32_t doc;    // -1: buffer tail (no document)
 };
 
-std::vector<Segment> build_segments(const thdcp_plan& p) {
+std::vector<Segment> build_segments(const thdcp_plan& p, int64_t r) {
   const auto& d = p.desc;
-  const int64_t cp = d.cp_size, r = d.rank;
+  const int64_t cp = d.cp_size;
   std::vector<Segment> segs;
   if (d.strategy == THDCP_DUAL_CHUNK_SWAP) {
     // [AG] "Why": 2*cp_size chunks per document; rank r holds chunks r and
@@ -158,7 +162,7 @@ std::vector<Segment> build_segments(const thdcp_plan& p) {
 
 void build_plan(thdcp_plan& p) {
   const auto& d = p.desc;
-  const std::vector<Segment> segs = build_segments(p);
+  const std::vector<Segment> segs = build_segments(p, d.rank);
 
   p.local_seqlens.assign(d.B, 0);
   p.pairs = 0;
@@ -276,17 +280,40 @@ void build_plan(thdcp_plan& p) {
     p.zero.push_back({(int32_t)cursor, (int32_t)d.T, (int32_t)before, 0});
   }
 
+  // Rank-major K/V: the inverse of the all-ranks permutation. Rank r's local
+  // row m sits at rank-major position r * n_local + m; under NO_LOAD_BALANCE
+  // (or cp_size 1) that is global row order and no map is needed.
+  p.kv_mapped = d.kv_layout == THDCP_KV_RANK_MAJOR && d.strategy == THDCP_DUAL_CHUNK_SWAP &&
+                d.cp_size > 1;
+  p.kv_row.clear();
+  if (p.kv_mapped) {
+    p.kv_row.assign(d.T, 0);
+    for (int32_t r = 0; r < d.cp_size; ++r)
+      for (const Segment& sg : build_segments(p, r))
+        for (int64_t i = 0; i < sg.len; ++i)
+          p.kv_row[sg.g0 + i] = (int32_t)(r * p.n_local + sg.m0 + i);
+  }
+
   // Host image of the device tables.
   p.off_fwd = 0;
   p.off_bwd = align256(p.off_fwd + p.fwd.size() * sizeof(FwdTile));
   p.off_zero = align256(p.off_bwd + p.bwd.size() * sizeof(BwdTile));
-  p.ws_bytes = align256(p.off_zero + p.zero.size() * sizeof(ZeroRange));
+  p.off_kvrow = align256(p.off_zero + p.zero.size() * sizeof(ZeroRange));
+  p.ws_bytes = align256(p.off_kvrow + p.kv_row.size() * sizeof(int32_t));
   if (p.ws_bytes == 0) p.ws_bytes = 256;
   p.blob.assign(p.ws_bytes, 0);
   if (!p.fwd.empty()) memcpy(p.blob.data() + p.off_fwd, p.fwd.data(), p.fwd.size() * sizeof(FwdTile));
   if (!p.bwd.empty()) memcpy(p.blob.data() + p.off_bwd, p.bwd.data(), p.bwd.size() * sizeof(BwdTile));
   if (!p.zero.empty())
     memcpy(p.blob.data() + p.off_zero, p.zero.data(), p.zero.size() * sizeof(ZeroRange));
+  if (!p.kv_row.empty())
+    memcpy(p.blob.data() + p.off_kvrow, p.kv_row.data(), p.kv_row.size() * sizeof(int32_t));
+}
+
+// Device map from global K/V row to its position in the caller's buffers
+// (nullptr: the identity).
+const int32_t* kv_map(const thdcp_plan* p) {
+  return p->kv_mapped ? reinterpret_cast<const int32_t*>(p->ws_dev + p->off_kvrow) : nullptr;
 }
 
 }  // namespace
@@ -431,17 +458,25 @@ thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan
   if (n_local * (int64_t)d.H * d.D > ((int64_t)1 << 40)) return fail(THDCP_ERR_ARG, "too large");
   {
     // The attention kernels reach one document's K/V rows, and the local
-    // Q/dO rows, through 32-bit buffer offsets.
+    // Q/dO rows, through 32-bit buffer offsets; rows they skip use an offset
+    // past every descriptor, so descriptors stay below 2 GiB.
     const int64_t row_bytes = (int64_t)d.H * d.D * 2;
     int64_t max_doc = 0;
     for (int32_t i = 0; i < d.B; ++i)
       max_doc = std::max<int64_t>(max_doc, (int64_t)d.cu_seqlens_padded_host[i + 1] -
                                                d.cu_seqlens_padded_host[i]);
-    if (max_doc * row_bytes >= ((int64_t)1 << 32) || n_local * row_bytes >= ((int64_t)1 << 32))
+    if (max_doc * row_bytes >= ((int64_t)1 << 31) || n_local * row_bytes >= ((int64_t)1 << 31))
       return fail(THDCP_ERR_UNSUPPORTED,
-                  "a document (%lld rows) or the local share (%lld rows) exceeds 4 GiB of "
+                  "a document (%lld rows) or the local share (%lld rows) exceeds 2 GiB of "
                   "bf16 rows of %lld bytes",
                   (long long)max_doc, (long long)n_local, (long long)row_bytes);
+    if (d.kv_layout != THDCP_KV_GLOBAL && d.kv_layout != THDCP_KV_RANK_MAJOR)
+      return fail(THDCP_ERR_ARG, "kv_layout %d (0 global, 1 rank-major)", d.kv_layout);
+    // Mapped K/V rows are addressed from the start of the buffer.
+    if (d.kv_layout == THDCP_KV_RANK_MAJOR && d.T * row_bytes >= ((int64_t)1 << 31))
+      return fail(THDCP_ERR_UNSUPPORTED,
+                  "rank-major K/V of %lld rows exceeds 2 GiB of bf16 rows of %lld bytes",
+                  (long long)d.T, (long long)row_bytes);
   }
   thdcp_plan* p = new (std::nothrow) thdcp_plan();
   if (!p) return fail(THDCP_ERR_ARG, "out of host memory");
@@ -509,8 +544,8 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, o, lse, p->n_local,
-                      p->scale, (hipStream_t)stream),
+                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->desc.T,
+                      o, lse, p->n_local, p->scale, (hipStream_t)stream),
       "cp_attn_fwd launch");
 }
 
@@ -573,9 +608,9 @@ thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t p, const void* q, const void* k, co
   if (p->bwd.empty()) return ok();
   return hip_status(
       launch_attn_bwd_dkdv(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
-                           (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, d_o, lse,
-                           static_cast<const float*>(scratch), dk, dv, p->n_local, p->scale,
-                           accumulate_dkv, (hipStream_t)stream),
+                           (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p),
+                           d_o, lse, static_cast<const float*>(scratch), dk, dv, p->n_local,
+                           p->scale, accumulate_dkv, (hipStream_t)stream),
       "cp_attn_bwd_dkdv launch");
 }
 
@@ -591,9 +626,9 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, d_o, lse,
-                         static_cast<const float*>(scratch), dq, p->n_local, p->scale,
-                         (hipStream_t)stream),
+                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p),
+                         p->desc.T, d_o, lse, static_cast<const float*>(scratch), dq,
+                         p->n_local, p->scale, (hipStream_t)stream),
       "cp_attn_bwd_dq launch");
 }
 
@@ -606,7 +641,7 @@ thdcp_status_t thdcp_zero_untouched(thdcp_plan_t p, float* dk, float* dv, void* 
   if (p->zero.empty()) return ok();
   const int64_t rows = p->desc.T - p->touched;
   return hip_status(launch_zero_rows(reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_zero),
-                                     (int32_t)p->zero.size(), rows,
+                                     (int32_t)p->zero.size(), rows, kv_map(p),
                                      (int64_t)p->desc.H * p->desc.D, dk, dv, (hipStream_t)stream),
                     "thdcp_zero_untouched launch");
 }

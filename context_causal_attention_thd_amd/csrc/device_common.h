@@ -109,7 +109,8 @@ __device__ __forceinline__ float shfl_xor32(float x) {
 // Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3):
 // loads at offsets past the end return 0 without touching memory, so a tile
 // whose last rows fall outside the data needs no branch around its loads.
-// `bytes` must be below 2^32; callers check that on the host.
+// `bytes` stays below 2^31 (checked on the host), so an offset of 0xFFFFFFF0
+// is always past the end.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);

@@ -61,20 +61,27 @@ hipError_t launch_scatter(int32_t n_tensors, const void* const* srcs, int64_t n,
 // Head-group pack ([n, cp, G] -> [cp, n, G]) or its inverse, G = group_bytes.
 hipError_t launch_a2a(int32_t n_tensors, const void* const* srcs, int64_t n_tokens, int32_t cp,
                       int64_t group_bytes, void* const* dsts, bool unpack, hipStream_t stream);
+// kv_row (nullable): global row -> row of a and b (identity when null).
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
-                            int64_t row_floats, float* a, float* b, hipStream_t stream);
+                            const int32_t* kv_row, int64_t row_floats, float* a, float* b,
+                            hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
+// kv_row (nullable, [T]): position of global K/V row g in k, v (and dk, dv);
+// null means global order. T is the number of K/V rows.
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, void* o, float* lse,
-                           int64_t n_local, float scale, hipStream_t stream);
+                           const void* q, const void* k, const void* v, const int32_t* kv_row,
+                           int64_t T, void* o, float* lse, int64_t n_local, float scale,
+                           hipStream_t stream);
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                                const void* q, const void* k, const void* v, const void* d_o,
+                                const void* q, const void* k, const void* v,
+                                const int32_t* kv_row, const void* d_o,
                                 const float* lse, const float* delta, float* dk, float* dv,
                                 int64_t n_local, float scale, int32_t accumulate,
                                 hipStream_t stream);
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                              const void* q, const void* k, const void* v, const void* d_o,
+                              const void* q, const void* k, const void* v, const int32_t* kv_row,
+                              int64_t T, const void* d_o,
                               const float* lse, const float* delta, float* dq, int64_t n_local,
                               float scale, hipStream_t stream);
 

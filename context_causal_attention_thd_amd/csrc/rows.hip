@@ -214,6 +214,7 @@ hipError_t launch_a2a(int32_t n_tensors, const void* const* srcs, int64_t n_toke
 __global__ void __launch_bounds__(256) zero_rows_kernel(const ZeroRange* __restrict__ ranges,
                                                         int32_t n_ranges, uint64_t total_vec,
                                                         uint32_t vec_per_row,
+                                                        const int32_t* __restrict__ kv_row,
                                                         float* __restrict__ a,
                                                         float* __restrict__ b) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -226,7 +227,8 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(const ZeroRange* __restr
       const int32_t mid = (lo + hi + 1) >> 1;
       if ((uint64_t)ranges[mid].before <= lin) lo = mid; else hi = mid - 1;
     }
-    const int64_t row = ranges[lo].r0 + (int64_t)(lin - ranges[lo].before);
+    const int64_t g = ranges[lo].r0 + (int64_t)(lin - ranges[lo].before);
+    const int64_t row = kv_row ? kv_row[g] : g;  // global row -> row of a and b
     const int64_t off = row * vec_per_row + c;
     reinterpret_cast<f32x4*>(a)[off] = z;
     reinterpret_cast<f32x4*>(b)[off] = z;
@@ -234,7 +236,8 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(const ZeroRange* __restr
 }
 
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
-                            int64_t row_floats, float* a, float* b, hipStream_t stream) {
+                            const int32_t* kv_row, int64_t row_floats, float* a, float* b,
+                            hipStream_t stream) {
   if (row_floats % 4 != 0) return hipErrorInvalidValue;
   const uint64_t vpr = (uint64_t)row_floats / 4;
   const uint64_t total = vpr * (uint64_t)total_rows;
@@ -242,7 +245,7 @@ hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t t
   uint64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ranges,
-                     n_ranges, total, (uint32_t)vpr, a, b);
+                     n_ranges, total, (uint32_t)vpr, kv_row, a, b);
   return hipGetLastError();
 }
 

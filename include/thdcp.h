@@ -44,6 +44,24 @@ typedef enum {
                                 [r*s_local, (r+1)*s_local), s_local = T/cp_size */
 } thdcp_strategy_t;
 
+/* Row order of the full K/V given to the attention calls, and of the dK/dV
+ * partials they return.
+ *   THDCP_KV_GLOBAL: global (document) order, i.e. after the restore of
+ *     [AG] sequence diagram ("restore K/V"); dK/dV come back in global order
+ *     and are unrestored by the caller before the reduce-scatter.
+ *   THDCP_KV_RANK_MAJOR: the order the all-gather delivers -- rank 0's local
+ *     rows, then rank 1's, ... (row p is global row idx[p] of the all-ranks
+ *     permutation, thd_partition_index with rank = -1). The kernels read K/V
+ *     rows and write dK/dV rows through the plan's map from global row to
+ *     rank-major position, so the restore before attention and the unrestore
+ *     after it are fused into their loads and stores, and dK/dV come back in
+ *     the order the reduce-scatter sends. Under NO_LOAD_BALANCE the two orders
+ *     are the same ([A2A] body: the reorder copy disappears). */
+typedef enum {
+  THDCP_KV_GLOBAL = 0,
+  THDCP_KV_RANK_MAJOR = 1
+} thdcp_kv_layout_t;
+
 typedef enum {
   THDCP_OK = 0,
   THDCP_ERR_ARG = 1,         /* bad pointer, size or flag combination */
@@ -183,6 +201,7 @@ typedef struct {
   int32_t window_left;       /* must be -1 */
   int32_t window_right;      /* must be 0  */
   int32_t pad_between_seqs;  /* -1 detect by value, 0 none, 1 present */
+  int32_t kv_layout;         /* thdcp_kv_layout_t of K/V in and dK/dV out */
 } thdcp_attn_desc;
 
 typedef struct {
@@ -201,8 +220,8 @@ typedef struct {
 /* Build a plan on the host. *plan_out receives a host object the caller
  * releases with thdcp_plan_destroy. No device work. Returns
  * THDCP_ERR_UNSUPPORTED when one document's rows, or the local share's rows,
- * of bf16 [H, D] exceed 4 GiB (the kernels address them with 32-bit buffer
- * offsets). */
+ * of bf16 [H, D] reach 2 GiB (the kernels address them with 32-bit buffer
+ * offsets), or, for THDCP_KV_RANK_MAJOR, when all T rows do. */
 thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan_out);
 thdcp_status_t thdcp_plan_get_info(thdcp_plan_t plan, thdcp_plan_info* info_out);
 /* Per-document count of real tokens this rank holds (int32 [B], host). */
@@ -223,7 +242,7 @@ void thdcp_plan_destroy(thdcp_plan_t plan);
  * j of its own document with j <= g:
  *   O = softmax(scale * q K^T) V,   LSE = log sum exp(scale * q K^T).
  *   q_local  bf16 [n_local, H, D]   local queries in local row order
- *   k, v     bf16 [T, H, D]         full K/V in global order (after restore)
+ *   k, v     bf16 [T, H, D]         full K/V in the plan's kv_layout
  *   o_local  bf16 [n_local, H, D]   written for every local row
  *   lse      fp32 [H, n_local]      natural log; -inf on padding rows
  * Padding rows get O = 0. Padding key rows are never read into a product.
@@ -237,8 +256,10 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k
  * reduce-scatter).
  *   o_local, lse  outputs of cp_attn_fwd;  d_o bf16 [n_local, H, D]
  *   dq      fp32 [n_local, H, D]   fully written (padding rows 0)
- *   dk, dv  fp32 [T, H, D]         this rank's partial: rows attended by at
- *                                  least one local query are written
+ *   k, v    bf16 [T, H, D] in the plan's kv_layout
+ *   dk, dv  fp32 [T, H, D]         this rank's partial, in the plan's
+ *                                  kv_layout: rows attended by at least one
+ *                                  local query are written
  *                                  (accumulate_dkv = 1: added to dk/dv)
  *   zero_untouched = 1: also write 0 to every other row of dk/dv -- padding
  *   rows, the buffer tail and keys no local query attends. The zeroing runs

@@ -55,9 +55,12 @@ def device():
 
 
 def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
-              accumulate=False):
+              accumulate=False, kv_layout="global"):
     """Product path on cuda:0 for one rank: partition index -> gather local Q
-    and dO -> plan -> forward -> backward. Returns numpy arrays."""
+    and dO -> plan -> forward -> backward. Returns numpy arrays. With
+    kv_layout="rank_major" K/V are passed in the all-gathered (rank-major)
+    order and dK/dV come back in that order; "perm" is the all-ranks
+    permutation (rank-major position p holds global row perm[p])."""
     import torch
     import context_causal_attention_thd_amd as thd
     dev = device()
@@ -67,7 +70,11 @@ def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
     idx = thd.partition_index(cup, cup_dev, w.T, w.cp_size, rank, w.strategy)
     q_local = thd.gather(q, idx)
     do_local = thd.gather(do, idx)
-    plan = thd.Plan(cu, cup, w.T, w.cp_size, rank, w.strategy, w.H, w.D)
+    perm = None
+    if kv_layout == "rank_major":
+        perm = thd.partition_index(cup, cup_dev, w.T, w.cp_size, -1, w.strategy)
+        k, v = thd.gather(k, perm), thd.gather(v, perm)
+    plan = thd.Plan(cu, cup, w.T, w.cp_size, rank, w.strategy, w.H, w.D, kv_layout=kv_layout)
     o, lse = thd.attn_fwd(plan, q_local, k, v)
     dk = None if dk_init is None else dk_init.to(dev).clone()
     dv = None if dv_init is None else dv_init.to(dev).clone()
@@ -75,7 +82,8 @@ def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
                               zero_untouched=zero_untouched, accumulate_dkv=accumulate)
     torch.cuda.synchronize()
     out = dict(idx=idx.cpu().numpy(), o=o.float().cpu().numpy(), lse=lse.cpu().numpy(),
-               dq=dq.cpu().numpy(), dk=dk.cpu().numpy(), dv=dv.cpu().numpy(), plan=plan)
+               dq=dq.cpu().numpy(), dk=dk.cpu().numpy(), dv=dv.cpu().numpy(), plan=plan,
+               perm=None if perm is None else perm.cpu().numpy())
     return out
 
 

@@ -125,6 +125,47 @@ def test_plan_rejects_unsupported(L):
     assert ei.value.status == 3
 
 
+def test_plan_kv_layout(L):
+    w = W.WORKLOADS["tiny_nlb"]
+    args = (w.cu_seqlens(), w.cu_seqlens_padded(), w.T, 2, 0, w.strategy, 2, 64)
+    with pytest.raises(ValueError):
+        thd.Plan(*args, upload=False, kv_layout="bogus")
+    # the C ABI rejects a value outside the enum
+    d = thd._Desc()
+    cup = np.ascontiguousarray(w.cu_seqlens_padded(), dtype=np.int32)
+    d.cu_seqlens_padded_host = cup.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    d.B, d.T, d.cp_size, d.rank, d.strategy, d.H, d.D = len(cup) - 1, w.T, 2, 0, 1, 2, 64
+    d.window_left, d.window_right, d.pad_between_seqs, d.kv_layout = -1, 0, -1, 7
+    h = ctypes.c_void_p()
+    assert L.thdcp_plan_create(ctypes.byref(d), ctypes.byref(h)) == 1
+    # the map from global row to rank-major position is part of the workspace
+    # only when the two orders differ (DUAL_CHUNK_SWAP, cp_size > 1)
+    for name in ("dcs_8k", "nlb_32k"):
+        x = W.WORKLOADS[name]
+        a = (x.cu_seqlens(), x.cu_seqlens_padded(), x.T, x.cp_size, x.rank, x.strategy, x.H, x.D)
+        g = thd.Plan(*a, upload=False)
+        m = thd.Plan(*a, upload=False, kv_layout="rank_major")
+        extra = m.info.workspace_bytes - g.info.workspace_bytes
+        if x.strategy == "dual_chunk_swap":
+            assert extra >= 4 * x.T
+        else:
+            assert extra == 0
+        assert (m.info.causal_pairs, m.info.n_fwd_tiles, m.info.n_bwd_tiles) == \
+            (g.info.causal_pairs, g.info.n_fwd_tiles, g.info.n_bwd_tiles)
+        g.close()
+        m.close()
+    # rank-major K/V are addressed as one buffer: 2 GiB of rows or more is
+    # refused (16 docs of 64Ki rows of 4 KiB, cp_size 4: every document and
+    # the local share stay below the per-document and per-share limits)
+    T = 1 << 20
+    cup = np.arange(0, T + 1, T // 16, dtype=np.int32)
+    a = (None, cup, T, 4, 0, "dual_chunk_swap", 16, 128)
+    thd.Plan(*a, upload=False).close()
+    with pytest.raises(thd.ThdcpError) as ei:
+        thd.Plan(*a, upload=False, kv_layout="rank_major")
+    assert ei.value.status == 3
+
+
 def test_batched_moves_reject_bad_tensor_counts(L):
     import ctypes
     pv = ctypes.c_void_p

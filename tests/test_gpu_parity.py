@@ -348,6 +348,34 @@ def test_zero_untouched_gate_and_accumulate():
     assert p.info.n_zero_ranges == 0 and p.info.untouched_rows == 0
 
 
+@pytest.mark.parametrize("name", ["dcs_pad_d128", "dcs_cp4_d64", "nlb_tail_d128", "dcs_8k",
+                                  "pad_131k"])
+def test_rank_major_kv_fuses_restore(name):
+    """K/V passed as the all-gather delivers them (rank-major) and dK/dV
+    returned in that order: the restore and unrestore are fused into the
+    kernels' loads and stores, so every output is bit-identical to the
+    global-order call (dK/dV permuted), which the other tests check against
+    the oracle; one small layout is also checked against the oracle directly."""
+    small = {x.name: x for x in SMALL}
+    w = small.get(name) or W.WORKLOADS[name]
+    t = W.bf16_tensors(w)
+    ranks = range(w.cp_size) if name in small else [w.rank]
+    for r in ranks:
+        _say("rank-major K/V", name, "rank", r)
+        g = run_share(w, r, t)
+        m = run_share(w, r, t, kv_layout="rank_major")
+        perm = m["perm"]
+        assert sorted(perm.tolist()) == list(range(w.T))
+        for n in ("o", "lse", "dq"):
+            assert np.array_equal(m[n], g[n]), n
+        for n in ("dk", "dv"):
+            assert np.array_equal(m[n], g[n][perm]), n
+        if name == "dcs_pad_d128":
+            ref = oracle_share(w, r, f64(t))
+            ref["dk"], ref["dv"] = ref["dk"][perm], ref["dv"][perm]
+            _cmp_all(m, ref, f"{name} r{r} rank-major")
+
+
 # ---------------------------------------------------------------- full sizes
 
 FULL = ["tiny_nlb", "dcs_8k", "nlb_32k", "flat_75k", "pad_131k"]
