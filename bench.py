@@ -7,9 +7,10 @@ A step is one pass of the whole hot path for the measured rank over one batch:
   attention forward (O, LSE) on K and V as the all-gather delivers them
     (rank-major): the restore to global order is fused into the kernels'
     K/V loads through the plan's row map,
-  attention backward (preprocess, dK/dV, dQ, gated zeroing of untouched rows),
-    whose dK/dV stores go straight to rank-major order for the reduce-scatter
-    (the unrestore fused the same way).
+  attention backward in two launches: dQ (which also computes the
+    preprocess term delta = rowsum(dO * O)), then dK/dV (whose grid ends with
+    the gated zeroing of untouched rows); the dK/dV stores go straight to
+    rank-major order for the reduce-scatter (the unrestore fused the same way).
 Inputs are synthetic and already resident in HBM when timing starts. The
 standalone K+V restore (one batched gather launch over all T rows) is timed
 separately for the gather roofline.
@@ -45,7 +46,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="dcs_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-a2a", action="store_true",
@@ -123,8 +124,8 @@ def main():
         mine = perm[r * n_local:(r + 1) * n_local]
         thd.gather_many([q, do], mine, [q_local, do_local])
         thd.attn_fwd(plan, q_local, k_rm, v_rm, o=o, lse=lse)
-        thd.attn_bwd_parts(plan, q_local, k_rm, v_rm, o, lse, do_local, dq, dk_rm, dv_rm,
-                           scratch, zero_untouched=True)
+        thd.attn_bwd(plan, q_local, k_rm, v_rm, o, lse, do_local, dq=dq, dk=dk_rm, dv=dv_rm,
+                     zero_untouched=True, scratch=scratch, stream=stream)
         return plan  # keep alive until the stream is synchronized
 
     # Whole steps: no events inside the timed region.

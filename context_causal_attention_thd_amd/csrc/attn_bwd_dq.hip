@@ -38,13 +38,17 @@ struct DqSmem {
 };
 
 // MAPPED: K/V rows are found through kv_row (rank-major K/V) instead of by key.
-template <int D, bool MAPPED>
+// DELTA: compute delta = rowsum(dO * O) for the tile's rows here (from the
+// dO fragments already loaded and the matching O fragments) and write it for
+// the dK/dV kernel, instead of reading it from a separate preprocess launch.
+template <int D, bool MAPPED, bool DELTA>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                    const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const int32_t* __restrict__ kv_row, uint32_t kv_bytes,
-                   const bf16* __restrict__ d_o, const float* __restrict__ lse,
-                   const float* __restrict__ delta, float* __restrict__ dq, int64_t n_local,
+                   const bf16* __restrict__ d_o, const bf16* __restrict__ o,
+                   const float* __restrict__ lse, float* __restrict__ delta,
+                   float* __restrict__ dq, int64_t n_local,
                    float scale, float scale_log2) {
   constexpr int BN = kFwdBN;
   constexpr int KSTEPS = D / 16;
@@ -84,7 +88,23 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
     }
   }
   const float lse2 = valid ? lse[(int64_t)h * n_local + m] * kLog2e : 0.f;
-  const float dlt = valid ? delta[(int64_t)h * n_local + m] : 0.f;
+  float dlt;
+  if constexpr (DELTA) {
+    // This lane holds head dims kk*16 + hh*8 .. +7 of its row's dO; the two
+    // halves of the wave hold the two halves of the row.
+    const int64_t off = m * rs + head_off + hh * 8;
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const bf16x8 of = valid ? load_bf16x8(o + off + kk * 16) : zero_bf16x8();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part = fmaf((float)dof[kk][j], (float)of[j], part);
+    }
+    dlt = part + __shfl_xor(part, 32, 64);  // 0 on padding rows (dO taken as 0)
+    if (hh == 0 && in_tile) delta[(int64_t)h * n_local + m] = dlt;
+  } else {
+    dlt = valid ? delta[(int64_t)h * n_local + m] : 0.f;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -242,11 +262,30 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
 
 }  // namespace
 
+namespace {
+
+template <int D, bool M>
+void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int32_t H,
+                  const bf16* q, const bf16* k, const bf16* v, const int32_t* kv_row,
+                  uint32_t kvb, const bf16* d_o, const bf16* o, const float* lse, float* delta,
+                  float* dq, int64_t n_local, float scale) {
+  if (o)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, true>), dim3((unsigned)blocks), dim3(kThreads),
+                       0, stream, tiles, H, q, k, v, kv_row, kvb, d_o, o, lse, delta, dq, n_local,
+                       scale, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, false>), dim3((unsigned)blocks), dim3(kThreads),
+                       0, stream, tiles, H, q, k, v, kv_row, kvb, d_o, o, lse, delta, dq, n_local,
+                       scale, scale * kLog2e);
+}
+
+}  // namespace
+
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                               const void* q, const void* k, const void* v, const int32_t* kv_row,
-                              int64_t T, const void* d_o,
-                              const float* lse, const float* delta, float* dq, int64_t n_local,
-                              float scale, hipStream_t stream) {
+                              int64_t T, const void* d_o, const void* o, const float* lse,
+                              float* delta, float* dq, int64_t n_local, float scale,
+                              hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -254,19 +293,20 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
   const bf16* db = static_cast<const bf16*>(d_o);
+  const bf16* ob = static_cast<const bf16*>(o);
   const int64_t kv_bytes = T * H * D * 2;
   if (kv_row && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const uint32_t kvb = kv_row ? (uint32_t)kv_bytes : 0u;
-#define THDCP_DQ_LAUNCH(DD, M)                                                               \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD, M>), dim3((unsigned)blocks), dim3(kThreads), 0,   \
-                     stream, tiles, H, qb, kb, vb, kv_row, kvb, db, lse, delta, dq, n_local,   \
-                     scale, scale * kLog2e)
-  if (D == 128 && kv_row) THDCP_DQ_LAUNCH(128, true);
-  else if (D == 128) THDCP_DQ_LAUNCH(128, false);
-  else if (D == 64 && kv_row) THDCP_DQ_LAUNCH(64, true);
-  else if (D == 64) THDCP_DQ_LAUNCH(64, false);
-  else return hipErrorInvalidValue;
-#undef THDCP_DQ_LAUNCH
+  if (D == 128 && kv_row)
+    launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
+  else if (D == 128)
+    launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
+  else if (D == 64 && kv_row)
+    launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
+  else if (D == 64)
+    launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

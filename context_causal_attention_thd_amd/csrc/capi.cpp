@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <string>
 #include <vector>
@@ -517,6 +518,91 @@ thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t p, int32_t* out) {
   return ok();
 }
 
+namespace {
+
+// Page-locked staging for plan uploads. An asynchronous host-to-device copy
+// inside the compute stream (pageable or page-locked source) left 15-30 us of
+// idle GPU time per upload on MI355X, the largest gap in a dcs_8k step. The
+// plan is instead copied into a page-locked slot on the host and moved into
+// the workspace by a small copy kernel on the same stream, which reads the
+// slot over the host link. One ring per process, allocated on first use and
+// kept until exit (never freed while a copy may read it). Each upload takes
+// the next slot; an event recorded after its copy says when the slot may be
+// refilled, which is normally long done (the host would have to run kSlots
+// uploads ahead of the GPU to wait on it).
+class StagingRing {
+ public:
+  static constexpr size_t kSlotBytes = size_t(1) << 20;
+  static constexpr int kSlots = 16;
+
+  // Enqueues the copy of n bytes at src to dst on stream. Returns false (and
+  // enqueues nothing) when the ring cannot take it: n above a slot, or the
+  // page-locked allocation failed; the caller then copies directly.
+  bool upload(void* dst, const void* src, size_t n, hipStream_t stream, hipError_t* err) {
+    if (n > kSlotBytes) return false;
+    std::lock_guard<std::mutex> lock(mu_);
+    if (!ready_ && !init()) return false;
+    Slot& sl = slots_[next_];
+    next_ = (next_ + 1) % kSlots;
+    if (sl.pending) {
+      *err = hipEventSynchronize(sl.ev);
+      if (*err != hipSuccess) return true;
+      sl.pending = false;
+    }
+    memcpy(sl.host, src, n);
+    *err = launch_copy16(sl.dev, dst, (int64_t)n, stream);
+    if (*err != hipSuccess) return true;
+    *err = hipEventRecord(sl.ev, stream);
+    sl.pending = *err == hipSuccess;
+    return true;
+  }
+
+ private:
+  struct Slot {
+    char* host = nullptr;
+    const void* dev = nullptr;  // the slot as the GPU addresses it
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+
+  bool init() {
+    if (failed_) return false;
+    char* base = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void**>(&base), kSlotBytes * kSlots,
+                      hipHostMallocPortable | hipHostMallocMapped) != hipSuccess) {
+      failed_ = true;
+      return false;
+    }
+    void* dbase = nullptr;
+    if (hipHostGetDevicePointer(&dbase, base, 0) != hipSuccess) {
+      failed_ = true;  // the page-locked block stays allocated until exit
+      return false;
+    }
+    for (int i = 0; i < kSlots; ++i) {
+      slots_[i].host = base + i * kSlotBytes;
+      slots_[i].dev = static_cast<const char*>(dbase) + i * kSlotBytes;
+      if (hipEventCreateWithFlags(&slots_[i].ev, hipEventDisableTiming) != hipSuccess) {
+        failed_ = true;  // the page-locked block stays allocated until exit
+        return false;
+      }
+    }
+    ready_ = true;
+    return true;
+  }
+
+  std::mutex mu_;
+  Slot slots_[kSlots];
+  int next_ = 0;
+  bool ready_ = false, failed_ = false;
+};
+
+StagingRing& staging_ring() {
+  static StagingRing* ring = new StagingRing();  // never destroyed: copies may be in flight at exit
+  return *ring;
+}
+
+}  // namespace
+
 thdcp_status_t thdcp_plan_upload(thdcp_plan_t p, void* ws, size_t bytes, void* stream) {
   if (!p || !ws) return fail(THDCP_ERR_ARG, "NULL argument");
   if (bytes < p->ws_bytes)
@@ -524,8 +610,10 @@ thdcp_status_t thdcp_plan_upload(thdcp_plan_t p, void* ws, size_t bytes, void* s
                 p->ws_bytes);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return fail(THDCP_ERR_ARG, "workspace must be 256-byte aligned");
-  hipError_t e = hipMemcpyAsync(ws, p->blob.data(), p->ws_bytes, hipMemcpyHostToDevice,
-                                (hipStream_t)stream);
+  hipError_t e = hipSuccess;
+  if (!staging_ring().upload(ws, p->blob.data(), p->ws_bytes, (hipStream_t)stream, &e))
+    e = hipMemcpyAsync(ws, p->blob.data(), p->ws_bytes, hipMemcpyHostToDevice,
+                       (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "plan upload");
   p->ws_dev = static_cast<char*>(ws);
   return ok();
@@ -610,7 +698,7 @@ thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t p, const void* q, const void* k, co
       launch_attn_bwd_dkdv(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
                            (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p),
                            d_o, lse, static_cast<const float*>(scratch), dk, dv, p->n_local,
-                           p->scale, accumulate_dkv, (hipStream_t)stream),
+                           p->scale, accumulate_dkv, nullptr, 0, 0, (hipStream_t)stream),
       "cp_attn_bwd_dkdv launch");
 }
 
@@ -627,8 +715,9 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
   return hip_status(
       launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                          (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p),
-                         p->desc.T, d_o, lse, static_cast<const float*>(scratch), dq,
-                         p->n_local, p->scale, (hipStream_t)stream),
+                         p->desc.T, d_o, nullptr, lse,
+                         static_cast<float*>(const_cast<void*>(scratch)), dq, p->n_local,
+                         p->scale, (hipStream_t)stream),
       "cp_attn_bwd_dq launch");
 }
 
@@ -664,14 +753,32 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (!scratch || scratch_bytes < scratch_need(p))
     return fail(THDCP_ERR_ARG, "scratch of %zu bytes is below the %zu needed", scratch_bytes,
                 scratch_need(p));
-  st = cp_attn_bwd_preprocess(p, o, lse, d_o, scratch, scratch_bytes, stream);
-  if (st != THDCP_OK) return st;
-  st = cp_attn_bwd_dkdv(p, q, k, v, lse, d_o, dk, dv, accumulate_dkv, scratch, scratch_bytes,
-                        stream);
-  if (st != THDCP_OK) return st;
-  st = cp_attn_bwd_dq(p, q, k, v, lse, d_o, dq, scratch, scratch_bytes, stream);
-  if (st != THDCP_OK) return st;
-  if (zero_untouched) return thdcp_zero_untouched(p, dk, dv, stream);
+  if (p->n_local == 0) {
+    if (zero_untouched) return thdcp_zero_untouched(p, dk, dv, stream);
+    return ok();
+  }
+  // Two launches: the dQ kernel also computes delta = rowsum(dO * O) into the
+  // scratch (no separate preprocess launch), then the dK/dV kernel, whose grid
+  // ends with the gated zeroing of untouched rows when the caller asks for it
+  // and the plan has such rows (no separate zeroing launch).
+  float* delta = static_cast<float*>(scratch);
+  if (!p->fwd.empty()) {
+    hipError_t e = launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
+                                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v,
+                                      kv_map(p), p->desc.T, d_o, o, lse, delta, dq, p->n_local,
+                                      p->scale, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dq launch");
+  }
+  const bool zero = zero_untouched && !p->zero.empty();
+  if (!p->bwd.empty() || zero) {
+    hipError_t e = launch_attn_bwd_dkdv(
+        reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd), (int32_t)p->bwd.size(),
+        p->desc.H, p->desc.D, q, k, v, kv_map(p), d_o, lse, delta, dk, dv, p->n_local, p->scale,
+        accumulate_dkv, zero ? reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_zero) : nullptr,
+        zero ? (int32_t)p->zero.size() : 0, zero ? p->desc.T - p->touched : 0,
+        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dkdv launch");
+  }
   return ok();
 }
 

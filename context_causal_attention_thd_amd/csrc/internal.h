@@ -61,6 +61,9 @@ hipError_t launch_scatter(int32_t n_tensors, const void* const* srcs, int64_t n,
 // Head-group pack ([n, cp, G] -> [cp, n, G]) or its inverse, G = group_bytes.
 hipError_t launch_a2a(int32_t n_tensors, const void* const* srcs, int64_t n_tokens, int32_t cp,
                       int64_t group_bytes, void* const* dsts, bool unpack, hipStream_t stream);
+// bytes (a multiple of 16) from src (device-readable, e.g. page-locked host
+// memory) to dst, by a kernel on `stream`.
+hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 // kv_row (nullable): global row -> row of a and b (identity when null).
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
                             const int32_t* kv_row, int64_t row_floats, float* a, float* b,
@@ -73,16 +76,20 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
                            const void* q, const void* k, const void* v, const int32_t* kv_row,
                            int64_t T, void* o, float* lse, int64_t n_local, float scale,
                            hipStream_t stream);
+// zr/n_zr/zero_rows (nullable / 0): also zero the dK/dV rows no local query
+// attends, with extra workgroups at the end of the same launch.
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                                 const void* q, const void* k, const void* v,
-                                const int32_t* kv_row, const void* d_o,
-                                const float* lse, const float* delta, float* dk, float* dv,
-                                int64_t n_local, float scale, int32_t accumulate,
-                                hipStream_t stream);
+                                const int32_t* kv_row, const void* d_o, const float* lse,
+                                const float* delta, float* dk, float* dv, int64_t n_local,
+                                float scale, int32_t accumulate, const ZeroRange* zr,
+                                int32_t n_zr, int64_t zero_rows, hipStream_t stream);
+// o (nullable): when given, delta = rowsum(dO * O) is computed by this launch
+// and written to `delta` for the dK/dV kernel; otherwise `delta` is read.
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                               const void* q, const void* k, const void* v, const int32_t* kv_row,
-                              int64_t T, const void* d_o,
-                              const float* lse, const float* delta, float* dq, int64_t n_local,
-                              float scale, hipStream_t stream);
+                              int64_t T, const void* d_o, const void* o, const float* lse,
+                              float* delta, float* dq, int64_t n_local, float scale,
+                              hipStream_t stream);
 
 }  // namespace thdcp

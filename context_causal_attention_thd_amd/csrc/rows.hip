@@ -250,6 +250,30 @@ hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t t
 }
 
 // ---------------------------------------------------------------------------
+// Plan upload: a plain 16-byte copy from page-locked host memory (read by the
+// GPU over the host link) into the caller's workspace. A kernel keeps the
+// upload on the compute queue; a copy-engine transfer inside the stream costs
+// ~15 us of idle GPU time for the queue hand-off (measured on MI355X).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) copy16_kernel(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (bytes % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(copy16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Backward preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32).
 // One group of D/8 lanes per (row, head); each lane reads 16 bytes of O and dO.
 // ---------------------------------------------------------------------------

@@ -229,8 +229,11 @@ thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
 /* Copy the plan's device tables into the caller's workspace (device,
  * >= workspace_bytes, 256-byte aligned) with one async host-to-device copy on
  * `stream`. The plan keeps the pointer; the workspace must stay alive and
- * unmodified while forward/backward calls using the plan are in flight. The
- * host source stays owned by the plan, which must outlive the copy. */
+ * unmodified while forward/backward calls using the plan are in flight.
+ * Tables up to 1 MiB are first copied into a page-locked staging slot the
+ * library keeps for the life of the process (16 slots, 16 MiB, allocated on
+ * the first upload); larger ones are copied from the plan itself, which must
+ * then outlive the copy. */
 thdcp_status_t thdcp_plan_upload(thdcp_plan_t plan, void* workspace_dev, size_t bytes,
                                  void* stream);
 void thdcp_plan_destroy(thdcp_plan_t plan);
@@ -267,6 +270,9 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k
  *   ([PAD] "Expected behavior": gate tail zeroing on the metadata).
  *   zero_untouched and accumulate_dkv are mutually exclusive.
  *   scratch  device, >= bwd_scratch_bytes, 256-byte aligned.
+ * Two launches: the dQ kernel, which also computes delta = rowsum(dO * O)
+ * into scratch, then the dK/dV kernel, whose grid ends with the zeroing
+ * workgroups when zero_untouched = 1 and the plan has such rows.
  * No atomics are used: every output row is written by exactly one workgroup,
  * so dQ, dK and dV are bit-identical from run to run.
  */
@@ -277,9 +283,12 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k
                            size_t scratch_bytes, void* stream);
 
 /*
- * The launches cp_attn_bwd makes, exposed for callers that schedule or time
- * them separately. Calling them in this order on one stream is exactly
- * cp_attn_bwd.
+ * The backward as separate launches, for callers that schedule or time them
+ * one by one. Calling preprocess, dkdv, dq and thdcp_zero_untouched in this
+ * order on one stream computes the gradients cp_attn_bwd computes (which
+ * folds the preprocess into its dQ launch and the zeroing into its dK/dV
+ * launch); delta is summed in a different order there, so the two agree to
+ * rounding, not bit for bit.
  *   cp_attn_bwd_preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32,
  *     [H, n_local], into scratch).
  *   cp_attn_bwd_dkdv: the dK/dV partials (key-tile-major; written, or added

@@ -376,6 +376,49 @@ def test_rank_major_kv_fuses_restore(name):
             _cmp_all(m, ref, f"{name} r{r} rank-major")
 
 
+@pytest.mark.parametrize("kv_layout", ["global", "rank_major"])
+def test_bwd_parts_match_composite(kv_layout):
+    """cp_attn_bwd (two launches: dQ computing delta, dK/dV with the zeroing
+    workgroups) against its separate launches (preprocess, dK/dV, dQ, zeroing):
+    the same gradients up to the summation order of delta."""
+    w = SMALL[0]
+    t = W.bf16_tensors(w)
+    dev = device()
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    cup_dev = torch.from_numpy(cup).to(dev)
+    q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
+    if kv_layout == "rank_major":
+        perm = thd.partition_index(cup, cup_dev, w.T, w.cp_size, -1, w.strategy)
+        k, v = thd.gather(k, perm), thd.gather(v, perm)
+    for r in range(w.cp_size):
+        _say("bwd parts vs composite", kv_layout, "rank", r)
+        idx = thd.partition_index(cup, cup_dev, w.T, w.cp_size, r, w.strategy)
+        ql, dol = thd.gather(q, idx), thd.gather(do, idx)
+        plan = thd.Plan(cu, cup, w.T, w.cp_size, r, w.strategy, w.H, w.D, kv_layout=kv_layout)
+        o, lse = thd.attn_fwd(plan, ql, k, v)
+        fill = torch.full((w.T, w.H, w.D), 3.0, device=dev)
+        a = thd.attn_bwd(plan, ql, k, v, o, lse, dol, dk=fill.clone(), dv=fill.clone())
+        scratch = torch.empty(int(plan.info.bwd_scratch_bytes), dtype=torch.uint8, device=dev)
+        dq = torch.empty_like(a[0])
+        b = thd.attn_bwd_parts(plan, ql, k, v, o, lse, dol, dq, fill.clone(), fill.clone(),
+                               scratch)
+        torch.cuda.synchronize()
+        # rows that must be exactly zero: padding query rows of dQ; untouched
+        # key rows of dK/dV (zeroed by the composite, by the zeroing launch in
+        # the parts), in the layout of dk/dv
+        _, _, valid = O.token_table(cu, cup, w.T)
+        gidx = idx.cpu().numpy()
+        untouched = ~O.touched_keys(cu, cup, w.T, gidx)
+        if kv_layout == "rank_major":
+            untouched = untouched[perm.cpu().numpy()]
+        must_zero = {"dq": ~valid[gidx], "dk": untouched, "dv": untouched}
+        for x, y, n in zip(a, b, ("dq", "dk", "dv")):
+            x, y = x.cpu().numpy(), y.cpu().numpy()
+            assert np.all(np.isfinite(x)), n
+            assert np.all(x[must_zero[n]] == 0) and np.all(y[must_zero[n]] == 0), n
+            assert np.abs(x - y).max() <= 1e-4 * max(1.0, np.abs(y).max()), n
+
+
 # ---------------------------------------------------------------- full sizes
 
 FULL = ["tiny_nlb", "dcs_8k", "nlb_32k", "flat_75k", "pad_131k"]
