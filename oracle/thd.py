@@ -396,6 +396,121 @@ def attention_bwd(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded, T
     return dq, dk, dv
 
 
+# --------------------------------------------------------------------------
+# P2P (ring) context parallelism
+# --------------------------------------------------------------------------
+# [PAD] "Describe the bug": under P2P context parallelism a rank's attention
+# runs in steps, each against the K/V one peer holds, with per-step sequence
+# metadata (get_cu_seqlens_on_cp_rank) and gradient tails to clear. The pages
+# do not spell out the ring, so the plainest reading is taken: at step i rank
+# r works on the keys held by rank (r - i) mod cp_size; the step results are
+# merged through their log-sum-exp; the backward of a step uses the softmax of
+# the whole key set (its LSE and delta = rowsum(dO * O) of the merged output).
+
+def owner_ranks(cu_seqlens_padded, T: int, cp_size: int, strategy: str) -> np.ndarray:
+    """owner[g] = the rank whose local share holds global row g."""
+    owner = np.full(T, -1, dtype=np.int64)
+    for r in range(cp_size):
+        owner[partition_index(cu_seqlens_padded, T, cp_size, r, strategy)] = r
+    return owner
+
+
+def p2p_source(rank: int, step: int, cp_size: int) -> int:
+    """Rank whose K/V rank ``rank`` attends at ring step ``step``."""
+    return (rank - step) % cp_size
+
+
+def attention_fwd_keys(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T: int, key_ok,
+                       scale: Optional[float] = None):
+    """``attention_fwd`` restricted to the keys j with key_ok[j] (one P2P step:
+    the keys one rank holds). A row with no allowed key gets O = 0, LSE = -inf."""
+    q_local = np.asarray(q_local, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    key_ok = np.asarray(key_ok, dtype=bool)
+    n, H, D = q_local.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = np.zeros((n, H, v.shape[2]), dtype=np.float64)
+    lse = np.full((H, n), -np.inf, dtype=np.float64)
+    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, None):
+        kend = int(gs.max()) + 1
+        drop = ~key_ok[a:kend]
+        for h in range(H):
+            kk = k[a:kend, h]
+            vv = v[a:kend, h]
+            for r0, r1 in _chunks(len(ms), kend - a):
+                s = _scores(q_local[ms[r0:r1], h], kk, gs[r0:r1], a, scale)
+                s[:, drop] = -np.inf
+                mx = s.max(axis=1)
+                some = np.isfinite(mx)
+                e = np.zeros_like(s)
+                e[some] = np.exp(s[some] - mx[some, None])
+                tot = e.sum(axis=1)
+                rows = ms[r0:r1]
+                lse[h, rows[some]] = mx[some] + np.log(tot[some])
+                out[rows[some], h] = (e[some] / tot[some, None]) @ vv
+    return out, lse
+
+
+def lse_merge(parts):
+    """Merge (O_i, LSE_i) of attention over disjoint key sets into the result
+    over their union: LSE = log sum_i exp LSE_i, O = sum_i exp(LSE_i - LSE) O_i.
+    O has shape [n, H, D] and LSE [H, n]; a part with LSE = -inf adds nothing."""
+    lses = np.stack([np.asarray(l, dtype=np.float64) for _, l in parts])
+    mx = lses.max(axis=0)
+    some = np.isfinite(mx)
+    safe = np.where(some, mx, 0.0)
+    w = np.exp(lses - safe[None])  # exp(-inf) = 0 for empty parts
+    tot = w.sum(axis=0)
+    lse = np.where(some, safe + np.log(np.where(some, tot, 1.0)), -np.inf)
+    o = np.zeros_like(np.asarray(parts[0][0], dtype=np.float64))
+    for (oi, li), wi in zip(parts, w):
+        coef = np.where(some, wi / np.where(some, tot, 1.0), 0.0)  # [H, n]
+        o += np.asarray(oi, dtype=np.float64) * coef.T[:, :, None]
+    return o, lse
+
+
+def attention_bwd_keys(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded, T: int,
+                       key_ok, lse, delta, scale: Optional[float] = None):
+    """One P2P step of the backward: the part of ``attention_bwd`` that flows
+    through the keys j with key_ok[j]. The probabilities are those of the whole
+    key set, P_j = exp(s_j - LSE) with the merged LSE [H, n], and
+    dS_j = P_j (dP_j - delta) with delta [H, n] = rowsum(dO * O) of the merged
+    output; then dQ_m = scale sum_j dS_j K_j over the step's keys, and dK_j,
+    dV_j for those keys (0 elsewhere)."""
+    q_local = np.asarray(q_local, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do_local = np.asarray(do_local, dtype=np.float64)
+    key_ok = np.asarray(key_ok, dtype=bool)
+    lse = np.asarray(lse, dtype=np.float64)
+    delta = np.asarray(delta, dtype=np.float64)
+    n, H, D = q_local.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = np.zeros((n, H, D), dtype=np.float64)
+    dk = np.zeros((T, H, D), dtype=np.float64)
+    dv = np.zeros((T, H, D), dtype=np.float64)
+    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, None):
+        kend = int(gs.max()) + 1
+        drop = ~key_ok[a:kend]
+        for h in range(H):
+            kk = k[a:kend, h]
+            vv = v[a:kend, h]
+            for r0, r1 in _chunks(len(ms), kend - a):
+                m_sel = ms[r0:r1]
+                qq = q_local[m_sel, h]
+                dd = do_local[m_sel, h]
+                s = _scores(qq, kk, gs[r0:r1], a, scale)
+                p = np.exp(s - lse[h, m_sel][:, None])
+                p[:, drop] = 0.0
+                dp = dd @ vv.T
+                ds = p * (dp - delta[h, m_sel][:, None])
+                dq[m_sel, h] = scale * (ds @ kk)
+                dk[a:kend, h] += scale * (ds.T @ qq)
+                dv[a:kend, h] += p.T @ dd
+    return dq, dk, dv
+
+
 def rank_share(q, k, v, do, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int,
                rank: int, strategy: str, scale: Optional[float] = None):
     """Everything one rank computes, from global-order inputs: idx, O, LSE,
