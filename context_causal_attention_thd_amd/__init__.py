@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "thd_a2a_unpack", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
     "thdcp_plan_upload", "thdcp_plan_destroy", "cp_attn_fwd", "cp_attn_bwd",
     "cp_attn_bwd_preprocess", "cp_attn_bwd_dkdv", "cp_attn_bwd_dq", "thdcp_zero_untouched",
+    "cp_attn_fwd_step", "thdcp_lse_merge", "cp_attn_bwd_step",
 )
 
 
@@ -52,6 +53,7 @@ class _Desc(ctypes.Structure):
         ("window_right", ctypes.c_int32),
         ("pad_between_seqs", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
+        ("p2p", ctypes.c_int32),
     ]
 
 
@@ -125,6 +127,13 @@ def lib() -> ctypes.CDLL:
     L.cp_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.thdcp_zero_untouched.restype = i32
     L.thdcp_zero_untouched.argtypes = [vp, vp, vp, vp]
+    L.cp_attn_fwd_step.restype = i32
+    L.cp_attn_fwd_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
+    L.thdcp_lse_merge.restype = i32
+    L.thdcp_lse_merge.argtypes = [i64, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+    L.cp_attn_bwd_step.restype = i32
+    L.cp_attn_bwd_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp, i32, vp, vp, i32,
+                                   vp]
     _lib_handle = L
     return L
 
@@ -326,7 +335,7 @@ class Plan:
     def __init__(self, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, rank: int, strategy,
                  H: int, D: int, softmax_scale: float = 0.0, window=(-1, 0),
                  pad_between_seqs: int = -1, device=None, stream=None, upload: bool = True,
-                 kv_layout: str = "global"):
+                 kv_layout: str = "global", p2p: bool = False):
         self._cup = _i32_host(cu_seqlens_padded)
         self._cu = None if cu_seqlens is None else _i32_host(cu_seqlens)
         d = _Desc()
@@ -346,6 +355,8 @@ class Plan:
             raise ValueError(f"unknown kv_layout {kv_layout!r} (one of {sorted(KV_LAYOUTS)})")
         d.kv_layout = KV_LAYOUTS[kv_layout]
         self.kv_layout = kv_layout
+        d.p2p = int(bool(p2p))
+        self.p2p = bool(p2p)
         self._handle = ctypes.c_void_p()
         _check(lib().thdcp_plan_create(ctypes.byref(d), ctypes.byref(self._handle)))
         self.T, self.H, self.D, self.cp_size, self.rank = int(T), int(H), int(D), cp_size, rank
@@ -485,6 +496,104 @@ def attn_bwd_parts(plan: Plan, q_local, k, v, o, lse, d_o, dq, dk, dv, scratch,
         _check(L.thdcp_zero_untouched(plan.handle, _dev_ptr(dk, "dk", torch.float32),
                                       _dev_ptr(dv, "dv", torch.float32), st))
     return dq, dk, dv
+
+
+def bwd_preprocess(plan: Plan, o, lse, d_o, scratch, stream=None):
+    """delta = rowsum(O * dO) into ``scratch`` (cp_attn_bwd_preprocess)."""
+    import torch
+    _check(lib().cp_attn_bwd_preprocess(plan.handle, _dev_ptr(o, "o", torch.bfloat16),
+                                        _dev_ptr(lse, "lse", torch.float32),
+                                        _dev_ptr(d_o, "d_o", torch.bfloat16),
+                                        _dev_ptr(scratch, "scratch"),
+                                        scratch.numel() * scratch.element_size(),
+                                        _stream(stream)))
+    return scratch
+
+
+# ---------------------------------------------------------------------------
+# P2P (ring) steps: the plan must be made with p2p=True
+# ---------------------------------------------------------------------------
+
+def attn_fwd_step(plan: Plan, src_rank: int, q_local, k_src, v_src, o_part=None, lse_part=None,
+                  stream=None):
+    """One ring step: local queries against rank src_rank's local K/V
+    ([n_local,H,D] each, in that rank's local order). Returns (o_part bf16
+    [n_local,H,D], lse_part fp32 [H,n_local]); rows with no key in the step
+    get O = 0, LSE = -inf."""
+    import torch
+    n, H, D = plan.n_local, plan.H, plan.D
+    _shape(q_local, (n, H, D), "q_local")
+    _shape(k_src, (n, H, D), "k_src")
+    _shape(v_src, (n, H, D), "v_src")
+    dev = q_local.device
+    if o_part is None:
+        o_part = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((H, n), dtype=torch.float32, device=dev)
+    _check(lib().cp_attn_fwd_step(plan.handle, int(src_rank),
+                                  _dev_ptr(q_local, "q_local", torch.bfloat16),
+                                  _dev_ptr(k_src, "k_src", torch.bfloat16),
+                                  _dev_ptr(v_src, "v_src", torch.bfloat16),
+                                  _dev_ptr(o_part, "o_part", torch.bfloat16),
+                                  _dev_ptr(lse_part, "lse_part", torch.float32),
+                                  _stream(stream)))
+    return o_part, lse_part
+
+
+def lse_merge(o_part, lse_part, o_acc, lse_acc, first: bool, o_out=None, stream=None):
+    """Fold one step's (o_part, lse_part) into (o_acc fp32, lse_acc fp32);
+    o_out (bf16, optional) receives the merged output."""
+    import torch
+    n, H, D = o_part.shape
+    _shape(lse_part, (H, n), "lse_part")
+    _shape(o_acc, (n, H, D), "o_acc")
+    _shape(lse_acc, (H, n), "lse_acc")
+    if o_out is not None:
+        _shape(o_out, (n, H, D), "o_out")
+    _check(lib().thdcp_lse_merge(int(n), int(H), int(D),
+                                 _dev_ptr(o_part, "o_part", torch.bfloat16),
+                                 _dev_ptr(lse_part, "lse_part", torch.float32),
+                                 _dev_ptr(o_acc, "o_acc", torch.float32),
+                                 _dev_ptr(lse_acc, "lse_acc", torch.float32), int(bool(first)),
+                                 None if o_out is None else _dev_ptr(o_out, "o_out",
+                                                                     torch.bfloat16),
+                                 _stream(stream)))
+    return o_acc, lse_acc
+
+
+def attn_bwd_step(plan: Plan, src_rank: int, q_local, k_src, v_src, lse, d_o, scratch, dq,
+                  accumulate_dq: bool, dk_src=None, dv_src=None, zero_untouched: bool = True,
+                  stream=None):
+    """Backward of one ring step with the merged LSE; ``scratch`` holds delta
+    of the merged output (bwd_preprocess). dq fp32 [n_local,H,D] is written or
+    added to; returns (dq, dk_src, dv_src), the last two fp32 [n_local,H,D] in
+    rank src_rank's local order."""
+    import torch
+    n, H, D = plan.n_local, plan.H, plan.D
+    _shape(k_src, (n, H, D), "k_src")
+    _shape(v_src, (n, H, D), "v_src")
+    _shape(dq, (n, H, D), "dq")
+    dev = q_local.device
+    mk = torch.empty if zero_untouched else torch.zeros
+    if dk_src is None:
+        dk_src = mk((n, H, D), dtype=torch.float32, device=dev)
+    if dv_src is None:
+        dv_src = mk((n, H, D), dtype=torch.float32, device=dev)
+    _shape(dk_src, (n, H, D), "dk_src")
+    _shape(dv_src, (n, H, D), "dv_src")
+    _check(lib().cp_attn_bwd_step(plan.handle, int(src_rank),
+                                  _dev_ptr(q_local, "q_local", torch.bfloat16),
+                                  _dev_ptr(k_src, "k_src", torch.bfloat16),
+                                  _dev_ptr(v_src, "v_src", torch.bfloat16),
+                                  _dev_ptr(lse, "lse", torch.float32),
+                                  _dev_ptr(d_o, "d_o", torch.bfloat16),
+                                  _dev_ptr(scratch, "scratch"),
+                                  scratch.numel() * scratch.element_size(),
+                                  _dev_ptr(dq, "dq", torch.float32), int(bool(accumulate_dq)),
+                                  _dev_ptr(dk_src, "dk_src", torch.float32),
+                                  _dev_ptr(dv_src, "dv_src", torch.float32),
+                                  int(bool(zero_untouched)), _stream(stream)))
+    return dq, dk_src, dv_src
 
 
 def _shape(t, shape: Sequence[int], name: str):

@@ -26,7 +26,7 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"),
     # Packed-fp32 VALU ops stay off: ordinary float code is used instead.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
 ]
 
 

@@ -53,8 +53,8 @@ constexpr int kZeroRowsPerBlock = 8;
 // run in the tail of the launch, on CUs the last key tiles leave idle.
 __device__ void zero_untouched_block(int64_t b, const ZeroRange* __restrict__ zr, int32_t n_zr,
                                      int64_t zero_rows, const int32_t* __restrict__ kv_row,
-                                     int64_t row_floats, float* __restrict__ dk,
-                                     float* __restrict__ dv) {
+                                     int32_t kv_sub, int64_t row_floats,
+                                     float* __restrict__ dk, float* __restrict__ dv) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   const int64_t vpr = row_floats / 4;
   for (int rr = 0; rr < kZeroRowsPerBlock; ++rr) {
@@ -66,7 +66,7 @@ __device__ void zero_untouched_block(int64_t b, const ZeroRange* __restrict__ zr
       if ((int64_t)zr[mid].before <= lin) lo = mid; else hi = mid - 1;
     }
     const int64_t g = zr[lo].r0 + (lin - zr[lo].before);
-    const int64_t row = kv_row ? kv_row[g] : g;  // global row -> row of dk/dv
+    const int64_t row = (kv_row ? kv_row[g] : g) - kv_sub;  // global row -> row of dk/dv
     f32x4* a = reinterpret_cast<f32x4*>(dk + row * row_floats);
     f32x4* c = reinterpret_cast<f32x4*>(dv + row * row_floats);
     for (int64_t i = threadIdx.x; i < vpr; i += blockDim.x) {
@@ -80,7 +80,8 @@ template <int D>
 __global__ void __launch_bounds__(kThreads, 1)
 attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                      const bf16* __restrict__ k, const bf16* __restrict__ v,
-                     const int32_t* __restrict__ kv_row, const bf16* __restrict__ d_o,
+                     const int32_t* __restrict__ kv_row, int32_t kv_sub,
+                     const bf16* __restrict__ d_o,
                      const float* __restrict__ lse,
                      const float* __restrict__ delta, float* __restrict__ dk,
                      float* __restrict__ dv, int64_t n_local, float scale, float scale_log2,
@@ -96,7 +97,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   S& sm = *reinterpret_cast<S*>(smem_raw);
 
   if ((int32_t)blockIdx.x >= n_attn_blocks) {
-    zero_untouched_block(blockIdx.x - n_attn_blocks, zr, n_zr, zero_rows, kv_row,
+    zero_untouched_block(blockIdx.x - n_attn_blocks, zr, n_zr, zero_rows, kv_row, kv_sub,
                          (int64_t)H * D, dk, dv);
     return;
   }
@@ -110,10 +111,13 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = (int64_t)h * D;
 
-  // Key j sits at row j of K/V and dK/dV (global order) or at row kv_row[j]
-  // (rank-major: the restore and the unrestore fused into these loads and
-  // stores).
-  auto key_row = [&](int key) -> int64_t { return kv_row ? kv_row[key] : key; };
+  // Key j sits at row j - kv_sub of K/V and dK/dV (global order, or one
+  // rank's block of it) or at row kv_row[j] - kv_sub (rank-major, or one
+  // rank's block of it: the restore and the unrestore fused into these loads
+  // and stores).
+  auto key_row = [&](int key) -> int64_t {
+    return (int64_t)(kv_row ? kv_row[key] : key) - kv_sub;
+  };
   const int my_key = t.k0 + w * 16 + l16;
   const bool key_ok = my_key < t.k1;
   bf16x8 kf[KS], vf[KS];
@@ -281,10 +285,11 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
 
 template <int D>
 hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const void* q,
-                        const void* k, const void* v, const int32_t* kv_row, const void* d_o,
-                        const float* lse, const float* delta, float* dk, float* dv,
-                        int64_t n_local, float scale, int32_t accumulate, const ZeroRange* zr,
-                        int32_t n_zr, int64_t zero_rows, hipStream_t stream) {
+                        const void* k, const void* v, const int32_t* kv_row, int32_t kv_sub,
+                        const void* d_o, const float* lse, const float* delta, float* dk,
+                        float* dv, int64_t n_local, float scale, int32_t accumulate,
+                        const ZeroRange* zr, int32_t n_zr, int64_t zero_rows,
+                        hipStream_t stream) {
   const int64_t attn_blocks = (int64_t)n_tiles * H;
   const int64_t zero_blocks =
       (zr && n_zr > 0) ? (zero_rows + kZeroRowsPerBlock - 1) / kZeroRowsPerBlock : 0;
@@ -306,8 +311,8 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
   }
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), smem,
                      stream, tiles, H, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), kv_row, static_cast<const bf16*>(d_o), lse,
-                     delta, dk, dv, n_local, scale, scale * kLog2e, accumulate,
+                     static_cast<const bf16*>(v), kv_row, kv_sub, static_cast<const bf16*>(d_o),
+                     lse, delta, dk, dv, n_local, scale, scale * kLog2e, accumulate,
                      (int32_t)attn_blocks, zr, n_zr, zero_rows);
   return hipGetLastError();
 }
@@ -315,17 +320,19 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
 }  // namespace
 
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                                const void* q, const void* k, const void* v,
-                                const int32_t* kv_row, const void* d_o, const float* lse,
-                                const float* delta, float* dk, float* dv, int64_t n_local,
-                                float scale, int32_t accumulate, const ZeroRange* zr,
-                                int32_t n_zr, int64_t zero_rows, hipStream_t stream) {
+                                const void* q, const void* k, const void* v, KvRows kv,
+                                const void* d_o, const float* lse, const float* delta, float* dk,
+                                float* dv, int64_t n_local, float scale, int32_t accumulate,
+                                const ZeroRange* zr, int32_t n_zr, int64_t zero_rows,
+                                hipStream_t stream) {
   if (D == 128)
-    return launch_bwd_d<128>(tiles, n_tiles, H, q, k, v, kv_row, d_o, lse, delta, dk, dv,
-                             n_local, scale, accumulate, zr, n_zr, zero_rows, stream);
+    return launch_bwd_d<128>(tiles, n_tiles, H, q, k, v, kv.map, (int32_t)kv.sub, d_o, lse,
+                             delta, dk, dv, n_local, scale, accumulate, zr, n_zr, zero_rows,
+                             stream);
   if (D == 64)
-    return launch_bwd_d<64>(tiles, n_tiles, H, q, k, v, kv_row, d_o, lse, delta, dk, dv,
-                            n_local, scale, accumulate, zr, n_zr, zero_rows, stream);
+    return launch_bwd_d<64>(tiles, n_tiles, H, q, k, v, kv.map, (int32_t)kv.sub, d_o, lse,
+                            delta, dk, dv, n_local, scale, accumulate, zr, n_zr, zero_rows,
+                            stream);
   return hipErrorInvalidValue;
 }
 

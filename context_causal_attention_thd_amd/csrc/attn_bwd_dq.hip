@@ -37,7 +37,9 @@ struct DqSmem {
   bf16 v[2][kFwdBN * P];
 };
 
-// MAPPED: K/V rows are found through kv_row (rank-major K/V) instead of by key.
+// K/V row of key j: j - kv_sub (global order, or one rank's block of it
+// under NO_LOAD_BALANCE), or, when MAPPED, kv_row[j] - kv_sub (rank-major
+// K/V, or one rank's block of it: the restore fused into the loads).
 // DELTA: compute delta = rowsum(dO * O) for the tile's rows here (from the
 // dO fragments already loaded and the matching O fragments) and write it for
 // the dK/dV kernel, instead of reading it from a separate preprocess launch.
@@ -45,10 +47,10 @@ template <int D, bool MAPPED, bool DELTA>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                    const bf16* __restrict__ k, const bf16* __restrict__ v,
-                   const int32_t* __restrict__ kv_row, uint32_t kv_bytes,
+                   const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
                    const bf16* __restrict__ d_o, const bf16* __restrict__ o,
                    const float* __restrict__ lse, float* __restrict__ delta,
-                   float* __restrict__ dq, int64_t n_local,
+                   float* __restrict__ dq, int64_t n_local, int32_t accumulate,
                    float scale, float scale_log2) {
   constexpr int BN = kFwdBN;
   constexpr int KSTEPS = D / 16;
@@ -129,27 +131,27 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   const int soff0 = krow0 * P + (threadIdx.x % CPR) * 8;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
   const uint32_t goff0 = (uint32_t)krow0 * row_bytes + coff;  // from the tile's first row
-  // Tile rows are fetched with buffer loads; a row past the last attended key
-  // reads 0 with no branch, and nothing uses the loads before they are written
-  // to LDS after the current tile's MFMAs, so they stay in flight.
-  //  - Global order: the descriptor runs from row k0 to the last attended
-  //    key, so the constant chunk offsets land past its end for those rows.
-  //  - Rank-major (MAPPED): key j sits at row kv_row[j] (the restore fused
-  //    into these loads); pos[] holds this thread's rows of a tile, looked up
-  //    one tile ahead of the loads that use them, and a skipped row gets an
-  //    offset past the descriptor, which spans all rows (below 2 GiB).
-  auto rows_pos = [&](int k0, int (&pos)[CH]) {
+  // Tile rows are fetched with buffer loads; a row at or past the end of the
+  // tile's key range reads 0 with no branch, and nothing uses the loads before
+  // they are written to LDS after the current tile's MFMAs, so they stay in
+  // flight.
+  //  - Unmapped: the descriptor runs from row k0 - kv_sub to the range end,
+  //    so the constant chunk offsets land past its end for those rows.
+  //  - MAPPED: pos[] holds this thread's rows of a tile, looked up one tile
+  //    ahead of the loads that use them, and a skipped row gets an offset
+  //    past the descriptor, which spans all kv rows (below 2 GiB).
+  auto rows_pos = [&](int k0, int kend, int (&pos)[CH]) {
     if constexpr (MAPPED) {
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         const int key = k0 + krow0 + j * RSTEP;
-        const int r = kv_row[min(key, t.kend - 1)];
-        pos[j] = key < t.kend ? r : -1;
+        const int r = kv_row[min(key, kend - 1)] - kv_sub;
+        pos[j] = key < kend ? r : -1;
       }
     }
   };
   u32x4 kreg[CH], vreg[CH];
-  auto load_tile = [&](int k0, const int (&pos)[CH]) {
+  auto load_tile = [&](int k0, int kend, const int (&pos)[CH]) {
     if constexpr (MAPPED) {
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, kv_bytes);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, kv_bytes);
@@ -160,10 +162,11 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
         vreg[j] = buffer_load16(rv, off);
       }
     } else {
-      const int64_t n = (int64_t)t.kend - k0;
+      const int64_t n = (int64_t)kend - k0;
       const uint32_t bytes = n > 0 ? (uint32_t)(n * rs * 2) : 0u;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (int64_t)k0 * rs + head_off, bytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (int64_t)k0 * rs + head_off, bytes);
+      const int64_t base = n > 0 ? (int64_t)(k0 - kv_sub) * rs : 0;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base + head_off, bytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base + head_off, bytes);
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         kreg[j] = buffer_load16(rk, goff0 + j * RSTEP * row_bytes);
@@ -179,24 +182,30 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
     }
   };
 
-  const int ntiles = t.kend > t.a ? (t.kend - t.a + BN - 1) / BN : 0;
+  // Key tiles: those of [ks0, ke0), then those of [ks1, ke1).
+  const int nt0 = t.ke0 > t.ks0 ? (t.ke0 - t.ks0 + BN - 1) / BN : 0;
+  const int nt1 = t.ke1 > t.ks1 ? (t.ke1 - t.ks1 + BN - 1) / BN : 0;
+  const int ntiles = nt0 + nt1;
+  auto tile_k0 = [&](int it) { return it < nt0 ? t.ks0 + it * BN : t.ks1 + (it - nt0) * BN; };
+  auto tile_kend = [&](int it) { return it < nt0 ? t.ke0 : t.ke1; };
   int pos[CH];
   if (ntiles > 0) {
-    rows_pos(t.a, pos);
-    load_tile(t.a, pos);
+    rows_pos(tile_k0(0), tile_kend(0), pos);
+    load_tile(tile_k0(0), tile_kend(0), pos);
     store_tile(0);
-    rows_pos(t.a + BN, pos);
+    if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos);
   }
   wait_vmem();  // Q/dO fragments have landed: the loop's MFMAs never wait on loads
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
-    const int k0 = t.a + it * BN;
+    const int k0 = tile_k0(it);
+    const int kend = tile_kend(it);
     const int cur = it & 1;
     const bool has_next = it + 1 < ntiles;
     if (has_next) {
-      load_tile(k0 + BN, pos);
-      rows_pos(k0 + 2 * BN, pos);
+      load_tile(tile_k0(it + 1), tile_kend(it + 1), pos);
+      if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
 
     if (k0 <= wave_kmax) {
@@ -216,13 +225,13 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
           dp[kb] = mfma32(load_bf16x8(vp + kk * 16), dof[kk], dp[kb]);
         }
       }
-      const bool diag = !wave_all_valid || k0 + BN - 1 > wave_gmin;
+      const bool diag = !wave_all_valid || k0 + BN - 1 > wave_gmin || k0 + BN > kend;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          const bool ok = !diag || key <= my_g;
+          const bool ok = !diag || (key <= my_g && key < kend);
           const float p = ok ? fast_exp2(fmaf(s[kb][i], scale_log2, -lse2)) : 0.f;
           dp[kb][i] = ok ? p * (dp[kb][i] - dlt) : 0.f;
         }
@@ -256,7 +265,13 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       f32x4 out;
 #pragma unroll
       for (int j = 0; j < 4; ++j) out[j] = acc[db][i4 * 4 + j] * scale;
-      *reinterpret_cast<f32x4*>(qp + db * 32 + i4 * 8 + hh * 4) = out;
+      f32x4* dst = reinterpret_cast<f32x4*>(qp + db * 32 + i4 * 8 + hh * 4);
+      if (accumulate) {
+        const f32x4 cur = *dst;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] += cur[j];
+      }
+      *dst = out;
     }
 }
 
@@ -267,24 +282,24 @@ namespace {
 template <int D, bool M>
 void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int32_t H,
                   const bf16* q, const bf16* k, const bf16* v, const int32_t* kv_row,
-                  uint32_t kvb, const bf16* d_o, const bf16* o, const float* lse, float* delta,
-                  float* dq, int64_t n_local, float scale) {
+                  int32_t kv_sub, uint32_t kvb, const bf16* d_o, const bf16* o, const float* lse,
+                  float* delta, float* dq, int64_t n_local, float scale, int32_t accumulate) {
   if (o)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, true>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, tiles, H, q, k, v, kv_row, kvb, d_o, o, lse, delta, dq, n_local,
-                       scale, scale * kLog2e);
+                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, d_o, o, lse, delta, dq,
+                       n_local, accumulate, scale, scale * kLog2e);
   else
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, false>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, tiles, H, q, k, v, kv_row, kvb, d_o, o, lse, delta, dq, n_local,
-                       scale, scale * kLog2e);
+                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, d_o, o, lse, delta, dq,
+                       n_local, accumulate, scale, scale * kLog2e);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                              const void* q, const void* k, const void* v, const int32_t* kv_row,
-                              int64_t T, const void* d_o, const void* o, const float* lse,
-                              float* delta, float* dq, int64_t n_local, float scale,
+                              const void* q, const void* k, const void* v, KvRows kv,
+                              const void* d_o, const void* o, const float* lse, float* delta,
+                              float* dq, int64_t n_local, float scale, int32_t accumulate,
                               hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
@@ -294,17 +309,22 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
   const bf16* vb = static_cast<const bf16*>(v);
   const bf16* db = static_cast<const bf16*>(d_o);
   const bf16* ob = static_cast<const bf16*>(o);
-  const int64_t kv_bytes = T * H * D * 2;
-  if (kv_row && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const uint32_t kvb = kv_row ? (uint32_t)kv_bytes : 0u;
-  if (D == 128 && kv_row)
-    launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
+  const int64_t kv_bytes = kv.rows * H * D * 2;
+  if (kv.map && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
+  const int32_t sub = (int32_t)kv.sub;
+  if (D == 128 && kv.map)
+    launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+                            delta, dq, n_local, scale, accumulate);
   else if (D == 128)
-    launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
-  else if (D == 64 && kv_row)
-    launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
+    launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+                             delta, dq, n_local, scale, accumulate);
+  else if (D == 64 && kv.map)
+    launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+                           delta, dq, n_local, scale, accumulate);
   else if (D == 64)
-    launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv_row, kvb, db, ob, lse, delta, dq, n_local, scale);
+    launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+                            delta, dq, n_local, scale, accumulate);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

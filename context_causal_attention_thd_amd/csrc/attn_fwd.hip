@@ -60,13 +60,16 @@ struct FwdSmem {
 template <int QB>
 constexpr int kFwdThreads = kFwdBM / (16 * QB) * 64;
 
-// MAPPED: K/V rows are found through kv_row (rank-major K/V) instead of by key.
+// K/V row of key j: j - kv_sub (global order, or one rank's block of it
+// under NO_LOAD_BALANCE), or, when MAPPED, kv_row[j] - kv_sub (rank-major
+// K/V, or one rank's block of it: the restore fused into the loads).
 template <int D, int QB, bool MAPPED>
 __global__ void __launch_bounds__(kFwdThreads<QB>, 2)
 attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                 const bf16* __restrict__ k, const bf16* __restrict__ v,
-                const int32_t* __restrict__ kv_row, uint32_t kv_bytes, bf16* __restrict__ o,
-                float* __restrict__ lse, int64_t n_local, float scale_log2) {
+                const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
+                bf16* __restrict__ o, float* __restrict__ lse, int64_t n_local,
+                float scale_log2) {
   constexpr int kThreads = kFwdThreads<QB>;
   constexpr int BN = kFwdBN;
   constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
@@ -131,26 +134,26 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int soff0 = krow0 * P + (threadIdx.x % CPR) * 8;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
   const uint32_t goff0 = (uint32_t)krow0 * row_bytes + coff;  // from the tile's first row
-  // Rows of tile k0 into registers with buffer loads; a row past the last
-  // attended key reads 0 with no branch.
-  //  - Global order: the descriptor runs from row k0 to the last attended
-  //    key, so the constant chunk offsets land past its end for those rows.
-  //  - Rank-major (MAPPED): key j sits at row kv_row[j] (the restore fused
-  //    into these loads); pos[] holds this thread's rows of a tile, looked up
-  //    one tile ahead of the loads that use them so the lookup's latency
-  //    stays off the prefetch path, and a skipped row gets an offset past the
-  //    descriptor, which spans all rows (below 2 GiB, checked on the host).
-  auto rows_pos = [&](int k0, int (&pos)[CH]) {
+  // Rows [k0, k0 + BN) of K or V into registers with buffer loads, for a
+  // tile of a key range ending at kend; a row at or past kend reads 0 with no
+  // branch.
+  //  - Unmapped: the descriptor runs from row k0 - kv_sub to the range end,
+  //    so the constant chunk offsets land past its end for those rows.
+  //  - MAPPED: pos[] holds this thread's rows of the tile, looked up one tile
+  //    ahead of the loads that use them so the lookup's latency stays off the
+  //    prefetch path; a skipped row gets an offset past the descriptor, which
+  //    spans all kv rows (below 2 GiB, checked on the host).
+  auto rows_pos = [&](int k0, int kend, int (&pos)[CH]) {
     if constexpr (MAPPED) {
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         const int key = k0 + krow0 + j * RSTEP;
-        const int r = kv_row[min(key, t.kend - 1)];
-        pos[j] = key < t.kend ? r : -1;
+        const int r = kv_row[min(key, kend - 1)] - kv_sub;
+        pos[j] = key < kend ? r : -1;
       }
     }
   };
-  auto load_rows = [&](const bf16* x, int k0, const int (&pos)[CH], u32x4* regs) {
+  auto load_rows = [&](const bf16* x, int k0, int kend, const int (&pos)[CH], u32x4* regs) {
     if constexpr (MAPPED) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(x + head_off, kv_bytes);
 #pragma unroll
@@ -159,9 +162,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
         regs[j] = buffer_load16(r, off);
       }
     } else {
-      const int64_t n = (int64_t)t.kend - k0;
+      const int64_t n = (int64_t)kend - k0;
       const __amdgpu_buffer_rsrc_t r =
-          n > 0 ? make_rsrc(x + (int64_t)k0 * rs + head_off, (uint32_t)(n * rs * 2))
+          n > 0 ? make_rsrc(x + (int64_t)(k0 - kv_sub) * rs + head_off, (uint32_t)(n * rs * 2))
                 : make_rsrc(x, 0u);
 #pragma unroll
       for (int j = 0; j < CH; ++j) regs[j] = buffer_load16(r, goff0 + j * RSTEP * row_bytes);
@@ -189,8 +192,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16(a, qf[qb][kk], s[qb][kb]);
       }
   };
-  // Causal / padding mask: key j is allowed iff j <= my_g.
-  auto mask = [&](int k0, f32x4 (&s)[QB][KB]) {
+  // Causal / padding mask: key j is allowed iff j <= my_g and j < kend (the
+  // end of the key range the tile belongs to).
+  auto mask = [&](int k0, int kend, f32x4 (&s)[QB][KB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -198,7 +202,7 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + kb * 16 + G * 4 + i;
-          if (key > my_g[qb]) s[qb][kb][i] = -INFINITY;
+          if (key > my_g[qb] || key >= kend) s[qb][kb][i] = -INFINITY;
         }
   };
   // Lazy rescale: the running max of a query moves only when some score of
@@ -269,7 +273,12 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     }
   };
 
-  const int ntiles = t.kend > t.a ? (t.kend - t.a + BN - 1) / BN : 0;
+  // Key tiles: those of [ks0, ke0), then those of [ks1, ke1).
+  const int nt0 = t.ke0 > t.ks0 ? (t.ke0 - t.ks0 + BN - 1) / BN : 0;
+  const int nt1 = t.ke1 > t.ks1 ? (t.ke1 - t.ks1 + BN - 1) / BN : 0;
+  const int ntiles = nt0 + nt1;
+  auto tile_k0 = [&](int it) { return it < nt0 ? t.ks0 + it * BN : t.ks1 + (it - nt0) * BN; };
+  auto tile_kend = [&](int it) { return it < nt0 ? t.ke0 : t.ke1; };
   u32x4 kreg[CH], vreg[CH];
 
   // Double-buffered K/V tiles: the next tile's loads are issued before the
@@ -284,28 +293,29 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       wave_uniform((row0 + QB * 16 - 1 < t.n) && (t.g0 + row0 + QB * 16 - 1 < t.e)) != 0;
   int pos[CH];
   if (ntiles > 0) {
-    rows_pos(t.a, pos);
-    load_rows(k, t.a, pos, kreg);
-    load_rows(v, t.a, pos, vreg);
+    rows_pos(tile_k0(0), tile_kend(0), pos);
+    load_rows(k, tile_k0(0), tile_kend(0), pos, kreg);
+    load_rows(v, tile_k0(0), tile_kend(0), pos, vreg);
     store_rows(sm.k[0], kreg);
     store_rows(sm.v[0], vreg);
-    rows_pos(t.a + BN, pos);
+    if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos);
   }
   wait_vmem();
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
-    const int k0 = t.a + it * BN;
+    const int k0 = tile_k0(it);
+    const int kend = tile_kend(it);
     const int cur = it & 1;
     const bool has_next = it + 1 < ntiles;
     if (has_next) {  // in flight during this tile's compute
-      load_rows(k, k0 + BN, pos, kreg);
-      load_rows(v, k0 + BN, pos, vreg);
-      rows_pos(k0 + 2 * BN, pos);
+      load_rows(k, tile_k0(it + 1), tile_kend(it + 1), pos, kreg);
+      load_rows(v, tile_k0(it + 1), tile_kend(it + 1), pos, vreg);
+      if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
     if (k0 <= wave_kmax) {
       f32x4 s[QB][KB];
       scores(cur, s);
-      if (!wave_all_valid || k0 + BN - 1 > wave_gmin) mask(k0, s);
+      if (!wave_all_valid || k0 + BN - 1 > wave_gmin || k0 + BN > kend) mask(k0, kend, s);
       softmax_max(s);
       softmax_pv(cur, s);
     }
@@ -345,26 +355,25 @@ constexpr int kFwdQB = 1;
 
 template <int D>
 hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const bf16* q,
-                        const bf16* k, const bf16* v, const int32_t* kv_row, uint32_t kv_bytes,
-                        bf16* o, float* lse, int64_t n_local, float scale_log2,
-                        hipStream_t stream) {
+                        const bf16* k, const bf16* v, const int32_t* kv_row, int32_t kv_sub,
+                        uint32_t kv_bytes, bf16* o, float* lse, int64_t n_local,
+                        float scale_log2, hipStream_t stream) {
   if (kv_row)
     hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, true>), dim3((unsigned)blocks),
-                       dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_bytes,
-                       o, lse, n_local, scale_log2);
+                       dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub,
+                       kv_bytes, o, lse, n_local, scale_log2);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, false>), dim3((unsigned)blocks),
-                       dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_bytes,
-                       o, lse, n_local, scale_log2);
+                       dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub,
+                       kv_bytes, o, lse, n_local, scale_log2);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, const int32_t* kv_row,
-                           int64_t T, void* o, float* lse, int64_t n_local, float scale,
-                           hipStream_t stream) {
+                           const void* q, const void* k, const void* v, KvRows kv, void* o,
+                           float* lse, int64_t n_local, float scale, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -373,15 +382,15 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
   bf16* ob = static_cast<bf16*>(o);
-  const int64_t kv_bytes = T * H * D * 2;
-  if (kv_row && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const uint32_t kvb = kv_row ? (uint32_t)kv_bytes : 0u;
+  const int64_t kv_bytes = kv.rows * H * D * 2;
+  if (kv.map && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
   if (D == 128)
-    return launch_fwd_d<128>(tiles, blocks, H, qb, kb, vb, kv_row, kvb, ob, lse, n_local,
-                             scale_log2, stream);
+    return launch_fwd_d<128>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, ob, lse,
+                             n_local, scale_log2, stream);
   if (D == 64)
-    return launch_fwd_d<64>(tiles, blocks, H, qb, kb, vb, kv_row, kvb, ob, lse, n_local,
-                            scale_log2, stream);
+    return launch_fwd_d<64>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, ob, lse,
+                            n_local, scale_log2, stream);
   return hipErrorInvalidValue;
 }
 

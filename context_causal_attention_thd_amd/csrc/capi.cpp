@@ -111,12 +111,26 @@ struct thdcp_plan {
   std::vector<FwdTile> fwd;
   std::vector<BwdTile> bwd;
   std::vector<ZeroRange> zero;
-  // THDCP_KV_RANK_MAJOR with a layout whose rank-major order differs from
-  // global order: kv_row[g] = rank-major position of global row g.
+  // kv_row[g] = rank-major position of global row g, built when rank-major
+  // order differs from global order (DUAL_CHUNK_SWAP, cp_size > 1) and either
+  // the all-gather calls take rank-major K/V (kv_mapped) or P2P steps read
+  // one rank's local K/V block through it.
   bool kv_mapped = false;
   std::vector<int32_t> kv_row;
+  // P2P ring steps (desc.p2p): per source rank s, forward tiles (one per
+  // query tile, holding the keys rank s has), key tiles over rank s's keys,
+  // and rank s's rows no local query attends. Concatenated over s.
+  struct Step {
+    int32_t fwd0, n_fwd, bwd0, n_bwd, zero0, n_zero;
+    int64_t untouched;
+  };
+  std::vector<Step> steps;
+  std::vector<FwdTile> step_fwd;
+  std::vector<BwdTile> step_bwd;
+  std::vector<ZeroRange> step_zero;
   std::vector<char> blob;  // host image of the device tables
   size_t off_fwd = 0, off_bwd = 0, off_zero = 0, off_kvrow = 0, ws_bytes = 0;
+  size_t off_sfwd = 0, off_sbwd = 0, off_szero = 0;
   char* ws_dev = nullptr;  // caller's workspace after upload
 };
 
@@ -161,6 +175,139 @@ std::vector<Segment> build_segments(const thdcp_plan& p, int64_t r) {
   return segs;
 }
 
+// Key tiles of a forward tile, the cost the LPT order sorts by.
+int64_t fwd_cost(const FwdTile& t) {
+  const int64_t n0 = t.ke0 > t.ks0 ? (t.ke0 - t.ks0 + kFwdBN - 1) / kFwdBN : 0;
+  const int64_t n1 = t.ke1 > t.ks1 ? (t.ke1 - t.ks1 + kFwdBN - 1) / kFwdBN : 0;
+  return n0 + n1;
+}
+
+// Longest first (LPT order over the workgroup queue), stable.
+template <typename Tile, typename Cost>
+std::vector<Tile> lpt_order(const std::vector<Tile>& tiles, Cost cost) {
+  std::vector<size_t> order(tiles.size());
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t x, size_t y) { return cost(tiles[x]) > cost(tiles[y]); });
+  std::vector<Tile> sorted;
+  sorted.reserve(tiles.size());
+  for (size_t i : order) sorted.push_back(tiles[i]);
+  return sorted;
+}
+
+// A document's real local rows: runs of consecutive local rows holding
+// consecutive global rows (one per DUAL_CHUNK_SWAP chunk, ascending in g).
+struct DocRows {
+  struct Run {
+    int64_t m0, g0, n;
+  };
+  int32_t doc;
+  int64_t a, gmax, m_hi, split, dga, dgb;
+  std::vector<Run> runs;
+};
+
+std::vector<DocRows> doc_rows(const std::vector<Segment>& segs) {
+  std::vector<DocRows> out;
+  for (size_t si = 0; si < segs.size();) {
+    const int32_t doc = segs[si].doc;
+    size_t sj = si;
+    while (sj < segs.size() && segs[sj].doc == doc && doc >= 0) ++sj;
+    if (doc < 0) {
+      ++si;
+      continue;
+    }
+    DocRows dr{};
+    dr.doc = doc;
+    for (size_t k = si; k < sj; ++k) {
+      const Segment& s = segs[k];
+      const int64_t nv = std::max<int64_t>(0, std::min(s.g0 + s.len, s.e) - s.g0);
+      if (nv > 0) dr.runs.push_back({s.m0, s.g0, nv});
+    }
+    dr.a = segs[si].a;
+    si = sj;
+    if (dr.runs.empty()) continue;
+    const DocRows::Run& last = dr.runs.back();
+    dr.gmax = last.g0 + last.n - 1;
+    dr.m_hi = last.m0 + last.n;
+    dr.split = dr.runs.size() > 1 ? dr.runs[1].m0 : dr.m_hi;
+    dr.dga = dr.runs[0].g0 - dr.runs[0].m0;
+    dr.dgb = dr.runs.size() > 1 ? dr.runs[1].g0 - dr.runs[1].m0 : dr.dga;
+    out.push_back(std::move(dr));
+  }
+  return out;
+}
+
+// Key tiles of kBwdBN keys over [lo, hi) of one document; each lists the
+// contiguous local query range that attends it (rows with g >= k0).
+void add_key_tiles(const DocRows& dr, int64_t lo, int64_t hi, std::vector<BwdTile>& out) {
+  for (int64_t k0 = lo; k0 < hi; k0 += kBwdBN) {
+    int64_t m_lo = -1;  // first local row with g >= k0
+    for (const DocRows::Run& rn : dr.runs) {
+      if (k0 <= rn.g0 + rn.n - 1) {
+        m_lo = rn.m0 + std::max<int64_t>(0, k0 - rn.g0);
+        break;
+      }
+    }
+    BwdTile t{};
+    t.k0 = (int32_t)k0;
+    t.k1 = (int32_t)std::min<int64_t>(k0 + kBwdBN, hi);
+    t.m_lo = (int32_t)m_lo;
+    t.m_hi = (int32_t)dr.m_hi;
+    t.m_split = (int32_t)dr.split;
+    t.dg_a = (int32_t)dr.dga;
+    t.dg_b = (int32_t)dr.dgb;
+    out.push_back(t);
+  }
+}
+
+// Rows of the sorted ranges `own` not covered by the sorted ranges `touched`,
+// with the running count of such rows before each range.
+std::vector<ZeroRange> untouched_ranges(const std::vector<std::pair<int64_t, int64_t>>& own,
+                                        const std::vector<std::pair<int64_t, int64_t>>& touched) {
+  std::vector<ZeroRange> out;
+  int64_t before = 0;
+  size_t ti = 0;
+  for (const auto& o : own) {
+    int64_t cur = o.first;
+    while (ti < touched.size() && touched[ti].second <= cur) ++ti;
+    for (size_t tj = ti; tj < touched.size() && touched[tj].first < o.second; ++tj) {
+      if (touched[tj].first > cur) {
+        out.push_back({(int32_t)cur, (int32_t)touched[tj].first, (int32_t)before, 0});
+        before += touched[tj].first - cur;
+      }
+      cur = std::max(cur, touched[tj].second);
+    }
+    if (cur < o.second) {
+      out.push_back({(int32_t)cur, (int32_t)o.second, (int32_t)before, 0});
+      before += o.second - cur;
+    }
+  }
+  return out;
+}
+
+// Keys that rank `src` holds inside document `doc`, as at most two ascending
+// global ranges: its DUAL_CHUNK_SWAP chunks src and 2*cp_size-1-src ([AG]
+// "Why"), or its NO_LOAD_BALANCE range [src*s_local, (src+1)*s_local) ([AG]
+// "What changed"), clipped to the document.
+int key_ranges_of(const thdcp_plan& p, int32_t doc, int64_t src, int64_t (&lo)[2],
+                  int64_t (&hi)[2]) {
+  const auto& d = p.desc;
+  const int64_t cp = d.cp_size;
+  const int64_t a = p.cup[doc], b = p.cup[doc + 1];
+  if (d.strategy == THDCP_DUAL_CHUNK_SWAP) {
+    const int64_t c = (b - a) / (2 * cp);
+    lo[0] = a + src * c;
+    hi[0] = lo[0] + c;
+    lo[1] = a + (2 * cp - 1 - src) * c;
+    hi[1] = lo[1] + c;
+    return 2;
+  }
+  const int64_t sl = d.T / cp;
+  lo[0] = std::max<int64_t>(a, src * sl);
+  hi[0] = std::min<int64_t>(b, (src + 1) * sl);
+  return 1;
+}
+
 void build_plan(thdcp_plan& p) {
   const auto& d = p.desc;
   const std::vector<Segment> segs = build_segments(p, d.rank);
@@ -177,117 +324,48 @@ void build_plan(thdcp_plan& p) {
   }
 
   // Forward tiles, longest first (LPT order over the workgroup queue).
-  p.fwd.clear();
-  std::vector<int64_t> fcost;
+  std::vector<FwdTile> fwd;
+  std::vector<int32_t> fwd_doc;
   for (const Segment& s : segs) {
     for (int64_t off = 0; off < s.len; off += kFwdBM) {
       FwdTile t{};
       t.m0 = (int32_t)(s.m0 + off);
       t.n = (int32_t)std::min<int64_t>(kFwdBM, s.len - off);
       t.g0 = (int32_t)(s.g0 + off);
-      t.a = (int32_t)s.a;
       t.e = (int32_t)s.e;
       const int64_t kend = std::min<int64_t>(t.g0 + t.n, s.e);
-      t.kend = kend > t.g0 ? (int32_t)kend : t.a;
-      p.fwd.push_back(t);
-      fcost.push_back((t.kend - t.a + kFwdBN - 1) / kFwdBN);
+      t.ks0 = (int32_t)s.a;
+      t.ke0 = kend > t.g0 ? (int32_t)kend : (int32_t)s.a;
+      fwd.push_back(t);
+      fwd_doc.push_back(s.doc);
     }
   }
-  {
-    std::vector<size_t> order(p.fwd.size());
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](size_t x, size_t y) { return fcost[x] > fcost[y]; });
-    std::vector<FwdTile> sorted;
-    sorted.reserve(order.size());
-    for (size_t i : order) sorted.push_back(p.fwd[i]);
-    p.fwd.swap(sorted);
-  }
+  p.fwd = lpt_order(fwd, [](const FwdTile& t) { return fwd_cost(t); });
 
   // Backward tiles: per document, its local real rows (a prefix of the
   // document's local rows, ascending in g) attend keys [a, g_max].
-  p.bwd.clear();
-  std::vector<int64_t> bcost;
+  const std::vector<DocRows> docs = doc_rows(segs);
+  std::vector<BwdTile> bwd;
   std::vector<std::pair<int64_t, int64_t>> touched;  // [r0, r1) per document
-  for (size_t si = 0; si < segs.size();) {
-    const int32_t doc = segs[si].doc;
-    size_t sj = si;
-    while (sj < segs.size() && segs[sj].doc == doc && doc >= 0) ++sj;
-    if (doc < 0) { ++si; continue; }
-    // Real rows of each segment of this document.
-    struct Run { int64_t m0, g0, n; };
-    std::vector<Run> runs;
-    for (size_t k = si; k < sj; ++k) {
-      const Segment& s = segs[k];
-      const int64_t nv = std::max<int64_t>(0, std::min(s.g0 + s.len, s.e) - s.g0);
-      if (nv > 0) runs.push_back({s.m0, s.g0, nv});
-    }
-    si = sj;
-    if (runs.empty()) continue;
-    const int64_t a = segs[si - 1].a;
-    const Run& last = runs.back();
-    const int64_t gmax = last.g0 + last.n - 1;
-    const int64_t m_hi = last.m0 + last.n;
-    touched.push_back({a, gmax + 1});
-    const int64_t split = runs.size() > 1 ? runs[1].m0 : m_hi;
-    const int64_t dga = runs[0].g0 - runs[0].m0;
-    const int64_t dgb = runs.size() > 1 ? runs[1].g0 - runs[1].m0 : dga;
-    for (int64_t k0 = a; k0 <= gmax; k0 += kBwdBN) {
-      // first local row with g >= k0
-      int64_t m_lo = -1;
-      for (const Run& rn : runs) {
-        if (k0 <= rn.g0 + rn.n - 1) {
-          m_lo = rn.m0 + std::max<int64_t>(0, k0 - rn.g0);
-          break;
-        }
-      }
-      BwdTile t{};
-      t.k0 = (int32_t)k0;
-      t.k1 = (int32_t)std::min<int64_t>(k0 + kBwdBN, gmax + 1);
-      t.m_lo = (int32_t)m_lo;
-      t.m_hi = (int32_t)m_hi;
-      t.m_split = (int32_t)split;
-      t.dg_a = (int32_t)dga;
-      t.dg_b = (int32_t)dgb;
-      p.bwd.push_back(t);
-      bcost.push_back(m_hi - m_lo);
-    }
+  for (const DocRows& dr : docs) {
+    add_key_tiles(dr, dr.a, dr.gmax + 1, bwd);
+    touched.push_back({dr.a, dr.gmax + 1});
   }
-  {
-    std::vector<size_t> order(p.bwd.size());
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](size_t x, size_t y) { return bcost[x] > bcost[y]; });
-    std::vector<BwdTile> sorted;
-    sorted.reserve(order.size());
-    for (size_t i : order) sorted.push_back(p.bwd[i]);
-    p.bwd.swap(sorted);
-  }
+  p.bwd = lpt_order(bwd, [](const BwdTile& t) { return (int64_t)t.m_hi - t.m_lo; });
 
   // Untouched key rows: the complement of the touched ranges in [0, T).
   std::sort(touched.begin(), touched.end());
-  p.zero.clear();
   p.touched = 0;
-  int64_t cursor = 0, before = 0;
-  for (auto& tr : touched) {
-    if (tr.first > cursor) {
-      p.zero.push_back({(int32_t)cursor, (int32_t)tr.first, (int32_t)before, 0});
-      before += tr.first - cursor;
-    }
-    p.touched += tr.second - tr.first;
-    cursor = std::max(cursor, tr.second);
-  }
-  if (cursor < d.T) {
-    p.zero.push_back({(int32_t)cursor, (int32_t)d.T, (int32_t)before, 0});
-  }
+  for (auto& tr : touched) p.touched += tr.second - tr.first;
+  p.zero = untouched_ranges({{0, d.T}}, touched);
 
   // Rank-major K/V: the inverse of the all-ranks permutation. Rank r's local
   // row m sits at rank-major position r * n_local + m; under NO_LOAD_BALANCE
   // (or cp_size 1) that is global row order and no map is needed.
-  p.kv_mapped = d.kv_layout == THDCP_KV_RANK_MAJOR && d.strategy == THDCP_DUAL_CHUNK_SWAP &&
-                d.cp_size > 1;
+  const bool reordered = d.strategy == THDCP_DUAL_CHUNK_SWAP && d.cp_size > 1;
+  p.kv_mapped = reordered && d.kv_layout == THDCP_KV_RANK_MAJOR;
   p.kv_row.clear();
-  if (p.kv_mapped) {
+  if (reordered && (p.kv_mapped || d.p2p)) {
     p.kv_row.assign(d.T, 0);
     for (int32_t r = 0; r < d.cp_size; ++r)
       for (const Segment& sg : build_segments(p, r))
@@ -295,26 +373,109 @@ void build_plan(thdcp_plan& p) {
           p.kv_row[sg.g0 + i] = (int32_t)(r * p.n_local + sg.m0 + i);
   }
 
+  // P2P steps ([PAD] "Describe the bug": per-step metadata of the P2P path,
+  // built here once per batch instead of by helper launches at every step).
+  p.steps.clear();
+  p.step_fwd.clear();
+  p.step_bwd.clear();
+  p.step_zero.clear();
+  if (d.p2p) {
+    for (int64_t src = 0; src < d.cp_size; ++src) {
+      thdcp_plan::Step st{};
+      // Forward: each query tile keeps the part of its causal key range that
+      // rank src holds (empty ranges still list the tile: its rows get O = 0,
+      // LSE = -inf for this step).
+      std::vector<FwdTile> sf;
+      for (size_t i = 0; i < fwd.size(); ++i) {
+        FwdTile t = fwd[i];
+        const int64_t klo = t.ks0, khi = t.ke0;
+        t.ks0 = t.ke0 = t.ks1 = t.ke1 = 0;
+        if (fwd_doc[i] >= 0 && khi > klo) {
+          int64_t lo[2], hi[2];
+          const int nr = key_ranges_of(p, fwd_doc[i], src, lo, hi);
+          int slot = 0;
+          for (int r = 0; r < nr; ++r) {
+            const int64_t x0 = std::max(lo[r], klo), x1 = std::min(hi[r], khi);
+            if (x1 <= x0) continue;
+            (slot == 0 ? t.ks0 : t.ks1) = (int32_t)x0;
+            (slot == 0 ? t.ke0 : t.ke1) = (int32_t)x1;
+            ++slot;
+          }
+        }
+        sf.push_back(t);
+      }
+      sf = lpt_order(sf, [](const FwdTile& t) { return fwd_cost(t); });
+      st.fwd0 = (int32_t)p.step_fwd.size();
+      st.n_fwd = (int32_t)sf.size();
+      p.step_fwd.insert(p.step_fwd.end(), sf.begin(), sf.end());
+      // Backward: key tiles over rank src's keys that local queries attend.
+      std::vector<BwdTile> sb;
+      std::vector<std::pair<int64_t, int64_t>> st_touched;
+      for (const DocRows& dr : docs) {
+        int64_t lo[2], hi[2];
+        const int nr = key_ranges_of(p, dr.doc, src, lo, hi);
+        for (int r = 0; r < nr; ++r) {
+          const int64_t x0 = std::max(lo[r], dr.a), x1 = std::min(hi[r], dr.gmax + 1);
+          if (x1 <= x0) continue;
+          add_key_tiles(dr, x0, x1, sb);
+          st_touched.push_back({x0, x1});
+        }
+      }
+      sb = lpt_order(sb, [](const BwdTile& t) { return (int64_t)t.m_hi - t.m_lo; });
+      st.bwd0 = (int32_t)p.step_bwd.size();
+      st.n_bwd = (int32_t)sb.size();
+      p.step_bwd.insert(p.step_bwd.end(), sb.begin(), sb.end());
+      // Rank src's rows (its local block, padding and tail included) that
+      // no local query attends: zeroed only when there are any.
+      std::vector<std::pair<int64_t, int64_t>> own;
+      for (const Segment& sg : build_segments(p, src)) own.push_back({sg.g0, sg.g0 + sg.len});
+      std::sort(own.begin(), own.end());
+      std::sort(st_touched.begin(), st_touched.end());
+      const std::vector<ZeroRange> sz = untouched_ranges(own, st_touched);
+      st.zero0 = (int32_t)p.step_zero.size();
+      st.n_zero = (int32_t)sz.size();
+      st.untouched = sz.empty() ? 0 : sz.back().before + (sz.back().r1 - sz.back().r0);
+      p.step_zero.insert(p.step_zero.end(), sz.begin(), sz.end());
+      p.steps.push_back(st);
+    }
+  }
+
   // Host image of the device tables.
   p.off_fwd = 0;
   p.off_bwd = align256(p.off_fwd + p.fwd.size() * sizeof(FwdTile));
   p.off_zero = align256(p.off_bwd + p.bwd.size() * sizeof(BwdTile));
   p.off_kvrow = align256(p.off_zero + p.zero.size() * sizeof(ZeroRange));
-  p.ws_bytes = align256(p.off_kvrow + p.kv_row.size() * sizeof(int32_t));
+  p.off_sfwd = align256(p.off_kvrow + p.kv_row.size() * sizeof(int32_t));
+  p.off_sbwd = align256(p.off_sfwd + p.step_fwd.size() * sizeof(FwdTile));
+  p.off_szero = align256(p.off_sbwd + p.step_bwd.size() * sizeof(BwdTile));
+  p.ws_bytes = align256(p.off_szero + p.step_zero.size() * sizeof(ZeroRange));
   if (p.ws_bytes == 0) p.ws_bytes = 256;
   p.blob.assign(p.ws_bytes, 0);
-  if (!p.fwd.empty()) memcpy(p.blob.data() + p.off_fwd, p.fwd.data(), p.fwd.size() * sizeof(FwdTile));
-  if (!p.bwd.empty()) memcpy(p.blob.data() + p.off_bwd, p.bwd.data(), p.bwd.size() * sizeof(BwdTile));
-  if (!p.zero.empty())
-    memcpy(p.blob.data() + p.off_zero, p.zero.data(), p.zero.size() * sizeof(ZeroRange));
-  if (!p.kv_row.empty())
-    memcpy(p.blob.data() + p.off_kvrow, p.kv_row.data(), p.kv_row.size() * sizeof(int32_t));
+  auto put = [&](size_t off, const void* src, size_t n) {
+    if (n) memcpy(p.blob.data() + off, src, n);
+  };
+  put(p.off_fwd, p.fwd.data(), p.fwd.size() * sizeof(FwdTile));
+  put(p.off_bwd, p.bwd.data(), p.bwd.size() * sizeof(BwdTile));
+  put(p.off_zero, p.zero.data(), p.zero.size() * sizeof(ZeroRange));
+  put(p.off_kvrow, p.kv_row.data(), p.kv_row.size() * sizeof(int32_t));
+  put(p.off_sfwd, p.step_fwd.data(), p.step_fwd.size() * sizeof(FwdTile));
+  put(p.off_sbwd, p.step_bwd.data(), p.step_bwd.size() * sizeof(BwdTile));
+  put(p.off_szero, p.step_zero.data(), p.step_zero.size() * sizeof(ZeroRange));
 }
 
-// Device map from global K/V row to its position in the caller's buffers
-// (nullptr: the identity).
-const int32_t* kv_map(const thdcp_plan* p) {
-  return p->kv_mapped ? reinterpret_cast<const int32_t*>(p->ws_dev + p->off_kvrow) : nullptr;
+// Row addressing of the all-gather calls' K/V (and dK/dV): rank-major
+// through the map, or global order.
+KvRows kv_map(const thdcp_plan* p) {
+  return {p->kv_mapped ? reinterpret_cast<const int32_t*>(p->ws_dev + p->off_kvrow) : nullptr, 0,
+          p->desc.T};
+}
+
+// Row addressing of a P2P step's K/V (and dK/dV): rank src's local block,
+// n_local rows, in which global key g sits at row pos(g) - src * n_local.
+KvRows kv_step(const thdcp_plan* p, int64_t src) {
+  const bool mapped = !p->kv_row.empty();
+  return {mapped ? reinterpret_cast<const int32_t*>(p->ws_dev + p->off_kvrow) : nullptr,
+          src * p->n_local, p->n_local};
 }
 
 }  // namespace
@@ -473,6 +634,7 @@ thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan
                   (long long)max_doc, (long long)n_local, (long long)row_bytes);
     if (d.kv_layout != THDCP_KV_GLOBAL && d.kv_layout != THDCP_KV_RANK_MAJOR)
       return fail(THDCP_ERR_ARG, "kv_layout %d (0 global, 1 rank-major)", d.kv_layout);
+    if (d.p2p != 0 && d.p2p != 1) return fail(THDCP_ERR_ARG, "p2p %d (0 or 1)", d.p2p);
     // Mapped K/V rows are addressed from the start of the buffer.
     if (d.kv_layout == THDCP_KV_RANK_MAJOR && d.T * row_bytes >= ((int64_t)1 << 31))
       return fail(THDCP_ERR_UNSUPPORTED,
@@ -632,8 +794,8 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->desc.T,
-                      o, lse, p->n_local, p->scale, (hipStream_t)stream),
+                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), o,
+                      lse, p->n_local, p->scale, (hipStream_t)stream),
       "cp_attn_fwd launch");
 }
 
@@ -714,10 +876,9 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p),
-                         p->desc.T, d_o, nullptr, lse,
-                         static_cast<float*>(const_cast<void*>(scratch)), dq, p->n_local,
-                         p->scale, (hipStream_t)stream),
+                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), d_o,
+                         nullptr, lse, static_cast<float*>(const_cast<void*>(scratch)), dq,
+                         p->n_local, p->scale, 0, (hipStream_t)stream),
       "cp_attn_bwd_dq launch");
 }
 
@@ -765,8 +926,8 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (!p->fwd.empty()) {
     hipError_t e = launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                                       (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v,
-                                      kv_map(p), p->desc.T, d_o, o, lse, delta, dq, p->n_local,
-                                      p->scale, (hipStream_t)stream);
+                                      kv_map(p), d_o, o, lse, delta, dq, p->n_local, p->scale, 0,
+                                      (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dq launch");
   }
   const bool zero = zero_untouched && !p->zero.empty();
@@ -778,6 +939,88 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
         zero ? (int32_t)p->zero.size() : 0, zero ? p->desc.T - p->touched : 0,
         (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dkdv launch");
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// P2P (ring) steps
+// ---------------------------------------------------------------------------
+namespace {
+
+thdcp_status_t check_step(thdcp_plan_t p, int32_t src) {
+  thdcp_status_t st = check_plan(p);
+  if (st != THDCP_OK) return st;
+  if (!p->desc.p2p) return fail(THDCP_ERR_ARG, "the plan was not made with p2p = 1");
+  if (src < 0 || src >= p->desc.cp_size)
+    return fail(THDCP_ERR_ARG, "src_rank %d outside [0, %d)", src, p->desc.cp_size);
+  return ok();
+}
+
+}  // namespace
+
+thdcp_status_t cp_attn_fwd_step(thdcp_plan_t p, int32_t src, const void* q, const void* k,
+                                const void* v, void* o, float* lse, void* stream) {
+  thdcp_status_t st = check_step(p, src);
+  if (st != THDCP_OK) return st;
+  if (p->n_local == 0) return ok();
+  if (!q || !k || !v || !o || !lse) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(THDCP_ERR_ARG, "Q/K/V/O must be 16-byte aligned");
+  const thdcp_plan::Step& sp = p->steps[src];
+  if (sp.n_fwd == 0) return ok();
+  return hip_status(
+      launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0,
+                      sp.n_fwd, p->desc.H, p->desc.D, q, k, v, kv_step(p, src), o, lse,
+                      p->n_local, p->scale, (hipStream_t)stream),
+      "cp_attn_fwd_step launch");
+}
+
+thdcp_status_t thdcp_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
+                               const float* lse_part, float* o_acc, float* lse_acc,
+                               int32_t first, void* o_out, void* stream) {
+  if (n < 0 || H < 1) return fail(THDCP_ERR_ARG, "bad size");
+  if (D != 64 && D != 128) return fail(THDCP_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (n == 0) return ok();
+  if (!o_part || !lse_part || !o_acc || !lse_acc) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(o_part) || !aligned16(o_acc) || (o_out && !aligned16(o_out)))
+    return fail(THDCP_ERR_ARG, "O buffers must be 16-byte aligned");
+  return hip_status(launch_lse_merge(n, H, D, o_part, lse_part, o_acc, lse_acc, first != 0,
+                                     o_out, (hipStream_t)stream),
+                    "thdcp_lse_merge launch");
+}
+
+thdcp_status_t cp_attn_bwd_step(thdcp_plan_t p, int32_t src, const void* q, const void* k,
+                                const void* v, const float* lse, const void* d_o,
+                                const void* scratch, size_t scratch_bytes, float* dq,
+                                int32_t accumulate_dq, float* dk, float* dv,
+                                int32_t zero_untouched, void* stream) {
+  thdcp_status_t st = check_step(p, src);
+  if (st != THDCP_OK) return st;
+  st = check_bwd_inputs(p, q, k, v, lse, d_o, scratch, scratch_bytes);
+  if (st != THDCP_OK) return st;
+  if (!dq || !dk || !dv) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(THDCP_ERR_ARG, "dQ/dK/dV must be 16-byte aligned");
+  if (p->n_local == 0) return ok();
+  const thdcp_plan::Step& sp = p->steps[src];
+  const KvRows kv = kv_step(p, src);
+  float* delta = static_cast<float*>(const_cast<void*>(scratch));
+  if (sp.n_fwd > 0) {
+    hipError_t e = launch_attn_bwd_dq(
+        reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0, sp.n_fwd,
+        p->desc.H, p->desc.D, q, k, v, kv, d_o, nullptr, lse, delta, dq, p->n_local, p->scale,
+        accumulate_dq != 0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dq launch");
+  }
+  const bool zero = zero_untouched && sp.n_zero > 0;
+  if (sp.n_bwd > 0 || zero) {
+    hipError_t e = launch_attn_bwd_dkdv(
+        reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_sbwd) + sp.bwd0, sp.n_bwd, p->desc.H,
+        p->desc.D, q, k, v, kv, d_o, lse, delta, dk, dv, p->n_local, p->scale, 0,
+        zero ? reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_szero) + sp.zero0 : nullptr,
+        zero ? sp.n_zero : 0, zero ? sp.untouched : 0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dkdv launch");
   }
   return ok();
 }

@@ -10,16 +10,18 @@ namespace thdcp {
 // Forward work item: up to kFwdBM consecutive local rows that lie in one
 // contiguous run of global rows of one document (a DUAL_CHUNK_SWAP chunk or a
 // NO_LOAD_BALANCE document piece), so row r of the tile is global row g0 + r.
-// Keys are walked from the document start `a` to `kend` (exclusive) in
-// doc-aligned blocks; kend == a marks a tile with no real rows.
+// The keys it attends are walked in doc-aligned blocks over [ks0, ke0), then
+// over [ks1, ke1) (either range may be empty): the whole causal range
+// [doc start, last real row + 1) for the all-gather pass; for one P2P step,
+// the parts of it that the step's source rank holds (at most two
+// DUAL_CHUNK_SWAP chunks of the document).
 struct FwdTile {
-  int32_t m0;    // first local row
-  int32_t n;     // rows in the tile (<= kFwdBM)
-  int32_t g0;    // global row of m0
-  int32_t a;     // physical start of the document
-  int32_t e;     // end of the document's real tokens (a + actual length)
-  int32_t kend;  // min(g0 + n, e): one past the last key any row attends
-  int32_t pad0, pad1;
+  int32_t m0;        // first local row
+  int32_t n;         // rows in the tile (<= kFwdBM)
+  int32_t g0;        // global row of m0
+  int32_t e;         // end of the document's real tokens (a + actual length)
+  int32_t ks0, ke0;  // first key range
+  int32_t ks1, ke1;  // second key range
 };
 
 // Backward work item: key rows [k0, k1) of one document (all attended by at
@@ -64,32 +66,43 @@ hipError_t launch_a2a(int32_t n_tensors, const void* const* srcs, int64_t n_toke
 // bytes (a multiple of 16) from src (device-readable, e.g. page-locked host
 // memory) to dst, by a kernel on `stream`.
 hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t stream);
-// kv_row (nullable): global row -> row of a and b (identity when null).
+// K/V row addressing shared by the attention and zeroing launches: global key
+// g sits at row (map ? map[g] : g) - sub of k, v (and dk, dv), which hold
+// `rows` rows. map is the rank-major map (null: identity); sub != 0 addresses
+// one rank's local block (a P2P step's source rank).
+struct KvRows {
+  const int32_t* map;
+  int64_t sub;
+  int64_t rows;
+};
+
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
-                            const int32_t* kv_row, int64_t row_floats, float* a, float* b,
+                            KvRows kv, int64_t row_floats, float* a, float* b,
                             hipStream_t stream);
+// Fold (o_part bf16, lse_part) into (o_acc fp32, lse_acc); see thdcp_lse_merge.
+hipError_t launch_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
+                            const float* lse_part, float* o_acc, float* lse_acc, int32_t first,
+                            void* o_out, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
-// kv_row (nullable, [T]): position of global K/V row g in k, v (and dk, dv);
-// null means global order. T is the number of K/V rows.
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, const int32_t* kv_row,
-                           int64_t T, void* o, float* lse, int64_t n_local, float scale,
-                           hipStream_t stream);
+                           const void* q, const void* k, const void* v, KvRows kv, void* o,
+                           float* lse, int64_t n_local, float scale, hipStream_t stream);
 // zr/n_zr/zero_rows (nullable / 0): also zero the dK/dV rows no local query
 // attends, with extra workgroups at the end of the same launch.
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                                const void* q, const void* k, const void* v,
-                                const int32_t* kv_row, const void* d_o, const float* lse,
+                                const void* q, const void* k, const void* v, KvRows kv,
+                                const void* d_o, const float* lse,
                                 const float* delta, float* dk, float* dv, int64_t n_local,
                                 float scale, int32_t accumulate, const ZeroRange* zr,
                                 int32_t n_zr, int64_t zero_rows, hipStream_t stream);
 // o (nullable): when given, delta = rowsum(dO * O) is computed by this launch
 // and written to `delta` for the dK/dV kernel; otherwise `delta` is read.
+// accumulate: add to dq (P2P steps after the first) instead of writing it.
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                              const void* q, const void* k, const void* v, const int32_t* kv_row,
-                              int64_t T, const void* d_o, const void* o, const float* lse,
-                              float* delta, float* dq, int64_t n_local, float scale,
+                              const void* q, const void* k, const void* v, KvRows kv,
+                              const void* d_o, const void* o, const float* lse, float* delta,
+                              float* dq, int64_t n_local, float scale, int32_t accumulate,
                               hipStream_t stream);
 
 }  // namespace thdcp

@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(const ZeroRange* __restr
                                                         int32_t n_ranges, uint64_t total_vec,
                                                         uint32_t vec_per_row,
                                                         const int32_t* __restrict__ kv_row,
-                                                        float* __restrict__ a,
+                                                        int32_t kv_sub, float* __restrict__ a,
                                                         float* __restrict__ b) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total_vec;
@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(const ZeroRange* __restr
       if ((uint64_t)ranges[mid].before <= lin) lo = mid; else hi = mid - 1;
     }
     const int64_t g = ranges[lo].r0 + (int64_t)(lin - ranges[lo].before);
-    const int64_t row = kv_row ? kv_row[g] : g;  // global row -> row of a and b
+    const int64_t row = (kv_row ? kv_row[g] : g) - kv_sub;  // global row -> row of a and b
     const int64_t off = row * vec_per_row + c;
     reinterpret_cast<f32x4*>(a)[off] = z;
     reinterpret_cast<f32x4*>(b)[off] = z;
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) zero_rows_kernel(const ZeroRange* __restr
 }
 
 hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t total_rows,
-                            const int32_t* kv_row, int64_t row_floats, float* a, float* b,
+                            KvRows kv, int64_t row_floats, float* a, float* b,
                             hipStream_t stream) {
   if (row_floats % 4 != 0) return hipErrorInvalidValue;
   const uint64_t vpr = (uint64_t)row_floats / 4;
@@ -245,7 +245,7 @@ hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t t
   uint64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ranges,
-                     n_ranges, total, (uint32_t)vpr, kv_row, a, b);
+                     n_ranges, total, (uint32_t)vpr, kv.map, (int32_t)kv.sub, a, b);
   return hipGetLastError();
 }
 
@@ -270,6 +270,91 @@ hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t 
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(copy16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// P2P step merge through the log-sum-exp. D/8 lanes per (row, head), each
+// taking 8 head dims (16 bytes of the bf16 step output, 32 of the fp32
+// accumulator). The lanes of one (row, head) are consecutive lanes of one
+// wave, so they all read lse_acc before lane 0 of the group writes it.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) lse_merge_kernel(int64_t n, int32_t H,
+                                                        const bf16* __restrict__ o_part,
+                                                        const float* __restrict__ lse_part,
+                                                        float* __restrict__ o_acc,
+                                                        float* __restrict__ lse_acc,
+                                                        int32_t first, bf16* __restrict__ o_out) {
+  constexpr int G = D / 8;
+  const int64_t pairs = n * H;
+  const int64_t pr = (int64_t)blockIdx.x * (blockDim.x / G) + threadIdx.x / G;
+  if (pr >= pairs) return;
+  const int sub = threadIdx.x % G;
+  const int64_t m = pr / H;
+  const int32_t h = (int32_t)(pr - m * H);
+  const int64_t li = (int64_t)h * n + m;
+  const int64_t off = pr * D + sub * 8;
+  const float lp = lse_part[li];
+  const bf16x8 op = load_bf16x8(o_part + off);
+  f32x4* acc = reinterpret_cast<f32x4*>(o_acc + off);
+  f32x4 r0, r1;
+  float lnew;
+  if (first) {
+    for (int j = 0; j < 4; ++j) {
+      r0[j] = (float)op[j];
+      r1[j] = (float)op[4 + j];
+    }
+    lnew = lp;
+  } else {
+    const float la = lse_acc[li];
+    const float mx = fmaxf(la, lp);
+    const f32x4 a0 = acc[0], a1 = acc[1];
+    if (mx == -INFINITY) {  // neither part has a key for this row
+      r0 = a0;
+      r1 = a1;
+      lnew = -INFINITY;
+    } else {
+      const float wa = __expf(la - mx), wp = __expf(lp - mx);
+      const float inv = 1.f / (wa + wp);
+      for (int j = 0; j < 4; ++j) {
+        r0[j] = (a0[j] * wa + (float)op[j] * wp) * inv;
+        r1[j] = (a1[j] * wa + (float)op[4 + j] * wp) * inv;
+      }
+      lnew = mx + __logf(wa + wp);
+    }
+  }
+  acc[0] = r0;
+  acc[1] = r1;
+  if (o_out) {
+    bf16x8 ob;
+    for (int j = 0; j < 4; ++j) {
+      ob[j] = (bf16)r0[j];
+      ob[4 + j] = (bf16)r1[j];
+    }
+    store_bf16x8(o_out + off, ob);
+  }
+  if (sub == 0) lse_acc[li] = lnew;
+}
+
+hipError_t launch_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
+                            const float* lse_part, float* o_acc, float* lse_acc, int32_t first,
+                            void* o_out, hipStream_t stream) {
+  const int64_t pairs = n * H;
+  if (pairs == 0) return hipSuccess;
+  const int64_t groups_per_block = 256 / (D / 8);
+  const int64_t blocks = (pairs + groups_per_block - 1) / groups_per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const bf16* op = static_cast<const bf16*>(o_part);
+  bf16* oo = static_cast<bf16*>(o_out);
+  if (D == 128)
+    hipLaunchKernelGGL(lse_merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, n, H,
+                       op, lse_part, o_acc, lse_acc, first, oo);
+  else if (D == 64)
+    hipLaunchKernelGGL(lse_merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, n, H,
+                       op, lse_part, o_acc, lse_acc, first, oo);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -32,6 +32,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Entry points are the library's only exported symbols (it is built with
+ * hidden default visibility). */
+#define THDCP_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -71,9 +75,11 @@ typedef enum {
 } thdcp_status_t;
 
 /* Message for the last non-OK status on this thread ("" if none). */
+THDCP_API
 const char* thdcp_last_error(void);
 
 /* Library version as major*10000 + minor*100 + patch. */
+THDCP_API
 int32_t thdcp_version(void);
 
 /*
@@ -90,6 +96,7 @@ int32_t thdcp_version(void);
  *   padding_present_out (nullable): 1 if padding exists, else 0.
  * Host pointers only; no device work.
  */
+THDCP_API
 thdcp_status_t thdcp_validate(const int32_t* cu_seqlens_host,
                               const int32_t* cu_seqlens_padded_host, int32_t B,
                               int64_t T, int32_t cp_size, int32_t rank,
@@ -107,6 +114,7 @@ thdcp_status_t thdcp_validate(const int32_t* cu_seqlens_host,
  * caller guarantees the layout rules of thdcp_validate; the kernel then still
  * stays inside its buffers.
  */
+THDCP_API
 thdcp_status_t thd_partition_index(const int32_t* cu_seqlens_padded_host,
                                    const int32_t* cu_seqlens_padded_dev, int32_t B,
                                    int64_t T, int32_t cp_size, int32_t rank,
@@ -121,6 +129,7 @@ thdcp_status_t thd_partition_index(const int32_t* cu_seqlens_padded_host,
  * [0, n_src) give an all-zero dst row. src and dst must not overlap.
  * row_bytes % 16 == 0 takes a 16-byte vector path.
  */
+THDCP_API
 thdcp_status_t thd_gather(const void* src_dev, int64_t n_src, const int32_t* idx_dev,
                           int64_t n, int64_t row_bytes, void* dst_dev, void* stream);
 
@@ -128,6 +137,7 @@ thdcp_status_t thd_gather(const void* src_dev, int64_t n_src, const int32_t* idx
  * Row scatter: dst[idx[m], :] = src[m, :] for m in [0, n). idx values outside
  * [0, n_dst) are skipped. Duplicate idx values race (last writer unspecified).
  */
+THDCP_API
 thdcp_status_t thd_scatter(const void* src_dev, int64_t n, const int32_t* idx_dev,
                            int64_t row_bytes, void* dst_dev, int64_t n_dst, void* stream);
 
@@ -139,9 +149,11 @@ thdcp_status_t thd_scatter(const void* src_dev, int64_t n, const int32_t* idx_de
  * of thd_gather / thd_scatter. A move of zero rows (n == 0) succeeds without
  * looking at the pointers and enqueues nothing.
  */
+THDCP_API
 thdcp_status_t thd_gather_batched(int32_t n_tensors, const void* const* src_list, int64_t n_src,
                                   const int32_t* idx_dev, int64_t n, int64_t row_bytes,
                                   void* const* dst_list, void* stream);
+THDCP_API
 thdcp_status_t thd_scatter_batched(int32_t n_tensors, const void* const* src_list, int64_t n,
                                    const int32_t* idx_dev, int64_t row_bytes,
                                    void* const* dst_list, int64_t n_dst, void* stream);
@@ -169,9 +181,11 @@ thdcp_status_t thd_scatter_batched(int32_t n_tensors, const void* const* src_lis
  * n_tokens * cp_size must be below 2^31; n_tokens == 0 succeeds without
  * looking at the pointers and enqueues nothing.
  */
+THDCP_API
 thdcp_status_t thd_a2a_pack(int32_t n_tensors, const void* const* src_list, int64_t n_tokens,
                             int32_t cp_size, int64_t group_bytes, void* const* dst_list,
                             void* stream);
+THDCP_API
 thdcp_status_t thd_a2a_unpack(int32_t n_tensors, const void* const* src_list, int64_t n_tokens,
                               int32_t cp_size, int64_t group_bytes, void* const* dst_list,
                               void* stream);
@@ -202,6 +216,8 @@ typedef struct {
   int32_t window_right;      /* must be 0  */
   int32_t pad_between_seqs;  /* -1 detect by value, 0 none, 1 present */
   int32_t kv_layout;         /* thdcp_kv_layout_t of K/V in and dK/dV out */
+  int32_t p2p;               /* 1: also build the P2P ring step tables
+                                (cp_attn_fwd_step / cp_attn_bwd_step) */
 } thdcp_attn_desc;
 
 typedef struct {
@@ -222,9 +238,12 @@ typedef struct {
  * THDCP_ERR_UNSUPPORTED when one document's rows, or the local share's rows,
  * of bf16 [H, D] reach 2 GiB (the kernels address them with 32-bit buffer
  * offsets), or, for THDCP_KV_RANK_MAJOR, when all T rows do. */
+THDCP_API
 thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan_out);
+THDCP_API
 thdcp_status_t thdcp_plan_get_info(thdcp_plan_t plan, thdcp_plan_info* info_out);
 /* Per-document count of real tokens this rank holds (int32 [B], host). */
+THDCP_API
 thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
 /* Copy the plan's device tables into the caller's workspace (device,
  * >= workspace_bytes, 256-byte aligned) with one async host-to-device copy on
@@ -234,8 +253,10 @@ thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
  * library keeps for the life of the process (16 slots, 16 MiB, allocated on
  * the first upload); larger ones are copied from the plan itself, which must
  * then outlive the copy. */
+THDCP_API
 thdcp_status_t thdcp_plan_upload(thdcp_plan_t plan, void* workspace_dev, size_t bytes,
                                  void* stream);
+THDCP_API
 void thdcp_plan_destroy(thdcp_plan_t plan);
 
 /*
@@ -250,6 +271,7 @@ void thdcp_plan_destroy(thdcp_plan_t plan);
  *   lse      fp32 [H, n_local]      natural log; -inf on padding rows
  * Padding rows get O = 0. Padding key rows are never read into a product.
  */
+THDCP_API
 thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k,
                            const void* v, void* o_local, float* lse, void* stream);
 
@@ -276,6 +298,7 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k
  * No atomics are used: every output row is written by exactly one workgroup,
  * so dQ, dK and dV are bit-identical from run to run.
  */
+THDCP_API
 thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k,
                            const void* v, const void* o_local, const float* lse,
                            const void* d_o, float* dq, float* dk, float* dv,
@@ -298,17 +321,80 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k
  *   thdcp_zero_untouched: writes 0 to every dk/dv row no local query attends;
  *     enqueues nothing when the plan has no such row.
  */
+THDCP_API
 thdcp_status_t cp_attn_bwd_preprocess(thdcp_plan_t plan, const void* o_local, const float* lse,
                                       const void* d_o, void* scratch, size_t scratch_bytes,
                                       void* stream);
+THDCP_API
 thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t plan, const void* q_local, const void* k,
                                 const void* v, const float* lse, const void* d_o, float* dk,
                                 float* dv, int32_t accumulate_dkv, const void* scratch,
                                 size_t scratch_bytes, void* stream);
+THDCP_API
 thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t plan, const void* q_local, const void* k,
                               const void* v, const float* lse, const void* d_o, float* dq,
                               const void* scratch, size_t scratch_bytes, void* stream);
+THDCP_API
 thdcp_status_t thdcp_zero_untouched(thdcp_plan_t plan, float* dk, float* dv, void* stream);
+
+/* ------------------------------------------------------------------------
+ * P2P (ring) context parallelism ([PAD] "Describe the bug": the P2P path runs
+ * a rank's attention in steps over its peers' K/V, with per-step sequence
+ * metadata and gradient tails to clear). At ring step i, rank `rank` works on
+ * the K/V that rank src = (rank - i) mod cp_size holds; the step results are
+ * merged through their log-sum-exp with thdcp_lse_merge. These calls need a
+ * plan made with p2p = 1: every step's tiles come from that one plan, built
+ * once per batch, so no step launches metadata work, and a step's gradient
+ * tail is zeroed only when the plan shows one.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * Attention of the local queries against the keys rank src_rank holds (same
+ * document, key <= query):
+ *   k_src, v_src  bf16 [n_local, H, D]  rank src's local K/V, in its local
+ *                                       row order (thd_partition_index order)
+ *   o_part        bf16 [n_local, H, D]  softmax over this step's keys times V;
+ *                                       0 on rows with no key in the step
+ *   lse_part      fp32 [H, n_local]     this step's LSE; -inf on such rows
+ */
+THDCP_API
+thdcp_status_t cp_attn_fwd_step(thdcp_plan_t plan, int32_t src_rank, const void* q_local,
+                                const void* k_src, const void* v_src, void* o_part,
+                                float* lse_part, void* stream);
+
+/*
+ * Fold one step's (o_part bf16 [n, H, D], lse_part fp32 [H, n]) into the
+ * running result (o_acc fp32 [n, H, D], lse_acc fp32 [H, n]):
+ *   lse = log(exp(lse_acc) + exp(lse_part)),
+ *   o_acc = (exp(lse_acc) o_acc + exp(lse_part) o_part) / exp(lse).
+ * first = 1 starts the accumulation (o_acc, lse_acc are only written). o_out
+ * (bf16 [n, H, D], nullable) also receives the merged output rounded to bf16,
+ * for the last step. Rows that are -inf in both stay O = 0, LSE = -inf. One
+ * elementwise launch; n == 0 enqueues nothing.
+ */
+THDCP_API
+thdcp_status_t thdcp_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
+                               const float* lse_part, float* o_acc, float* lse_acc,
+                               int32_t first, void* o_out, void* stream);
+
+/*
+ * Backward of one step with the softmax of the whole key set: lse is the
+ * merged LSE, scratch holds delta of the merged output (cp_attn_bwd_preprocess
+ * on the merged O and dO).
+ *   dq      fp32 [n_local, H, D]  written (accumulate_dq = 0, the first step)
+ *                                 or added to
+ *   dk_src, dv_src  fp32 [n_local, H, D], rank src's local row order: this
+ *           rank's partial for rank src's keys (what the ring sends back);
+ *           rows attended by a local query are written. zero_untouched = 1
+ *           also writes 0 to the other rows, only when the plan has such rows.
+ * Two launches (dQ, then dK/dV with the zeroing workgroups); no atomics.
+ */
+THDCP_API
+thdcp_status_t cp_attn_bwd_step(thdcp_plan_t plan, int32_t src_rank, const void* q_local,
+                                const void* k_src, const void* v_src, const float* lse,
+                                const void* d_o, const void* scratch, size_t scratch_bytes,
+                                float* dq, int32_t accumulate_dq, float* dk_src, float* dv_src,
+                                int32_t zero_untouched, void* stream);
 
 #ifdef __cplusplus
 }

@@ -43,6 +43,21 @@ def test_every_declared_symbol_is_exported(L):
     assert L.thdcp_version() >= 100
 
 
+def test_no_undeclared_exports(L):
+    # Internal helpers and launchers stay hidden: the dynamic symbol table's
+    # defined functions are exactly the header's entry points.
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", thd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3
+             and ln.split()[1] == "T"}
+    assert funcs == set(_declared_functions())
+
+
 STRAT = {O.DUAL_CHUNK_SWAP: thd.DUAL_CHUNK_SWAP, O.NO_LOAD_BALANCE: thd.NO_LOAD_BALANCE}
 
 
@@ -123,6 +138,30 @@ def test_plan_rejects_unsupported(L):
     with pytest.raises(thd.ThdcpError) as ei:
         thd.Plan(w.cu_seqlens(), w.cu_seqlens_padded(), w.T, 2, 0, w.strategy, 2, 96, upload=False)
     assert ei.value.status == 3
+
+
+def test_plan_p2p(L):
+    w = W.WORKLOADS["tiny_nlb"]
+    d = thd._Desc()
+    cup = np.ascontiguousarray(w.cu_seqlens_padded(), dtype=np.int32)
+    d.cu_seqlens_padded_host = cup.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    d.B, d.T, d.cp_size, d.rank, d.strategy, d.H, d.D = len(cup) - 1, w.T, 2, 0, 1, 2, 64
+    d.window_left, d.window_right, d.pad_between_seqs, d.kv_layout = -1, 0, -1, 0
+    d.p2p = 2
+    h = ctypes.c_void_p()
+    assert L.thdcp_plan_create(ctypes.byref(d), ctypes.byref(h)) == 1
+    # per-step tables are extra workspace; the all-gather tables are unchanged
+    for name in ("dcs_8k", "nlb_32k", "pad_131k"):
+        x = W.WORKLOADS[name]
+        a = (x.cu_seqlens(), x.cu_seqlens_padded(), x.T, x.cp_size, x.rank, x.strategy, x.H, x.D)
+        g = thd.Plan(*a, upload=False)
+        s = thd.Plan(*a, upload=False, p2p=True)
+        assert s.info.workspace_bytes > g.info.workspace_bytes
+        assert (s.info.causal_pairs, s.info.n_fwd_tiles, s.info.n_bwd_tiles,
+                s.info.n_zero_ranges) == (g.info.causal_pairs, g.info.n_fwd_tiles,
+                                          g.info.n_bwd_tiles, g.info.n_zero_ranges)
+        g.close()
+        s.close()
 
 
 def test_plan_kv_layout(L):
