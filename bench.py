@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="dcs_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-p2p", action="store_true",
+                    help="skip the P2P (ring) step measurement")
     ap.add_argument("--no-a2a", action="store_true",
                     help="skip the all-to-all layout measurement (flat vs dual-chunk)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -241,6 +243,9 @@ def main():
                      "host_wall_per_step": round(wall / args.steps * 1e3, 4),
                      "kernel_reps": reps},
     }
+    if cp > 1 and not args.no_p2p:
+        result["p2p_ring"] = p2p_ring(w, q, k, v, do, cup_dev, stream, args.warmup, args.steps,
+                                      reps, flop_fwd + flop_bwd, ms_step)
     if not args.no_a2a:
         result["a2a_layout"] = a2a_layout(stream)
         if w.name == "flat_75k":
@@ -254,6 +259,101 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, t)
     print(json.dumps(result), flush=True)
+
+
+def p2p_ring(w, q, k, v, do, cup_dev, stream, warmup, steps, reps, flops, ms_allgather):
+    """The same rank's fwd+bwd as P2P (ring) steps on one GPU: every peer's
+    local K/V is already resident (what the ring's sends deliver). A ring
+    step = p2p plan + upload, partition index, gather of local Q and dO,
+    cp forward steps each folded by the LSE merge, delta of the merged
+    output, cp backward steps (dQ accumulated, the peer's dK/dV into its own
+    buffer for the return trip). The transfers themselves are not here."""
+    import torch
+    import context_causal_attention_thd_amd as thd
+    dev = q.device
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    T, H, D, cp, r = w.T, w.H, w.D, w.cp_size, w.rank
+    n = T // cp
+    idxs = [thd.partition_index(cup, cup_dev, T, cp, s, w.strategy) for s in range(cp)]
+    kl = [thd.gather(k, i) for i in idxs]
+    vl = [thd.gather(v, i) for i in idxs]
+    probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, p2p=True)
+    ws = torch.empty(int(probe.info.workspace_bytes) + 4096, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(int(probe.info.bwd_scratch_bytes) + 256, dtype=torch.uint8,
+                          device=dev)
+    probe.close()
+    idx = torch.empty(n, dtype=torch.int32, device=dev)
+    ql = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
+    dol = torch.empty_like(ql)
+    o_part = torch.empty_like(ql)
+    lse_part = torch.empty((H, n), dtype=torch.float32, device=dev)
+    o_acc = torch.empty((n, H, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((H, n), dtype=torch.float32, device=dev)
+    o = torch.empty_like(ql)
+    dq = torch.empty((n, H, D), dtype=torch.float32, device=dev)
+    dkp = torch.empty((cp, n, H, D), dtype=torch.float32, device=dev)
+    dvp = torch.empty_like(dkp)
+    srcs = [(r - i) % cp for i in range(cp)]
+
+    def fwd(plan):
+        for i, s in enumerate(srcs):
+            thd.attn_fwd_step(plan, s, ql, kl[s], vl[s], o_part=o_part, lse_part=lse_part)
+            thd.lse_merge(o_part, lse_part, o_acc, lse, first=(i == 0),
+                          o_out=o if i == cp - 1 else None)
+
+    def bwd(plan):
+        thd.bwd_preprocess(plan, o, lse, dol, scratch)
+        for i, s in enumerate(srcs):
+            thd.attn_bwd_step(plan, s, ql, kl[s], vl[s], lse, dol, scratch, dq, i > 0,
+                              dk_src=dkp[s], dv_src=dvp[s])
+
+    def step():
+        plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, p2p=True)
+        plan.upload_into(ws, stream)
+        thd.partition_index(cup, cup_dev, T, cp, r, w.strategy, out=idx)
+        thd.gather_many([q, do], idx, [ql, dol])
+        fwd(plan)
+        bwd(plan)
+        return plan
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    plans = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        plans.append(step())
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plans.clear()
+    ms = e0.elapsed_time(e1) / steps
+
+    plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, p2p=True)
+    plan.upload_into(ws, stream)
+
+    def timed(fn):
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_fwd = timed(lambda: fwd(plan))
+    t_merge = timed(lambda: thd.lse_merge(o_part, lse_part, o_acc, lse, first=False))
+    t_bwd = timed(lambda: bwd(plan))
+    return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "vs_allgather_step": round(ms_allgather / ms, 4), "ring_steps": cp,
+            "times_ms": {"fwd_steps_and_merges": round(t_fwd, 4),
+                         "one_merge": round(t_merge, 4),
+                         "bwd_preprocess_and_steps": round(t_bwd, 4)},
+            "note": "per-rank compute of the ring on one GPU; peer K/V resident, "
+                    "transfers not included"}
 
 
 def a2a_layout(stream, seqlens=(8192, 32768, 75600), cp=8, heads=40, head_dim=128):
