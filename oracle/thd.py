@@ -31,6 +31,13 @@ Readings of points the pages leave open (each is listed in the design notes):
   * Causality is by position inside the document, diagonal included
     (window_size = (-1, 0), [AG] "Scope and constraints"), and the mask is
     identical to cp_size = 1 ([A2A] body).
+  * Other masks ([A2A] body: after the a2a exchange every attn_mask_type and
+    window_size stays valid): window = (left, right) lets a real query at
+    position p attend the real tokens of its document at positions
+    [p - left, p + right], -1 meaning no bound on that side. (-1, 0) is the
+    causal mask (every causal variant, since queries and keys share one
+    layout), (-1, -1) the padding-only mask (the whole document), (w, 0) a
+    causal sliding window.
   * softmax scale 1/sqrt(D); LSE is the natural log; padding rows give
     O = 0 and LSE = -inf; gradients of padding rows and of keys that no
     local query attends are 0.
@@ -170,25 +177,52 @@ def local_valid_lengths(cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, ran
     return out
 
 
-def causal_pairs(cu_seqlens, cu_seqlens_padded, T: int, idx) -> int:
+CAUSAL = (-1, 0)
+
+
+def key_bounds(g, a: int, e: int, window=CAUSAL):
+    """First and last key (global rows, inclusive) that real query row(s) g of
+    a document with real tokens [a, e) attend: the positions within
+    [g - left, g + right] of that range, -1 meaning unbounded."""
+    left, right = int(window[0]), int(window[1])
+    g = np.asarray(g, dtype=np.int64)
+    lo = np.full_like(g, a) if left < 0 else np.maximum(a, g - left)
+    hi = np.full_like(g, e - 1) if right < 0 else np.minimum(e - 1, g + right)
+    return lo, hi
+
+
+def _doc_real_end(cu_seqlens, cu_seqlens_padded, d: int) -> int:
+    cu, cup = _as_list(cu_seqlens), _as_list(cu_seqlens_padded)
+    return cup[d] + (cu[d + 1] - cu[d])
+
+
+def causal_pairs(cu_seqlens, cu_seqlens_padded, T: int, idx, window=CAUSAL) -> int:
     """Number of (query, key) pairs the mask allows, summed over local rows
-    (per head): query g attends keys j of its own document with j <= g."""
+    (per head): under the causal mask query g attends keys j of its own
+    document with j <= g; in general the keys of ``key_bounds``."""
     doc, pos, valid = token_table(cu_seqlens, cu_seqlens_padded, T)
+    cup = _as_list(cu_seqlens_padded)
     total = 0
     for g in _as_list(idx):
         if valid[g]:
-            total += int(pos[g]) + 1
+            d = int(doc[g])
+            lo, hi = key_bounds(g, cup[d], _doc_real_end(cu_seqlens, cu_seqlens_padded, d),
+                                window)
+            total += int(hi) - int(lo) + 1
     return total
 
 
-def touched_keys(cu_seqlens, cu_seqlens_padded, T: int, idx) -> np.ndarray:
+def touched_keys(cu_seqlens, cu_seqlens_padded, T: int, idx, window=CAUSAL) -> np.ndarray:
     """bool [T]: key rows attended by at least one local query."""
     doc, pos, valid = token_table(cu_seqlens, cu_seqlens_padded, T)
     cup = _as_list(cu_seqlens_padded)
     out = np.zeros(T, dtype=bool)
     for g in _as_list(idx):
         if valid[g]:
-            out[cup[doc[g]]:g + 1] = True
+            d = int(doc[g])
+            lo, hi = key_bounds(g, cup[d], _doc_real_end(cu_seqlens, cu_seqlens_padded, d),
+                                window)
+            out[int(lo):int(hi) + 1] = True
     return out
 
 
@@ -290,7 +324,8 @@ def a2a_after_attn(full_outputs, cu_seqlens_padded, T: int, cp_size: int,
 # --------------------------------------------------------------------------
 
 def _groups(idx, cu_seqlens, cu_seqlens_padded, T: int, rows: Optional[Sequence[int]]):
-    """Valid local rows grouped by document: (doc start, local rows, globals)."""
+    """Valid local rows grouped by document: (doc start, local rows, globals,
+    end of the document's real tokens)."""
     doc, _, valid = token_table(cu_seqlens, cu_seqlens_padded, T)
     cup = _as_list(cu_seqlens_padded)
     idx = np.asarray(idx, dtype=np.int64)
@@ -304,15 +339,16 @@ def _groups(idx, cu_seqlens, cu_seqlens_padded, T: int, rows: Optional[Sequence[
     out = []
     for d in sorted(by_doc):
         ms = np.asarray(by_doc[d], dtype=np.int64)
-        out.append((cup[d], ms, idx[ms]))
+        out.append((cup[d], ms, idx[ms], _doc_real_end(cu_seqlens, cu_seqlens_padded, d)))
     return out
 
 
-def _scores(q_rows, k_keys, g_rows, key0: int, scale: float):
-    """scale * q k^T with keys j > g (other rows of the future) set to -inf."""
+def _scores(q_rows, k_keys, lo_rows, hi_rows, key0: int, scale: float):
+    """scale * q k^T over keys key0.. with keys outside a row's [lo, hi] set
+    to -inf (under the causal mask: the keys j > g of the future)."""
     s = (q_rows @ k_keys.T) * scale
     keys = key0 + np.arange(k_keys.shape[0])
-    s[keys[None, :] > g_rows[:, None]] = -np.inf
+    s[(keys[None, :] > hi_rows[:, None]) | (keys[None, :] < lo_rows[:, None])] = -np.inf
     return s
 
 
@@ -323,7 +359,8 @@ def _chunks(n_rows: int, n_keys: int):
 
 
 def attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T: int,
-                  scale: Optional[float] = None, rows: Optional[Sequence[int]] = None):
+                  scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
+                  window=CAUSAL):
     """O [n, H, D] and LSE [H, n] of local queries against the full K/V.
 
     A local row m with global row g = idx[m] that is a real token attends the
@@ -331,6 +368,7 @@ def attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T: int,
     the end of a document): s_j = scale * <Q_m, K_j>, LSE = log sum_j exp s_j,
     O_m = sum_j exp(s_j - LSE) V_j. Padding rows: O = 0, LSE = -inf.
     ``rows`` restricts the computation to those local rows (others stay 0/-inf).
+    ``window`` (see ``key_bounds``) replaces j <= g by the window's keys.
     """
     q_local = np.asarray(q_local, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -339,13 +377,14 @@ def attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T: int,
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     out = np.zeros((n, H, v.shape[2]), dtype=np.float64)
     lse = np.full((H, n), -np.inf, dtype=np.float64)
-    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, rows):
-        kend = int(gs.max()) + 1
+    for a, ms, gs, e_doc in _groups(idx, cu_seqlens, cu_seqlens_padded, T, rows):
+        lo, hi = key_bounds(gs, a, e_doc, window)
+        k0, kend = int(lo.min()), int(hi.max()) + 1
         for h in range(H):
-            kk = k[a:kend, h]
-            vv = v[a:kend, h]
-            for r0, r1 in _chunks(len(ms), kend - a):
-                s = _scores(q_local[ms[r0:r1], h], kk, gs[r0:r1], a, scale)
+            kk = k[k0:kend, h]
+            vv = v[k0:kend, h]
+            for r0, r1 in _chunks(len(ms), kend - k0):
+                s = _scores(q_local[ms[r0:r1], h], kk, lo[r0:r1], hi[r0:r1], k0, scale)
                 mx = s.max(axis=1)
                 e = np.exp(s - mx[:, None])
                 tot = e.sum(axis=1)
@@ -355,7 +394,8 @@ def attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T: int,
 
 
 def attention_bwd(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded, T: int,
-                  scale: Optional[float] = None, rows: Optional[Sequence[int]] = None):
+                  scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
+                  window=CAUSAL):
     """Gradients of sum(dO * O) for ``attention_fwd``: dQ [n,H,D] (local rows)
     and this rank's partial dK, dV [T,H,D] in global order.
 
@@ -364,7 +404,8 @@ def attention_bwd(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded, T
     dK_j += scale dS_j Q_m, dV_j += P_j dO_m. These partials are what the
     rank hands to the reduce-scatter ([AG] sequence diagram: dK/dV are
     unrestored for reduce-scatter). Rows that are padding or that no local
-    query attends stay 0. ``rows`` restricts the query rows that contribute.
+    query attends stay 0. ``rows`` restricts the query rows that contribute;
+    ``window`` is the mask of ``attention_fwd``.
     """
     q_local = np.asarray(q_local, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -375,24 +416,25 @@ def attention_bwd(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded, T
     dq = np.zeros((n, H, D), dtype=np.float64)
     dk = np.zeros((T, H, D), dtype=np.float64)
     dv = np.zeros((T, H, D), dtype=np.float64)
-    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, rows):
-        kend = int(gs.max()) + 1
+    for a, ms, gs, e_doc in _groups(idx, cu_seqlens, cu_seqlens_padded, T, rows):
+        lo, hi = key_bounds(gs, a, e_doc, window)
+        k0, kend = int(lo.min()), int(hi.max()) + 1
         for h in range(H):
-            kk = k[a:kend, h]
-            vv = v[a:kend, h]
-            for r0, r1 in _chunks(len(ms), kend - a):
+            kk = k[k0:kend, h]
+            vv = v[k0:kend, h]
+            for r0, r1 in _chunks(len(ms), kend - k0):
                 m_sel = ms[r0:r1]
                 qq = q_local[m_sel, h]
                 dd = do_local[m_sel, h]
-                s = _scores(qq, kk, gs[r0:r1], a, scale)
+                s = _scores(qq, kk, lo[r0:r1], hi[r0:r1], k0, scale)
                 mx = s.max(axis=1)
                 e = np.exp(s - mx[:, None])
                 p = e / e.sum(axis=1)[:, None]
                 dp = dd @ vv.T
                 ds = p * (dp - (p * dp).sum(axis=1)[:, None])
                 dq[m_sel, h] = scale * (ds @ kk)
-                dk[a:kend, h] += scale * (ds.T @ qq)
-                dv[a:kend, h] += p.T @ dd
+                dk[k0:kend, h] += scale * (ds.T @ qq)
+                dv[k0:kend, h] += p.T @ dd
     return dq, dk, dv
 
 
@@ -432,14 +474,15 @@ def attention_fwd_keys(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T: int
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     out = np.zeros((n, H, v.shape[2]), dtype=np.float64)
     lse = np.full((H, n), -np.inf, dtype=np.float64)
-    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, None):
+    for a, ms, gs, _ in _groups(idx, cu_seqlens, cu_seqlens_padded, T, None):
         kend = int(gs.max()) + 1
         drop = ~key_ok[a:kend]
         for h in range(H):
             kk = k[a:kend, h]
             vv = v[a:kend, h]
             for r0, r1 in _chunks(len(ms), kend - a):
-                s = _scores(q_local[ms[r0:r1], h], kk, gs[r0:r1], a, scale)
+                s = _scores(q_local[ms[r0:r1], h], kk, np.full(r1 - r0, a), gs[r0:r1], a,
+                            scale)
                 s[:, drop] = -np.inf
                 mx = s.max(axis=1)
                 some = np.isfinite(mx)
@@ -490,7 +533,7 @@ def attention_bwd_keys(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padd
     dq = np.zeros((n, H, D), dtype=np.float64)
     dk = np.zeros((T, H, D), dtype=np.float64)
     dv = np.zeros((T, H, D), dtype=np.float64)
-    for a, ms, gs in _groups(idx, cu_seqlens, cu_seqlens_padded, T, None):
+    for a, ms, gs, _ in _groups(idx, cu_seqlens, cu_seqlens_padded, T, None):
         kend = int(gs.max()) + 1
         drop = ~key_ok[a:kend]
         for h in range(H):
@@ -500,7 +543,7 @@ def attention_bwd_keys(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padd
                 m_sel = ms[r0:r1]
                 qq = q_local[m_sel, h]
                 dd = do_local[m_sel, h]
-                s = _scores(qq, kk, gs[r0:r1], a, scale)
+                s = _scores(qq, kk, np.full(r1 - r0, a), gs[r0:r1], a, scale)
                 p = np.exp(s - lse[h, m_sel][:, None])
                 p[:, drop] = 0.0
                 dp = dd @ vv.T
@@ -512,13 +555,14 @@ def attention_bwd_keys(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padd
 
 
 def rank_share(q, k, v, do, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int,
-               rank: int, strategy: str, scale: Optional[float] = None):
+               rank: int, strategy: str, scale: Optional[float] = None, window=CAUSAL):
     """Everything one rank computes, from global-order inputs: idx, O, LSE,
     dQ (local rows) and the dK/dV partials (global rows)."""
     idx = partition_index(cu_seqlens_padded, T, cp_size, rank, strategy)
     q_local = gather(q, idx)
     do_local = gather(do, idx)
-    o, lse = attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T, scale)
+    o, lse = attention_fwd(q_local, k, v, idx, cu_seqlens, cu_seqlens_padded, T, scale,
+                           window=window)
     dq, dk, dv = attention_bwd(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padded,
-                               T, scale)
+                               T, scale, window=window)
     return idx, o, lse, dq, dk, dv
