@@ -42,7 +42,8 @@ struct BwdSmem {
   bf16 dO[2][kBM * P];
   float lse2[2][kBM];
   float dlt[2][kBM];
-  int32_t gq[2][kBM];
+  int32_t ghi[2][kBM];  // last key a query row attends (g + wr); -1 past the row range
+  int32_t glo[2][kBM];  // first key (g - wl); read only for non-causal bands
 };
 
 // Untouched key rows each zeroing workgroup clears (dK and dV, all heads).
@@ -76,11 +77,13 @@ __device__ void zero_untouched_block(int64_t b, const ZeroRange* __restrict__ zr
   }
 }
 
-template <int D>
+// BAND: the mask is a general band [g - wl, g + wr] (a lower-bound test
+// per element); otherwise it is causal (key <= g only).
+template <int D, bool BAND>
 __global__ void __launch_bounds__(kThreads, 1)
 attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                      const bf16* __restrict__ k, const bf16* __restrict__ v,
-                     const int32_t* __restrict__ kv_row, int32_t kv_sub,
+                     const int32_t* __restrict__ kv_row, int32_t kv_sub, int32_t wl, int32_t wr,
                      const bf16* __restrict__ d_o,
                      const float* __restrict__ lse,
                      const float* __restrict__ delta, float* __restrict__ dk,
@@ -154,7 +157,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   // written to LDS after the current block's MFMAs, so they stay in flight.
   u32x4 qreg[CH], dreg[CH];
   float lreg = 0.f, dlreg = 0.f;
-  int greg = -1;
+  int hreg = -1, loreg = 0;
   auto load_block = [&](int mb) {
     const int64_t base = (int64_t)mb * rs + head_off;
     const uint32_t bytes = (uint32_t)((int64_t)(t.m_hi - mb) * rs * 2);
@@ -171,7 +174,9 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
       lreg = buffer_load_f32(make_rsrc(lse + row, rbytes), (uint32_t)lane * 4u);
       dlreg = buffer_load_f32(make_rsrc(delta + row, rbytes), (uint32_t)lane * 4u);
       const int m = mb + lane;
-      greg = m < t.m_hi ? m + (m < t.m_split ? t.dg_a : t.dg_b) : -1;
+      const int g = m + (m < t.m_split ? t.dg_a : t.dg_b);
+      hreg = m < t.m_hi ? g + wr : -1;
+      if constexpr (BAND) loreg = g - wl;
     }
   };
   auto store_block = [&](int buf) {
@@ -183,7 +188,8 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     if (wave_uniform(w) == 0) {
       sm.lse2[buf][lane] = lreg * kLog2e;
       sm.dlt[buf][lane] = dlreg;
-      sm.gq[buf][lane] = greg;
+      sm.ghi[buf][lane] = hreg;
+      if constexpr (BAND) sm.glo[buf][lane] = loreg;
     }
   };
 
@@ -223,10 +229,13 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
       const int qr0 = qm * 16 + G * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
-      const i32x4 g4 = *reinterpret_cast<const i32x4*>(&sm.gq[cur][qr0]);
+      const i32x4 hi4 = *reinterpret_cast<const i32x4*>(&sm.ghi[cur][qr0]);
+      i32x4 lo4 = {0, 0, 0, 0};
+      if constexpr (BAND) lo4 = *reinterpret_cast<const i32x4*>(&sm.glo[cur][qr0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = key_ok & (my_key <= g4[i]);
+        bool ok = key_ok & (my_key <= hi4[i]);
+        if constexpr (BAND) ok &= my_key >= lo4[i];
         const float p = ok ? fast_exp2(fmaf(s[qm][i], scale_log2, -l4[i])) : 0.f;
         const float dsv = ok ? p * (dp[qm][i] - d4[i]) : 0.f;
         s[qm][i] = p;
@@ -283,10 +292,10 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     }
 }
 
-template <int D>
+template <int D, bool BAND>
 hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const void* q,
                         const void* k, const void* v, const int32_t* kv_row, int32_t kv_sub,
-                        const void* d_o, const float* lse, const float* delta, float* dk,
+                        Band band, const void* d_o, const float* lse, const float* delta, float* dk,
                         float* dv, int64_t n_local, float scale, int32_t accumulate,
                         const ZeroRange* zr, int32_t n_zr, int64_t zero_rows,
                         hipStream_t stream) {
@@ -304,14 +313,15 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_set.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, BAND>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), smem,
-                     stream, tiles, H, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), kv_row, kv_sub, static_cast<const bf16*>(d_o),
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BAND>), dim3((unsigned)blocks), dim3(kThreads),
+                     smem, stream, tiles, H, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), kv_row, kv_sub,
+                     band.wl, band.wr, static_cast<const bf16*>(d_o),
                      lse, delta, dk, dv, n_local, scale, scale * kLog2e, accumulate,
                      (int32_t)attn_blocks, zr, n_zr, zero_rows);
   return hipGetLastError();
@@ -321,18 +331,19 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
 
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                                 const void* q, const void* k, const void* v, KvRows kv,
-                                const void* d_o, const float* lse, const float* delta, float* dk,
-                                float* dv, int64_t n_local, float scale, int32_t accumulate,
-                                const ZeroRange* zr, int32_t n_zr, int64_t zero_rows,
-                                hipStream_t stream) {
-  if (D == 128)
-    return launch_bwd_d<128>(tiles, n_tiles, H, q, k, v, kv.map, (int32_t)kv.sub, d_o, lse,
-                             delta, dk, dv, n_local, scale, accumulate, zr, n_zr, zero_rows,
-                             stream);
-  if (D == 64)
-    return launch_bwd_d<64>(tiles, n_tiles, H, q, k, v, kv.map, (int32_t)kv.sub, d_o, lse,
-                            delta, dk, dv, n_local, scale, accumulate, zr, n_zr, zero_rows,
-                            stream);
+                                Band band, const void* d_o, const float* lse,
+                                const float* delta, float* dk, float* dv, int64_t n_local,
+                                float scale, int32_t accumulate, const ZeroRange* zr,
+                                int32_t n_zr, int64_t zero_rows, hipStream_t stream) {
+  const int32_t sub = (int32_t)kv.sub;
+#define THDCP_DKDV(DD, BB)                                                                   \
+  return launch_bwd_d<DD, BB>(tiles, n_tiles, H, q, k, v, kv.map, sub, band, d_o, lse, delta, \
+                              dk, dv, n_local, scale, accumulate, zr, n_zr, zero_rows, stream)
+  if (D == 128 && band.causal) THDCP_DKDV(128, false);
+  if (D == 128) THDCP_DKDV(128, true);
+  if (D == 64 && band.causal) THDCP_DKDV(64, false);
+  if (D == 64) THDCP_DKDV(64, true);
+#undef THDCP_DKDV
   return hipErrorInvalidValue;
 }
 

@@ -48,7 +48,8 @@ __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                    const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
-                   const bf16* __restrict__ d_o, const bf16* __restrict__ o,
+                   int32_t wl, int32_t wr, const bf16* __restrict__ d_o,
+                   const bf16* __restrict__ o,
                    const float* __restrict__ lse, float* __restrict__ delta,
                    float* __restrict__ dq, int64_t n_local, int32_t accumulate,
                    float scale, float scale_log2) {
@@ -77,7 +78,10 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   const int g = t.g0 + r;
   const bool valid = in_tile && g < t.e;
   const int64_t m = (int64_t)t.m0 + r;
-  const int my_g = valid ? g : -1;
+  // Key j is allowed iff my_lo <= j <= my_hi (and below the tile range's
+  // end); padding rows allow nothing.
+  const int my_lo = g - wl;
+  const int my_hi = valid ? g + wr : -1;
 
   // Q and dO fragments (B operands): query li, head dims kk*16 + hh*8 .. +7
   bf16x8 qf[KSTEPS], dof[KSTEPS];
@@ -116,8 +120,12 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
 
   const int wrow_last = min(w * 32 + 31, t.n - 1);
   const bool wave_has_rows = (w * 32 < t.n) && (t.g0 + w * 32 < t.e);
-  const int wave_kmax = wave_uniform(wave_has_rows ? min(t.g0 + wrow_last, t.e - 1) : -1);
+  // Keys the wave's rows can reach: [wave_kmin, wave_kmax].
+  const int wave_kmax =
+      wave_uniform(wave_has_rows ? min(t.g0 + wrow_last + wr, t.e - 1) : -1);
+  const int wave_kmin = wave_uniform(t.g0 + w * 32 - wl);
   const int wave_gmin = wave_uniform(t.g0 + w * 32);
+  const int wave_gmax = wave_uniform(t.g0 + w * 32 + 31);
   const bool wave_all_valid =
       wave_uniform((w * 32 + 31 < t.n) && (t.g0 + w * 32 + 31 < t.e)) != 0;
 
@@ -208,7 +216,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
 
-    if (k0 <= wave_kmax) {
+    if (k0 <= wave_kmax && k0 + BN - 1 >= wave_kmin) {
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -225,13 +233,14 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
           dp[kb] = mfma32(load_bf16x8(vp + kk * 16), dof[kk], dp[kb]);
         }
       }
-      const bool diag = !wave_all_valid || k0 + BN - 1 > wave_gmin || k0 + BN > kend;
+      const bool diag = !wave_all_valid || k0 + BN - 1 > wave_gmin + wr ||
+                        k0 < wave_gmax - wl || k0 + BN > kend;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          const bool ok = !diag || (key <= my_g && key < kend);
+          const bool ok = !diag || (key <= my_hi && key >= my_lo && key < kend);
           const float p = ok ? fast_exp2(fmaf(s[kb][i], scale_log2, -lse2)) : 0.f;
           dp[kb][i] = ok ? p * (dp[kb][i] - dlt) : 0.f;
         }
@@ -282,25 +291,26 @@ namespace {
 template <int D, bool M>
 void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int32_t H,
                   const bf16* q, const bf16* k, const bf16* v, const int32_t* kv_row,
-                  int32_t kv_sub, uint32_t kvb, const bf16* d_o, const bf16* o, const float* lse,
-                  float* delta, float* dq, int64_t n_local, float scale, int32_t accumulate) {
+                  int32_t kv_sub, uint32_t kvb, Band band, const bf16* d_o, const bf16* o,
+                  const float* lse, float* delta, float* dq, int64_t n_local, float scale,
+                  int32_t accumulate) {
   if (o)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, true>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, d_o, o, lse, delta, dq,
-                       n_local, accumulate, scale, scale * kLog2e);
+                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,
+                       o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e);
   else
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, false>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, d_o, o, lse, delta, dq,
-                       n_local, accumulate, scale, scale * kLog2e);
+                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,
+                       o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                               const void* q, const void* k, const void* v, KvRows kv,
-                              const void* d_o, const void* o, const float* lse, float* delta,
-                              float* dq, int64_t n_local, float scale, int32_t accumulate,
-                              hipStream_t stream) {
+                              Band band, const void* d_o, const void* o, const float* lse,
+                              float* delta, float* dq, int64_t n_local, float scale,
+                              int32_t accumulate, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -314,16 +324,16 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
   const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
   const int32_t sub = (int32_t)kv.sub;
   if (D == 128 && kv.map)
-    launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+    launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
                             delta, dq, n_local, scale, accumulate);
   else if (D == 128)
-    launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+    launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
                              delta, dq, n_local, scale, accumulate);
   else if (D == 64 && kv.map)
-    launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+    launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
                            delta, dq, n_local, scale, accumulate);
   else if (D == 64)
-    launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, db, ob, lse,
+    launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
                             delta, dq, n_local, scale, accumulate);
   else
     return hipErrorInvalidValue;

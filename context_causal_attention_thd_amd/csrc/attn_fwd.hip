@@ -68,8 +68,8 @@ __global__ void __launch_bounds__(kFwdThreads<QB>, 2)
 attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                 const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
-                bf16* __restrict__ o, float* __restrict__ lse, int64_t n_local,
-                float scale_log2) {
+                int32_t wl, int32_t wr, bf16* __restrict__ o, float* __restrict__ lse,
+                int64_t n_local, float scale_log2) {
   constexpr int kThreads = kFwdThreads<QB>;
   constexpr int BN = kFwdBN;
   constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
@@ -92,7 +92,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int64_t head_off = (int64_t)h * D;
 
   // Query rows of this lane: block qb holds tile row (w*QB + qb)*16 + l16.
-  int my_g[QB];
+  // Key j is allowed iff my_lo <= j <= my_hi (and j is below the tile range's
+  // end); padding rows have my_hi = -1 and allow nothing.
+  int my_g[QB], my_lo[QB], my_hi[QB];
   bool in_tile[QB];
   int64_t m_row[QB];
   bf16x8 qf[QB][KS];  // B operand of S^T: query l16, head dims kk*32 + G*8 .. +7
@@ -103,7 +105,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     const int g = t.g0 + r;
     const bool valid = in_tile[qb] && g < t.e;
     m_row[qb] = (int64_t)t.m0 + r;
-    my_g[qb] = valid ? g : -1;  // key j is allowed iff j <= my_g
+    my_g[qb] = valid ? g : -1;
+    my_lo[qb] = g - wl;
+    my_hi[qb] = valid ? g + wr : -1;
     const bf16* qp = q + m_row[qb] * rs + head_off + G * 8;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
@@ -192,8 +196,8 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16(a, qf[qb][kk], s[qb][kb]);
       }
   };
-  // Causal / padding mask: key j is allowed iff j <= my_g and j < kend (the
-  // end of the key range the tile belongs to).
+  // Band / padding mask: key j is allowed iff my_lo <= j <= my_hi and
+  // j < kend (the end of the key range the tile belongs to).
   auto mask = [&](int k0, int kend, f32x4 (&s)[QB][KB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -202,7 +206,7 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + kb * 16 + G * 4 + i;
-          if (key > my_g[qb] || key >= kend) s[qb][kb][i] = -INFINITY;
+          if (key > my_hi[qb] || key < my_lo[qb] || key >= kend) s[qb][kb][i] = -INFINITY;
         }
   };
   // Lazy rescale: the running max of a query moves only when some score of
@@ -287,8 +291,13 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int row0 = w * QB * 16;
   const bool wave_has_rows = (row0 < t.n) && (t.g0 + row0 < t.e);
   const int wrow_last = min(row0 + QB * 16 - 1, t.n - 1);
-  const int wave_kmax = wave_uniform(wave_has_rows ? min(t.g0 + wrow_last, t.e - 1) : -1);
+  // Keys the wave's rows can reach: [wave_kmin, wave_kmax]; a tile needs the
+  // per-element mask unless every key of it is inside every row's band.
+  const int wave_kmax =
+      wave_uniform(wave_has_rows ? min(t.g0 + wrow_last + wr, t.e - 1) : -1);
+  const int wave_kmin = wave_uniform(t.g0 + row0 - wl);
   const int wave_gmin = wave_uniform(t.g0 + row0);
+  const int wave_gmax = wave_uniform(t.g0 + row0 + QB * 16 - 1);
   const bool wave_all_valid =
       wave_uniform((row0 + QB * 16 - 1 < t.n) && (t.g0 + row0 + QB * 16 - 1 < t.e)) != 0;
   int pos[CH];
@@ -312,10 +321,12 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       load_rows(v, tile_k0(it + 1), tile_kend(it + 1), pos, vreg);
       if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
-    if (k0 <= wave_kmax) {
+    if (k0 <= wave_kmax && k0 + BN - 1 >= wave_kmin) {
       f32x4 s[QB][KB];
       scores(cur, s);
-      if (!wave_all_valid || k0 + BN - 1 > wave_gmin || k0 + BN > kend) mask(k0, kend, s);
+      if (!wave_all_valid || k0 + BN - 1 > wave_gmin + wr || k0 < wave_gmax - wl ||
+          k0 + BN > kend)
+        mask(k0, kend, s);
       softmax_max(s);
       softmax_pv(cur, s);
     }
@@ -356,24 +367,25 @@ constexpr int kFwdQB = 1;
 template <int D>
 hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const bf16* q,
                         const bf16* k, const bf16* v, const int32_t* kv_row, int32_t kv_sub,
-                        uint32_t kv_bytes, bf16* o, float* lse, int64_t n_local,
+                        uint32_t kv_bytes, Band band, bf16* o, float* lse, int64_t n_local,
                         float scale_log2, hipStream_t stream) {
   if (kv_row)
     hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, true>), dim3((unsigned)blocks),
                        dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub,
-                       kv_bytes, o, lse, n_local, scale_log2);
+                       kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, false>), dim3((unsigned)blocks),
                        dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub,
-                       kv_bytes, o, lse, n_local, scale_log2);
+                       kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, KvRows kv, void* o,
-                           float* lse, int64_t n_local, float scale, hipStream_t stream) {
+                           const void* q, const void* k, const void* v, KvRows kv, Band band,
+                           void* o, float* lse, int64_t n_local, float scale,
+                           hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -386,11 +398,11 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
   if (kv.map && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
   if (D == 128)
-    return launch_fwd_d<128>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, ob, lse,
-                             n_local, scale_log2, stream);
+    return launch_fwd_d<128>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, band,
+                             ob, lse, n_local, scale_log2, stream);
   if (D == 64)
-    return launch_fwd_d<64>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, ob, lse,
-                            n_local, scale_log2, stream);
+    return launch_fwd_d<64>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, band,
+                            ob, lse, n_local, scale_log2, stream);
   return hipErrorInvalidValue;
 }
 

@@ -58,10 +58,9 @@ thdcp_status_t check_layout(const int32_t* cu, const int32_t* cup, int32_t B, in
   if (rank < 0 || rank >= cp) return fail(THDCP_ERR_ARG, "rank %d outside [0, %d)", rank, cp);
   if (strategy != THDCP_DUAL_CHUNK_SWAP && strategy != THDCP_NO_LOAD_BALANCE)
     return fail(THDCP_ERR_ARG, "unknown strategy %d", strategy);
-  if (wl != -1 || wr != 0)
-    return fail(THDCP_ERR_UNSUPPORTED,
-                "only causal attention without a sliding window, window_size=(-1, 0), is "
-                "supported (got (%d, %d))", wl, wr);
+  if (wl < -1 || wr < -1)
+    return fail(THDCP_ERR_ARG, "window_size (%d, %d): each side must be >= 0 or -1 (no bound)",
+                wl, wr);
   if (T < 0 || T > INT32_MAX / 2) return fail(THDCP_ERR_ARG, "T=%lld out of range", (long long)T);
   if (pad_flag < -1 || pad_flag > 1) return fail(THDCP_ERR_ARG, "pad_between_seqs must be -1, 0 or 1");
   if (cup[0] != 0 || (cu && cu[0] != 0))
@@ -102,6 +101,7 @@ thdcp_status_t check_layout(const int32_t* cu, const int32_t* cup, int32_t B, in
 // ---------------------------------------------------------------------------
 struct thdcp_plan {
   thdcp_attn_desc desc;
+  Band band{kUnbounded, 0, true};  // the mask's key band (causal by default)
   std::vector<int32_t> cu, cup;
   int64_t n_local = 0;
   float scale = 0.f;
@@ -137,6 +137,11 @@ struct thdcp_plan {
 namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Keys a real query at global row g of a document with real rows [a, e)
+// attends: the band [g - wl, g + wr] inside [a, e) (causal: [a, g]).
+int64_t key_lo(const Band& b, int64_t a, int64_t g) { return std::max<int64_t>(a, g - b.wl); }
+int64_t key_hi(const Band& b, int64_t e, int64_t g) { return std::min<int64_t>(e - 1, g + b.wr); }
 
 struct Segment {  // consecutive local rows holding consecutive global rows of one document
   int64_t m0, g0, len;
@@ -202,7 +207,7 @@ struct DocRows {
     int64_t m0, g0, n;
   };
   int32_t doc;
-  int64_t a, gmax, m_hi, split, dga, dgb;
+  int64_t a, e, gmax, m_hi, split, dga, dgb;
   std::vector<Run> runs;
 };
 
@@ -224,6 +229,7 @@ std::vector<DocRows> doc_rows(const std::vector<Segment>& segs) {
       if (nv > 0) dr.runs.push_back({s.m0, s.g0, nv});
     }
     dr.a = segs[si].a;
+    dr.e = segs[si].e;
     si = sj;
     if (dr.runs.empty()) continue;
     const DocRows::Run& last = dr.runs.back();
@@ -238,21 +244,33 @@ std::vector<DocRows> doc_rows(const std::vector<Segment>& segs) {
 }
 
 // Key tiles of kBwdBN keys over [lo, hi) of one document; each lists the
-// contiguous local query range that attends it (rows with g >= k0).
-void add_key_tiles(const DocRows& dr, int64_t lo, int64_t hi, std::vector<BwdTile>& out) {
+// contiguous local query range that can attend it: real rows with
+// g + wr >= k0 and g - wl <= k1 - 1 (causal: the rows with g >= k0). Local
+// rows of a document ascend in g, so that range is contiguous.
+void add_key_tiles(const DocRows& dr, const Band& band, int64_t lo, int64_t hi,
+                   std::vector<BwdTile>& out) {
   for (int64_t k0 = lo; k0 < hi; k0 += kBwdBN) {
-    int64_t m_lo = -1;  // first local row with g >= k0
+    const int64_t k1 = std::min<int64_t>(k0 + kBwdBN, hi);
+    const int64_t gfirst = k0 - band.wr, glast = k1 - 1 + (int64_t)band.wl;
+    int64_t m_lo = -1;  // first local row with g >= gfirst
     for (const DocRows::Run& rn : dr.runs) {
-      if (k0 <= rn.g0 + rn.n - 1) {
-        m_lo = rn.m0 + std::max<int64_t>(0, k0 - rn.g0);
+      if (gfirst <= rn.g0 + rn.n - 1) {
+        m_lo = rn.m0 + std::max<int64_t>(0, gfirst - rn.g0);
+        break;
+      }
+    }
+    int64_t m_hi = m_lo;  // one past the last local row with g <= glast
+    for (auto it = dr.runs.rbegin(); it != dr.runs.rend(); ++it) {
+      if (it->g0 <= glast) {
+        m_hi = it->m0 + std::min<int64_t>(it->n, glast - it->g0 + 1);
         break;
       }
     }
     BwdTile t{};
     t.k0 = (int32_t)k0;
-    t.k1 = (int32_t)std::min<int64_t>(k0 + kBwdBN, hi);
+    t.k1 = (int32_t)k1;
     t.m_lo = (int32_t)m_lo;
-    t.m_hi = (int32_t)dr.m_hi;
+    t.m_hi = (int32_t)m_hi;
     t.m_split = (int32_t)dr.split;
     t.dg_a = (int32_t)dr.dga;
     t.dg_b = (int32_t)dr.dgb;
@@ -318,9 +336,14 @@ void build_plan(thdcp_plan& p) {
     if (s.doc < 0) continue;
     const int64_t nvalid = std::max<int64_t>(0, std::min(s.g0 + s.len, s.e) - s.g0);
     p.local_seqlens[s.doc] += (int32_t)nvalid;
-    // sum over real rows g in [g0, g0+nvalid) of (g - a + 1)
-    const int64_t f = s.g0 - s.a + 1;
-    p.pairs += nvalid * f + nvalid * (nvalid - 1) / 2;
+    if (p.band.causal) {
+      // sum over real rows g in [g0, g0+nvalid) of (g - a + 1)
+      const int64_t f = s.g0 - s.a + 1;
+      p.pairs += nvalid * f + nvalid * (nvalid - 1) / 2;
+    } else {
+      for (int64_t g = s.g0; g < s.g0 + nvalid; ++g)
+        p.pairs += key_hi(p.band, s.e, g) - key_lo(p.band, s.a, g) + 1;
+    }
   }
 
   // Forward tiles, longest first (LPT order over the workgroup queue).
@@ -333,23 +356,37 @@ void build_plan(thdcp_plan& p) {
       t.n = (int32_t)std::min<int64_t>(kFwdBM, s.len - off);
       t.g0 = (int32_t)(s.g0 + off);
       t.e = (int32_t)s.e;
-      const int64_t kend = std::min<int64_t>(t.g0 + t.n, s.e);
-      t.ks0 = (int32_t)s.a;
-      t.ke0 = kend > t.g0 ? (int32_t)kend : (int32_t)s.a;
+      // keys of the tile's real rows [g0, rend): from the first row's band
+      // start to the last row's band end (rows' bands ascend with g)
+      const int64_t rend = std::min<int64_t>(t.g0 + t.n, s.e);
+      t.ks0 = rend > t.g0 ? (int32_t)key_lo(p.band, s.a, t.g0) : (int32_t)s.a;
+      t.ke0 = rend > t.g0 ? (int32_t)(key_hi(p.band, s.e, rend - 1) + 1) : (int32_t)s.a;
       fwd.push_back(t);
       fwd_doc.push_back(s.doc);
     }
   }
   p.fwd = lpt_order(fwd, [](const FwdTile& t) { return fwd_cost(t); });
 
-  // Backward tiles: per document, its local real rows (a prefix of the
-  // document's local rows, ascending in g) attend keys [a, g_max].
+  // Backward tiles: per document, the keys its local real rows attend -- per
+  // run of consecutive rows, from the first row's band start to the last
+  // row's band end (causal: [a, g_max] for the whole document) -- merged.
   const std::vector<DocRows> docs = doc_rows(segs);
   std::vector<BwdTile> bwd;
-  std::vector<std::pair<int64_t, int64_t>> touched;  // [r0, r1) per document
+  std::vector<std::pair<int64_t, int64_t>> touched;  // [r0, r1), ascending, disjoint
   for (const DocRows& dr : docs) {
-    add_key_tiles(dr, dr.a, dr.gmax + 1, bwd);
-    touched.push_back({dr.a, dr.gmax + 1});
+    std::vector<std::pair<int64_t, int64_t>> ivs;
+    for (const DocRows::Run& rn : dr.runs) {
+      const int64_t x0 = key_lo(p.band, dr.a, rn.g0);
+      const int64_t x1 = key_hi(p.band, dr.e, rn.g0 + rn.n - 1) + 1;
+      if (!ivs.empty() && x0 <= ivs.back().second)
+        ivs.back().second = std::max(ivs.back().second, x1);
+      else
+        ivs.push_back({x0, x1});
+    }
+    for (const auto& iv : ivs) {
+      add_key_tiles(dr, p.band, iv.first, iv.second, bwd);
+      touched.push_back(iv);
+    }
   }
   p.bwd = lpt_order(bwd, [](const BwdTile& t) { return (int64_t)t.m_hi - t.m_lo; });
 
@@ -417,7 +454,7 @@ void build_plan(thdcp_plan& p) {
         for (int r = 0; r < nr; ++r) {
           const int64_t x0 = std::max(lo[r], dr.a), x1 = std::min(hi[r], dr.gmax + 1);
           if (x1 <= x0) continue;
-          add_key_tiles(dr, x0, x1, sb);
+          add_key_tiles(dr, p.band, x0, x1, sb);
           st_touched.push_back({x0, x1});
         }
       }
@@ -635,6 +672,10 @@ thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan
     if (d.kv_layout != THDCP_KV_GLOBAL && d.kv_layout != THDCP_KV_RANK_MAJOR)
       return fail(THDCP_ERR_ARG, "kv_layout %d (0 global, 1 rank-major)", d.kv_layout);
     if (d.p2p != 0 && d.p2p != 1) return fail(THDCP_ERR_ARG, "p2p %d (0 or 1)", d.p2p);
+    if (d.p2p && (d.window_left != -1 || d.window_right != 0))
+      return fail(THDCP_ERR_UNSUPPORTED,
+                  "P2P steps take the causal mask only, window_size=(-1, 0) (got (%d, %d))",
+                  d.window_left, d.window_right);
     // Mapped K/V rows are addressed from the start of the buffer.
     if (d.kv_layout == THDCP_KV_RANK_MAJOR && d.T * row_bytes >= ((int64_t)1 << 31))
       return fail(THDCP_ERR_UNSUPPORTED,
@@ -654,6 +695,10 @@ thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan
   p->n_local = n_local;
   p->scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.0f / std::sqrt((float)d.D);
   p->padding = padding;
+  // A side at or past T is no bound (T < 2^30, so kUnbounded covers it).
+  const int32_t wl = (d.window_left < 0 || d.window_left >= d.T) ? kUnbounded : d.window_left;
+  const int32_t wr = (d.window_right < 0 || d.window_right >= d.T) ? kUnbounded : d.window_right;
+  p->band = Band{wl, wr, wl == kUnbounded && wr == 0};
   build_plan(*p);
   *plan_out = p;
   return ok();
@@ -794,7 +839,7 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), o,
+                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, o,
                       lse, p->n_local, p->scale, (hipStream_t)stream),
       "cp_attn_fwd launch");
 }
@@ -858,7 +903,7 @@ thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t p, const void* q, const void* k, co
   if (p->bwd.empty()) return ok();
   return hip_status(
       launch_attn_bwd_dkdv(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
-                           (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p),
+                           (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band,
                            d_o, lse, static_cast<const float*>(scratch), dk, dv, p->n_local,
                            p->scale, accumulate_dkv, nullptr, 0, 0, (hipStream_t)stream),
       "cp_attn_bwd_dkdv launch");
@@ -876,7 +921,7 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), d_o,
+                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o,
                          nullptr, lse, static_cast<float*>(const_cast<void*>(scratch)), dq,
                          p->n_local, p->scale, 0, (hipStream_t)stream),
       "cp_attn_bwd_dq launch");
@@ -926,7 +971,7 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (!p->fwd.empty()) {
     hipError_t e = launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                                       (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v,
-                                      kv_map(p), d_o, o, lse, delta, dq, p->n_local, p->scale, 0,
+                                      kv_map(p), p->band, d_o, o, lse, delta, dq, p->n_local, p->scale, 0,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dq launch");
   }
@@ -934,7 +979,7 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (!p->bwd.empty() || zero) {
     hipError_t e = launch_attn_bwd_dkdv(
         reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd), (int32_t)p->bwd.size(),
-        p->desc.H, p->desc.D, q, k, v, kv_map(p), d_o, lse, delta, dk, dv, p->n_local, p->scale,
+        p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o, lse, delta, dk, dv, p->n_local, p->scale,
         accumulate_dkv, zero ? reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_zero) : nullptr,
         zero ? (int32_t)p->zero.size() : 0, zero ? p->desc.T - p->touched : 0,
         (hipStream_t)stream);
@@ -971,7 +1016,7 @@ thdcp_status_t cp_attn_fwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   if (sp.n_fwd == 0) return ok();
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0,
-                      sp.n_fwd, p->desc.H, p->desc.D, q, k, v, kv_step(p, src), o, lse,
+                      sp.n_fwd, p->desc.H, p->desc.D, q, k, v, kv_step(p, src), p->band, o, lse,
                       p->n_local, p->scale, (hipStream_t)stream),
       "cp_attn_fwd_step launch");
 }
@@ -1009,7 +1054,7 @@ thdcp_status_t cp_attn_bwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   if (sp.n_fwd > 0) {
     hipError_t e = launch_attn_bwd_dq(
         reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0, sp.n_fwd,
-        p->desc.H, p->desc.D, q, k, v, kv, d_o, nullptr, lse, delta, dq, p->n_local, p->scale,
+        p->desc.H, p->desc.D, q, k, v, kv, p->band, d_o, nullptr, lse, delta, dq, p->n_local, p->scale,
         accumulate_dq != 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dq launch");
   }
@@ -1017,7 +1062,7 @@ thdcp_status_t cp_attn_bwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   if (sp.n_bwd > 0 || zero) {
     hipError_t e = launch_attn_bwd_dkdv(
         reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_sbwd) + sp.bwd0, sp.n_bwd, p->desc.H,
-        p->desc.D, q, k, v, kv, d_o, lse, delta, dk, dv, p->n_local, p->scale, 0,
+        p->desc.D, q, k, v, kv, p->band, d_o, lse, delta, dk, dv, p->n_local, p->scale, 0,
         zero ? reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_szero) + sp.zero0 : nullptr,
         zero ? sp.n_zero : 0, zero ? sp.untouched : 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dkdv launch");

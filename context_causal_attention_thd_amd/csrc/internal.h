@@ -70,6 +70,17 @@ hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t 
 // g sits at row (map ? map[g] : g) - sub of k, v (and dk, dv), which hold
 // `rows` rows. map is the rank-major map (null: identity); sub != 0 addresses
 // one rank's local block (a P2P step's source rank).
+// Key band of the attention mask: a real query at global row g attends keys
+// [g - wl, g + wr] of its document's real rows (the plan's tile ranges keep
+// the keys inside the document). kUnbounded stands for "no bound" on a side:
+// with T below 2^30 every g +- kUnbounded stays inside int32. The causal
+// mask is {kUnbounded, 0}; `causal` says so, which lets the dK/dV kernel skip
+// the lower-bound test.
+constexpr int32_t kUnbounded = 1 << 30;
+struct Band {
+  int32_t wl, wr;
+  bool causal;
+};
 struct KvRows {
   const int32_t* map;
   int64_t sub;
@@ -86,13 +97,14 @@ hipError_t launch_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, KvRows kv, void* o,
-                           float* lse, int64_t n_local, float scale, hipStream_t stream);
+                           const void* q, const void* k, const void* v, KvRows kv, Band band,
+                           void* o, float* lse, int64_t n_local, float scale,
+                           hipStream_t stream);
 // zr/n_zr/zero_rows (nullable / 0): also zero the dK/dV rows no local query
 // attends, with extra workgroups at the end of the same launch.
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                                 const void* q, const void* k, const void* v, KvRows kv,
-                                const void* d_o, const float* lse,
+                                Band band, const void* d_o, const float* lse,
                                 const float* delta, float* dk, float* dv, int64_t n_local,
                                 float scale, int32_t accumulate, const ZeroRange* zr,
                                 int32_t n_zr, int64_t zero_rows, hipStream_t stream);
@@ -101,7 +113,8 @@ hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H
 // accumulate: add to dq (P2P steps after the first) instead of writing it.
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                               const void* q, const void* k, const void* v, KvRows kv,
-                              const void* d_o, const void* o, const float* lse, float* delta,
+                              Band band, const void* d_o, const void* o, const float* lse,
+                              float* delta,
                               float* dq, int64_t n_local, float scale, int32_t accumulate,
                               hipStream_t stream);
 

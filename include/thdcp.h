@@ -86,8 +86,9 @@ int32_t thdcp_version(void);
  * Validate THD metadata and detect inter-sequence padding by value.
  * [AG] "Why" / "Scope and constraints": DUAL_CHUNK_SWAP needs every padded
  * length divisible by 2*cp_size and T == cu_seqlens_padded[B];
- * NO_LOAD_BALANCE needs only T divisible by cp_size ([A2A] body);
- * window must be (-1, 0). [PAD] "Expected behavior": padding is present iff
+ * NO_LOAD_BALANCE needs only T divisible by cp_size ([A2A] body); each
+ * window side is >= 0 or -1 (see thdcp_attn_desc). [PAD] "Expected
+ * behavior": padding is present iff
  * some document's actual length is below its padded length or
  * T > cu_seqlens_padded[B] -- decided from the values, never from whether the
  * two arrays are the same object.
@@ -212,8 +213,14 @@ typedef struct {
   int32_t H;                 /* heads of Q, K and V (self-attention, equal) */
   int32_t D;                 /* head dim: 64 or 128 */
   float softmax_scale;       /* <= 0 selects 1/sqrt(D) */
-  int32_t window_left;       /* must be -1 */
-  int32_t window_right;      /* must be 0  */
+  int32_t window_left;       /* key band of a real query at document position  */
+  int32_t window_right;      /* p: real keys at [p - left, p + right]; -1 = no
+                                bound. (-1, 0) causal (the default; every causal
+                                mask type, queries and keys sharing one layout),
+                                (-1, -1) the whole document (padding-only mask),
+                                (w, 0) a causal sliding window ([A2A] body:
+                                after the a2a exchange every mask type and
+                                window size stays valid). P2P plans: (-1, 0). */
   int32_t pad_between_seqs;  /* -1 detect by value, 0 none, 1 present */
   int32_t kv_layout;         /* thdcp_kv_layout_t of K/V in and dK/dV out */
   int32_t p2p;               /* 1: also build the P2P ring step tables
@@ -263,7 +270,8 @@ void thdcp_plan_destroy(thdcp_plan_t plan);
  * Forward ([AG] "Why": DUAL_CHUNK_SWAP's two attention steps and
  * NO_LOAD_BALANCE's one are all query tiles of this single launch; the mask is
  * the cp_size = 1 mask, [A2A] body). Each real local query g attends the keys
- * j of its own document with j <= g:
+ * j of its own document with j <= g (in general: the real keys of its
+ * document inside the plan's window):
  *   O = softmax(scale * q K^T) V,   LSE = log sum exp(scale * q K^T).
  *   q_local  bf16 [n_local, H, D]   local queries in local row order
  *   k, v     bf16 [T, H, D]         full K/V in the plan's kv_layout

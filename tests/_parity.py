@@ -55,7 +55,7 @@ def device():
 
 
 def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
-              accumulate=False, kv_layout="global"):
+              accumulate=False, kv_layout="global", window=(-1, 0)):
     """Product path on cuda:0 for one rank: partition index -> gather local Q
     and dO -> plan -> forward -> backward. Returns numpy arrays. With
     kv_layout="rank_major" K/V are passed in the all-gathered (rank-major)
@@ -74,7 +74,8 @@ def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
     if kv_layout == "rank_major":
         perm = thd.partition_index(cup, cup_dev, w.T, w.cp_size, -1, w.strategy)
         k, v = thd.gather(k, perm), thd.gather(v, perm)
-    plan = thd.Plan(cu, cup, w.T, w.cp_size, rank, w.strategy, w.H, w.D, kv_layout=kv_layout)
+    plan = thd.Plan(cu, cup, w.T, w.cp_size, rank, w.strategy, w.H, w.D, kv_layout=kv_layout,
+                    window=window)
     o, lse = thd.attn_fwd(plan, q_local, k, v)
     dk = None if dk_init is None else dk_init.to(dev).clone()
     dv = None if dv_init is None else dv_init.to(dev).clone()
@@ -91,13 +92,15 @@ def f64(tensors):
     return {n: t.double().numpy() for n, t in tensors.items()}
 
 
-def oracle_share(w, rank, t64, rows=None):
+def oracle_share(w, rank, t64, rows=None, window=(-1, 0)):
     cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
     idx = O.partition_index(cup, w.T, w.cp_size, rank, w.strategy)
     ql = t64["q"][idx]
     dol = t64["do"][idx]
-    o, lse = O.attention_fwd(ql, t64["k"], t64["v"], idx, cu, cup, w.T, rows=rows)
-    dq, dk, dv = O.attention_bwd(ql, t64["k"], t64["v"], dol, idx, cu, cup, w.T, rows=rows)
+    o, lse = O.attention_fwd(ql, t64["k"], t64["v"], idx, cu, cup, w.T, rows=rows,
+                             window=window)
+    dq, dk, dv = O.attention_bwd(ql, t64["k"], t64["v"], dol, idx, cu, cup, w.T, rows=rows,
+                                 window=window)
     return dict(idx=idx, o=o, lse=lse, dq=dq, dk=dk, dv=dv)
 
 

@@ -95,10 +95,57 @@ def test_validate_rejects_bad_layouts(L, args, status):
         O.check_layout(*args)
 
 
-def test_window_other_than_causal_is_unsupported(L):
+def test_window_validation(L):
+    # each side >= 0 or -1 (no bound); anything below -1 is an argument error
+    for win in ((128, 0), (-1, -1), (3, 5), (0, 0), (-1, 7)):
+        thd.validate([0, 8], [0, 8], 8, 2, 0, "no_load_balance", window=win)
+    for win in ((-2, 0), (0, -3)):
+        with pytest.raises(thd.ThdcpError) as ei:
+            thd.validate([0, 8], [0, 8], 8, 2, 0, "no_load_balance", window=win)
+        assert ei.value.status == 1
+    # P2P steps keep the causal mask only
     with pytest.raises(thd.ThdcpError) as ei:
-        thd.validate([0, 8], [0, 8], 8, 2, 0, "no_load_balance", window=(128, 0))
+        thd.Plan([0, 8], [0, 8], 8, 2, 0, "no_load_balance", 1, 64, upload=False, p2p=True,
+                 window=(4, 0))
     assert ei.value.status == 3
+
+
+WINDOWS = [(-1, -1), (5, 0), (3, 2), (0, 4), (-1, 9), (40, -1), (0, 0), (1000, 0)]
+
+
+@pytest.mark.parametrize("strategy", ["dual_chunk_swap", "no_load_balance"])
+def test_plan_window_metadata_matches_oracle(L, strategy):
+    """Allowed pairs and touched key rows of windowed plans against the
+    oracle, on random padded layouts, every rank. The causal default gives
+    the same tiles as before (a window at or past T is no bound)."""
+    rng = np.random.default_rng(17)
+    for trial in range(12):
+        cp = int(rng.integers(1, 5))
+        mult = 2 * cp if strategy == "dual_chunk_swap" else 1
+        n = int(rng.integers(1, 6))
+        lens = rng.integers(0, 120, size=n)
+        pads = ((lens + mult - 1) // mult) * mult + rng.integers(0, 3, size=n) * mult
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        cup = np.concatenate([[0], np.cumsum(pads)]).astype(np.int32)
+        T = int(cup[-1])
+        if strategy == "no_load_balance":
+            T = ((T + int(rng.integers(0, 20)) + cp - 1) // cp) * cp
+        if T == 0:
+            continue
+        for r in range(cp):
+            idx = O.partition_index(cup, T, cp, r, strategy)
+            base = thd.Plan(cu, cup, T, cp, r, strategy, 1, 64, upload=False)
+            for win in WINDOWS:
+                p = thd.Plan(cu, cup, T, cp, r, strategy, 1, 64, upload=False, window=win)
+                assert p.info.causal_pairs == O.causal_pairs(cu, cup, T, idx, window=win), \
+                    (trial, r, win)
+                touched = O.touched_keys(cu, cup, T, idx, window=win)
+                assert p.info.touched_rows == int(touched.sum()), (trial, r, win)
+                if win == (1000, 0) and T <= 1000:
+                    assert (p.info.n_fwd_tiles, p.info.n_bwd_tiles, p.info.n_zero_ranges) == \
+                        (base.info.n_fwd_tiles, base.info.n_bwd_tiles, base.info.n_zero_ranges)
+                p.close()
+            base.close()
 
 
 def _plan(w, rank=None, **kw):
