@@ -49,6 +49,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="dcs_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, nargs=2, default=(-1, 0), metavar=("LEFT", "RIGHT"),
+                    help="attention window of the timed step: real keys at document "
+                         "positions [p-LEFT, p+RIGHT], -1 unbounded; (-1, 0) causal")
+    ap.add_argument("--no-masks", action="store_true",
+                    help="skip the mask-variant measurement on the flat share")
     ap.add_argument("--no-p2p", action="store_true",
                     help="skip the P2P (ring) step measurement")
     ap.add_argument("--no-a2a", action="store_true",
@@ -112,7 +117,9 @@ def main():
     dq = torch.empty((n_local, H, D), dtype=torch.float32, device=dev)
     dk_rm = torch.empty((T, H, D), dtype=torch.float32, device=dev)   # rank-major partials
     dv_rm = torch.empty_like(dk_rm)
-    probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major")
+    window = tuple(args.window)
+    probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
+                     window=window)
     ws = torch.empty(int(probe.info.workspace_bytes) + 4096, dtype=torch.uint8, device=dev)
     scratch = torch.empty(int(probe.info.bwd_scratch_bytes) + 256, dtype=torch.uint8, device=dev)
     pairs = int(probe.info.causal_pairs)
@@ -120,7 +127,7 @@ def main():
 
     def step():
         plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
-                        kv_layout="rank_major")
+                        kv_layout="rank_major", window=window)
         plan.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
@@ -150,7 +157,8 @@ def main():
     # Per-kernel durations, live on the same stream and inputs: events around
     # REPS back-to-back launches of one kernel, so the events' own cost is
     # amortized. Each launch recomputes the same outputs.
-    plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major")
+    plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
+                    window=window)
     plan.upload_into(ws, stream)
     reps = max(5, min(50, int(20.0 / max(ms_step, 1e-3))))
 
@@ -216,6 +224,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "heads": H, "head_dim": D, "cp_size": cp,
+                   "window": list(window),
                    "rank": r, "strategy": w.strategy, "docs": w.B, "causal_pairs_per_head": pairs,
                    "parallelism": "one simulated CP rank on one GPU"},
         "roofline": {"bound": "mfma", "kernel": "attn_bwd_dkdv_kernel",
@@ -243,7 +252,9 @@ def main():
                      "host_wall_per_step": round(wall / args.steps * 1e3, 4),
                      "kernel_reps": reps},
     }
-    if cp > 1 and not args.no_p2p:
+    if not args.no_masks:
+        result["mask_variants"] = mask_variants(stream, args.warmup)
+    if cp > 1 and not args.no_p2p and window == (-1, 0):
         result["p2p_ring"] = p2p_ring(w, q, k, v, do, cup_dev, stream, args.warmup, args.steps,
                                       reps, flop_fwd + flop_bwd, ms_step)
     if not args.no_a2a:
@@ -354,6 +365,66 @@ def p2p_ring(w, q, k, v, do, cup_dev, stream, warmup, steps, reps, flops, ms_all
                          "bwd_preprocess_and_steps": round(t_bwd, 4)},
             "note": "per-rank compute of the ring on one GPU; peer K/V resident, "
                     "transfers not included"}
+
+
+def mask_variants(stream, warmup, windows=((-1, 0), (-1, -1), (4096, 0), (512, 512))):
+    """The flat post-a2a share (one 75600-token sequence, 5 heads x 128: cp_size
+    1 math) under masks other than causal. Per window: the pairs the mask
+    allows, the forward and backward (dQ + dK/dV) times from back-to-back
+    launches on the same inputs, and the algorithmic TFLOP/s (4 and 10 FLOP per
+    pair and head dim)."""
+    import torch
+    import context_causal_attention_thd_amd as thd
+    import workloads as W
+    w = W.WORKLOADS["flat_75k"]
+    dev = torch.device("cuda", 0)
+    t = W.bf16_tensors(w)
+    q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    T, H, D = w.T, w.H, w.D
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    out = {"workload": "flat_75k", "note": "forward / backward kernels of one share, "
+           "back-to-back launches; backward = dQ (with delta) + dK/dV"}
+    for win in windows:
+        plan = thd.Plan(cu, cup, T, 1, 0, w.strategy, H, D, window=win)
+        scratch = torch.empty(int(plan.info.bwd_scratch_bytes) + 256, dtype=torch.uint8,
+                              device=dev)
+        pairs = int(plan.info.causal_pairs)
+
+        def fwd():
+            thd.attn_fwd(plan, q, k, v, o=o, lse=lse)
+
+        def bwd():
+            thd.attn_bwd(plan, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, scratch=scratch)
+
+        for _ in range(max(2, warmup // 10)):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        times = []
+        for fn in (fwd, bwd):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            reps = 5
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / reps)
+        tf = 4.0 * D * H * pairs / (times[0] * 1e-3) / 1e12
+        tb = 10.0 * D * H * pairs / (times[1] * 1e-3) / 1e12
+        out[f"w{win[0]}_{win[1]}"] = {
+            "window": list(win), "pairs_per_head": pairs, "fwd_ms": round(times[0], 4),
+            "bwd_ms": round(times[1], 4), "fwd_tflops": round(tf, 2), "bwd_tflops": round(tb, 2),
+            "fwd_bwd_tflops": round(14.0 * D * H * pairs / ((times[0] + times[1]) * 1e-3) / 1e12,
+                                    2)}
+        plan.close()
+    return out
 
 
 def a2a_layout(stream, seqlens=(8192, 32768, 75600), cp=8, heads=40, head_dim=128):

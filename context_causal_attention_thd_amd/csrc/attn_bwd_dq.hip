@@ -43,12 +43,14 @@ struct DqSmem {
 // DELTA: compute delta = rowsum(dO * O) for the tile's rows here (from the
 // dO fragments already loaded and the matching O fragments) and write it for
 // the dK/dV kernel, instead of reading it from a separate preprocess launch.
-template <int D, bool MAPPED, bool DELTA>
+// BAND: a general key band [g - wl, g + wr]; otherwise the causal mask
+// (wl unbounded, wr = 0, folded at compile time).
+template <int D, bool MAPPED, bool DELTA, bool BAND>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                    const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
-                   int32_t wl, int32_t wr, const bf16* __restrict__ d_o,
+                   int32_t wl_arg, int32_t wr_arg, const bf16* __restrict__ d_o,
                    const bf16* __restrict__ o,
                    const float* __restrict__ lse, float* __restrict__ delta,
                    float* __restrict__ dq, int64_t n_local, int32_t accumulate,
@@ -80,6 +82,8 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   const int64_t m = (int64_t)t.m0 + r;
   // Key j is allowed iff my_lo <= j <= my_hi (and below the tile range's
   // end); padding rows allow nothing.
+  const int wl = BAND ? wl_arg : kUnbounded;
+  const int wr = BAND ? wr_arg : 0;
   const int my_lo = g - wl;
   const int my_hi = valid ? g + wr : -1;
 
@@ -216,7 +220,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
 
-    if (k0 <= wave_kmax && k0 + BN - 1 >= wave_kmin) {
+    if (k0 <= wave_kmax && (!BAND || k0 + BN - 1 >= wave_kmin)) {
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -234,13 +238,14 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
         }
       }
       const bool diag = !wave_all_valid || k0 + BN - 1 > wave_gmin + wr ||
-                        k0 < wave_gmax - wl || k0 + BN > kend;
+                        (BAND && k0 < wave_gmax - wl) || k0 + BN > kend;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          const bool ok = !diag || (key <= my_hi && key >= my_lo && key < kend);
+          const bool ok =
+              !diag || (key <= my_hi && (!BAND || key >= my_lo) && key < kend);
           const float p = ok ? fast_exp2(fmaf(s[kb][i], scale_log2, -lse2)) : 0.f;
           dp[kb][i] = ok ? p * (dp[kb][i] - dlt) : 0.f;
         }
@@ -294,14 +299,19 @@ void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int3
                   int32_t kv_sub, uint32_t kvb, Band band, const bf16* d_o, const bf16* o,
                   const float* lse, float* delta, float* dq, int64_t n_local, float scale,
                   int32_t accumulate) {
-  if (o)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, true>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,
-                       o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e);
+#define THDCP_DQ(DL, BB)                                                                      \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, DL, BB>), dim3((unsigned)blocks), dim3(kThreads), \
+                     0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,  \
+                     o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e)
+  if (o && band.causal)
+    THDCP_DQ(true, false);
+  else if (o)
+    THDCP_DQ(true, true);
+  else if (band.causal)
+    THDCP_DQ(false, false);
   else
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, false>), dim3((unsigned)blocks), dim3(kThreads),
-                       0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,
-                       o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e);
+    THDCP_DQ(false, true);
+#undef THDCP_DQ
 }
 
 }  // namespace

@@ -63,12 +63,14 @@ constexpr int kFwdThreads = kFwdBM / (16 * QB) * 64;
 // K/V row of key j: j - kv_sub (global order, or one rank's block of it
 // under NO_LOAD_BALANCE), or, when MAPPED, kv_row[j] - kv_sub (rank-major
 // K/V, or one rank's block of it: the restore fused into the loads).
-template <int D, int QB, bool MAPPED>
+// BAND: a general key band [g - wl, g + wr]; otherwise the causal mask
+// (wl unbounded, wr = 0, folded at compile time).
+template <int D, int QB, bool MAPPED, bool BAND>
 __global__ void __launch_bounds__(kFwdThreads<QB>, 2)
 attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                 const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
-                int32_t wl, int32_t wr, bf16* __restrict__ o, float* __restrict__ lse,
+                int32_t wl_arg, int32_t wr_arg, bf16* __restrict__ o, float* __restrict__ lse,
                 int64_t n_local, float scale_log2) {
   constexpr int kThreads = kFwdThreads<QB>;
   constexpr int BN = kFwdBN;
@@ -90,6 +92,8 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int G = lane >> 4;    // 16-lane group
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = (int64_t)h * D;
+  const int wl = BAND ? wl_arg : kUnbounded;
+  const int wr = BAND ? wr_arg : 0;
 
   // Query rows of this lane: block qb holds tile row (w*QB + qb)*16 + l16.
   // Key j is allowed iff my_lo <= j <= my_hi (and j is below the tile range's
@@ -206,7 +210,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + kb * 16 + G * 4 + i;
-          if (key > my_hi[qb] || key < my_lo[qb] || key >= kend) s[qb][kb][i] = -INFINITY;
+          bool out = key > my_hi[qb] || key >= kend;
+          if constexpr (BAND) out = out || key < my_lo[qb];
+          if (out) s[qb][kb][i] = -INFINITY;
         }
   };
   // Lazy rescale: the running max of a query moves only when some score of
@@ -321,10 +327,10 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       load_rows(v, tile_k0(it + 1), tile_kend(it + 1), pos, vreg);
       if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
-    if (k0 <= wave_kmax && k0 + BN - 1 >= wave_kmin) {
+    if (k0 <= wave_kmax && (!BAND || k0 + BN - 1 >= wave_kmin)) {
       f32x4 s[QB][KB];
       scores(cur, s);
-      if (!wave_all_valid || k0 + BN - 1 > wave_gmin + wr || k0 < wave_gmax - wl ||
+      if (!wave_all_valid || k0 + BN - 1 > wave_gmin + wr || (BAND && k0 < wave_gmax - wl) ||
           k0 + BN > kend)
         mask(k0, kend, s);
       softmax_max(s);
@@ -369,14 +375,19 @@ hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const b
                         const bf16* k, const bf16* v, const int32_t* kv_row, int32_t kv_sub,
                         uint32_t kv_bytes, Band band, bf16* o, float* lse, int64_t n_local,
                         float scale_log2, hipStream_t stream) {
-  if (kv_row)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, true>), dim3((unsigned)blocks),
-                       dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub,
-                       kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2);
+#define THDCP_FWD(MM, BB)                                                                  \
+  hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, MM, BB>), dim3((unsigned)blocks),           \
+                     dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub, \
+                     kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2)
+  if (kv_row && band.causal)
+    THDCP_FWD(true, false);
+  else if (kv_row)
+    THDCP_FWD(true, true);
+  else if (band.causal)
+    THDCP_FWD(false, false);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, false>), dim3((unsigned)blocks),
-                       dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub,
-                       kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2);
+    THDCP_FWD(false, true);
+#undef THDCP_FWD
   return hipGetLastError();
 }
 
