@@ -554,6 +554,51 @@ def attention_bwd_keys(q_local, k, v, do_local, idx, cu_seqlens, cu_seqlens_padd
     return dq, dk, dv
 
 
+def sequence_shard(S: int, cp_size: int, rank: int, strategy: str) -> np.ndarray:
+    """Positions of one sequence of S tokens that ``rank`` holds: chunks r and
+    2*cp_size-1-r of 2*cp_size under DUAL_CHUNK_SWAP ([AG] "Why"), the range
+    [r*S/cp_size, (r+1)*S/cp_size) under NO_LOAD_BALANCE ([A2A] body)."""
+    if strategy == DUAL_CHUNK_SWAP:
+        if S % (2 * cp_size):
+            raise ValueError("DUAL_CHUNK_SWAP needs S divisible by 2*cp_size")
+        c = S // (2 * cp_size)
+        return np.concatenate([np.arange(rank * c, (rank + 1) * c),
+                               np.arange((2 * cp_size - 1 - rank) * c,
+                                         (2 * cp_size - rank) * c)]).astype(np.int64)
+    if S % cp_size:
+        raise ValueError("NO_LOAD_BALANCE needs S divisible by cp_size")
+    s = S // cp_size
+    return np.arange(rank * s, (rank + 1) * s, dtype=np.int64)
+
+
+def dense_rank_share(q, k, v, do, layout: str, cp_size: int, rank: int, strategy: str,
+                     window=CAUSAL, scale: Optional[float] = None):
+    """One rank's share of attention over a dense batch, bshd [B, S, H, D] or
+    sbhd [S, B, H, D] ([A2A] body: flat a2a is tested over bshd, sbhd and
+    THD). Every batch element is its own sequence of S tokens, sharded along S
+    by ``sequence_shard`` and attended with ``window`` as one document.
+    Returns (pos, O [B, n, H, D], LSE [B, H, n], dQ [B, n, H, D],
+    dK [B, S, H, D], dV [B, S, H, D]) with pos the rank's positions (n of
+    them), batch-major whatever the input layout."""
+    def bsd(x):
+        x = np.asarray(x, dtype=np.float64)
+        return x if layout == "bshd" else x.transpose(1, 0, 2, 3)
+    if layout not in ("bshd", "sbhd"):
+        raise ValueError(layout)
+    q, k, v, do = bsd(q), bsd(k), bsd(v), bsd(do)
+    B, S = q.shape[:2]
+    pos = sequence_shard(S, cp_size, rank, strategy)
+    cu = [0, S]
+    outs = [], [], [], [], []
+    for b in range(B):
+        o, lse = attention_fwd(q[b][pos], k[b], v[b], pos, cu, cu, S, scale, window=window)
+        dq, dk, dv = attention_bwd(q[b][pos], k[b], v[b], do[b][pos], pos, cu, cu, S, scale,
+                                   window=window)
+        for lst, x in zip(outs, (o, lse, dq, dk, dv)):
+            lst.append(x)
+    return (pos,) + tuple(np.stack(x) for x in outs)
+
+
 def rank_share(q, k, v, do, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int,
                rank: int, strategy: str, scale: Optional[float] = None, window=CAUSAL):
     """Everything one rank computes, from global-order inputs: idx, O, LSE,
