@@ -511,6 +511,50 @@ def bwd_preprocess(plan: Plan, o, lse, d_o, scratch, stream=None):
 
 
 # ---------------------------------------------------------------------------
+# Dense layouts as THD views (no copies)
+# ---------------------------------------------------------------------------
+# Attention is independent per (batch element, head), so a dense tensor is a
+# THD buffer under a reshape: bshd [B, S, H, D] is B documents of S tokens
+# with H heads; sbhd [S, B, H, D] is one document of S tokens with B*H heads
+# (the row of position s holds every batch element's heads). CP shards the
+# sequence dimension of every batch element: for sbhd under either strategy,
+# and for bshd under DUAL_CHUNK_SWAP, that is the THD partition of the view.
+# bshd with B > 1 under NO_LOAD_BALANCE is not (the THD partition would cut
+# the packed B*S rows instead of each sequence) and is refused.
+
+def dense_as_thd(layout: str, B: int, S: int, H: int):
+    """(cu_seqlens int32 [docs+1], heads) of the THD view of a dense layout."""
+    if layout == "bshd":
+        return np.arange(0, (B + 1) * S, S, dtype=np.int32)[:B + 1], int(H)
+    if layout == "sbhd":
+        return np.array([0, S], dtype=np.int32), int(B) * int(H)
+    raise ValueError(f"unknown dense layout {layout!r} (bshd or sbhd)")
+
+
+def dense_view(x, layout: str):
+    """[rows, heads, D] view of a contiguous bshd or sbhd tensor."""
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("expected a contiguous 4-D tensor")
+    a, b, h, d = x.shape
+    if layout == "bshd":
+        return x.view(a * b, h, d)
+    if layout == "sbhd":
+        return x.view(a, b * h, d)
+    raise ValueError(f"unknown dense layout {layout!r} (bshd or sbhd)")
+
+
+def dense_plan(layout: str, B: int, S: int, H: int, D: int, cp_size: int, rank: int, strategy,
+               **kw) -> "Plan":
+    """Plan for one rank of a dense bshd/sbhd batch (its THD view)."""
+    cu, heads = dense_as_thd(layout, B, S, H)
+    if layout == "bshd" and B > 1 and _strategy(strategy) == 1:
+        raise ValueError("bshd with batch > 1 under NO_LOAD_BALANCE shards each sequence, "
+                         "which its THD view does not: pass the batch as sbhd")
+    T = int(cu[-1])
+    return Plan(cu, cu, T, cp_size, rank, strategy, heads, D, **kw)
+
+
+# ---------------------------------------------------------------------------
 # P2P (ring) steps: the plan must be made with p2p=True
 # ---------------------------------------------------------------------------
 

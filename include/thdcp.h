@@ -192,6 +192,24 @@ thdcp_status_t thd_a2a_unpack(int32_t n_tensors, const void* const* src_list, in
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * Dense layouts ([A2A] body: flat a2a is tested over bshd, sbhd and THD).
+ * Attention is independent per (batch element, head), so a dense batch is
+ * passed as a THD view of the same memory, with no copy:
+ *   bshd [B, S, H, D]: B documents of S tokens (cu_seqlens = cu_seqlens_padded
+ *                      = {0, S, 2S, ...}), H heads;
+ *   sbhd [S, B, H, D]: one document of S tokens (cu_seqlens = {0, S}), B*H
+ *                      heads -- the row of position s holds every batch
+ *                      element's heads.
+ * CP shards the sequence of every batch element. For sbhd under either
+ * strategy, and for bshd under DUAL_CHUNK_SWAP (or B = 1), that is exactly
+ * the THD partition of the view. bshd with B > 1 under NO_LOAD_BALANCE is
+ * not (the THD partition would cut the packed B*S rows): pass it as sbhd.
+ * The a2a pack/unpack around an sbhd batch takes the [S*B, H, D] row view
+ * (heads split per batch element; dual chunks of that one-document view are
+ * whole sequence positions).
+ * ---------------------------------------------------------------------- */
+
+/* ------------------------------------------------------------------------
  * Rank plan: the THD metadata of one rank ([AG] sequence diagram "partition
  * and build THD metadata"), built once per batch on the host and shared by
  * forward and backward so both use the same token layout ([AG] "What changed":

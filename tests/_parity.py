@@ -130,3 +130,47 @@ def sample_plan(w, rank, rng, n_rows=96, max_attending=400):
                 keys.append(j)
                 rows |= set(attending.tolist())
     return sorted(rows), sorted(set(keys))
+
+
+def exchange(send):
+    """The all-to-all itself (communication, simulated with device copies):
+    rank r receives block r of every rank's send buffer, rank-major."""
+    import torch
+    cp = len(send)
+    return [torch.cat([send[c][r] for c in range(cp)], dim=0) for r in range(cp)]
+
+
+def a2a_round_trip(cup, T, cp, H, strategy, tensors):
+    """Forward exchange of every rank, checked against the global head
+    slices, then the return exchange, checked against the local shards."""
+    import torch
+    import context_causal_attention_thd_amd as thd
+    dev = device()
+    cup_dev = torch.from_numpy(np.asarray(cup, dtype=np.int32)).to(dev)
+    perm = thd.partition_index(np.asarray(cup, dtype=np.int32), cup_dev, T, cp, -1, strategy)
+    s_local, hl = T // cp, H // cp
+    shards = [thd.gather_many(tensors, perm[r * s_local:(r + 1) * s_local]) for r in range(cp)]
+    send = [thd.a2a_pack(sh, cp) for sh in shards]           # per rank: list over tensors
+    full = []
+    for i in range(len(tensors)):
+        recv = exchange([send[r][i] for r in range(cp)])     # [T, hl, D], rank-major
+        if strategy == "dual_chunk_swap":
+            glob = [torch.empty_like(x) for x in recv]
+            for r in range(cp):
+                thd.scatter(recv[r], perm, glob[r])
+            recv = glob
+        full.append(recv)
+    for i, x in enumerate(tensors):
+        for r in range(cp):
+            assert torch.equal(full[i][r], x[:, r * hl:(r + 1) * hl]), (i, r)
+    # return exchange of the (unchanged) full-sequence head slices
+    for i, x in enumerate(tensors):
+        outs = full[i]
+        if strategy == "dual_chunk_swap":
+            outs = [thd.gather(o, perm) for o in outs]        # global -> rank-major
+        send_back = [[o[c * s_local:(c + 1) * s_local] for c in range(cp)] for o in outs]
+        recv = [torch.stack([send_back[c][r] for c in range(cp)]) for r in range(cp)]
+        for r in range(cp):
+            (local,) = thd.a2a_unpack([recv[r]])
+            assert torch.equal(local, shards[r][i]), (i, r)
+    return full

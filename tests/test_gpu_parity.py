@@ -14,8 +14,8 @@ import pytest
 
 import oracle as O
 import workloads as W
-from _parity import (assert_close, assert_lse, err, f64, oracle_share, run_share,
-                     sample_plan, device)
+from _parity import (a2a_round_trip, assert_close, assert_lse, err, f64, oracle_share,
+                     run_share, sample_plan, device)
 
 pytestmark = pytest.mark.gpu
 
@@ -182,53 +182,12 @@ def test_a2a_pack_unpack_byte_exact(n, cp, hl, tail, dtype, n_tensors):
         assert np.array_equal(bits(b.cpu()), bits(x))
 
 
-def _exchange(send):
-    """The all-to-all itself (communication, simulated with device copies):
-    rank r receives block r of every rank's send buffer, rank-major."""
-    cp = len(send)
-    return [torch.cat([send[c][r] for c in range(cp)], dim=0) for r in range(cp)]
-
-
-def _a2a_round_trip(cup, T, cp, H, strategy, tensors):
-    """Forward exchange of every rank, checked against the global head
-    slices, then the return exchange, checked against the local shards."""
-    dev = device()
-    cup_dev = torch.from_numpy(np.asarray(cup, dtype=np.int32)).to(dev)
-    perm = thd.partition_index(np.asarray(cup, dtype=np.int32), cup_dev, T, cp, -1, strategy)
-    s_local, hl = T // cp, H // cp
-    shards = [thd.gather_many(tensors, perm[r * s_local:(r + 1) * s_local]) for r in range(cp)]
-    send = [thd.a2a_pack(sh, cp) for sh in shards]           # per rank: list over tensors
-    full = []
-    for i in range(len(tensors)):
-        recv = _exchange([send[r][i] for r in range(cp)])     # [T, hl, D], rank-major
-        if strategy == "dual_chunk_swap":
-            glob = [torch.empty_like(x) for x in recv]
-            for r in range(cp):
-                thd.scatter(recv[r], perm, glob[r])
-            recv = glob
-        full.append(recv)
-    for i, x in enumerate(tensors):
-        for r in range(cp):
-            assert torch.equal(full[i][r], x[:, r * hl:(r + 1) * hl]), (i, r)
-    # return exchange of the (unchanged) full-sequence head slices
-    for i, x in enumerate(tensors):
-        outs = full[i]
-        if strategy == "dual_chunk_swap":
-            outs = [thd.gather(o, perm) for o in outs]        # global -> rank-major
-        send_back = [[o[c * s_local:(c + 1) * s_local] for c in range(cp)] for o in outs]
-        recv = [torch.stack([send_back[c][r] for c in range(cp)]) for r in range(cp)]
-        for r in range(cp):
-            (local,) = thd.a2a_unpack([recv[r]])
-            assert torch.equal(local, shards[r][i]), (i, r)
-    return full
-
-
 @pytest.mark.parametrize("strategy", ["dual_chunk_swap", "no_load_balance"])
 def test_a2a_exchange_small_vs_oracle(strategy):
     cup, T, cp, H, D = [0, 48, 176, 192, 320], 320, 4, 8, 64
     _say("a2a exchange small", strategy)
     x = torch.randn((T, H, D), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
-    full = _a2a_round_trip(cup, T, cp, H, strategy, [x.to(device())])
+    full = a2a_round_trip(cup, T, cp, H, strategy, [x.to(device())])
     shards = [x.view(torch.int16).numpy()[O.partition_index(cup, T, cp, r, strategy)]
               for r in range(cp)]
     exp = O.a2a_before_attn(shards, cup, T, cp, strategy)
@@ -245,7 +204,7 @@ def test_a2a_exchange_bshd_full_size(s, strategy):
     g = torch.Generator(device=device()).manual_seed(s)
     qkv = [torch.randn((s, 40, 128), generator=g, device=device()).to(torch.bfloat16)
            for _ in range(3)]
-    _a2a_round_trip([0, s], s, 8, 40, strategy, qkv)
+    a2a_round_trip([0, s], s, 8, 40, strategy, qkv)
 
 
 # ---------------------------------------------------------------- attention, element by element

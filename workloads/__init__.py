@@ -147,3 +147,18 @@ def bf16_tensors(w: Workload, names=("q", "k", "v", "do"), seed_offset: int = 0)
     import torch
     return {n: torch.from_numpy(normal_f32(w, n, seed_offset)).to(torch.bfloat16)
             for n in names}
+
+
+def dense_bf16(layout: str, B: int, S: int, H: int, D: int, seed: int,
+               names=("q", "k", "v", "do")):
+    """Dict of torch.bfloat16 CPU tensors of a dense batch, bshd [B, S, H, D]
+    or sbhd [S, B, H, D]: i.i.d. N(0,1) float32 from numpy's default_rng(seed
+    + tensor id), rounded to bf16."""
+    import torch
+    shape = (B, S, H, D) if layout == "bshd" else (S, B, H, D)
+    out = {}
+    for n in names:
+        rng = np.random.default_rng(seed + TENSOR_IDS[n])
+        out[n] = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(
+            torch.bfloat16)
+    return out
