@@ -8,20 +8,23 @@ A step is one pass of the whole hot path for the measured rank over one batch:
     (rank-major): the restore to global order is fused into the kernels'
     K/V loads through the plan's row map,
   attention backward in two launches: dQ (which also computes the
-    preprocess term delta = rowsum(dO * O)), then dK/dV (whose grid ends with
-    the gated zeroing of untouched rows); the dK/dV stores go straight to
-    rank-major order for the reduce-scatter (the unrestore fused the same way).
+    preprocess term delta = rowsum(dO * O), and whose grid ends with the
+    gated zeroing of untouched dK/dV rows), then dK/dV; the dK/dV stores go
+    straight to rank-major order for the reduce-scatter (the unrestore fused
+    the same way).
 Inputs are synthetic and already resident in HBM when timing starts. The
 standalone K+V restore (one batched gather launch over all T rows) is timed
 separately for the gather roofline.
 
-value = 14 * D * H * causal_pairs / step time (TFLOP/s; causal-masked FLOPs
-only), the steps timed with no events inside. The roofline object is for the
-dominant kernel, the backward dK/dV kernel (8 * D * H * pairs algorithmic
-FLOPs: S, dP, dV, dK); its duration is measured live with HIP events on the
-stream it runs on, around back-to-back launches on the same inputs right after
-the timed steps. The dQ kernel, the forward and the K/V restore (gather
-roofline) are reported beside it.
+value = 14 * D * H * causal_pairs / step time (TFLOP/s; masked-in FLOPs only),
+the steps timed with no events inside. A second pass puts an event pair around
+each step (mean / median / p90 of the step). A third pass runs the same steps
+with the backward as its separate launches (preprocess, dK/dV, dQ, gated
+zeroing) and an event pair around each attention kernel: those in-step
+durations give the roofline object of the dominant kernel, the backward dK/dV
+kernel (8 * D * H * pairs algorithmic FLOPs: S, dP, dV, dK), and the dQ and
+forward figures beside it. The standalone K+V restore (the gather roofline,
+warm and cold) and the plan upload are timed apart, after the steps.
 
     python bench.py [--steps K] [--warmup W] [--workload dcs_8k] [--no-cpu-baseline]
 """
@@ -123,6 +126,7 @@ def main():
     ws = torch.empty(int(probe.info.workspace_bytes) + 4096, dtype=torch.uint8, device=dev)
     scratch = torch.empty(int(probe.info.bwd_scratch_bytes) + 256, dtype=torch.uint8, device=dev)
     pairs = int(probe.info.causal_pairs)
+    probe_touched = int(probe.info.touched_rows)
     probe.close()
 
     def step():
@@ -154,9 +158,27 @@ def main():
     plans.clear()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    # Per-kernel durations, live on the same stream and inputs: events around
-    # REPS back-to-back launches of one kernel, so the events' own cost is
-    # amortized. Each launch recomputes the same outputs.
+    # Spread of the step time: a second pass with an event pair around each
+    # step (the events add a little queue time, so value stays the bare mean).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        plans.append(step())
+        b.record(stream)
+    torch.cuda.synchronize()
+    plans.clear()
+    per_step = sorted(a.elapsed_time(b) for a, b in evs)
+    # Host cost of the plan (validate, tiles, queues) and its upload, apart.
+    t0 = time.perf_counter()
+    for _ in range(20):
+        pl = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
+                      window=window)
+        pl.close()
+    plan_host_us = (time.perf_counter() - t0) / 20 * 1e6
+
+    # The standalone K/V restore and the plan upload: events around REPS
+    # back-to-back launches, so the events' own cost is amortized.
     plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
                     window=window)
     plan.upload_into(ws, stream)
@@ -173,17 +195,64 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    L = thd.lib()
-    pargs = (thd._dev_ptr(q_local, "q"), thd._dev_ptr(k_rm, "k"), thd._dev_ptr(v_rm, "v"),
-             thd._dev_ptr(lse, "lse"), thd._dev_ptr(do_local, "do"))
-    sp, sn, st = thd._dev_ptr(scratch, "scratch"), scratch.numel(), thd._stream(stream)
     t_restore = timed(lambda: thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g]))
-    t_fwd = timed(lambda: thd.attn_fwd(plan, q_local, k_rm, v_rm, o=o, lse=lse))
-    t_dkdv = timed(lambda: thd._check(L.cp_attn_bwd_dkdv(
-        plan.handle, *pargs, thd._dev_ptr(dk_rm, "dk"), thd._dev_ptr(dv_rm, "dv"), 0, sp, sn,
-        st)))
-    t_dq = timed(lambda: thd._check(L.cp_attn_bwd_dq(
-        plan.handle, *pargs, thd._dev_ptr(dq, "dq"), sp, sn, st)))
+    t_upload = timed(lambda: plan.upload_into(ws, stream))
+    # The same restore cold: rotate buffer sets (K, V in and out) totalling
+    # more than twice the 256 MB last-level cache, so no launch finds its
+    # rows cached by the one before.
+    set_bytes = 4 * k.numel() * k.element_size()
+    n_sets = max(3, -(-(600 << 20) // set_bytes))
+    sets = [[torch.empty_like(k_rm) for _ in range(4)] for _ in range(n_sets - 1)]
+    sets.insert(0, [k_rm, v_rm, k_g, v_g])
+    for st_ in sets[1:]:
+        st_[0].copy_(k_rm)
+        st_[1].copy_(v_rm)
+    torch.cuda.synchronize()
+    ec0 = torch.cuda.Event(enable_timing=True)
+    ec1 = torch.cuda.Event(enable_timing=True)
+    cold_reps = 3 * n_sets
+    ec0.record(stream)
+    for i in range(cold_reps):
+        a_, b_, c_, d_ = sets[i % n_sets]
+        thd.scatter_many([a_, b_], perm, [c_, d_])
+    ec1.record(stream)
+    torch.cuda.synchronize()
+    t_restore_cold = ec0.elapsed_time(ec1) / cold_reps
+    del sets
+    # Per-kernel durations inside steps: the same steps with the backward as
+    # its separate launches (preprocess, dK/dV, dQ, gated zeroing -- the same
+    # dK/dV kernel and tiles as the composite call, without the zeroing
+    # workgroups at the end of its grid) and an event pair around each
+    # attention kernel. Each kernel runs on the cache state a step leaves,
+    # not on that of its own previous launch.
+    kev = {n: [] for n in ("fwd", "dkdv", "dq")}
+
+    def step_evented():
+        pl = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
+                      kv_layout="rank_major", window=window)
+        pl.upload_into(ws, stream)
+        thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
+        mine = perm[r * n_local:(r + 1) * n_local]
+        thd.gather_many([q, do], mine, [q_local, do_local])
+        ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for n in kev}
+        ev["fwd"][0].record(stream)
+        thd.attn_fwd(pl, q_local, k_rm, v_rm, o=o, lse=lse)
+        ev["fwd"][1].record(stream)
+        thd.attn_bwd_parts(pl, q_local, k_rm, v_rm, o, lse, do_local, dq, dk_rm, dv_rm, scratch,
+                           zero_untouched=True, stream=stream, events=ev)
+        for n in kev:
+            kev[n].append(ev[n])
+        return pl
+
+    for _ in range(args.steps):
+        plans.append(step_evented())
+    torch.cuda.synchronize()
+    plans.clear()
+    kms = {n: sorted(a.elapsed_time(b) for a, b in kev[n]) for n in kev}
+    t_fwd = sum(kms["fwd"]) / len(kms["fwd"])
+    t_dkdv = sum(kms["dkdv"]) / len(kms["dkdv"])
+    t_dq = sum(kms["dq"]) / len(kms["dq"])
     t_bwd = t_dkdv + t_dq
 
     flop_fwd = 4.0 * D * H * pairs      # QK^T, PV
@@ -198,6 +267,16 @@ def main():
     row_bytes = H * D * 2
     restore_bytes = 2 * (2 * T * row_bytes + 4 * T)    # K and V: read + write rows, read idx
     gbs_restore = restore_bytes / (t_restore * 1e-3) / 1e9
+    gbs_restore_cold = restore_bytes / (t_restore_cold * 1e-3) / 1e9
+    # Algorithmic HBM bytes of the step (each tensor once): local Q, O, dO
+    # (bf16) and dQ (fp32); K, V (bf16) and dK, dV (fp32) of the touched key
+    # rows, plus zeros written to the untouched ones; LSE and delta (fp32);
+    # the gather of local Q and dO (read + write).
+    touched = int(probe_touched)
+    step_bytes = (3 * n_local * row_bytes + n_local * row_bytes * 2
+                  + 2 * touched * row_bytes + 2 * touched * row_bytes * 2
+                  + 2 * (T - touched) * row_bytes * 2 + 2 * 4 * H * n_local
+                  + 2 * 2 * n_local * row_bytes)
 
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -243,21 +322,46 @@ def main():
         "roofline_gather": {"bound": "hbm", "kernel": "move_rows_kernel (K and V restore, one launch)",
                             "achieved": round(gbs_restore, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs_restore / PEAK_HBM_GBS, 4),
-                            "bytes": restore_bytes},
-        "times_ms": {"step": round(ms_step, 4), "fwd": round(t_fwd, 4),
+                            "bytes": restore_bytes, "cold_achieved": round(gbs_restore_cold, 1),
+                            "cold_frac": round(gbs_restore_cold / PEAK_HBM_GBS, 4),
+                            "note": "achieved: back-to-back on the same buffers (warm); cold: "
+                                    "buffer sets rotated through > 512 MB"},
+        "step_hbm": {"bytes": step_bytes,
+                     "achieved": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "unit": "GB/s", "frac": round(step_bytes / (ms_step * 1e-3) / 1e9
+                                                   / PEAK_HBM_GBS, 4)},
+        "times_ms": {"step": round(ms_step, 4),
+                     "step_mean_evented": round(sum(per_step) / len(per_step), 4),
+                     "step_median_evented": round(per_step[len(per_step) // 2], 4),
+                     "step_p90_evented": round(per_step[int(0.9 * (len(per_step) - 1))], 4),
+                     "plan_build_host_us": round(plan_host_us, 1),
+                     "plan_upload": round(t_upload, 4),
+                     "fwd": round(t_fwd, 4),
                      "bwd_dkdv": round(t_dkdv, 4), "bwd_dq": round(t_dq, 4),
                      "kv_restore": round(t_restore, 4),
+                     "kv_restore_cold": round(t_restore_cold, 4),
                      "attn_kernels_tflops": round(
                          (flop_fwd + flop_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
                      "host_wall_per_step": round(wall / args.steps * 1e3, 4),
                      "kernel_reps": reps},
     }
-    if not args.no_masks:
-        result["mask_variants"] = mask_variants(stream, args.warmup)
+    # Side measurements, each on a clean allocator cache: a block that frees
+    # gigabytes of buffers (mask_variants) left the P2P ring's Python loop up
+    # to 3x slower afterwards, with every kernel and phase of it unchanged.
+    def fresh():
+        import gc
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     if cp > 1 and not args.no_p2p and window == (-1, 0):
+        fresh()
         result["p2p_ring"] = p2p_ring(w, q, k, v, do, cup_dev, stream, args.warmup, args.steps,
                                       reps, flop_fwd + flop_bwd, ms_step)
+    if not args.no_masks:
+        fresh()
+        result["mask_variants"] = mask_variants(stream, args.warmup)
     if not args.no_a2a:
+        fresh()
         result["a2a_layout"] = a2a_layout(stream)
         if w.name == "flat_75k":
             # the gather this workload is quoted on: the dual-chunk reorder of

@@ -46,37 +46,6 @@ struct BwdSmem {
   int32_t glo[2][kBM];  // first key (g - wl); read only for non-causal bands
 };
 
-// Untouched key rows each zeroing workgroup clears (dK and dV, all heads).
-constexpr int kZeroRowsPerBlock = 8;
-
-// Workgroups past the attention tiles zero dK/dV rows that no local query
-// attends (the gated tail zeroing): they sit at the end of the grid, so they
-// run in the tail of the launch, on CUs the last key tiles leave idle.
-__device__ void zero_untouched_block(int64_t b, const ZeroRange* __restrict__ zr, int32_t n_zr,
-                                     int64_t zero_rows, const int32_t* __restrict__ kv_row,
-                                     int32_t kv_sub, int64_t row_floats,
-                                     float* __restrict__ dk, float* __restrict__ dv) {
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  const int64_t vpr = row_floats / 4;
-  for (int rr = 0; rr < kZeroRowsPerBlock; ++rr) {
-    const int64_t lin = b * kZeroRowsPerBlock + rr;  // index among all untouched rows
-    if (lin >= zero_rows) break;
-    int32_t lo = 0, hi = n_zr - 1;  // last range with before <= lin
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if ((int64_t)zr[mid].before <= lin) lo = mid; else hi = mid - 1;
-    }
-    const int64_t g = zr[lo].r0 + (lin - zr[lo].before);
-    const int64_t row = (kv_row ? kv_row[g] : g) - kv_sub;  // global row -> row of dk/dv
-    f32x4* a = reinterpret_cast<f32x4*>(dk + row * row_floats);
-    f32x4* c = reinterpret_cast<f32x4*>(dv + row * row_floats);
-    for (int64_t i = threadIdx.x; i < vpr; i += blockDim.x) {
-      a[i] = z;
-      c[i] = z;
-    }
-  }
-}
-
 // BAND: the mask is a general band [g - wl, g + wr] (a lower-bound test
 // per element); otherwise it is causal (key <= g only).
 template <int D, bool BAND>
@@ -88,8 +57,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
                      const float* __restrict__ lse,
                      const float* __restrict__ delta, float* __restrict__ dk,
                      float* __restrict__ dv, int64_t n_local, float scale, float scale_log2,
-                     int32_t accumulate, int32_t n_attn_blocks, const ZeroRange* __restrict__ zr,
-                     int32_t n_zr, int64_t zero_rows) {
+                     int32_t accumulate) {
   constexpr int KS = D / 32;                  // 16x16x32 k-steps over the head dim
   constexpr int NB = D / 16;                  // 16-wide blocks of the head dim
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -99,11 +67,6 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   S& sm = *reinterpret_cast<S*>(smem_raw);
 
-  if ((int32_t)blockIdx.x >= n_attn_blocks) {
-    zero_untouched_block(blockIdx.x - n_attn_blocks, zr, n_zr, zero_rows, kv_row, kv_sub,
-                         (int64_t)H * D, dk, dv);
-    return;
-  }
   const int tile_id = blockIdx.x / H;
   const int h = blockIdx.x - tile_id * H;
   const BwdTile t = tiles[tile_id];
@@ -297,12 +260,8 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
                         const void* k, const void* v, const int32_t* kv_row, int32_t kv_sub,
                         Band band, const void* d_o, const float* lse, const float* delta, float* dk,
                         float* dv, int64_t n_local, float scale, int32_t accumulate,
-                        const ZeroRange* zr, int32_t n_zr, int64_t zero_rows,
                         hipStream_t stream) {
-  const int64_t attn_blocks = (int64_t)n_tiles * H;
-  const int64_t zero_blocks =
-      (zr && n_zr > 0) ? (zero_rows + kZeroRowsPerBlock - 1) / kZeroRowsPerBlock : 0;
-  const int64_t blocks = attn_blocks + zero_blocks;
+  const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const size_t smem = sizeof(BwdSmem<D>);
@@ -322,8 +281,7 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
                      smem, stream, tiles, H, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v), kv_row, kv_sub,
                      band.wl, band.wr, static_cast<const bf16*>(d_o),
-                     lse, delta, dk, dv, n_local, scale, scale * kLog2e, accumulate,
-                     (int32_t)attn_blocks, zr, n_zr, zero_rows);
+                     lse, delta, dk, dv, n_local, scale, scale * kLog2e, accumulate);
   return hipGetLastError();
 }
 
@@ -333,12 +291,11 @@ hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H
                                 const void* q, const void* k, const void* v, KvRows kv,
                                 Band band, const void* d_o, const float* lse,
                                 const float* delta, float* dk, float* dv, int64_t n_local,
-                                float scale, int32_t accumulate, const ZeroRange* zr,
-                                int32_t n_zr, int64_t zero_rows, hipStream_t stream) {
+                                float scale, int32_t accumulate, hipStream_t stream) {
   const int32_t sub = (int32_t)kv.sub;
 #define THDCP_DKDV(DD, BB)                                                                   \
   return launch_bwd_d<DD, BB>(tiles, n_tiles, H, q, k, v, kv.map, sub, band, d_o, lse, delta, \
-                              dk, dv, n_local, scale, accumulate, zr, n_zr, zero_rows, stream)
+                              dk, dv, n_local, scale, accumulate, stream)
   if (D == 128 && band.causal) THDCP_DKDV(128, false);
   if (D == 128) THDCP_DKDV(128, true);
   if (D == 64 && band.causal) THDCP_DKDV(64, false);

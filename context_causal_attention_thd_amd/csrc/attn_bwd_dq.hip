@@ -54,7 +54,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
                    const bf16* __restrict__ o,
                    const float* __restrict__ lse, float* __restrict__ delta,
                    float* __restrict__ dq, int64_t n_local, int32_t accumulate,
-                   float scale, float scale_log2) {
+                   float scale, float scale_log2, int32_t n_attn_blocks, DqExtras ex) {
   constexpr int BN = kFwdBN;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
@@ -63,6 +63,11 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   constexpr int CH = BN * CPR / kThreads;
   __shared__ DqSmem<D> sm;
 
+  if ((int)blockIdx.x >= n_attn_blocks) {  // gated zeroing workgroups
+    zero_untouched_block(blockIdx.x - n_attn_blocks, ex.zr, ex.n_zr, ex.zero_rows, kv_row, kv_sub,
+                         (int64_t)H * D, ex.dk, ex.dv);
+    return;
+  }
   const int tile_id = blockIdx.x / H;
   const int h = blockIdx.x - tile_id * H;
   const FwdTile t = tiles[tile_id];
@@ -298,11 +303,11 @@ void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int3
                   const bf16* q, const bf16* k, const bf16* v, const int32_t* kv_row,
                   int32_t kv_sub, uint32_t kvb, Band band, const bf16* d_o, const bf16* o,
                   const float* lse, float* delta, float* dq, int64_t n_local, float scale,
-                  int32_t accumulate) {
+                  int32_t accumulate, int32_t n_attn, const DqExtras& ex) {
 #define THDCP_DQ(DL, BB)                                                                      \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, DL, BB>), dim3((unsigned)blocks), dim3(kThreads), \
                      0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,  \
-                     o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e)
+                     o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e, n_attn, ex)
   if (o && band.causal)
     THDCP_DQ(true, false);
   else if (o)
@@ -320,8 +325,11 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
                               const void* q, const void* k, const void* v, KvRows kv,
                               Band band, const void* d_o, const void* o, const float* lse,
                               float* delta, float* dq, int64_t n_local, float scale,
-                              int32_t accumulate, hipStream_t stream) {
-  const int64_t blocks = (int64_t)n_tiles * H;
+                              int32_t accumulate, const DqExtras& ex, hipStream_t stream) {
+  const int64_t attn_blocks = (int64_t)n_tiles * H;
+  const int64_t zero_blocks =
+      (ex.zr && ex.n_zr > 0) ? (ex.zero_rows + kZeroRowsPerBlock - 1) / kZeroRowsPerBlock : 0;
+  const int64_t blocks = attn_blocks + zero_blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const bf16* qb = static_cast<const bf16*>(q);
@@ -335,16 +343,16 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
   const int32_t sub = (int32_t)kv.sub;
   if (D == 128 && kv.map)
     launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                            delta, dq, n_local, scale, accumulate);
+                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
   else if (D == 128)
     launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                             delta, dq, n_local, scale, accumulate);
+                             delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
   else if (D == 64 && kv.map)
     launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                           delta, dq, n_local, scale, accumulate);
+                           delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
   else if (D == 64)
     launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                            delta, dq, n_local, scale, accumulate);
+                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

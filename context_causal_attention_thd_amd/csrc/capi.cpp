@@ -905,7 +905,7 @@ thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t p, const void* q, const void* k, co
       launch_attn_bwd_dkdv(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
                            (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band,
                            d_o, lse, static_cast<const float*>(scratch), dk, dv, p->n_local,
-                           p->scale, accumulate_dkv, nullptr, 0, 0, (hipStream_t)stream),
+                           p->scale, accumulate_dkv, (hipStream_t)stream),
       "cp_attn_bwd_dkdv launch");
 }
 
@@ -923,7 +923,7 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
       launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                          (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o,
                          nullptr, lse, static_cast<float*>(const_cast<void*>(scratch)), dq,
-                         p->n_local, p->scale, 0, (hipStream_t)stream),
+                         p->n_local, p->scale, 0, DqExtras{}, (hipStream_t)stream),
       "cp_attn_bwd_dq launch");
 }
 
@@ -963,26 +963,31 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
     if (zero_untouched) return thdcp_zero_untouched(p, dk, dv, stream);
     return ok();
   }
-  // Two launches: the dQ kernel also computes delta = rowsum(dO * O) into the
-  // scratch (no separate preprocess launch), then the dK/dV kernel, whose grid
-  // ends with the gated zeroing of untouched rows when the caller asks for it
-  // and the plan has such rows (no separate zeroing launch).
+  // Two launches. The dQ kernel also computes delta = rowsum(dO * O) into the
+  // scratch (no separate preprocess launch), and its grid ends with the gated
+  // zeroing of untouched dK/dV rows when the caller asks for it and the plan
+  // has such rows (no separate zeroing launch). Then the dK/dV kernel.
   float* delta = static_cast<float*>(scratch);
-  if (!p->fwd.empty()) {
+  DqExtras ex;
+  if (zero_untouched && !p->zero.empty()) {
+    ex.zr = reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_zero);
+    ex.n_zr = (int32_t)p->zero.size();
+    ex.zero_rows = p->desc.T - p->touched;
+    ex.dk = dk;
+    ex.dv = dv;
+  }
+  {
     hipError_t e = launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                                       (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v,
-                                      kv_map(p), p->band, d_o, o, lse, delta, dq, p->n_local, p->scale, 0,
-                                      (hipStream_t)stream);
+                                      kv_map(p), p->band, d_o, o, lse, delta, dq, p->n_local,
+                                      p->scale, 0, ex, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dq launch");
   }
-  const bool zero = zero_untouched && !p->zero.empty();
-  if (!p->bwd.empty() || zero) {
+  if (!p->bwd.empty()) {
     hipError_t e = launch_attn_bwd_dkdv(
         reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd), (int32_t)p->bwd.size(),
-        p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o, lse, delta, dk, dv, p->n_local, p->scale,
-        accumulate_dkv, zero ? reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_zero) : nullptr,
-        zero ? (int32_t)p->zero.size() : 0, zero ? p->desc.T - p->touched : 0,
-        (hipStream_t)stream);
+        p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o, lse, delta, dk, dv, p->n_local,
+        p->scale, accumulate_dkv, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dkdv launch");
   }
   return ok();
@@ -1051,20 +1056,28 @@ thdcp_status_t cp_attn_bwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   const thdcp_plan::Step& sp = p->steps[src];
   const KvRows kv = kv_step(p, src);
   float* delta = static_cast<float*>(const_cast<void*>(scratch));
-  if (sp.n_fwd > 0) {
+  // The dQ launch also zeroes the peer's rows no local query reaches, with
+  // workgroups at the end of its grid, when there are any.
+  DqExtras ex;
+  if (zero_untouched && sp.n_zero > 0) {
+    ex.zr = reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_szero) + sp.zero0;
+    ex.n_zr = sp.n_zero;
+    ex.zero_rows = sp.untouched;
+    ex.dk = dk;
+    ex.dv = dv;
+  }
+  if (sp.n_fwd > 0 || ex.zr) {
     hipError_t e = launch_attn_bwd_dq(
         reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0, sp.n_fwd,
-        p->desc.H, p->desc.D, q, k, v, kv, p->band, d_o, nullptr, lse, delta, dq, p->n_local, p->scale,
-        accumulate_dq != 0, (hipStream_t)stream);
+        p->desc.H, p->desc.D, q, k, v, kv, p->band, d_o, nullptr, lse, delta, dq, p->n_local,
+        p->scale, accumulate_dq != 0, ex, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dq launch");
   }
-  const bool zero = zero_untouched && sp.n_zero > 0;
-  if (sp.n_bwd > 0 || zero) {
+  if (sp.n_bwd > 0) {
     hipError_t e = launch_attn_bwd_dkdv(
         reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_sbwd) + sp.bwd0, sp.n_bwd, p->desc.H,
         p->desc.D, q, k, v, kv, p->band, d_o, lse, delta, dk, dv, p->n_local, p->scale, 0,
-        zero ? reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_szero) + sp.zero0 : nullptr,
-        zero ? sp.n_zero : 0, zero ? sp.untouched : 0, (hipStream_t)stream);
+        (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dkdv launch");
   }
   return ok();

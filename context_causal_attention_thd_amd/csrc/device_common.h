@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace thdcp {
 
 typedef __bf16 bf16;
@@ -146,6 +148,39 @@ __device__ __forceinline__ float group_sum4(float x) {
   const uint32_t u2 = __float_as_uint(x);
   auto b = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Gated tail zeroing by whole workgroups: workgroup b of the zeroing part of
+// a grid writes 0 to kZeroRowsPerBlock of the dK/dV rows no local query
+// attends (all heads), found among the plan's untouched ranges (`before` is
+// the count of such rows ahead of each range). Key row g is row
+// (kv_row ? kv_row[g] : g) - kv_sub of dk and dv.
+constexpr int kZeroRowsPerBlock = 8;
+
+__device__ inline void zero_untouched_block(int64_t b, const ZeroRange* __restrict__ zr,
+                                            int32_t n_zr, int64_t zero_rows,
+                                            const int32_t* __restrict__ kv_row, int32_t kv_sub,
+                                            int64_t row_floats, float* __restrict__ dk,
+                                            float* __restrict__ dv) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const int64_t vpr = row_floats / 4;
+  for (int rr = 0; rr < kZeroRowsPerBlock; ++rr) {
+    const int64_t lin = b * kZeroRowsPerBlock + rr;  // index among all untouched rows
+    if (lin >= zero_rows) break;
+    int32_t lo = 0, hi = n_zr - 1;  // last range with before <= lin
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if ((int64_t)zr[mid].before <= lin) lo = mid; else hi = mid - 1;
+    }
+    const int64_t g = zr[lo].r0 + (lin - zr[lo].before);
+    const int64_t row = (kv_row ? kv_row[g] : g) - kv_sub;  // global row -> row of dk/dv
+    f32x4* a = reinterpret_cast<f32x4*>(dk + row * row_floats);
+    f32x4* c = reinterpret_cast<f32x4*>(dv + row * row_floats);
+    for (int64_t i = threadIdx.x; i < vpr; i += blockDim.x) {
+      a[i] = z;
+      c[i] = z;
+    }
+  }
 }
 
 }  // namespace thdcp

@@ -100,14 +100,22 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
                            const void* q, const void* k, const void* v, KvRows kv, Band band,
                            void* o, float* lse, int64_t n_local, float scale,
                            hipStream_t stream);
-// zr/n_zr/zero_rows (nullable / 0): also zero the dK/dV rows no local query
-// attends, with extra workgroups at the end of the same launch.
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                                 const void* q, const void* k, const void* v, KvRows kv,
                                 Band band, const void* d_o, const float* lse,
                                 const float* delta, float* dk, float* dv, int64_t n_local,
-                                float scale, int32_t accumulate, const ZeroRange* zr,
-                                int32_t n_zr, int64_t zero_rows, hipStream_t stream);
+                                float scale, int32_t accumulate, hipStream_t stream);
+// Work a dQ launch carries besides dQ: workgroups at the end of its grid that
+// zero the dK/dV rows no local query attends (zr/n_zr/zero_rows, rows found
+// through the launch's KvRows). It is independent of dQ and fills the
+// launch's tail.
+struct DqExtras {
+  const ZeroRange* zr = nullptr;
+  int32_t n_zr = 0;
+  int64_t zero_rows = 0;
+  float* dk = nullptr;
+  float* dv = nullptr;
+};
 // o (nullable): when given, delta = rowsum(dO * O) is computed by this launch
 // and written to `delta` for the dK/dV kernel; otherwise `delta` is read.
 // accumulate: add to dq (P2P steps after the first) instead of writing it.
@@ -116,6 +124,6 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
                               Band band, const void* d_o, const void* o, const float* lse,
                               float* delta,
                               float* dq, int64_t n_local, float scale, int32_t accumulate,
-                              hipStream_t stream);
+                              const DqExtras& extras, hipStream_t stream);
 
 }  // namespace thdcp

@@ -319,8 +319,8 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k
  *   zero_untouched and accumulate_dkv are mutually exclusive.
  *   scratch  device, >= bwd_scratch_bytes, 256-byte aligned.
  * Two launches: the dQ kernel, which also computes delta = rowsum(dO * O)
- * into scratch, then the dK/dV kernel, whose grid ends with the zeroing
- * workgroups when zero_untouched = 1 and the plan has such rows.
+ * into scratch and whose grid ends with the zeroing workgroups when
+ * zero_untouched = 1 and the plan has such rows, then the dK/dV kernel.
  * No atomics are used: every output row is written by exactly one workgroup,
  * so dQ, dK and dV are bit-identical from run to run.
  */
@@ -413,7 +413,7 @@ thdcp_status_t thdcp_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_pa
  *           rank's partial for rank src's keys (what the ring sends back);
  *           rows attended by a local query are written. zero_untouched = 1
  *           also writes 0 to the other rows, only when the plan has such rows.
- * Two launches (dQ, then dK/dV with the zeroing workgroups); no atomics.
+ * Two launches (dQ with the zeroing workgroups, then dK/dV); no atomics.
  */
 THDCP_API
 thdcp_status_t cp_attn_bwd_step(thdcp_plan_t plan, int32_t src_rank, const void* q_local,
