@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--window", type=int, nargs=2, default=(-1, 0), metavar=("LEFT", "RIGHT"),
                     help="attention window of the timed step: real keys at document "
                          "positions [p-LEFT, p+RIGHT], -1 unbounded; (-1, 0) causal")
+    ap.add_argument("--max-key-splits", type=int, default=0,
+                    help="the plan's max_key_splits for the timed step: 0 automatic, "
+                         "1 never split a forward / dQ key walk, n at most n parts")
     ap.add_argument("--no-masks", action="store_true",
                     help="skip the mask-variant measurement on the flat share")
     ap.add_argument("--no-p2p", action="store_true",
@@ -121,8 +124,9 @@ def main():
     dk_rm = torch.empty((T, H, D), dtype=torch.float32, device=dev)   # rank-major partials
     dv_rm = torch.empty_like(dk_rm)
     window = tuple(args.window)
+    splits = args.max_key_splits
     probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
-                     window=window)
+                     window=window, max_key_splits=splits)
     ws = torch.empty(int(probe.info.workspace_bytes) + 4096, dtype=torch.uint8, device=dev)
     scratch = torch.empty(int(probe.info.bwd_scratch_bytes) + 256, dtype=torch.uint8, device=dev)
     pairs = int(probe.info.causal_pairs)
@@ -131,7 +135,7 @@ def main():
 
     def step():
         plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
-                        kv_layout="rank_major", window=window)
+                        kv_layout="rank_major", window=window, max_key_splits=splits)
         plan.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
@@ -173,14 +177,14 @@ def main():
     t0 = time.perf_counter()
     for _ in range(20):
         pl = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
-                      window=window)
+                      window=window, max_key_splits=splits)
         pl.close()
     plan_host_us = (time.perf_counter() - t0) / 20 * 1e6
 
     # The standalone K/V restore and the plan upload: events around REPS
     # back-to-back launches, so the events' own cost is amortized.
     plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
-                    window=window)
+                    window=window, max_key_splits=splits)
     plan.upload_into(ws, stream)
     reps = max(5, min(50, int(20.0 / max(ms_step, 1e-3))))
 
@@ -229,7 +233,7 @@ def main():
 
     def step_evented():
         pl = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
-                      kv_layout="rank_major", window=window)
+                      kv_layout="rank_major", window=window, max_key_splits=splits)
         pl.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
@@ -303,7 +307,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "heads": H, "head_dim": D, "cp_size": cp,
-                   "window": list(window),
+                   "window": list(window), "max_key_splits": splits,
                    "rank": r, "strategy": w.strategy, "docs": w.B, "causal_pairs_per_head": pairs,
                    "parallelism": "one simulated CP rank on one GPU"},
         "roofline": {"bound": "mfma", "kernel": "attn_bwd_dkdv_kernel",

@@ -54,6 +54,7 @@ class _Desc(ctypes.Structure):
         ("pad_between_seqs", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
         ("p2p", ctypes.c_int32),
+        ("max_key_splits", ctypes.c_int32),
     ]
 
 
@@ -69,6 +70,8 @@ class PlanInfo(ctypes.Structure):
         ("n_zero_ranges", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
         ("bwd_scratch_bytes", ctypes.c_size_t),
+        ("n_split_tiles", ctypes.c_int32),
+        ("n_fwd_parts", ctypes.c_int32),
     ]
 
 
@@ -335,7 +338,7 @@ class Plan:
     def __init__(self, cu_seqlens, cu_seqlens_padded, T: int, cp_size: int, rank: int, strategy,
                  H: int, D: int, softmax_scale: float = 0.0, window=(-1, 0),
                  pad_between_seqs: int = -1, device=None, stream=None, upload: bool = True,
-                 kv_layout: str = "global", p2p: bool = False):
+                 kv_layout: str = "global", p2p: bool = False, max_key_splits: int = 0):
         self._cup = _i32_host(cu_seqlens_padded)
         self._cu = None if cu_seqlens is None else _i32_host(cu_seqlens)
         d = _Desc()
@@ -357,6 +360,7 @@ class Plan:
         self.kv_layout = kv_layout
         d.p2p = int(bool(p2p))
         self.p2p = bool(p2p)
+        d.max_key_splits = int(max_key_splits)
         self._handle = ctypes.c_void_p()
         _check(lib().thdcp_plan_create(ctypes.byref(d), ctypes.byref(self._handle)))
         self.T, self.H, self.D, self.cp_size, self.rank = int(T), int(H), int(D), cp_size, rank

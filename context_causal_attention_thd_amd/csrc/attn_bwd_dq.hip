@@ -54,7 +54,8 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
                    const bf16* __restrict__ o,
                    const float* __restrict__ lse, float* __restrict__ delta,
                    float* __restrict__ dq, int64_t n_local, int32_t accumulate,
-                   float scale, float scale_log2, int32_t n_attn_blocks, DqExtras ex) {
+                   float scale, float scale_log2, int32_t n_attn_blocks, SplitWs split,
+                   DqExtras ex) {
   constexpr int BN = kFwdBN;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
@@ -116,7 +117,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       for (int j = 0; j < 8; ++j) part = fmaf((float)dof[kk][j], (float)of[j], part);
     }
     dlt = part + __shfl_xor(part, 32, 64);  // 0 on padding rows (dO taken as 0)
-    if (hh == 0 && in_tile) delta[(int64_t)h * n_local + m] = dlt;
+    if (hh == 0 && in_tile && t.part == 0) delta[(int64_t)h * n_local + m] = dlt;
   } else {
     dlt = valid ? delta[(int64_t)h * n_local + m] : 0.f;
   }
@@ -275,6 +276,38 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
     __syncthreads();
   }
 
+  if (t.nparts > 1) {
+    // Split key walk: this part's accumulators go to its scratch slot in lane
+    // order; the last part to finish sums all parts in part order.
+    auto acc_at = [&](int x, int db, int i4) {
+      return reinterpret_cast<f32x4*>(split_slot(split.part, x, h, H, D)) +
+             ((db * 4 + i4) * kThreads + threadIdx.x);
+    };
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 a;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = acc[db][i4 * 4 + j];
+        *acc_at(t.slot + t.part, db, i4) = a;
+      }
+    if (!split_arrive(split.cnt + (int64_t)t.group * H + h, t.nparts)) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 a = *acc_at(t.slot, db, i4);
+        for (int p = 1; p < t.nparts; ++p) {
+          const f32x4 b = *acc_at(t.slot + p, db, i4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a[j] += b[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[db][i4 * 4 + j] = a[j];
+      }
+  }
+
   if (!in_tile) return;
   float* qp = dq + m * rs + head_off;
 #pragma unroll
@@ -303,11 +336,12 @@ void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int3
                   const bf16* q, const bf16* k, const bf16* v, const int32_t* kv_row,
                   int32_t kv_sub, uint32_t kvb, Band band, const bf16* d_o, const bf16* o,
                   const float* lse, float* delta, float* dq, int64_t n_local, float scale,
-                  int32_t accumulate, int32_t n_attn, const DqExtras& ex) {
+                  int32_t accumulate, int32_t n_attn, SplitWs split, const DqExtras& ex) {
 #define THDCP_DQ(DL, BB)                                                                      \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, DL, BB>), dim3((unsigned)blocks), dim3(kThreads), \
                      0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,  \
-                     o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e, n_attn, ex)
+                     o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e, n_attn, split,  \
+                     ex)
   if (o && band.causal)
     THDCP_DQ(true, false);
   else if (o)
@@ -325,7 +359,8 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
                               const void* q, const void* k, const void* v, KvRows kv,
                               Band band, const void* d_o, const void* o, const float* lse,
                               float* delta, float* dq, int64_t n_local, float scale,
-                              int32_t accumulate, const DqExtras& ex, hipStream_t stream) {
+                              int32_t accumulate, SplitWs split, const DqExtras& ex,
+                              hipStream_t stream) {
   const int64_t attn_blocks = (int64_t)n_tiles * H;
   const int64_t zero_blocks =
       (ex.zr && ex.n_zr > 0) ? (ex.zero_rows + kZeroRowsPerBlock - 1) / kZeroRowsPerBlock : 0;
@@ -343,16 +378,16 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
   const int32_t sub = (int32_t)kv.sub;
   if (D == 128 && kv.map)
     launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
+                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
   else if (D == 128)
     launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                             delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
+                             delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
   else if (D == 64 && kv.map)
     launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                           delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
+                           delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
   else if (D == 64)
     launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, ex);
+                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

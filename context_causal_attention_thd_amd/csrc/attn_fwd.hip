@@ -65,13 +65,15 @@ constexpr int kFwdThreads = kFwdBM / (16 * QB) * 64;
 // K/V, or one rank's block of it: the restore fused into the loads).
 // BAND: a general key band [g - wl, g + wr]; otherwise the causal mask
 // (wl unbounded, wr = 0, folded at compile time).
+// The second bound is waves per SIMD: two workgroups per CU (the LDS holds
+// two), which caps the registers at 512 / that.
 template <int D, int QB, bool MAPPED, bool BAND>
-__global__ void __launch_bounds__(kFwdThreads<QB>, 2)
+__global__ void __launch_bounds__(kFwdThreads<QB>, 2 * kFwdThreads<QB> / 256)
 attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                 const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
                 int32_t wl_arg, int32_t wr_arg, bf16* __restrict__ o, float* __restrict__ lse,
-                int64_t n_local, float scale_log2) {
+                int64_t n_local, float scale_log2, SplitWs split) {
   constexpr int kThreads = kFwdThreads<QB>;
   constexpr int BN = kFwdBN;
   constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
@@ -343,6 +345,54 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     __syncthreads();
   }
 
+  if (t.nparts > 1) {
+    // Split key walk: this part's state (accumulators, then per query block
+    // the running max and this lane's row-sum share) goes to its scratch slot
+    // in lane order; the last part to finish rescales every part's state to
+    // the largest running max and sums them in part order, which is the
+    // online softmax's own merge of two key ranges.
+    constexpr int NBLK = kFwdBM / 16;
+    auto acc_at = [&](int x, int b, int nb) {
+      return reinterpret_cast<f32x4*>(split_slot(split.part, x, h, H, D)) +
+             ((b * NB + nb) * 64 + lane);
+    };
+    auto st_at = [&](int x, int b) {
+      return reinterpret_cast<float2*>(split_slot(split.part, x, h, H, D) + NBLK * NB * 256) +
+             (b * 64 + lane);
+    };
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int b = w * QB + qb;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) *acc_at(t.slot + t.part, b, nb) = oacc[qb][nb];
+      *st_at(t.slot + t.part, b) = make_float2(m_run[qb], l_part[qb]);
+    }
+    if (!split_arrive(split.cnt + (int64_t)t.group * H + h, t.nparts)) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int b = w * QB + qb;
+      float mx = -INFINITY;
+      for (int p = 0; p < t.nparts; ++p) mx = fmaxf(mx, st_at(t.slot + p, b)->x);
+      l_part[qb] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[qb][nb][i] = 0.f;
+      for (int p = 0; p < t.nparts; ++p) {
+        const float2 st = *st_at(t.slot + p, b);
+        const float f = st.x == -INFINITY ? 0.f : fast_exp2(st.x - mx);
+        l_part[qb] = fmaf(st.y, f, l_part[qb]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const f32x4 a = *acc_at(t.slot + p, b, nb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[qb][nb][i] = fmaf(a[i], f, oacc[qb][nb][i]);
+        }
+      }
+      m_run[qb] = mx;
+    }
+  }
+
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = group_sum4(l_part[qb]);
@@ -374,11 +424,11 @@ template <int D>
 hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const bf16* q,
                         const bf16* k, const bf16* v, const int32_t* kv_row, int32_t kv_sub,
                         uint32_t kv_bytes, Band band, bf16* o, float* lse, int64_t n_local,
-                        float scale_log2, hipStream_t stream) {
+                        float scale_log2, SplitWs split, hipStream_t stream) {
 #define THDCP_FWD(MM, BB)                                                                  \
   hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, MM, BB>), dim3((unsigned)blocks),           \
                      dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub, \
-                     kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2)
+                     kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2, split)
   if (kv_row && band.causal)
     THDCP_FWD(true, false);
   else if (kv_row)
@@ -395,7 +445,7 @@ hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const b
 
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                            const void* q, const void* k, const void* v, KvRows kv, Band band,
-                           void* o, float* lse, int64_t n_local, float scale,
+                           void* o, float* lse, int64_t n_local, float scale, SplitWs split,
                            hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
@@ -410,10 +460,10 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
   const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
   if (D == 128)
     return launch_fwd_d<128>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, band,
-                             ob, lse, n_local, scale_log2, stream);
+                             ob, lse, n_local, scale_log2, split, stream);
   if (D == 64)
     return launch_fwd_d<64>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, band,
-                            ob, lse, n_local, scale_log2, stream);
+                            ob, lse, n_local, scale_log2, split, stream);
   return hipErrorInvalidValue;
 }
 

@@ -128,9 +128,12 @@ struct thdcp_plan {
   std::vector<FwdTile> step_fwd;
   std::vector<BwdTile> step_bwd;
   std::vector<ZeroRange> step_zero;
-  std::vector<char> blob;  // host image of the device tables
+  // Split key walks of the all-gather forward / dQ tiles: groups (one counter
+  // per group and head) and scratch slots (one per part and head).
+  int32_t split_groups = 0, split_slots = 0, split_tiles = 0;
+  std::vector<char> blob;  // host image of the device tables (and zeroed counters)
   size_t off_fwd = 0, off_bwd = 0, off_zero = 0, off_kvrow = 0, ws_bytes = 0;
-  size_t off_sfwd = 0, off_sbwd = 0, off_szero = 0;
+  size_t off_sfwd = 0, off_sbwd = 0, off_szero = 0, off_cnt = 0, off_part = 0;
   char* ws_dev = nullptr;  // caller's workspace after upload
 };
 
@@ -198,6 +201,81 @@ std::vector<Tile> lpt_order(const std::vector<Tile>& tiles, Cost cost) {
   sorted.reserve(tiles.size());
   for (size_t i : order) sorted.push_back(tiles[i]);
   return sorted;
+}
+
+// Split key walks. A forward or dQ launch runs one workgroup per (tile,
+// head), and the chip holds kConcurrentWGs of them at once. When that grid
+// barely fills the chip and the walks are very uneven (few heads over long
+// causal documents: the last query tile of a document walks all of it), the
+// longest walks, not the total work, set the launch's duration. Then every
+// walk longer than the balanced load (the total key tiles over the
+// concurrent workgroups) is divided into parts of consecutive key tiles no
+// longer than that load, at most max_parts (kMaxParts when 0). Measured on
+// MI355X, splitting pays (forward -17..20%, dQ -25..28%) when the longest
+// walk is twice the balanced load, and does not at 1.25 and 1.5 times, where
+// the tail's workgroups already run faster on emptied CUs and each part adds
+// a prologue; hence the kSplitImbalance threshold for the automatic choice
+// (a forced max_parts >= 2 splits from the balanced load on). Returns the
+// table in LPT order.
+constexpr int64_t kConcurrentWGs = 512;  // 256 CUs x 2 forward (or dQ) workgroups
+constexpr int64_t kMinPartTiles = 6;     // shorter parts do not repay their merge
+constexpr double kSplitImbalance = 1.75;
+constexpr int32_t kMaxParts = 8;
+
+std::vector<FwdTile> split_walks(const std::vector<FwdTile>& tiles, int32_t H, int32_t max_parts,
+                                 int32_t* n_groups, int32_t* n_slots, int32_t* n_split) {
+  int64_t total = 0;
+  for (const FwdTile& t : tiles) total += fwd_cost(t);
+  total *= H;
+  const int64_t target =
+      std::max<int64_t>(kMinPartTiles, (total + kConcurrentWGs - 1) / kConcurrentWGs);
+  int64_t longest = 0;
+  for (const FwdTile& t : tiles) longest = std::max(longest, fwd_cost(t));
+  int32_t cap = max_parts == 0 ? kMaxParts : std::min(max_parts, kMaxParts);
+  if (max_parts == 0 && (double)longest < kSplitImbalance * (double)target) cap = 1;
+  std::vector<FwdTile> out;
+  int32_t groups = 0, slots = 0;
+  for (const FwdTile& t : tiles) {
+    const int64_t c = fwd_cost(t);
+    const int32_t np = (int32_t)std::min<int64_t>(cap, (c + target - 1) / target);
+    if (np < 2) {
+      FwdTile u = t;
+      u.part = 0;
+      u.nparts = 1;
+      u.slot = u.group = 0;
+      out.push_back(u);
+      continue;
+    }
+    // key tiles of the walk: n0 of [ks0, ke0), then those of [ks1, ke1)
+    const int64_t n0 = t.ke0 > t.ks0 ? (t.ke0 - t.ks0 + kFwdBN - 1) / kFwdBN : 0;
+    for (int32_t part = 0; part < np; ++part) {
+      const int64_t a = c * part / np, b = c * (part + 1) / np;  // key tiles [a, b)
+      FwdTile u = t;
+      if (a < n0) {
+        u.ks0 = (int32_t)(t.ks0 + a * kFwdBN);
+        u.ke0 = (int32_t)std::min<int64_t>(t.ke0, t.ks0 + std::min(b, n0) * kFwdBN);
+      } else {
+        u.ks0 = u.ke0 = 0;
+      }
+      if (b > n0) {
+        u.ks1 = (int32_t)(t.ks1 + (std::max(a, n0) - n0) * kFwdBN);
+        u.ke1 = (int32_t)std::min<int64_t>(t.ke1, t.ks1 + (b - n0) * kFwdBN);
+      } else {
+        u.ks1 = u.ke1 = 0;
+      }
+      u.part = part;
+      u.nparts = np;
+      u.slot = slots;
+      u.group = groups;
+      out.push_back(u);
+    }
+    ++groups;
+    slots += np;
+  }
+  *n_groups = groups;
+  *n_slots = slots;
+  *n_split = groups;
+  return lpt_order(out, [](const FwdTile& t) { return fwd_cost(t); });
 }
 
 // A document's real local rows: runs of consecutive local rows holding
@@ -365,7 +443,8 @@ void build_plan(thdcp_plan& p) {
       fwd_doc.push_back(s.doc);
     }
   }
-  p.fwd = lpt_order(fwd, [](const FwdTile& t) { return fwd_cost(t); });
+  p.fwd = split_walks(lpt_order(fwd, [](const FwdTile& t) { return fwd_cost(t); }), d.H,
+                      d.max_key_splits, &p.split_groups, &p.split_slots, &p.split_tiles);
 
   // Backward tiles: per document, the keys its local real rows attend -- per
   // run of consecutive rows, from the first row's band start to the last
@@ -485,9 +564,12 @@ void build_plan(thdcp_plan& p) {
   p.off_sfwd = align256(p.off_kvrow + p.kv_row.size() * sizeof(int32_t));
   p.off_sbwd = align256(p.off_sfwd + p.step_fwd.size() * sizeof(FwdTile));
   p.off_szero = align256(p.off_sbwd + p.step_bwd.size() * sizeof(BwdTile));
-  p.ws_bytes = align256(p.off_szero + p.step_zero.size() * sizeof(ZeroRange));
+  p.off_cnt = align256(p.off_szero + p.step_zero.size() * sizeof(ZeroRange));
+  p.off_part = align256(p.off_cnt + (size_t)p.split_groups * d.H * sizeof(int32_t));
+  p.ws_bytes = p.off_part + (size_t)p.split_slots * d.H * kSplitFloats(d.D) * sizeof(float);
   if (p.ws_bytes == 0) p.ws_bytes = 256;
-  p.blob.assign(p.ws_bytes, 0);
+  // the image covers the tables and the split counters (zero), not the scratch
+  p.blob.assign(std::max<size_t>(p.off_part, 256), 0);
   auto put = [&](size_t off, const void* src, size_t n) {
     if (n) memcpy(p.blob.data() + off, src, n);
   };
@@ -498,6 +580,12 @@ void build_plan(thdcp_plan& p) {
   put(p.off_sfwd, p.step_fwd.data(), p.step_fwd.size() * sizeof(FwdTile));
   put(p.off_sbwd, p.step_bwd.data(), p.step_bwd.size() * sizeof(BwdTile));
   put(p.off_szero, p.step_zero.data(), p.step_zero.size() * sizeof(ZeroRange));
+}
+
+// Counters and scratch of the all-gather tables' split key walks.
+SplitWs split_ws(const thdcp_plan* p) {
+  return {reinterpret_cast<int32_t*>(p->ws_dev + p->off_cnt),
+          reinterpret_cast<float*>(p->ws_dev + p->off_part)};
 }
 
 // Row addressing of the all-gather calls' K/V (and dK/dV): rank-major
@@ -672,6 +760,9 @@ thdcp_status_t thdcp_plan_create(const thdcp_attn_desc* desc, thdcp_plan_t* plan
     if (d.kv_layout != THDCP_KV_GLOBAL && d.kv_layout != THDCP_KV_RANK_MAJOR)
       return fail(THDCP_ERR_ARG, "kv_layout %d (0 global, 1 rank-major)", d.kv_layout);
     if (d.p2p != 0 && d.p2p != 1) return fail(THDCP_ERR_ARG, "p2p %d (0 or 1)", d.p2p);
+    if (d.max_key_splits < 0)
+      return fail(THDCP_ERR_ARG, "max_key_splits %d (0 automatic, 1 never, n at most n)",
+                  d.max_key_splits);
     if (d.p2p && (d.window_left != -1 || d.window_right != 0))
       return fail(THDCP_ERR_UNSUPPORTED,
                   "P2P steps take the causal mask only, window_size=(-1, 0) (got (%d, %d))",
@@ -711,11 +802,14 @@ thdcp_status_t thdcp_plan_get_info(thdcp_plan_t p, thdcp_plan_info* info) {
   info->touched_rows = p->touched;
   info->untouched_rows = p->desc.T - p->touched;
   info->padding_present = p->padding;
-  info->n_fwd_tiles = (int32_t)p->fwd.size();
+  info->n_fwd_tiles = 0;
+  for (const FwdTile& t : p->fwd) info->n_fwd_tiles += t.part == 0;
   info->n_bwd_tiles = (int32_t)p->bwd.size();
   info->n_zero_ranges = (int32_t)p->zero.size();
   info->workspace_bytes = p->ws_bytes;
   info->bwd_scratch_bytes = align256((size_t)p->n_local * p->desc.H * sizeof(float));
+  info->n_split_tiles = p->split_tiles;
+  info->n_fwd_parts = (int32_t)p->fwd.size();
   return ok();
 }
 
@@ -818,8 +912,8 @@ thdcp_status_t thdcp_plan_upload(thdcp_plan_t p, void* ws, size_t bytes, void* s
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return fail(THDCP_ERR_ARG, "workspace must be 256-byte aligned");
   hipError_t e = hipSuccess;
-  if (!staging_ring().upload(ws, p->blob.data(), p->ws_bytes, (hipStream_t)stream, &e))
-    e = hipMemcpyAsync(ws, p->blob.data(), p->ws_bytes, hipMemcpyHostToDevice,
+  if (!staging_ring().upload(ws, p->blob.data(), p->blob.size(), (hipStream_t)stream, &e))
+    e = hipMemcpyAsync(ws, p->blob.data(), p->blob.size(), hipMemcpyHostToDevice,
                        (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "plan upload");
   p->ws_dev = static_cast<char*>(ws);
@@ -840,7 +934,7 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t p, const void* q, const void* k, const v
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                       (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, o,
-                      lse, p->n_local, p->scale, (hipStream_t)stream),
+                      lse, p->n_local, p->scale, split_ws(p), (hipStream_t)stream),
       "cp_attn_fwd launch");
 }
 
@@ -923,7 +1017,7 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
       launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                          (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o,
                          nullptr, lse, static_cast<float*>(const_cast<void*>(scratch)), dq,
-                         p->n_local, p->scale, 0, DqExtras{}, (hipStream_t)stream),
+                         p->n_local, p->scale, 0, split_ws(p), DqExtras{}, (hipStream_t)stream),
       "cp_attn_bwd_dq launch");
 }
 
@@ -980,7 +1074,7 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
     hipError_t e = launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                                       (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v,
                                       kv_map(p), p->band, d_o, o, lse, delta, dq, p->n_local,
-                                      p->scale, 0, ex, (hipStream_t)stream);
+                                      p->scale, 0, split_ws(p), ex, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dq launch");
   }
   if (!p->bwd.empty()) {
@@ -1022,7 +1116,7 @@ thdcp_status_t cp_attn_fwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0,
                       sp.n_fwd, p->desc.H, p->desc.D, q, k, v, kv_step(p, src), p->band, o, lse,
-                      p->n_local, p->scale, (hipStream_t)stream),
+                      p->n_local, p->scale, SplitWs{}, (hipStream_t)stream),
       "cp_attn_fwd_step launch");
 }
 
@@ -1070,7 +1164,7 @@ thdcp_status_t cp_attn_bwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
     hipError_t e = launch_attn_bwd_dq(
         reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0, sp.n_fwd,
         p->desc.H, p->desc.D, q, k, v, kv, p->band, d_o, nullptr, lse, delta, dq, p->n_local,
-        p->scale, accumulate_dq != 0, ex, (hipStream_t)stream);
+        p->scale, accumulate_dq != 0, SplitWs{}, ex, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dq launch");
   }
   if (sp.n_bwd > 0) {

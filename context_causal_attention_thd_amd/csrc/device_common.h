@@ -183,4 +183,38 @@ __device__ inline void zero_untouched_block(int64_t b, const ZeroRange* __restri
   }
 }
 
+// Split key walks: every thread of a part's workgroup calls this after
+// writing the part's partial result. Each wave waits until its stores have
+// reached the L2; one agent-scope release (a write-back of the XCD's L2)
+// then publishes the whole workgroup's stores before the workgroup is counted
+// on *cnt. The workgroup that completes the count of nparts gets true in
+// every thread: it resets the counter for the next launch and performs one
+// agent-scope acquire (invalidating its CU's L1 and its XCD's L2) before any
+// of its waves reads the other parts' results. No workgroup waits for
+// another. One release and one acquire per workgroup, not per wave: the
+// cache maintenance is cache-wide, and per-wave fences measured several
+// times slower.
+__device__ inline bool split_arrive(int32_t* cnt, int32_t nparts) {
+  __shared__ int32_t s_last;
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int32_t before =
+        __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == nparts - 1;
+    if (s_last) {
+      __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+  }
+  __syncthreads();
+  return s_last != 0;
+}
+
+// Scratch of one part of a split key walk (slot x, head h).
+__device__ inline float* split_slot(float* part, int32_t x, int32_t h, int32_t H, int D) {
+  return part + ((int64_t)x * H + h) * kSplitFloats(D);
+}
+
 }  // namespace thdcp

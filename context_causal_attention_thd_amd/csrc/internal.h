@@ -15,6 +15,13 @@ namespace thdcp {
 // [doc start, last real row + 1) for the all-gather pass; for one P2P step,
 // the parts of it that the step's source rank holds (at most two
 // DUAL_CHUNK_SWAP chunks of the document).
+//
+// Split key walk: when nparts > 1 the tile's key tiles are walked by nparts
+// workgroups, part p taking the p-th of nparts equal runs of them in walk
+// order (so only the last part reaches the diagonal). Each part writes its
+// partial result to scratch slot `slot + part`; the one that finishes last
+// (counted on counter `group`) combines all of them in part order, so the
+// result does not depend on which part finished last.
 struct FwdTile {
   int32_t m0;        // first local row
   int32_t n;         // rows in the tile (<= kFwdBM)
@@ -22,6 +29,8 @@ struct FwdTile {
   int32_t e;         // end of the document's real tokens (a + actual length)
   int32_t ks0, ke0;  // first key range
   int32_t ks1, ke1;  // second key range
+  int32_t part, nparts;
+  int32_t slot, group;
 };
 
 // Backward work item: key rows [k0, k1) of one document (all attended by at
@@ -45,9 +54,19 @@ struct ZeroRange {
   int32_t pad0;
 };
 
-constexpr int kFwdBM = 128;  // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdBM = 128;  // query rows per forward / dQ workgroup
 constexpr int kFwdBN = 64;   // keys per forward K/V tile
 constexpr int kBwdBN = 128;  // keys per backward workgroup (4 waves x 32)
+
+// Scratch of split key walks: per (slot, head) kSplitFloats(D) floats hold
+// one part's partial result (forward: accumulators, running max and row-sum
+// shares; dQ: accumulators), in the owning kernel's lane order; cnt[group * H
+// + head] counts the parts that have finished (0 between launches).
+constexpr int64_t kSplitFloats(int D) { return 128 * (int64_t)D + 1024; }
+struct SplitWs {
+  int32_t* cnt;
+  float* part;
+};
 
 // Kernel launchers (defined in the .hip files). All enqueue on `stream`.
 hipError_t launch_partition(const int32_t* cup, int32_t B, int64_t T, int32_t cp,
@@ -98,7 +117,7 @@ hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, flo
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                            const void* q, const void* k, const void* v, KvRows kv, Band band,
-                           void* o, float* lse, int64_t n_local, float scale,
+                           void* o, float* lse, int64_t n_local, float scale, SplitWs split,
                            hipStream_t stream);
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                                 const void* q, const void* k, const void* v, KvRows kv,
@@ -124,6 +143,6 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
                               Band band, const void* d_o, const void* o, const float* lse,
                               float* delta,
                               float* dq, int64_t n_local, float scale, int32_t accumulate,
-                              const DqExtras& extras, hipStream_t stream);
+                              SplitWs split, const DqExtras& extras, hipStream_t stream);
 
 }  // namespace thdcp

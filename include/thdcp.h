@@ -243,6 +243,14 @@ typedef struct {
   int32_t kv_layout;         /* thdcp_kv_layout_t of K/V in and dK/dV out */
   int32_t p2p;               /* 1: also build the P2P ring step tables
                                 (cp_attn_fwd_step / cp_attn_bwd_step) */
+  int32_t max_key_splits;    /* key walks of the forward / dQ query tiles:
+                                0 = the plan splits the walks longer than the
+                                balanced load of a full MI355X when the
+                                longest is 1.75x that load or more (few heads
+                                over long causal documents), 1 = never split,
+                                n >= 2 = split from the balanced load on, at
+                                most n parts (capped at 8). Results are
+                                deterministic either way. */
 } thdcp_attn_desc;
 
 typedef struct {
@@ -251,11 +259,13 @@ typedef struct {
   int64_t touched_rows;      /* key rows attended by >= 1 local query */
   int64_t untouched_rows;    /* T - touched_rows */
   int32_t padding_present;   /* by value, see thdcp_validate */
-  int32_t n_fwd_tiles;
+  int32_t n_fwd_tiles;       /* query tiles of the forward / dQ launches */
   int32_t n_bwd_tiles;
   int32_t n_zero_ranges;     /* untouched key-row ranges */
   size_t workspace_bytes;    /* device bytes thdcp_plan_upload needs */
   size_t bwd_scratch_bytes;  /* device bytes cp_attn_bwd needs as scratch */
+  int32_t n_split_tiles;     /* query tiles whose key walk is split */
+  int32_t n_fwd_parts;       /* workgroups per head of a forward / dQ launch */
 } thdcp_plan_info;
 
 /* Build a plan on the host. *plan_out receives a host object the caller
@@ -274,6 +284,11 @@ thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
  * >= workspace_bytes, 256-byte aligned) with one async host-to-device copy on
  * `stream`. The plan keeps the pointer; the workspace must stay alive and
  * unmodified while forward/backward calls using the plan are in flight.
+ * Past the tables it holds the split key walks' counters (uploaded as zero,
+ * left at zero by every launch) and their partial results, so the plan's
+ * forward and dQ launches must not overlap: enqueue calls that use one
+ * workspace on one stream (or order them). The copy covers the tables and
+ * counters only.
  * Tables up to 1 MiB are first copied into a page-locked staging slot the
  * library keeps for the life of the process (16 slots, 16 MiB, allocated on
  * the first upload); larger ones are copied from the plan itself, which must
@@ -296,6 +311,10 @@ void thdcp_plan_destroy(thdcp_plan_t plan);
  *   o_local  bf16 [n_local, H, D]   written for every local row
  *   lse      fp32 [H, n_local]      natural log; -inf on padding rows
  * Padding rows get O = 0. Padding key rows are never read into a product.
+ * A query tile whose key walk the plan split (max_key_splits) is computed by
+ * several workgroups of the same launch; the last to finish merges their
+ * (max, sum, accumulator) states in key order, so the output is
+ * bit-identical from run to run.
  */
 THDCP_API
 thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k,
@@ -321,8 +340,10 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t plan, const void* q_local, const void* k
  * Two launches: the dQ kernel, which also computes delta = rowsum(dO * O)
  * into scratch and whose grid ends with the zeroing workgroups when
  * zero_untouched = 1 and the plan has such rows, then the dK/dV kernel.
- * No atomics are used: every output row is written by exactly one workgroup,
- * so dQ, dK and dV are bit-identical from run to run.
+ * Every output row is written by exactly one workgroup (a split dQ walk's
+ * parts are summed in key order by the last part to finish; a counter
+ * atomic only decides which part that is), so dQ, dK and dV are
+ * bit-identical from run to run.
  */
 THDCP_API
 thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k,

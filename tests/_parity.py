@@ -55,7 +55,7 @@ def device():
 
 
 def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
-              accumulate=False, kv_layout="global", window=(-1, 0)):
+              accumulate=False, kv_layout="global", window=(-1, 0), max_key_splits=0):
     """Product path on cuda:0 for one rank: partition index -> gather local Q
     and dO -> plan -> forward -> backward. Returns numpy arrays. With
     kv_layout="rank_major" K/V are passed in the all-gathered (rank-major)
@@ -75,7 +75,7 @@ def run_share(w, rank, tensors, zero_untouched=True, dk_init=None, dv_init=None,
         perm = thd.partition_index(cup, cup_dev, w.T, w.cp_size, -1, w.strategy)
         k, v = thd.gather(k, perm), thd.gather(v, perm)
     plan = thd.Plan(cu, cup, w.T, w.cp_size, rank, w.strategy, w.H, w.D, kv_layout=kv_layout,
-                    window=window)
+                    window=window, max_key_splits=max_key_splits)
     o, lse = thd.attn_fwd(plan, q_local, k, v)
     dk = None if dk_init is None else dk_init.to(dev).clone()
     dv = None if dv_init is None else dv_init.to(dev).clone()

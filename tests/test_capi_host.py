@@ -291,3 +291,48 @@ def test_empty_moves_ignore_pointers(L):
     assert L.thd_a2a_unpack(2, nul, 0, 4, 16, nul, None) == 0
     # the tensor count is still checked
     assert L.thd_gather_batched(0, nul, 0, None, 0, 16, nul, None) == 1
+
+
+def test_plan_split_walks(L):
+    # Forward / dQ key walks are split automatically only where the grid is
+    # small against a full chip (512 concurrent workgroups) and very uneven:
+    # few heads over one long causal document. The large shares and the
+    # short-document DUAL_CHUNK_SWAP share are left whole; a forced part
+    # count splits from the balanced load on.
+    def plan(name, **kw):
+        x = W.WORKLOADS[name]
+        return thd.Plan(x.cu_seqlens(), x.cu_seqlens_padded(), x.T, x.cp_size, x.rank,
+                        x.strategy, x.H, x.D, upload=False, **kw)
+    for name in ("dcs_8k", "nlb_32k", "pad_131k", "flat_75k"):
+        p = plan(name)
+        assert p.info.n_split_tiles == 0 and p.info.n_fwd_parts == p.info.n_fwd_tiles, name
+        p.close()
+    forced, never = plan("dcs_8k", max_key_splits=2), plan("dcs_8k", max_key_splits=1)
+    assert forced.info.n_split_tiles > 0
+    assert forced.info.n_fwd_parts == forced.info.n_fwd_tiles + forced.info.n_split_tiles
+    assert never.info.n_split_tiles == 0 and never.info.n_fwd_parts == never.info.n_fwd_tiles
+    assert forced.info.n_fwd_tiles == never.info.n_fwd_tiles
+    # each part of a split walk has one scratch slot per head of 128*D + 1024 floats
+    x = W.WORKLOADS["dcs_8k"]
+    assert forced.info.workspace_bytes - never.info.workspace_bytes >= \
+        2 * forced.info.n_split_tiles * x.H * (128 * x.D + 1024) * 4
+    # one 16k-token document over 4 heads: 512 workgroups whose walks run
+    # from 2 to 256 key tiles (twice the balanced load) -- split in two
+    doc = thd.Plan([0, 16384], [0, 16384], 16384, 1, 0, "no_load_balance", 4, 128,
+                   upload=False)
+    assert doc.info.n_fwd_tiles == 128 and doc.info.n_split_tiles == 64
+    assert doc.info.n_fwd_parts == 192
+    # the same document under DUAL_CHUNK_SWAP, cp_size 4: walks within 1.25x
+    # of the balance, left whole
+    dcs = thd.Plan([0, 32768], [0, 32768], 32768, 4, 3, "dual_chunk_swap", 8, 128,
+                   upload=False)
+    assert dcs.info.n_split_tiles == 0
+    # parts are capped at 8
+    one = thd.Plan([0, 8000], [0, 8000], 8000, 1, 0, "no_load_balance", 1, 128, upload=False,
+                   max_key_splits=100)
+    assert one.info.n_split_tiles > 0
+    assert one.info.n_fwd_parts <= 8 * one.info.n_fwd_tiles
+    with pytest.raises(thd.ThdcpError):
+        plan("dcs_8k", max_key_splits=-1)
+    for p in (forced, never, doc, dcs, one):
+        p.close()

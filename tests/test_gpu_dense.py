@@ -29,11 +29,12 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def run_dense(layout, B, S, H, D, cp, rank, strategy, t, window=(-1, 0)):
+def run_dense(layout, B, S, H, D, cp, rank, strategy, t, window=(-1, 0), max_key_splits=0):
     """Product path for one rank of a dense batch; outputs batch-major like
     the oracle's: O/dQ [B, n, H, D], LSE [B, H, n], dK/dV [B, S, H, D]."""
     dev = device()
-    plan = thd.dense_plan(layout, B, S, H, D, cp, rank, strategy, window=window)
+    plan = thd.dense_plan(layout, B, S, H, D, cp, rank, strategy, window=window,
+                          max_key_splits=max_key_splits)
     cu, heads = thd.dense_as_thd(layout, B, S, H)
     T = int(cu[-1])
     q, k, v, do = (thd.dense_view(t[n].to(dev), layout) for n in ("q", "k", "v", "do"))
@@ -106,16 +107,19 @@ def test_dense_bshd_nlb_batch_refused():
 def test_sbhd_full_size_equals_per_batch_element(cp, strategy):
     """sbhd [8192, 4, 5, 128] (the flat post-a2a share of 40 heads over 8
     ranks, four sequences): bit-identical to each sequence run alone as a
-    single-document THD share with 5 heads."""
+    single-document THD share with 5 heads, given the same key walks (the
+    automatic walk split depends on the launch's head count, so both sides
+    take max_key_splits = 1)."""
     layout, B, S, H, D = "sbhd", 4, 8192, 5, 128
     _say("sbhd full size", cp, strategy)
     t = W.dense_bf16(layout, B, S, H, D, seed=7100)
     r = cp - 1
-    _, o, lse, dq, dk, dv = run_dense(layout, B, S, H, D, cp, r, strategy, t)
+    _, o, lse, dq, dk, dv = run_dense(layout, B, S, H, D, cp, r, strategy, t, max_key_splits=1)
     for b in range(B):
         tb = {n: x[:, b].contiguous() for n, x in t.items()}
         _, o1, l1, dq1, dk1, dv1 = run_dense("bshd", 1, S, H, D, cp, r, strategy,
-                                             {n: x[None] for n, x in tb.items()})
+                                             {n: x[None] for n, x in tb.items()},
+                                             max_key_splits=1)
         for a, c, n in ((o[b], o1[0], "O"), (lse[b], l1[0], "LSE"), (dq[b], dq1[0], "dQ"),
                         (dk[b], dk1[0], "dK"), (dv[b], dv1[0], "dV")):
             assert np.array_equal(a, c), (b, n)

@@ -274,7 +274,8 @@ def test_padding_poison():
 
 
 def test_determinism_run_to_run():
-    # No atomics anywhere: every output is bit-identical across runs.
+    # Every output row has one writer (split key walks are merged in key
+    # order), so every output is bit-identical across runs.
     w = SMALL[2]
     t = W.bf16_tensors(w)
     a = run_share(w, 1, t)
