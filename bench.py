@@ -211,6 +211,12 @@ def main():
     for st_ in sets[1:]:
         st_[0].copy_(k_rm)
         st_[1].copy_(v_rm)
+    # One untimed pass touches every destination once: the first write to a
+    # freshly allocated buffer costs extra (measured 37 us against 24 us per
+    # launch), which is allocation, not bandwidth. The timed passes stay cold:
+    # each set was last touched n_sets - 1 launches (> 512 MB) earlier.
+    for a_, b_, c_, d_ in sets:
+        thd.scatter_many([a_, b_], perm, [c_, d_])
     torch.cuda.synchronize()
     ec0 = torch.cuda.Event(enable_timing=True)
     ec1 = torch.cuda.Event(enable_timing=True)
@@ -324,12 +330,13 @@ def main():
                          "achieved": round(tflops_fwd, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops_fwd / PEAK_BF16_TFLOPS, 4)},
         "roofline_gather": {"bound": "hbm", "kernel": "move_rows_kernel (K and V restore, one launch)",
-                            "achieved": round(gbs_restore, 1), "peak": PEAK_HBM_GBS,
-                            "unit": "GB/s", "frac": round(gbs_restore / PEAK_HBM_GBS, 4),
-                            "bytes": restore_bytes, "cold_achieved": round(gbs_restore_cold, 1),
-                            "cold_frac": round(gbs_restore_cold / PEAK_HBM_GBS, 4),
-                            "note": "achieved: back-to-back on the same buffers (warm); cold: "
-                                    "buffer sets rotated through > 512 MB"},
+                            "achieved": round(gbs_restore_cold, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs_restore_cold / PEAK_HBM_GBS, 4),
+                            "bytes": restore_bytes, "warm_achieved": round(gbs_restore, 1),
+                            "warm_frac": round(gbs_restore / PEAK_HBM_GBS, 4),
+                            "note": "achieved: buffer sets rotated through > 512 MB so every "
+                                    "launch reads and writes HBM (cold); warm: back-to-back on "
+                                    "the same buffers, served largely from the 256 MB cache"},
         "step_hbm": {"bytes": step_bytes,
                      "achieved": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "unit": "GB/s", "frac": round(step_bytes / (ms_step * 1e-3) / 1e9

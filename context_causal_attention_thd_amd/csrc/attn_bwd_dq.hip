@@ -206,12 +206,16 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   const int ntiles = nt0 + nt1;
   auto tile_k0 = [&](int it) { return it < nt0 ? t.ks0 + it * BN : t.ks1 + (it - nt0) * BN; };
   auto tile_kend = [&](int it) { return it < nt0 ? t.ke0 : t.ke1; };
-  int pos[CH];
+  // The second tile's rows are looked up beside the first's, so the prologue
+  // waits on one row-map round trip before the first K/V loads, not two.
+  int pos[CH], pos1[CH] = {};
   if (ntiles > 0) {
     rows_pos(tile_k0(0), tile_kend(0), pos);
+    if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos1);
     load_tile(tile_k0(0), tile_kend(0), pos);
     store_tile(0);
-    if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) pos[j] = pos1[j];
   }
   wait_vmem();  // Q/dO fragments have landed: the loop's MFMAs never wait on loads
   __syncthreads();

@@ -308,14 +308,18 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int wave_gmax = wave_uniform(t.g0 + row0 + QB * 16 - 1);
   const bool wave_all_valid =
       wave_uniform((row0 + QB * 16 - 1 < t.n) && (t.g0 + row0 + QB * 16 - 1 < t.e)) != 0;
-  int pos[CH];
+  // The second tile's rows are looked up beside the first's, so the prologue
+  // waits on one row-map round trip before the first K/V loads, not two.
+  int pos[CH], pos1[CH] = {};
   if (ntiles > 0) {
     rows_pos(tile_k0(0), tile_kend(0), pos);
+    if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos1);
     load_rows(k, tile_k0(0), tile_kend(0), pos, kreg);
     load_rows(v, tile_k0(0), tile_kend(0), pos, vreg);
     store_rows(sm.k[0], kreg);
     store_rows(sm.v[0], vreg);
-    if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) pos[j] = pos1[j];
   }
   wait_vmem();
   __syncthreads();

@@ -10,6 +10,8 @@
 //
 // All of these are HBM-bound: each maps (row, 16-byte chunk) pairs onto
 // consecutive lanes so that every wave issues contiguous 16-byte accesses.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -71,8 +73,15 @@ template <> struct Vec<4> { typedef uint32_t T; };
 template <> struct Vec<2> { typedef uint16_t T; };
 template <> struct Vec<1> { typedef uint8_t T; };
 
+// One 16-byte (or narrower) chunk per thread per grid-stride step, plain
+// loads and nontemporal stores, index arithmetic in 32 bits unless the launch
+// has 2^32 chunks or more (WIDE). Measured on MI355X for the K+V restore of
+// one 8192-row, 4 KiB-row share (134 MB moved): 5.59 TB/s with the source
+// and destination rotated through more than the 256 MB last-level cache,
+// 6.41 TB/s when they stay in it; four chunks per thread with nontemporal
+// loads and a 64-bit division per chunk gave 5.22 / 5.65, and a plain
+// device-to-device copy of the same bytes 4.74 / 6.46.
 constexpr int kRowThreads = 256;
-constexpr int kRowUnroll = 4;
 
 // Up to kMaxTensors tensors moved by one launch (blockIdx.y picks the tensor).
 struct RowPtrs {
@@ -96,60 +105,59 @@ struct RowMap {
   int64_t cp;       // a2a modes: groups
 };
 
-template <int VB, int MODE>
+template <int VB, int MODE, bool WIDE>
 __global__ void __launch_bounds__(kRowThreads) move_rows_kernel(
     const RowPtrs ptrs, const RowMap map, uint32_t chunks_per_row, uint64_t total_chunks,
     int64_t row_bytes) {
   typedef typename Vec<VB>::T V;
+  typedef typename std::conditional<WIDE, uint64_t, uint32_t>::type I;
   const char* __restrict__ src = ptrs.src[blockIdx.y];
   char* __restrict__ dst = ptrs.dst[blockIdx.y];
-  const uint64_t stride = (uint64_t)gridDim.x * kRowThreads * kRowUnroll;
-  for (uint64_t base = (uint64_t)blockIdx.x * kRowThreads * kRowUnroll + threadIdx.x;
-       base < total_chunks; base += stride) {
-    V val[kRowUnroll];
-    int64_t drow[kRowUnroll];
-    uint32_t dchunk[kRowUnroll];
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
-      const uint64_t t = base + (uint64_t)u * kRowThreads;
-      drow[u] = -1;
-      if (t < total_chunks) {
-        const uint64_t row = t / chunks_per_row;
-        const uint32_t c = (uint32_t)(t - row * chunks_per_row);
-        int64_t srow;
-        bool load = true;
-        if (MODE == kGather || MODE == kScatter) {
-          const int64_t other = map.idx[row];
-          const bool in = other >= 0 && other < map.n_other;
-          srow = MODE == kScatter ? (int64_t)row : other;
-          drow[u] = MODE == kScatter ? (in ? other : -1) : (int64_t)row;
-          load = MODE == kScatter || in;
-        } else if (MODE == kPack) {
-          const int64_t grp = (int64_t)row / map.n;
-          srow = ((int64_t)row - grp * map.n) * map.cp + grp;
-          drow[u] = (int64_t)row;
-        } else {
-          const int64_t tok = (int64_t)row / map.cp;
-          srow = ((int64_t)row - tok * map.cp) * map.n + tok;
-          drow[u] = (int64_t)row;
-        }
-        dchunk[u] = c;
-        if (load) {
-          val[u] = __builtin_nontemporal_load(
-              reinterpret_cast<const V*>(src + srow * row_bytes + (int64_t)c * VB));
-        } else {
-          val[u] = V{};
-        }
-      }
+  const uint64_t stride = (uint64_t)gridDim.x * kRowThreads;
+  for (uint64_t t = (uint64_t)blockIdx.x * kRowThreads + threadIdx.x; t < total_chunks;
+       t += stride) {
+    const I row = (I)t / (I)chunks_per_row;
+    const uint32_t c = (uint32_t)((I)t - row * (I)chunks_per_row);
+    int64_t srow, drow;
+    bool load = true;
+    if (MODE == kGather || MODE == kScatter) {
+      const int64_t other = map.idx[row];
+      const bool in = other >= 0 && other < map.n_other;
+      srow = MODE == kScatter ? (int64_t)row : other;
+      drow = MODE == kScatter ? (in ? other : -1) : (int64_t)row;
+      load = MODE == kScatter || in;
+    } else if (MODE == kPack) {
+      const int64_t grp = (int64_t)row / map.n;
+      srow = ((int64_t)row - grp * map.n) * map.cp + grp;
+      drow = (int64_t)row;
+    } else {
+      const int64_t tok = (int64_t)row / map.cp;
+      srow = ((int64_t)row - tok * map.cp) * map.n + tok;
+      drow = (int64_t)row;
     }
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
-      if (drow[u] >= 0) {
-        __builtin_nontemporal_store(
-            val[u], reinterpret_cast<V*>(dst + drow[u] * row_bytes + (int64_t)dchunk[u] * VB));
-      }
-    }
+    if (drow < 0) continue;
+    const V val =
+        load ? *reinterpret_cast<const V*>(src + srow * row_bytes + (int64_t)c * VB) : V{};
+    __builtin_nontemporal_store(val,
+                                reinterpret_cast<V*>(dst + drow * row_bytes + (int64_t)c * VB));
   }
+}
+
+template <int MODE, bool WIDE>
+hipError_t launch_move_vb(int vb, dim3 grid, dim3 block, const RowPtrs& ptrs, const RowMap& map,
+                          uint64_t cpr, uint64_t total, int64_t row_bytes, hipStream_t stream) {
+#define THDCP_MOVE(VB)                                                                        \
+  hipLaunchKernelGGL((move_rows_kernel<VB, MODE, WIDE>), grid, block, 0, stream, ptrs, map, \
+                     (uint32_t)cpr, total, row_bytes)
+  switch (vb) {
+    case 16: THDCP_MOVE(16); break;
+    case 8: THDCP_MOVE(8); break;
+    case 4: THDCP_MOVE(4); break;
+    case 2: THDCP_MOVE(2); break;
+    default: THDCP_MOVE(1); break;
+  }
+#undef THDCP_MOVE
+  return hipGetLastError();
 }
 
 // n: rows the launch walks (dst rows for gather / pack / unpack, src rows for
@@ -173,17 +181,11 @@ hipError_t launch_move(int32_t n_tensors, const void* const* srcs, void* const* 
   const uint64_t total = cpr * (uint64_t)n;
   if (cpr > 0xffffffffull) return hipErrorInvalidValue;
   if (total == 0) return hipSuccess;
-  uint64_t blocks = (total + kRowThreads * kRowUnroll - 1) / (kRowThreads * kRowUnroll);
+  uint64_t blocks = (total + kRowThreads - 1) / kRowThreads;
   if (blocks > 65536) blocks = 65536;
   const dim3 grid((unsigned)blocks, (unsigned)n_tensors), block(kRowThreads);
-  switch (vb) {
-    case 16: hipLaunchKernelGGL((move_rows_kernel<16, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
-    case 8:  hipLaunchKernelGGL((move_rows_kernel<8, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
-    case 4:  hipLaunchKernelGGL((move_rows_kernel<4, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
-    case 2:  hipLaunchKernelGGL((move_rows_kernel<2, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
-    default: hipLaunchKernelGGL((move_rows_kernel<1, MODE>), grid, block, 0, stream, ptrs, map, (uint32_t)cpr, total, row_bytes); break;
-  }
-  return hipGetLastError();
+  if (total >= (1ull << 32)) return launch_move_vb<MODE, true>(vb, grid, block, ptrs, map, cpr, total, row_bytes, stream);
+  return launch_move_vb<MODE, false>(vb, grid, block, ptrs, map, cpr, total, row_bytes, stream);
 }
 
 hipError_t launch_gather(int32_t n_tensors, const void* const* srcs, int64_t n_src,
