@@ -391,9 +391,11 @@ def p2p_ring(w, q, k, v, do, cup_dev, stream, warmup, steps, reps, flops, ms_all
     """The same rank's fwd+bwd as P2P (ring) steps on one GPU: every peer's
     local K/V is already resident (what the ring's sends deliver). A ring
     step = p2p plan + upload, partition index, gather of local Q and dO,
-    cp forward steps each folded by the LSE merge, delta of the merged
-    output, cp backward steps (dQ accumulated, the peer's dK/dV into its own
-    buffer for the return trip). The transfers themselves are not here."""
+    cp forward steps (each step's result kept), one LSE merge of all of them,
+    delta of the merged output, cp backward steps (dQ accumulated, the peer's
+    dK/dV into its own buffer for the return trip). The transfers themselves
+    are not here. The forward with a merge after every step into an fp32
+    accumulator is timed beside it."""
     import torch
     import context_causal_attention_thd_amd as thd
     dev = q.device
@@ -411,8 +413,8 @@ def p2p_ring(w, q, k, v, do, cup_dev, stream, warmup, steps, reps, flops, ms_all
     idx = torch.empty(n, dtype=torch.int32, device=dev)
     ql = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
     dol = torch.empty_like(ql)
-    o_part = torch.empty_like(ql)
-    lse_part = torch.empty((H, n), dtype=torch.float32, device=dev)
+    o_parts = torch.empty((cp, n, H, D), dtype=torch.bfloat16, device=dev)
+    lse_parts = torch.empty((cp, H, n), dtype=torch.float32, device=dev)
     o_acc = torch.empty((n, H, D), dtype=torch.float32, device=dev)
     lse = torch.empty((H, n), dtype=torch.float32, device=dev)
     o = torch.empty_like(ql)
@@ -423,8 +425,15 @@ def p2p_ring(w, q, k, v, do, cup_dev, stream, warmup, steps, reps, flops, ms_all
 
     def fwd(plan):
         for i, s in enumerate(srcs):
-            thd.attn_fwd_step(plan, s, ql, kl[s], vl[s], o_part=o_part, lse_part=lse_part)
-            thd.lse_merge(o_part, lse_part, o_acc, lse, first=(i == 0),
+            thd.attn_fwd_step(plan, s, ql, kl[s], vl[s], o_part=o_parts[i],
+                              lse_part=lse_parts[i])
+        thd.lse_merge_parts(o_parts, lse_parts, o_out=o, lse_out=lse)
+
+    def fwd_stepwise(plan):
+        for i, s in enumerate(srcs):
+            thd.attn_fwd_step(plan, s, ql, kl[s], vl[s], o_part=o_parts[0],
+                              lse_part=lse_parts[0])
+            thd.lse_merge(o_parts[0], lse_parts[0], o_acc, lse, first=(i == 0),
                           o_out=o if i == cp - 1 else None)
 
     def bwd(plan):
@@ -471,12 +480,18 @@ def p2p_ring(w, q, k, v, do, cup_dev, stream, warmup, steps, reps, flops, ms_all
         return a.elapsed_time(b) / reps
 
     t_fwd = timed(lambda: fwd(plan))
-    t_merge = timed(lambda: thd.lse_merge(o_part, lse_part, o_acc, lse, first=False))
+    t_merge = timed(lambda: thd.lse_merge_parts(o_parts, lse_parts, o_out=o, lse_out=lse))
+    t_fwd_stepwise = timed(lambda: fwd_stepwise(plan))
+    t_step_merge = timed(lambda: thd.lse_merge(o_parts[0], lse_parts[0], o_acc, lse,
+                                               first=False))
+    fwd(plan)  # leave the one-pass merge's O and LSE for the backward
     t_bwd = timed(lambda: bwd(plan))
     return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "vs_allgather_step": round(ms_allgather / ms, 4), "ring_steps": cp,
-            "times_ms": {"fwd_steps_and_merges": round(t_fwd, 4),
-                         "one_merge": round(t_merge, 4),
+            "times_ms": {"fwd_steps_and_merge": round(t_fwd, 4),
+                         "merge_all_steps": round(t_merge, 4),
+                         "fwd_with_stepwise_merges": round(t_fwd_stepwise, 4),
+                         "one_stepwise_merge": round(t_step_merge, 4),
                          "bwd_preprocess_and_steps": round(t_bwd, 4)},
             "note": "per-rank compute of the ring on one GPU; peer K/V resident, "
                     "transfers not included"}

@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = (
     "thd_a2a_unpack", "thdcp_plan_create", "thdcp_plan_get_info", "thdcp_plan_local_seqlens",
     "thdcp_plan_upload", "thdcp_plan_destroy", "cp_attn_fwd", "cp_attn_bwd",
     "cp_attn_bwd_preprocess", "cp_attn_bwd_dkdv", "cp_attn_bwd_dq", "thdcp_zero_untouched",
-    "cp_attn_fwd_step", "thdcp_lse_merge", "cp_attn_bwd_step",
+    "cp_attn_fwd_step", "thdcp_lse_merge", "thdcp_lse_merge_parts", "cp_attn_bwd_step",
 )
 
 
@@ -134,6 +134,8 @@ def lib() -> ctypes.CDLL:
     L.cp_attn_fwd_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
     L.thdcp_lse_merge.restype = i32
     L.thdcp_lse_merge.argtypes = [i64, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+    L.thdcp_lse_merge_parts.restype = i32
+    L.thdcp_lse_merge_parts.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp, vp]
     L.cp_attn_bwd_step.restype = i32
     L.cp_attn_bwd_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp, i32, vp, vp, i32,
                                    vp]
@@ -607,6 +609,27 @@ def lse_merge(o_part, lse_part, o_acc, lse_acc, first: bool, o_out=None, stream=
                                                                      torch.bfloat16),
                                  _stream(stream)))
     return o_acc, lse_acc
+
+
+def lse_merge_parts(o_parts, lse_parts, o_out=None, lse_out=None, stream=None):
+    """Merge all step results at once: o_parts bf16 [parts, n, H, D], lse_parts
+    fp32 [parts, H, n] -> (o_out bf16 [n, H, D], lse_out fp32 [H, n])."""
+    import torch
+    parts, n, H, D = o_parts.shape
+    _shape(lse_parts, (parts, H, n), "lse_parts")
+    if o_out is None:
+        o_out = torch.empty((n, H, D), dtype=torch.bfloat16, device=o_parts.device)
+    if lse_out is None:
+        lse_out = torch.empty((H, n), dtype=torch.float32, device=o_parts.device)
+    _shape(o_out, (n, H, D), "o_out")
+    _shape(lse_out, (H, n), "lse_out")
+    _check(lib().thdcp_lse_merge_parts(int(n), int(H), int(D), int(parts),
+                                       _dev_ptr(o_parts, "o_parts", torch.bfloat16),
+                                       _dev_ptr(lse_parts, "lse_parts", torch.float32),
+                                       _dev_ptr(o_out, "o_out", torch.bfloat16),
+                                       _dev_ptr(lse_out, "lse_out", torch.float32),
+                                       _stream(stream)))
+    return o_out, lse_out
 
 
 def attn_bwd_step(plan: Plan, src_rank: int, q_local, k_src, v_src, lse, d_o, scratch, dq,

@@ -1021,6 +1021,20 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
       "cp_attn_bwd_dq launch");
 }
 
+thdcp_status_t thdcp_lse_merge_parts(int64_t n, int32_t H, int32_t D, int32_t parts,
+                                     const void* o_parts, const float* lse_parts, void* o_out,
+                                     float* lse_out, void* stream) {
+  if (n < 0 || H < 1 || parts < 1) return fail(THDCP_ERR_ARG, "bad size");
+  if (D != 64 && D != 128) return fail(THDCP_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (n == 0) return ok();
+  if (!o_parts || !lse_parts || !o_out) return fail(THDCP_ERR_ARG, "NULL device pointer");
+  if (!aligned16(o_parts) || !aligned16(o_out))
+    return fail(THDCP_ERR_ARG, "O buffers must be 16-byte aligned");
+  return hip_status(launch_lse_merge_parts(n, H, D, parts, o_parts, lse_parts, o_out, lse_out,
+                                           (hipStream_t)stream),
+                    "thdcp_lse_merge_parts launch");
+}
+
 thdcp_status_t thdcp_zero_untouched(thdcp_plan_t p, float* dk, float* dv, void* stream) {
   thdcp_status_t st = check_plan(p);
   if (st != THDCP_OK) return st;

@@ -113,6 +113,11 @@ hipError_t launch_zero_rows(const ZeroRange* ranges, int32_t n_ranges, int64_t t
 hipError_t launch_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
                             const float* lse_part, float* o_acc, float* lse_acc, int32_t first,
                             void* o_out, hipStream_t stream);
+// Merge `parts` step results (o_parts bf16 [parts, n, H, D], lse_parts fp32
+// [parts, H, n]) into o_out bf16 [n, H, D] and lse_out fp32 [H, n] (nullable).
+hipError_t launch_lse_merge_parts(int64_t n, int32_t H, int32_t D, int32_t parts,
+                                  const void* o_parts, const float* lse_parts, void* o_out,
+                                  float* lse_out, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,

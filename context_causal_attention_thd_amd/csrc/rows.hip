@@ -361,6 +361,68 @@ hipError_t launch_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
 }
 
 // ---------------------------------------------------------------------------
+// All of a ring's step results merged at once: per (row, head), with the
+// parts' LSEs l_p and M = max_p l_p, O = sum_p e^(l_p - M) O_p / sum_p
+// e^(l_p - M) and LSE = M + log sum_p e^(l_p - M), summed in part order. One
+// group of D/8 lanes per (row, head), 16 bytes of each part per lane.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) lse_merge_parts_kernel(
+    int64_t n, int32_t H, int32_t parts, const bf16* __restrict__ o_parts,
+    const float* __restrict__ lse_parts, bf16* __restrict__ o_out, float* __restrict__ lse_out) {
+  constexpr int G = D / 8;
+  const int64_t pairs = n * H;
+  const int64_t pr = (int64_t)blockIdx.x * (blockDim.x / G) + threadIdx.x / G;
+  if (pr >= pairs) return;
+  const int sub = threadIdx.x % G;
+  const int64_t m = pr / H;
+  const int32_t h = (int32_t)(pr - m * H);
+  const int64_t li = (int64_t)h * n + m;
+  const int64_t off = pr * D + sub * 8;
+  const int64_t lstride = (int64_t)H * n, ostride = n * H * D;
+  float mx = -INFINITY;
+  for (int p = 0; p < parts; ++p) mx = fmaxf(mx, lse_parts[p * lstride + li]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != -INFINITY) {  // else no part has a key for this row: O = 0, LSE = -inf
+    for (int p = 0; p < parts; ++p) {
+      const float w = __expf(lse_parts[p * lstride + li] - mx);
+      const bf16x8 op = load_bf16x8(o_parts + p * ostride + off);
+      wsum += w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, (float)op[j], acc[j]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  bf16x8 ob;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ob[j] = (bf16)(acc[j] * inv);
+  store_bf16x8(o_out + off, ob);
+  if (sub == 0 && lse_out) lse_out[li] = wsum > 0.f ? mx + __logf(wsum) : -INFINITY;
+}
+
+hipError_t launch_lse_merge_parts(int64_t n, int32_t H, int32_t D, int32_t parts,
+                                  const void* o_parts, const float* lse_parts, void* o_out,
+                                  float* lse_out, hipStream_t stream) {
+  const int64_t pairs = n * H;
+  if (pairs == 0) return hipSuccess;
+  const int64_t groups_per_block = 256 / (D / 8);
+  const int64_t blocks = (pairs + groups_per_block - 1) / groups_per_block;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const bf16* op = static_cast<const bf16*>(o_parts);
+  bf16* oo = static_cast<bf16*>(o_out);
+  if (D == 128)
+    hipLaunchKernelGGL(lse_merge_parts_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       n, H, parts, op, lse_parts, oo, lse_out);
+  else if (D == 64)
+    hipLaunchKernelGGL(lse_merge_parts_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       n, H, parts, op, lse_parts, oo, lse_out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Backward preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32).
 // One group of D/8 lanes per (row, head); each lane reads 16 bytes of O and dO.
 // ---------------------------------------------------------------------------

@@ -389,7 +389,8 @@ thdcp_status_t thdcp_zero_untouched(thdcp_plan_t plan, float* dk, float* dv, voi
  * a rank's attention in steps over its peers' K/V, with per-step sequence
  * metadata and gradient tails to clear). At ring step i, rank `rank` works on
  * the K/V that rank src = (rank - i) mod cp_size holds; the step results are
- * merged through their log-sum-exp with thdcp_lse_merge. These calls need a
+ * merged through their log-sum-exp, all at once with thdcp_lse_merge_parts
+ * once every step has run, or step by step with thdcp_lse_merge. These calls need a
  * plan made with p2p = 1: every step's tiles come from that one plan, built
  * once per batch, so no step launches metadata work, and a step's gradient
  * tail is zeroed only when the plan shows one.
@@ -423,6 +424,26 @@ THDCP_API
 thdcp_status_t thdcp_lse_merge(int64_t n, int32_t H, int32_t D, const void* o_part,
                                const float* lse_part, float* o_acc, float* lse_acc,
                                int32_t first, void* o_out, void* stream);
+
+/*
+ * Merge every step's result at once: with the parts' LSEs l_p and
+ * M = max_p l_p,
+ *   lse = M + log sum_p exp(l_p - M),
+ *   o   = sum_p exp(l_p - M) o_p / sum_p exp(l_p - M),
+ * summed in part order (bit-identical from run to run).
+ *   o_parts    bf16 [parts, n, H, D]  step p's o_part at o_parts + p*n*H*D
+ *   lse_parts  fp32 [parts, H, n]     step p's lse_part
+ *   o_out      bf16 [n, H, D]         the merged output
+ *   lse_out    fp32 [H, n]            the merged LSE (nullable)
+ * Rows that are -inf in every part get O = 0, LSE = -inf. One elementwise
+ * launch that reads each part once, in place of parts merges into an fp32
+ * accumulator that is read and written at every step. n == 0 enqueues
+ * nothing.
+ */
+THDCP_API
+thdcp_status_t thdcp_lse_merge_parts(int64_t n, int32_t H, int32_t D, int32_t parts,
+                                     const void* o_parts, const float* lse_parts, void* o_out,
+                                     float* lse_out, void* stream);
 
 /*
  * Backward of one step with the softmax of the whole key set: lse is the

@@ -44,11 +44,12 @@ SMALL = [
 ]
 
 
-def run_p2p(w, rank, tensors, fill=None, zero_untouched=True, keep_steps=True):
+def run_p2p(w, rank, tensors, fill=None, zero_untouched=True, keep_steps=True, merge="stepwise"):
     """The ring on one GPU for one rank: every peer's local K/V is gathered
-    (what the ring delivers), then forward steps + merge, delta of the merged
-    output, backward steps. Returns numpy arrays (per-step ones in the
-    source rank's local order) and the global-order sums of dK/dV."""
+    (what the ring delivers), then forward steps + merge (after every step
+    into an fp32 accumulator, or merge="parts": all steps at once), delta of
+    the merged output, backward steps. Returns numpy arrays (per-step ones in
+    the source rank's local order) and the global-order sums of dK/dV."""
     dev = device()
     cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
     cp = w.cp_size
@@ -63,13 +64,21 @@ def run_p2p(w, rank, tensors, fill=None, zero_untouched=True, keep_steps=True):
     o_acc = torch.empty((n, H, D), dtype=torch.float32, device=dev)
     lse_acc = torch.empty((H, n), dtype=torch.float32, device=dev)
     o = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
+    o_parts = torch.empty((cp, n, H, D), dtype=torch.bfloat16, device=dev)
+    lse_parts = torch.empty((cp, H, n), dtype=torch.float32, device=dev)
     fwd_steps = []
     for i in range(cp):
         src = O.p2p_source(rank, i, cp)
-        op, lp = thd.attn_fwd_step(plan, src, ql, kl[src], vl[src])
+        op, lp = thd.attn_fwd_step(plan, src, ql, kl[src], vl[src], o_part=o_parts[i],
+                                   lse_part=lse_parts[i])
         if keep_steps:
             fwd_steps.append((src, op.float().cpu().numpy(), lp.cpu().numpy()))
-        thd.lse_merge(op, lp, o_acc, lse_acc, first=(i == 0), o_out=o if i == cp - 1 else None)
+        if merge == "stepwise":
+            thd.lse_merge(op, lp, o_acc, lse_acc, first=(i == 0),
+                          o_out=o if i == cp - 1 else None)
+    if merge == "parts":
+        thd.lse_merge_parts(o_parts, lse_parts, o_out=o, lse_out=lse_acc)
+        o_acc.copy_(o.float())
     scratch = torch.empty(max(int(plan.info.bwd_scratch_bytes), 256), dtype=torch.uint8,
                           device=dev)
     thd.bwd_preprocess(plan, o, lse_acc, dol, scratch)
@@ -149,6 +158,13 @@ def test_p2p_steps_elementwise_all_ranks(w):
         assert_close(got["dq"], dq1, f"{w.name} r{r} dQ")
         assert_close(got["dk"], dk1, f"{w.name} r{r} dK (summed steps)")
         assert_close(got["dv"], dv1, f"{w.name} r{r} dV (summed steps)")
+        # the same ring with all steps merged at once
+        par = run_p2p(w, r, t, keep_steps=False, merge="parts")
+        assert_close(par["o"], o_ref, f"{w.name} r{r} one-pass merged O")
+        assert_lse(par["lse"], lse_ref, f"{w.name} r{r} one-pass merged LSE")
+        assert np.all(par["o"][pad_local] == 0)
+        for nm, ref_ in (("dq", dq1), ("dk", dk1), ("dv", dv1)):
+            assert_close(par[nm], ref_, f"{w.name} r{r} one-pass {nm}")
 
 
 def test_p2p_zero_gate_and_determinism():
@@ -172,6 +188,46 @@ def test_p2p_zero_gate_and_determinism():
     assert some_untouched
     for n in ("o", "lse", "dq"):
         assert np.array_equal(b[n], c[n]), n
+
+
+def _random_parts(rng, n, H, D, steps):
+    """Step results with rows empty in some steps and in every step."""
+    parts = []
+    for s in range(steps):
+        o = torch.from_numpy(rng.standard_normal((n, H, D))).to(torch.bfloat16)
+        lse = rng.standard_normal((H, n)) * 4
+        lse[rng.random((H, n)) < 0.3] = -np.inf   # rows with no key in this step
+        lse[:, :7] = -np.inf                      # rows with no key in any step
+        o_np = o.double().numpy()
+        o_np[np.isneginf(lse).T] = 0.0
+        o = torch.from_numpy(o_np).to(torch.bfloat16)
+        parts.append((o, torch.from_numpy(lse).float()))
+    return parts
+
+
+@pytest.mark.parametrize("D,steps", [(128, 4), (64, 8), (128, 1)])
+def test_lse_merge_parts_kernel_vs_oracle(D, steps):
+    # all steps merged at once; the oracle's merge is the log-sum-exp over
+    # parts written out (pinned on the CPU against pairwise and closed forms)
+    dev = device()
+    parts = _random_parts(np.random.default_rng(5 + steps), 263, 3, D, steps)
+    o_parts = torch.stack([o for o, _ in parts]).to(dev)
+    lse_parts = torch.stack([l for _, l in parts]).to(dev)
+    o_out, lse_out = thd.lse_merge_parts(o_parts, lse_parts)
+    o2, l2 = thd.lse_merge_parts(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    assert torch.equal(o_out, o2) and torch.equal(lse_out, l2)   # fixed summation order
+    ref_o, ref_l = O.lse_merge([(o.double().numpy(), l.double().numpy()) for o, l in parts])
+    got_l = lse_out.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.abs(got_l[fin] - ref_l[fin]).max() < 1e-5
+    got_o = o_out.float().cpu().numpy()
+    assert np.all(got_o[:7] == 0)
+    assert np.abs(got_o - ref_o).max() <= 2 ** -7 * np.abs(ref_o).max()
+    if steps == 1:   # one part: weight 1, the part itself
+        assert torch.equal(o_out.cpu(), parts[0][0])
+        assert torch.equal(lse_out.cpu(), parts[0][1])
 
 
 def test_lse_merge_kernel_vs_oracle():
@@ -212,7 +268,7 @@ def test_p2p_full_size(name):
     w = W.WORKLOADS[name]
     _say("p2p full-size", name)
     t = W.bf16_tensors(w)
-    got = run_p2p(w, w.rank, t, fill=float("nan"), keep_steps=False)
+    got = run_p2p(w, w.rank, t, fill=float("nan"), keep_steps=False, merge="parts")
     ag = run_share(w, w.rank, t)
     assert np.array_equal(got["idx"], ag["idx"])
     for n in ("o", "dq", "dk", "dv"):
