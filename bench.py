@@ -231,9 +231,9 @@ def main():
     del sets
     # Per-kernel durations inside steps: the same steps with the backward as
     # its separate launches (preprocess, dK/dV, dQ, gated zeroing -- the same
-    # dK/dV kernel and tiles as the composite call, without the zeroing
-    # workgroups at the end of its grid) and an event pair around each
-    # attention kernel. Each kernel runs on the cache state a step leaves,
+    # dK/dV launch as the composite call, whose dQ launch carries the delta
+    # and the zeroing workgroups) and an event pair around each attention
+    # kernel. Each kernel runs on the cache state a step leaves,
     # not on that of its own previous launch.
     kev = {n: [] for n in ("fwd", "dkdv", "dq")}
 

@@ -356,9 +356,8 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k
  * The backward as separate launches, for callers that schedule or time them
  * one by one. Calling preprocess, dkdv, dq and thdcp_zero_untouched in this
  * order on one stream computes the gradients cp_attn_bwd computes (which
- * folds the preprocess into its dQ launch and the zeroing into its dK/dV
- * launch); delta is summed in a different order there, so the two agree to
- * rounding, not bit for bit.
+ * folds the preprocess and the zeroing into its dQ launch); delta is summed
+ * in a different order there, so the two agree to rounding, not bit for bit.
  *   cp_attn_bwd_preprocess: delta[h, m] = sum_d dO[m,h,d] * O[m,h,d] (fp32,
  *     [H, n_local], into scratch).
  *   cp_attn_bwd_dkdv: the dK/dV partials (key-tile-major; written, or added
