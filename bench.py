@@ -75,7 +75,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build simulates every CP rank on a single "
+        print(f"bench.py measures one GPU only: the library simulates every CP rank on a single "
               f"device and has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
