@@ -642,22 +642,38 @@ def _kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def cpu_baseline(w, t):
+def cpu_baseline(w, t, min_seconds=10.0, max_run_seconds=20.0, nominal_tflops=0.07):
     """The fp64 oracle, as it stands, on the host cores: the same rank share's
-    forward + backward (every local row, every head), timed once."""
+    forward + backward, on a bounded sample. When one run of the whole share
+    would take more than max_run_seconds at the nominal rate, the sample keeps
+    every k-th local row and a prefix of the heads; the sample is then run
+    until min_seconds have passed (at least once), and the rate is the
+    sample's causal-masked FLOPs over the time."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle as O
     cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
-    t64 = {n: x.double().numpy() for n, x in t.items()}
     idx = O.partition_index(cup, w.T, w.cp_size, w.rank, w.strategy)
+    pairs_all = O.causal_pairs(cu, cup, w.T, idx)
+    est = 14.0 * w.D * w.H * pairs_all / (nominal_tflops * 1e12)
+    heads, step = w.H, 1
+    while est * (heads / w.H) / step > max_run_seconds and heads > 1:
+        heads = max(1, heads // 2)
+    while est * (heads / w.H) / step > max_run_seconds:
+        step *= 2
+    rows = np.arange(0, len(idx), step)
+    t64 = {n: x[:, :heads].double().numpy() for n, x in t.items()}
     ql, dol = t64["q"][idx], t64["do"][idx]
-    t0 = time.perf_counter()
-    O.attention_fwd(ql, t64["k"], t64["v"], idx, cu, cup, w.T)
-    O.attention_bwd(ql, t64["k"], t64["v"], dol, idx, cu, cup, w.T)
-    dt = time.perf_counter() - t0
-    pairs = O.causal_pairs(cu, cup, w.T, idx)
+    sel = None if step == 1 else rows
+    pairs = pairs_all if step == 1 else O.causal_pairs(cu, cup, w.T, idx[rows])
+    runs, dt = 0, 0.0
+    while runs == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        O.attention_fwd(ql, t64["k"], t64["v"], idx, cu, cup, w.T, rows=sel)
+        O.attention_bwd(ql, t64["k"], t64["v"], dol, idx, cu, cup, w.T, rows=sel)
+        dt += time.perf_counter() - t0
+        runs += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     cpu = "unknown"
     try:
@@ -668,13 +684,13 @@ def cpu_baseline(w, t):
                     break
     except OSError:
         pass
-    return {"value": round(14.0 * w.D * w.H * pairs / dt / 1e12, 6), "unit": "TFLOP/s",
+    what = (f"{w.name} rank-{w.rank} share, fwd+bwd, {len(rows)} of {len(idx)} local rows "
+            f"({'all' if step == 1 else f'every {step}th'}), {heads} of {w.H} heads")
+    return {"value": round(14.0 * w.D * heads * pairs * runs / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(threads), "kind": "oracle",
-            "sample": f"full {w.name} rank-{w.rank} share (fwd+bwd, {len(idx)} local rows, "
-                      f"{w.H} heads), fp64 numpy, one run of {dt:.2f} s",
+            "sample": f"{what}; fp64 numpy, {runs} runs in {dt:.1f} s",
             "seconds": round(dt, 3), "cpu_model": cpu,
             "affinity_cores": len(os.sched_getaffinity(0))}
-
 
 if __name__ == "__main__":
     main()
