@@ -6,21 +6,24 @@
 // query rows that are not real tokens are not listed, key rows past the tile
 // end are zeroed, and masked probabilities are selected to 0 (NaN-safe).
 //
-// gfx950 design: a workgroup of 8 waves (two per SIMD) owns 128 consecutive
-// keys of one document, 16 per wave, with K and V fragments in registers, and
-// walks the local query rows that attend them in blocks of 64. Query blocks
-// (Q, dO, LSE, delta) are double-buffered in LDS and the next block's global
-// loads are in flight while the current one is computed; one barrier per
-// block. Per block each wave computes with v_mfma_f32_16x16x32_bf16
-//   S = Q K^T, dP = dO V^T          (A = Q / dO rows from LDS, B = K / V regs)
+// gfx950 design: a workgroup of 4 waves owns 128 consecutive keys of one
+// document, 32 per wave (two 16-key blocks), with the K fragments in
+// registers and the V rows in LDS, and walks the local query rows that attend
+// them in blocks of 32. Query blocks (Q, dO, LSE, delta) are double-buffered
+// in LDS and the next block's global loads are in flight while the current
+// one is computed; one barrier per block. Per block each wave computes with
+// v_mfma_f32_16x16x32_bf16
+//   S = Q K^T, dP = dO V^T          (A = Q / dO rows from LDS, B = K regs / V LDS)
 //   P = exp(S - LSE), dS = P (dP - delta)
 //   dV += P^T dO, dK += dS^T Q       (accumulators stay in registers)
 // P and dS come out of the first products already in the A-operand layout of
 // the last two; their B operands (dO and Q, sliced by column) are transposing
-// LDS reads of the row-major tiles. 16-key waves keep the per-wave state at
-// ~230 registers, so two waves share each SIMD and hide each other's LDS and
-// exp latency (a 32-key, 4-wave variant needed ~400 registers and ran at one
-// wave per SIMD, 25-35% slower).
+// LDS reads of the row-major tiles. Every Q / dO fragment read from LDS feeds
+// both key blocks, so a wave reads 0.625 KB of LDS per MFMA (1 KB with 16 keys
+// per wave, which made the LDS as busy as the MFMA pipe). At <= 256 registers
+// per wave and ~75 KB of LDS per workgroup, two workgroups share a CU (two
+// waves per SIMD), and one workgroup's prologue and stores overlap the other's
+// block loop.
 #include <atomic>
 
 #include "device_common.h"
@@ -30,9 +33,9 @@ namespace thdcp {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 64;  // query rows per block (four 16-query M-blocks)
+constexpr int kBM = 32;  // query rows per block (two 16-query M-blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -44,12 +47,13 @@ struct BwdSmem {
   float dlt[2][kBM];
   int32_t ghi[2][kBM];  // last key a query row attends (g + wr); -1 past the row range
   int32_t glo[2][kBM];  // first key (g - wl); read only for non-causal bands
+  bf16 v[kWaves * 32 * P];  // the tile's V rows (wave w's keys at rows 32w..), pitch P
 };
 
 // BAND: the mask is a general band [g - wl, g + wr] (a lower-bound test
 // per element); otherwise it is causal (key <= g only).
 template <int D, bool BAND>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
 attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                      const bf16* __restrict__ k, const bf16* __restrict__ v,
                      const int32_t* __restrict__ kv_row, int32_t kv_sub, int32_t wl, int32_t wr,
@@ -58,10 +62,10 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
                      const float* __restrict__ delta, float* __restrict__ dk,
                      float* __restrict__ dv, int64_t n_local, float scale, float scale_log2,
                      int32_t accumulate) {
-  constexpr int KS = D / 32;                  // 16x16x32 k-steps over the head dim
-  constexpr int NB = D / 16;                  // 16-wide blocks of the head dim
-  constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  constexpr int CH = kBM * CPR / kThreads;    // chunks per thread per block and tensor
+  constexpr int KS = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int CH = kBM * CPR / kThreads;
   typedef BwdSmem<D> S;
   constexpr int P = S::P;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -72,8 +76,8 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   const BwdTile t = tiles[tile_id];
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int l16 = lane & 15;   // key column of S / dP; row of the dV / dK A operand
-  const int G = lane >> 4;     // 16-lane group: k-slot block and accumulator row block
+  const int l16 = lane & 15;
+  const int G = lane >> 4;
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = (int64_t)h * D;
 
@@ -84,25 +88,41 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   auto key_row = [&](int key) -> int64_t {
     return (int64_t)(kv_row ? kv_row[key] : key) - kv_sub;
   };
-  const int my_key = t.k0 + w * 16 + l16;
-  const bool key_ok = my_key < t.k1;
-  bf16x8 kf[KS], vf[KS];
-  {
-    const int64_t off = key_row(min(my_key, t.k1 - 1)) * rs + head_off + G * 8;
+  // Lane l16 of key block nk holds key t.k0 + 32w + 16nk + l16: the column of
+  // S / dP and the row of the dV / dK A operand.
+  int my_key[2];
+  bool key_ok[2];
+  bf16x8 kf[2][KS];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      kf[kk] = key_ok ? load_bf16x8(k + off + kk * 32) : zero_bf16x8();
-      vf[kk] = key_ok ? load_bf16x8(v + off + kk * 32) : zero_bf16x8();
-    }
+  for (int nk = 0; nk < 2; ++nk) {
+    my_key[nk] = t.k0 + w * 32 + nk * 16 + l16;
+    key_ok[nk] = my_key[nk] < t.k1;
+    const int64_t off = key_row(min(my_key[nk], t.k1 - 1)) * rs + head_off + G * 8;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      kf[nk][kk] = key_ok[nk] ? load_bf16x8(k + off + kk * 32) : zero_bf16x8();
   }
-  f32x4 dka[NB], dva[NB];
+  // V rows of this wave's 32 keys into LDS (only this wave reads them; rows
+  // past the tile end are 0): 32 rows x CPR 16-byte chunks over 64 lanes.
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int j = 0; j < 32 * CPR / 64; ++j) {
+    const int c = lane + j * 64;
+    const int rr = c / CPR, dc = c - rr * CPR;
+    const int key = t.k0 + w * 32 + rr;
+    const bf16x8 x = key < t.k1 ? load_bf16x8(v + key_row(key) * rs + head_off + dc * 8)
+                                : zero_bf16x8();
+    *reinterpret_cast<bf16x8*>(&sm.v[(w * 32 + rr) * P + dc * 8]) = x;
+  }
+  f32x4 dka[2][NB], dva[2][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dka[nb][i] = 0.f;
-      dva[nb][i] = 0.f;
-    }
+  for (int nk = 0; nk < 2; ++nk)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dka[nk][nb][i] = 0.f;
+        dva[nk][nb][i] = 0.f;
+      }
 
   // Per-thread staging slots: chunk c = threadIdx + j*kThreads is row c/CPR,
   // 16-byte column c%CPR of the query block.
@@ -148,7 +168,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
       *reinterpret_cast<u32x4*>(&sm.q[buf][soff[j]]) = qreg[j];
       *reinterpret_cast<u32x4*>(&sm.dO[buf][soff[j]]) = dreg[j];
     }
-    if (wave_uniform(w) == 0) {
+    if (wave_uniform(w) == 0 && lane < kBM) {
       sm.lse2[buf][lane] = lreg * kLog2e;
       sm.dlt[buf][lane] = dlreg;
       sm.ghi[buf][lane] = hreg;
@@ -159,7 +179,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   const int nblocks = (t.m_hi - t.m_lo + kBM - 1) / kBM;
   load_block(t.m_lo);
   store_block(0);
-  wait_vmem();  // K/V fragments have landed: the loop's MFMAs never wait on loads
+  wait_vmem();  // K fragments and V rows have landed: the loop's MFMAs never wait on loads
   __syncthreads();
 
   for (int it = 0; it < nblocks; ++it) {
@@ -168,27 +188,38 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     const bool has_next = it + 1 < nblocks;
     if (has_next) load_block(mb + kBM);
 
-    // S and dP for four 16-query M-blocks (rows = queries, column = my_key).
-    f32x4 s[4], dp[4];
+    // S and dP, [16-query M-block qm][key block nk]; element i of s[qm][nk] is
+    // query row qm*16 + 4*G + i, key my_key[nk].
+    f32x4 s[2][2], dp[2][2];
 #pragma unroll
-    for (int qm = 0; qm < 4; ++qm) {
+    for (int qm = 0; qm < 2; ++qm)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[qm][i] = 0.f;
-        dp[qm][i] = 0.f;
+      for (int nk = 0; nk < 2; ++nk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[qm][nk][i] = 0.f;
+          dp[qm][nk][i] = 0.f;
+        }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      bf16x8 vb[2];
+#pragma unroll
+      for (int nk = 0; nk < 2; ++nk)
+        vb[nk] = load_bf16x8(&sm.v[(w * 32 + nk * 16 + l16) * P + kk * 32 + G * 8]);
+#pragma unroll
+      for (int qm = 0; qm < 2; ++qm) {
+        const int o = (qm * 16 + l16) * P + kk * 32 + G * 8;
+        const bf16x8 aq = load_bf16x8(&sm.q[cur][o]);
+        const bf16x8 ad = load_bf16x8(&sm.dO[cur][o]);
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk) {
+          s[qm][nk] = mfma16(aq, kf[nk][kk], s[qm][nk]);
+          dp[qm][nk] = mfma16(ad, vb[nk], dp[qm][nk]);
+        }
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int qm = 0; qm < 4; ++qm) {
-        const int o = (qm * 16 + l16) * P + kk * 32 + G * 8;
-        s[qm] = mfma16(load_bf16x8(&sm.q[cur][o]), kf[kk], s[qm]);
-        dp[qm] = mfma16(load_bf16x8(&sm.dO[cur][o]), vf[kk], dp[qm]);
-      }
-    // Element i of s[qm]: query row qm*16 + 4*G + i, key my_key.
-#pragma unroll
-    for (int qm = 0; qm < 4; ++qm) {
+    for (int qm = 0; qm < 2; ++qm) {
       const int qr0 = qm * 16 + G * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
@@ -196,63 +227,69 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
       i32x4 lo4 = {0, 0, 0, 0};
       if constexpr (BAND) lo4 = *reinterpret_cast<const i32x4*>(&sm.glo[cur][qr0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bool ok = key_ok & (my_key <= hi4[i]);
-        if constexpr (BAND) ok &= my_key >= lo4[i];
-        const float p = ok ? fast_exp2(fmaf(s[qm][i], scale_log2, -l4[i])) : 0.f;
-        const float dsv = ok ? p * (dp[qm][i] - d4[i]) : 0.f;
-        s[qm][i] = p;
-        dp[qm][i] = dsv;
-      }
+      for (int nk = 0; nk < 2; ++nk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bool ok = key_ok[nk] & (my_key[nk] <= hi4[i]);
+          if constexpr (BAND) ok &= my_key[nk] >= lo4[i];
+          const float p = ok ? fast_exp2(fmaf(s[qm][nk][i], scale_log2, -l4[i])) : 0.f;
+          const float dsv = ok ? p * (dp[qm][nk][i] - d4[i]) : 0.f;
+          s[qm][nk][i] = p;
+          dp[qm][nk][i] = dsv;
+        }
     }
-    // dV += P^T dO and dK += dS^T Q. k-step ks covers the M-blocks 2ks and
-    // 2ks+1: slot j of this lane is query (2ks + j/4)*16 + 4*G + j%4, i.e.
-    // accumulator entries of s[2ks], s[2ks+1] (P needs no data movement).
-    // B operands (lane = head dim, slots = those queries) are two
-    // transposing reads each of the row-major dO and Q tiles.
+    // dV += P^T dO, dK += dS^T Q over the block's 32 queries (one k-step):
+    // slot j of this lane is query (j/4)*16 + 4*G + j%4. Each transposed dO
+    // / Q read feeds both key blocks.
+    bf16x8 pa[2], dsa[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pa = pack8(s[2 * ks], s[2 * ks + 1]);
-      const bf16x8 dsa = pack8(dp[2 * ks], dp[2 * ks + 1]);
-      const int o1 = (2 * ks * 16 + G * 4 + (l16 >> 2)) * P + 4 * (l16 & 3);
-      const int o2 = o1 + 16 * P;
+    for (int nk = 0; nk < 2; ++nk) {
+      pa[nk] = pack8(s[0][nk], s[1][nk]);
+      dsa[nk] = pack8(dp[0][nk], dp[1][nk]);
+    }
+    const int o1 = (G * 4 + (l16 >> 2)) * P + 4 * (l16 & 3);
+    const int o2 = o1 + 16 * P;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 bdo = concat4(lds_read_tr4(&sm.dO[cur][o1 + nb * 16]), lds_read_tr4(&sm.dO[cur][o2 + nb * 16]));
-        dva[nb] = mfma16(pa, bdo, dva[nb]);
-        const bf16x8 bq = concat4(lds_read_tr4(&sm.q[cur][o1 + nb * 16]), lds_read_tr4(&sm.q[cur][o2 + nb * 16]));
-        dka[nb] = mfma16(dsa, bq, dka[nb]);
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8 bdo = concat4(lds_read_tr4(&sm.dO[cur][o1 + nb * 16]), lds_read_tr4(&sm.dO[cur][o2 + nb * 16]));
+      dva[0][nb] = mfma16(pa[0], bdo, dva[0][nb]);
+      dva[1][nb] = mfma16(pa[1], bdo, dva[1][nb]);
+      const bf16x8 bq = concat4(lds_read_tr4(&sm.q[cur][o1 + nb * 16]), lds_read_tr4(&sm.q[cur][o2 + nb * 16]));
+      dka[0][nb] = mfma16(dsa[0], bq, dka[0][nb]);
+      dka[1][nb] = mfma16(dsa[1], bq, dka[1][nb]);
     }
     if (has_next) store_block(cur ^ 1);
     __syncthreads();
   }
 
   // dK (scaled) and dV rows of this wave's keys; lane holds head dim nb*16 + l16
-  // for keys 4*G + i of the wave's 16.
-  int64_t out_row[4];
+  // for keys 16*nk + 4*G + i of the wave's 32.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = t.k0 + w * 16 + G * 4 + i;
-    out_row[i] = key < t.k1 ? key_row(key) : -1;
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nk = 0; nk < 2; ++nk) {
+    int64_t out_row[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (out_row[i] >= 0) {
-        const int64_t off = out_row[i] * rs + head_off + nb * 16 + l16;
-        const float kval = dka[nb][i] * scale;
-        const float vval = dva[nb][i];
-        if (accumulate) {
-          dk[off] += kval;
-          dv[off] += vval;
-        } else {
-          dk[off] = kval;
-          dv[off] = vval;
+      const int key = t.k0 + w * 32 + nk * 16 + G * 4 + i;
+      out_row[i] = key < t.k1 ? key_row(key) : -1;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (out_row[i] >= 0) {
+          const int64_t off = out_row[i] * rs + head_off + nb * 16 + l16;
+          const float kval = dka[nk][nb][i] * scale;
+          const float vval = dva[nk][nb][i];
+          if (accumulate) {
+            dk[off] += kval;
+            dv[off] += vval;
+          } else {
+            dk[off] = kval;
+            dv[off] = vval;
+          }
         }
       }
-    }
+  }
 }
 
 template <int D, bool BAND>
