@@ -249,12 +249,21 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     }
     const int o1 = (G * 4 + (l16 >> 2)) * P + 4 * (l16 & 3);
     const int o2 = o1 + 16 * P;
+    auto read_b = [&](const bf16* tile, int nb) {
+      return concat4(lds_read_tr4(tile + o1 + nb * 16), lds_read_tr4(tile + o2 + nb * 16));
+    };
+    // The B operands of head-dim block nb + 1 are read while block nb's MFMAs
+    // run (without it every MFMA pair waited on its own reads; -3..-6%).
+    bf16x8 bdo_next = read_b(sm.dO[cur], 0), bq_next = read_b(sm.q[cur], 0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 bdo = concat4(lds_read_tr4(&sm.dO[cur][o1 + nb * 16]), lds_read_tr4(&sm.dO[cur][o2 + nb * 16]));
+      const bf16x8 bdo = bdo_next, bq = bq_next;
+      if (nb + 1 < NB) {
+        bdo_next = read_b(sm.dO[cur], nb + 1);
+        bq_next = read_b(sm.q[cur], nb + 1);
+      }
       dva[0][nb] = mfma16(pa[0], bdo, dva[0][nb]);
       dva[1][nb] = mfma16(pa[1], bdo, dva[1][nb]);
-      const bf16x8 bq = concat4(lds_read_tr4(&sm.q[cur][o1 + nb * 16]), lds_read_tr4(&sm.q[cur][o2 + nb * 16]));
       dka[0][nb] = mfma16(dsa[0], bq, dka[0][nb]);
       dka[1][nb] = mfma16(dsa[1], bq, dka[1][nb]);
     }
