@@ -254,6 +254,9 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     };
     // The B operands of head-dim block nb + 1 are read while block nb's MFMAs
     // run (without it every MFMA pair waited on its own reads; -3..-6%).
+    // Raised wave priority over these products lets this wave's MFMAs issue
+    // ahead of the softmax of the other workgroup's wave on the SIMD.
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 bdo_next = read_b(sm.dO[cur], 0), bq_next = read_b(sm.q[cur], 0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -267,6 +270,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
       dka[0][nb] = mfma16(dsa[0], bq, dka[0][nb]);
       dka[1][nb] = mfma16(dsa[1], bq, dka[1][nb]);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (has_next) store_block(cur ^ 1);
     __syncthreads();
   }
