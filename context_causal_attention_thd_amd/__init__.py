@@ -236,6 +236,7 @@ def gather(src, idx, out=None, stream=None):
     rb = _row_bytes(src)
     if _row_bytes(out) != rb:
         raise ValueError("src and out rows differ in size")
+    _idx_rows(idx, out.shape[0], "out")
     _check(lib().thd_gather(_dev_ptr(src, "src"), src.shape[0], _dev_ptr(idx, "idx", torch.int32),
                             idx.shape[0], rb, _dev_ptr(out, "out"), _stream(stream)))
     return out
@@ -247,10 +248,20 @@ def scatter(src, idx, out, stream=None):
     rb = _row_bytes(src)
     if _row_bytes(out) != rb:
         raise ValueError("src and out rows differ in size")
+    _idx_rows(idx, src.shape[0], "src")
     _check(lib().thd_scatter(_dev_ptr(src, "src"), src.shape[0],
                              _dev_ptr(idx, "idx", torch.int32), rb, _dev_ptr(out, "out"),
                              out.shape[0], _stream(stream)))
     return out
+
+
+def _idx_rows(idx, rows: int, name: str):
+    """The index is 1-D with one entry per row of ``name`` (the gather's
+    output or the scatter's input): the kernel walks idx.shape[0] rows of it."""
+    if idx.dim() != 1:
+        raise ValueError(f"idx must be 1-D, got shape {tuple(idx.shape)}")
+    if idx.shape[0] != rows:
+        raise ValueError(f"idx has {idx.shape[0]} entries but {name} has {rows} rows")
 
 
 def _ptr_list(ts, name):
@@ -271,6 +282,8 @@ def gather_many(srcs, idx, outs=None, stream=None):
         raise ValueError("all rows must have the same size")
     if any(x.shape[0] != srcs[0].shape[0] for x in srcs):
         raise ValueError("all sources must have the same number of rows")
+    for i, x in enumerate(outs):
+        _idx_rows(idx, x.shape[0], f"outs[{i}]")
     _check(lib().thd_gather_batched(len(srcs), _ptr_list(srcs, "src"), srcs[0].shape[0],
                                     _dev_ptr(idx, "idx", torch.int32), idx.shape[0], rb,
                                     _ptr_list(outs, "out"), _stream(stream)))
@@ -285,6 +298,8 @@ def scatter_many(srcs, idx, outs, stream=None):
         raise ValueError("all rows must have the same size")
     if any(x.shape[0] != outs[0].shape[0] for x in outs):
         raise ValueError("all destinations must have the same number of rows")
+    for i, x in enumerate(srcs):
+        _idx_rows(idx, x.shape[0], f"srcs[{i}]")
     _check(lib().thd_scatter_batched(len(srcs), _ptr_list(srcs, "src"), srcs[0].shape[0],
                                      _dev_ptr(idx, "idx", torch.int32), rb,
                                      _ptr_list(outs, "out"), outs[0].shape[0], _stream(stream)))
@@ -421,18 +436,15 @@ class Plan:
 def attn_fwd(plan: Plan, q_local, k, v, o=None, lse=None, stream=None):
     """O bf16 [n_local,H,D] and LSE fp32 [H,n_local]."""
     import torch
-    n, H, D = plan.n_local, plan.H, plan.D
-    _shape(q_local, (n, H, D), "q_local")
-    _shape(k, (plan.T, H, D), "k")
-    _shape(v, (plan.T, H, D), "v")
+    n, H, D, T = plan.n_local, plan.H, plan.D, plan.T
     if o is None:
         o = torch.empty((n, H, D), dtype=torch.bfloat16, device=q_local.device)
     if lse is None:
         lse = torch.empty((H, n), dtype=torch.float32, device=q_local.device)
-    _check(lib().cp_attn_fwd(plan.handle, _dev_ptr(q_local, "q_local", torch.bfloat16),
-                             _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
-                             _dev_ptr(o, "o", torch.bfloat16), _dev_ptr(lse, "lse", torch.float32),
-                             _stream(stream)))
+    bf, f32 = torch.bfloat16, torch.float32
+    ptrs = _args((q_local, (n, H, D), bf, "q_local"), (k, (T, H, D), bf, "k"),
+                 (v, (T, H, D), bf, "v"), (o, (n, H, D), bf, "o"), (lse, (H, n), f32, "lse"))
+    _check(lib().cp_attn_fwd(plan.handle, *ptrs, _stream(stream)))
     return o, lse
 
 
@@ -443,7 +455,6 @@ def attn_bwd(plan: Plan, q_local, k, v, o, lse, d_o, dq=None, dk=None, dv=None,
     import torch
     n, H, D, T = plan.n_local, plan.H, plan.D, plan.T
     dev = q_local.device
-    _shape(d_o, (n, H, D), "d_o")
     if dq is None:
         dq = torch.empty((n, H, D), dtype=torch.float32, device=dev)
     if dk is None:
@@ -455,16 +466,25 @@ def attn_bwd(plan: Plan, q_local, k, v, o, lse, d_o, dq=None, dk=None, dv=None,
     need = int(plan.info.bwd_scratch_bytes)
     if scratch is None:
         scratch = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check(lib().cp_attn_bwd(plan.handle, _dev_ptr(q_local, "q_local", torch.bfloat16),
-                             _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
-                             _dev_ptr(o, "o", torch.bfloat16),
-                             _dev_ptr(lse, "lse", torch.float32),
-                             _dev_ptr(d_o, "d_o", torch.bfloat16),
-                             _dev_ptr(dq, "dq", torch.float32), _dev_ptr(dk, "dk", torch.float32),
-                             _dev_ptr(dv, "dv", torch.float32), int(bool(zero_untouched)),
-                             int(bool(accumulate_dkv)), _dev_ptr(scratch, "scratch"),
+    q_p, k_p, v_p, lse_p, do_p, o_p, dq_p, dk_p, dv_p = _bwd_ptrs(
+        plan, q_local, k, v, lse, d_o, o, dq, dk, dv)
+    _check(lib().cp_attn_bwd(plan.handle, q_p, k_p, v_p, o_p, lse_p, do_p, dq_p, dk_p, dv_p,
+                             int(bool(zero_untouched)), int(bool(accumulate_dkv)),
+                             _dev_ptr(scratch, "scratch"),
                              scratch.numel() * scratch.element_size(), _stream(stream)))
     return dq, dk, dv
+
+
+def _bwd_ptrs(plan: Plan, q_local, k, v, lse, d_o, o, dq, dk, dv):
+    """Checked pointers of a backward call's tensors, in this order."""
+    import torch
+    n, H, D, T = plan.n_local, plan.H, plan.D, plan.T
+    bf, f32 = torch.bfloat16, torch.float32
+    return _args((q_local, (n, H, D), bf, "q_local"), (k, (T, H, D), bf, "k"),
+                 (v, (T, H, D), bf, "v"), (lse, (H, n), f32, "lse"),
+                 (d_o, (n, H, D), bf, "d_o"), (o, (n, H, D), bf, "o"),
+                 (dq, (n, H, D), f32, "dq"), (dk, (T, H, D), f32, "dk"),
+                 (dv, (T, H, D), f32, "dv"))
 
 
 def attn_bwd_parts(plan: Plan, q_local, k, v, o, lse, d_o, dq, dk, dv, scratch,
@@ -475,41 +495,37 @@ def attn_bwd_parts(plan: Plan, q_local, k, v, o, lse, d_o, dq, dk, dv, scratch,
     two kernels."""
     import torch
     L = lib()
+    ptrs = _bwd_ptrs(plan, q_local, k, v, lse, d_o, o, dq, dk, dv)
+    args, (o_p, dq_p, dk_p, dv_p) = ptrs[:5], ptrs[5:]
     st = _stream(stream)
     nbytes = scratch.numel() * scratch.element_size()
     sp = _dev_ptr(scratch, "scratch")
-    _check(L.cp_attn_bwd_preprocess(plan.handle, _dev_ptr(o, "o", torch.bfloat16),
-                                    _dev_ptr(lse, "lse", torch.float32),
-                                    _dev_ptr(d_o, "d_o", torch.bfloat16), sp, nbytes, st))
-    args = (_dev_ptr(q_local, "q_local", torch.bfloat16), _dev_ptr(k, "k", torch.bfloat16),
-            _dev_ptr(v, "v", torch.bfloat16), _dev_ptr(lse, "lse", torch.float32),
-            _dev_ptr(d_o, "d_o", torch.bfloat16))
+    _check(L.cp_attn_bwd_preprocess(plan.handle, o_p, args[3], args[4], sp, nbytes, st))
     ev = events or {}
     if "dkdv" in ev:
         ev["dkdv"][0].record()
-    _check(L.cp_attn_bwd_dkdv(plan.handle, *args, _dev_ptr(dk, "dk", torch.float32),
-                              _dev_ptr(dv, "dv", torch.float32), int(bool(accumulate_dkv)), sp,
+    _check(L.cp_attn_bwd_dkdv(plan.handle, *args, dk_p, dv_p, int(bool(accumulate_dkv)), sp,
                               nbytes, st))
     if "dkdv" in ev:
         ev["dkdv"][1].record()
     if "dq" in ev:
         ev["dq"][0].record()
-    _check(L.cp_attn_bwd_dq(plan.handle, *args, _dev_ptr(dq, "dq", torch.float32), sp, nbytes,
-                            st))
+    _check(L.cp_attn_bwd_dq(plan.handle, *args, dq_p, sp, nbytes, st))
     if "dq" in ev:
         ev["dq"][1].record()
     if zero_untouched:
-        _check(L.thdcp_zero_untouched(plan.handle, _dev_ptr(dk, "dk", torch.float32),
-                                      _dev_ptr(dv, "dv", torch.float32), st))
+        _check(L.thdcp_zero_untouched(plan.handle, dk_p, dv_p, st))
     return dq, dk, dv
 
 
 def bwd_preprocess(plan: Plan, o, lse, d_o, scratch, stream=None):
     """delta = rowsum(O * dO) into ``scratch`` (cp_attn_bwd_preprocess)."""
     import torch
-    _check(lib().cp_attn_bwd_preprocess(plan.handle, _dev_ptr(o, "o", torch.bfloat16),
-                                        _dev_ptr(lse, "lse", torch.float32),
-                                        _dev_ptr(d_o, "d_o", torch.bfloat16),
+    n, H, D = plan.n_local, plan.H, plan.D
+    _check(lib().cp_attn_bwd_preprocess(plan.handle,
+                                        *_args((o, (n, H, D), torch.bfloat16, "o"),
+                                               (lse, (H, n), torch.float32, "lse"),
+                                               (d_o, (n, H, D), torch.bfloat16, "d_o")),
                                         _dev_ptr(scratch, "scratch"),
                                         scratch.numel() * scratch.element_size(),
                                         _stream(stream)))
@@ -580,6 +596,8 @@ def attn_fwd_step(plan: Plan, src_rank: int, q_local, k_src, v_src, o_part=None,
         o_part = torch.empty((n, H, D), dtype=torch.bfloat16, device=dev)
     if lse_part is None:
         lse_part = torch.empty((H, n), dtype=torch.float32, device=dev)
+    _shape(o_part, (n, H, D), "o_part")
+    _shape(lse_part, (H, n), "lse_part")
     _check(lib().cp_attn_fwd_step(plan.handle, int(src_rank),
                                   _dev_ptr(q_local, "q_local", torch.bfloat16),
                                   _dev_ptr(k_src, "k_src", torch.bfloat16),
@@ -641,8 +659,11 @@ def attn_bwd_step(plan: Plan, src_rank: int, q_local, k_src, v_src, lse, d_o, sc
     rank src_rank's local order."""
     import torch
     n, H, D = plan.n_local, plan.H, plan.D
+    _shape(q_local, (n, H, D), "q_local")
     _shape(k_src, (n, H, D), "k_src")
     _shape(v_src, (n, H, D), "v_src")
+    _shape(lse, (H, n), "lse")
+    _shape(d_o, (n, H, D), "d_o")
     _shape(dq, (n, H, D), "dq")
     dev = q_local.device
     mk = torch.empty if zero_untouched else torch.zeros
@@ -670,3 +691,14 @@ def attn_bwd_step(plan: Plan, src_rank: int, q_local, k_src, v_src, lse, d_o, sc
 def _shape(t, shape: Sequence[int], name: str):
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _args(*specs):
+    """Device pointers of tensor arguments given as (tensor, shape, dtype,
+    name): every shape is checked first (ValueError), then dtype, device and
+    contiguity (TypeError / ValueError). The C ABI takes raw pointers with no
+    sizes, so an undersized buffer must be refused here, before a kernel
+    writes past its end."""
+    for t, shape, _, name in specs:
+        _shape(t, shape, name)
+    return tuple(_dev_ptr(t, name, dtype) for t, _, dtype, name in specs)

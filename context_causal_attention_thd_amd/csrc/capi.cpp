@@ -631,6 +631,11 @@ thdcp_status_t thd_partition_index(const int32_t* cup_host, const int32_t* cup_d
   if (T % cp_size != 0) return fail(THDCP_ERR_LAYOUT, "T is not divisible by cp_size");
   if (strategy != THDCP_DUAL_CHUNK_SWAP && strategy != THDCP_NO_LOAD_BALANCE)
     return fail(THDCP_ERR_ARG, "unknown strategy %d", strategy);
+  // Checked on every call (no host data needed): DUAL_CHUNK_SWAP cuts
+  // documents into chunks, so rows with no document at all cannot be placed.
+  if (strategy == THDCP_DUAL_CHUNK_SWAP && B == 0 && T > 0)
+    return fail(THDCP_ERR_LAYOUT, "DUAL_CHUNK_SWAP with no documents needs T == 0 (got %lld)",
+                (long long)T);
   if (cup_host) {
     thdcp_status_t st = check_layout(nullptr, cup_host, B, T, cp_size, rank < 0 ? 0 : rank,
                                      strategy, -1, 0, -1, nullptr);
@@ -826,36 +831,63 @@ namespace {
 // idle GPU time per upload on MI355X, the largest gap in a dcs_8k step. The
 // plan is instead copied into a page-locked slot on the host and moved into
 // the workspace by a small copy kernel on the same stream, which reads the
-// slot over the host link. One ring per process, allocated on first use and
-// kept until exit (never freed while a copy may read it). Each upload takes
-// the next slot; an event recorded after its copy says when the slot may be
-// refilled, which is normally long done (the host would have to run kSlots
-// uploads ahead of the GPU to wait on it).
+// slot over the host link. Slots live until the process exits (never freed
+// while a copy may read them). Each upload takes a slot whose last copy has
+// finished, found with non-blocking event queries; when every slot is still
+// in use (the host is that many uploads ahead of the GPU) a new block of
+// slots is allocated, up to kMaxSlots. Only past that does an upload wait for
+// the oldest slot's copy.
 class StagingRing {
  public:
   static constexpr size_t kSlotBytes = size_t(1) << 20;
-  static constexpr int kSlots = 16;
+  static constexpr int kBlockSlots = 16;
+  static constexpr int kMaxSlots = 64;
 
   // Enqueues the copy of n bytes at src to dst on stream. Returns false (and
   // enqueues nothing) when the ring cannot take it: n above a slot, or the
-  // page-locked allocation failed; the caller then copies directly.
+  // first page-locked allocation failed; the caller then copies directly.
   bool upload(void* dst, const void* src, size_t n, hipStream_t stream, hipError_t* err) {
     if (n > kSlotBytes) return false;
     std::lock_guard<std::mutex> lock(mu_);
-    if (!ready_ && !init()) return false;
-    Slot& sl = slots_[next_];
-    next_ = (next_ + 1) % kSlots;
-    if (sl.pending) {
-      *err = hipEventSynchronize(sl.ev);
-      if (*err != hipSuccess) return true;
-      sl.pending = false;
+    if (slots_.empty() && !grow()) return false;
+    Slot* sl = nullptr;
+    const size_t count = slots_.size();
+    for (size_t i = 0; i < count && !sl; ++i) {  // round robin from the last used slot
+      Slot& c = slots_[(next_ + i) % count];
+      if (c.pending) {
+        const hipError_t q = hipEventQuery(c.ev);
+        if (q == hipErrorNotReady) continue;
+        if (q != hipSuccess) {
+          *err = q;
+          return true;
+        }
+        c.pending = false;
+      }
+      sl = &c;
+      next_ = (next_ + i + 1) % count;
     }
-    memcpy(sl.host, src, n);
-    *err = launch_copy16(sl.dev, dst, (int64_t)n, stream);
+    if (!sl && count < (size_t)kMaxSlots && grow()) {
+      sl = &slots_[count];  // the first slot of the new block
+      next_ = (count + 1) % slots_.size();
+    }
+    if (!sl) {  // kMaxSlots copies in flight: wait for the oldest
+      sl = &slots_[next_];
+      next_ = (next_ + 1) % count;
+      *err = hipEventSynchronize(sl->ev);
+      if (*err != hipSuccess) return true;
+      sl->pending = false;
+    }
+    memcpy(sl->host, src, n);
+    *err = launch_copy16(sl->dev, dst, (int64_t)n, stream);
     if (*err != hipSuccess) return true;
-    *err = hipEventRecord(sl.ev, stream);
-    sl.pending = *err == hipSuccess;
+    *err = hipEventRecord(sl->ev, stream);
+    sl->pending = *err == hipSuccess;
     return true;
+  }
+
+  size_t slots() {
+    std::lock_guard<std::mutex> lock(mu_);
+    return slots_.size();
   }
 
  private:
@@ -866,35 +898,38 @@ class StagingRing {
     bool pending = false;
   };
 
-  bool init() {
+  // One more block of kBlockSlots slots; false (and the ring unchanged) if
+  // an allocation fails. A block that fails half way stays allocated.
+  bool grow() {
     if (failed_) return false;
     char* base = nullptr;
-    if (hipHostMalloc(reinterpret_cast<void**>(&base), kSlotBytes * kSlots,
+    if (hipHostMalloc(reinterpret_cast<void**>(&base), kSlotBytes * kBlockSlots,
                       hipHostMallocPortable | hipHostMallocMapped) != hipSuccess) {
-      failed_ = true;
+      failed_ = slots_.empty();
       return false;
     }
     void* dbase = nullptr;
     if (hipHostGetDevicePointer(&dbase, base, 0) != hipSuccess) {
-      failed_ = true;  // the page-locked block stays allocated until exit
+      failed_ = slots_.empty();
       return false;
     }
-    for (int i = 0; i < kSlots; ++i) {
-      slots_[i].host = base + i * kSlotBytes;
-      slots_[i].dev = static_cast<const char*>(dbase) + i * kSlotBytes;
-      if (hipEventCreateWithFlags(&slots_[i].ev, hipEventDisableTiming) != hipSuccess) {
-        failed_ = true;  // the page-locked block stays allocated until exit
+    std::vector<Slot> block(kBlockSlots);
+    for (int i = 0; i < kBlockSlots; ++i) {
+      block[i].host = base + i * kSlotBytes;
+      block[i].dev = static_cast<const char*>(dbase) + i * kSlotBytes;
+      if (hipEventCreateWithFlags(&block[i].ev, hipEventDisableTiming) != hipSuccess) {
+        failed_ = slots_.empty();
         return false;
       }
     }
-    ready_ = true;
+    slots_.insert(slots_.end(), block.begin(), block.end());
     return true;
   }
 
   std::mutex mu_;
-  Slot slots_[kSlots];
-  int next_ = 0;
-  bool ready_ = false, failed_ = false;
+  std::vector<Slot> slots_;
+  size_t next_ = 0;
+  bool failed_ = false;
 };
 
 StagingRing& staging_ring() {

@@ -14,8 +14,9 @@
  *     frees or keeps device memory; the plan's device tables and the backward
  *     scratch live in caller-provided workspaces whose sizes the plan reports.
  *   - "stream" is a hipStream_t passed as void* (NULL = the default stream).
- *     Device work is only enqueued on it; no call synchronizes with the
- *     device or copies device memory back to the host.
+ *     Device work is only enqueued on it; no call copies device memory back
+ *     to the host, and none synchronizes with the device except
+ *     thdcp_plan_upload when 64 earlier uploads are still queued (see there).
  *   - Tensors are row-major THD [rows, H, D] with D contiguous (bshd with
  *     batch 1 is the same memory as THD with one document). Q/K/V/O/dO are
  *     bfloat16; LSE, the backward scratch and dQ/dK/dV are float32.
@@ -111,9 +112,12 @@ thdcp_status_t thdcp_validate(const int32_t* cu_seqlens_host,
  * rank == -1 writes every rank's indices rank-major (int32 [T]): the
  * permutation that restores an all-gathered buffer to global order.
  * cu_seqlens_padded_host (nullable) is used only to validate; the kernel reads
- * cu_seqlens_padded_dev (int32 [B+1], device). Without the host copy the
- * caller guarantees the layout rules of thdcp_validate; the kernel then still
- * stays inside its buffers.
+ * cu_seqlens_padded_dev (int32 [B+1], device). Without the host copy the call
+ * is not validated against the layout rules of thdcp_validate: it checks only
+ * what needs no host data (sizes, rank, strategy, and DUAL_CHUNK_SWAP with
+ * B == 0 and T > 0), and the caller guarantees the rest. A device array that
+ * breaks them gives wrong indices with no error, but the kernel still stays
+ * inside its buffers.
  */
 THDCP_API
 thdcp_status_t thd_partition_index(const int32_t* cu_seqlens_padded_host,
@@ -290,9 +294,13 @@ thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
  * workspace on one stream (or order them). The copy covers the tables and
  * counters only.
  * Tables up to 1 MiB are first copied into a page-locked staging slot the
- * library keeps for the life of the process (16 slots, 16 MiB, allocated on
- * the first upload); larger ones are copied from the plan itself, which must
- * then outlive the copy. */
+ * library keeps for the life of the process (1 MiB each, allocated 16 at a
+ * time: 16 on the first upload, 16 more whenever every slot still feeds a
+ * copy the GPU has not run, up to 64 slots), so the plan may be destroyed
+ * right after this call. Like every other call it does not wait for the
+ * device, with one exception: when 64 uploads are still queued on the GPU,
+ * the next one waits until the oldest of them has run. Larger tables are
+ * copied from the plan itself, which must then outlive the copy. */
 THDCP_API
 thdcp_status_t thdcp_plan_upload(thdcp_plan_t plan, void* workspace_dev, size_t bytes,
                                  void* stream);

@@ -336,3 +336,76 @@ def test_plan_split_walks(L):
         plan("dcs_8k", max_key_splits=-1)
     for p in (forced, never, doc, dcs, one):
         p.close()
+
+
+def test_partition_index_device_only_checks(L):
+    # With no host copy of cu_seqlens_padded the call still refuses what needs
+    # no host data: DUAL_CHUNK_SWAP with no documents but T > 0 cannot place
+    # any row. The pointers are never dereferenced on an error path.
+    dummy = ctypes.c_void_p(256)
+    st = L.thd_partition_index(None, dummy, 0, 64, 2, 0, thd.DUAL_CHUNK_SWAP, dummy, None)
+    assert st == 2  # THDCP_ERR_LAYOUT
+    assert b"DUAL_CHUNK_SWAP" in L.thdcp_last_error()
+    # NO_LOAD_BALANCE with no documents is a valid all-tail layout; cp_size and
+    # rank are still checked.
+    st = L.thd_partition_index(None, dummy, 0, 64, 2, 5, thd.NO_LOAD_BALANCE, dummy, None)
+    assert st == 1  # THDCP_ERR_ARG
+
+
+def test_binding_refuses_wrong_shapes(L):
+    # The C ABI takes raw pointers with no sizes, so the binding checks every
+    # tensor argument's shape before a pointer crosses it (an undersized
+    # buffer would be written past its end). Shapes are checked before the
+    # device, so CPU tensors show the refusal without a GPU.
+    import torch
+    w = W.WORKLOADS["tiny_nlb"]
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    plan = thd.Plan(cu, cup, w.T, w.cp_size, 0, w.strategy, w.H, w.D, upload=False)
+    n, H, D, T = plan.n_local, w.H, w.D, w.T
+    bf, f32 = torch.bfloat16, torch.float32
+    ok = dict(q_local=torch.zeros(n, H, D, dtype=bf), k=torch.zeros(T, H, D, dtype=bf),
+              v=torch.zeros(T, H, D, dtype=bf), o=torch.zeros(n, H, D, dtype=bf),
+              lse=torch.zeros(H, n, dtype=f32), d_o=torch.zeros(n, H, D, dtype=bf),
+              dq=torch.zeros(n, H, D, dtype=f32), dk=torch.zeros(T, H, D, dtype=f32),
+              dv=torch.zeros(T, H, D, dtype=f32))
+    bad = dict(q_local=(n + 1, H, D), k=(T - 1, H, D), v=(T, H + 1, D), o=(n, H, D - 8),
+               lse=(n, H), d_o=(n - 1, H, D), dq=(n, H, D + 8), dk=(n, H, D), dv=(T - 1, H, D))
+    scratch = torch.zeros(4096, dtype=torch.uint8)
+
+    def fwd(a):
+        return thd.attn_fwd(plan, a["q_local"], a["k"], a["v"], o=a["o"], lse=a["lse"])
+
+    def bwd(a):
+        return thd.attn_bwd(plan, a["q_local"], a["k"], a["v"], a["o"], a["lse"], a["d_o"],
+                            dq=a["dq"], dk=a["dk"], dv=a["dv"], scratch=scratch)
+
+    def parts(a):
+        return thd.attn_bwd_parts(plan, a["q_local"], a["k"], a["v"], a["o"], a["lse"],
+                                  a["d_o"], a["dq"], a["dk"], a["dv"], scratch)
+
+    def prep(a):
+        return thd.bwd_preprocess(plan, a["o"], a["lse"], a["d_o"], scratch)
+
+    uses = {fwd: ("q_local", "k", "v", "o", "lse"),
+            bwd: tuple(ok), parts: tuple(ok), prep: ("o", "lse", "d_o")}
+    for fn, names in uses.items():
+        for name in names:
+            args = dict(ok)
+            args[name] = torch.zeros(bad[name], dtype=ok[name].dtype)
+            with pytest.raises(ValueError, match=name):
+                fn(args)
+        # right shapes, wrong device: refused as well (never a host pointer)
+        with pytest.raises(TypeError):
+            fn(ok)
+    idx = torch.zeros(10, dtype=torch.int32)
+    with pytest.raises(ValueError, match="idx"):
+        thd.gather(torch.zeros(20, 8), idx, out=torch.zeros(9, 8))
+    with pytest.raises(ValueError, match="idx"):
+        thd.scatter(torch.zeros(11, 8), idx, torch.zeros(20, 8))
+    with pytest.raises(ValueError, match="idx"):
+        thd.gather_many([torch.zeros(20, 8)], idx, [torch.zeros(12, 8)])
+    with pytest.raises(ValueError, match="idx"):
+        thd.scatter_many([torch.zeros(8, 8)], idx, [torch.zeros(20, 8)])
+    with pytest.raises(ValueError, match="1-D"):
+        thd.gather(torch.zeros(20, 8), idx.view(2, 5), out=torch.zeros(2, 8))
+    plan.close()
