@@ -12,21 +12,25 @@ A step is one pass of the whole hot path for the measured rank over one batch:
     gated zeroing of untouched dK/dV rows), then dK/dV; the dK/dV stores go
     straight to rank-major order for the reduce-scatter (the unrestore fused
     the same way).
-Inputs are synthetic and already resident in HBM when timing starts. The
-standalone K+V restore (one batched gather launch over all T rows) is timed
-separately for the gather roofline.
+Inputs are synthetic and already resident in HBM when timing starts.
 
+The headline workload (default flat_75k: the post-exchange share of one
+75600-token sequence, 5 heads of 128, the largest of the five) gives
 value = 14 * D * H * causal_pairs / step time (TFLOP/s; masked-in FLOPs only),
 the steps timed with no events inside. A second pass puts an event pair around
-each step (mean / median / p90 of the step). A third pass runs the same steps
-with the backward as its separate launches (preprocess, dK/dV, dQ, gated
-zeroing) and an event pair around each attention kernel: those in-step
-durations give the roofline object of the dominant kernel, the backward dK/dV
-kernel (8 * D * H * pairs algorithmic FLOPs: S, dP, dV, dK), and the dQ and
-forward figures beside it. The standalone K+V restore (the gather roofline,
-warm and cold) and the plan upload are timed apart, after the steps.
+each step (mean / median / p90). A third pass runs the same steps with the
+backward as its separate launches (preprocess, dK/dV, dQ, gated zeroing) and
+an event pair around each attention kernel: from those in-step durations the
+"roofline" object names the step's longest kernel with its own algorithmic
+work (forward 4, dK/dV 8, dQ 2 x D x H x pairs FLOPs; the dQ kernel's S and
+dP recompute is reported beside it as executed work), and the other kernels'
+figures sit beside it. The standalone K+V restore (warm and cold) and the plan
+upload are timed apart. "configs" holds the same block for each of the other
+four workloads, measured in the same run; "cpu_baseline" times the fp64
+oracle on a bounded sample of the headline share on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload dcs_8k] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload flat_75k] [--no-cpu-baseline]
+    python bench.py --gather-only --workload dcs_8k --steps 40   # gather launches alone
 """
 from __future__ import annotations
 
@@ -50,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="dcs_8k")
+    ap.add_argument("--workload", default="flat_75k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window", type=int, nargs=2, default=(-1, 0), metavar=("LEFT", "RIGHT"),
                     help="attention window of the timed step: real keys at document "
@@ -64,8 +68,11 @@ def parse():
                     help="skip the P2P (ring) step measurement")
     ap.add_argument("--no-a2a", action="store_true",
                     help="skip the all-to-all layout measurement (flat vs dual-chunk)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="HBM bytes per launch measured with rocprofv3 --pmc (optional)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload blocks of the other four workloads")
+    ap.add_argument("--gather-only", action="store_true",
+                    help="time only the workload's restore gather (--steps launches, cold); "
+                         "for a rocprofv3 kernel trace of the gather alone")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 512 MiB device copy (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -80,14 +87,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import context_causal_attention_thd_amd as thd
     import workloads as W
 
     thd.lib()
-    w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -99,8 +104,94 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    if args.gather_only:
+        print(json.dumps(gather_only(W.WORKLOADS[args.workload], stream, args.steps)), flush=True)
+        return
+
+    w = W.WORKLOADS[args.workload]
     t = W.bf16_tensors(w)
+    block = measure_workload(w, t, args, dev, stream, args.steps, args.warmup,
+                             tuple(args.window), args.max_key_splits)
+    head = block.pop("_head")
+    result = {
+        "metric": METRIC,
+        "value": block["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": block["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"],
+    }
+    result.update(block)
+    # Side measurements, each on a clean allocator cache: a block that frees
+    # gigabytes of buffers (mask_variants) left the P2P ring's Python loop up
+    # to 3x slower afterwards, with every kernel and phase of it unchanged.
+    q, k, v, do, cup_dev = head["tensors"]
+    ms_step, flops, reps = block["ms_per_step"], head["flops"], head["reps"]
+    del head
+
+    def fresh():
+        import gc
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    window = tuple(args.window)
+    if w.cp_size > 1 and not args.no_p2p and window == (-1, 0):
+        fresh()
+        result["p2p_ring"] = p2p_ring(w, q, k, v, do, cup_dev, stream, args.warmup, args.steps,
+                                      reps, flops, ms_step)
+    del q, k, v, do, cup_dev
+    if not args.no_masks:
+        fresh()
+        result["mask_variants"] = mask_variants(stream, args.warmup)
+    if not args.no_a2a:
+        fresh()
+        result["a2a_layout"] = a2a_layout(stream)
+        if w.name == "flat_75k":
+            # the gather this workload is quoted on: the dual-chunk reorder of
+            # q, k and v that flat sharding removes (s = 75600, cp = 8)
+            row = result["a2a_layout"]["s75600"]
+            result["roofline_gather"] = {
+                "bound": "hbm", "kernel": "move_rows_kernel (q, k, v dual-chunk reorder, one launch)",
+                "achieved": row["reorder_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(row["reorder_gbs"] / PEAK_HBM_GBS, 4), "bytes": row["reorder_bytes"],
+                "note": "cold: launches rotate over buffer sets the 256 MB cache cannot hold"}
+    if not args.no_configs:
+        # The other workloads, each a parity-tested configuration: the same
+        # step, timed the same way, in one block per workload.
+        others = {}
+        for name in W.ORDER:
+            if name == w.name:
+                continue
+            fresh()
+            wo = W.WORKLOADS[name]
+            b = measure_workload(wo, W.bf16_tensors(wo), args, dev, stream,
+                                 max(10, args.steps // 2), max(3, args.warmup // 2), (-1, 0), 0)
+            hb = b.pop("_head")
+            b["config"] = hb["config"]
+            del hb
+            others[name] = b
+        result["configs"] = others
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, t)
+    print(json.dumps(result), flush=True)
+
+
+def measure_workload(w, t, args, dev, stream, steps, warmup, window, splits):
+    """One workload's step, timed bare, evented, and kernel by kernel, with its
+    rooflines; the standalone restore gather timed warm and cold. Returns the
+    block; "_head" holds what the caller needs besides the JSON fields."""
+    import torch
+
+    import context_causal_attention_thd_amd as thd
+
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
     q, k, v, do = (t[n].to(dev) for n in ("q", "k", "v", "do"))
     cup_dev = torch.from_numpy(cup).to(dev)
     T, H, D, cp, r = w.T, w.H, w.D, w.cp_size, w.rank
@@ -116,26 +207,25 @@ def main():
     perm = torch.empty(T, dtype=torch.int32, device=dev)
     q_local = torch.empty((n_local, H, D), dtype=torch.bfloat16, device=dev)
     do_local = torch.empty_like(q_local)
-    k_g = torch.empty_like(k)     # global order (standalone restore timing only)
-    v_g = torch.empty_like(v)
     o = torch.empty_like(q_local)
     lse = torch.empty((H, n_local), dtype=torch.float32, device=dev)
     dq = torch.empty((n_local, H, D), dtype=torch.float32, device=dev)
     dk_rm = torch.empty((T, H, D), dtype=torch.float32, device=dev)   # rank-major partials
     dv_rm = torch.empty_like(dk_rm)
-    window = tuple(args.window)
-    splits = args.max_key_splits
     probe = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
                      window=window, max_key_splits=splits)
     ws = torch.empty(int(probe.info.workspace_bytes) + 4096, dtype=torch.uint8, device=dev)
     scratch = torch.empty(int(probe.info.bwd_scratch_bytes) + 256, dtype=torch.uint8, device=dev)
     pairs = int(probe.info.causal_pairs)
-    probe_touched = int(probe.info.touched_rows)
+    touched = int(probe.info.touched_rows)
     probe.close()
 
-    def step():
-        plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
+    def new_plan():
+        return thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
                         kv_layout="rank_major", window=window, max_key_splits=splits)
+
+    def step():
+        plan = new_plan()
         plan.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
@@ -146,7 +236,7 @@ def main():
         return plan  # keep alive until the stream is synchronized
 
     # Whole steps: no events inside the timed region.
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     plans = []
@@ -154,18 +244,18 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     wall0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         plans.append(step())
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     plans.clear()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = t_start.elapsed_time(t_end) / steps
 
     # Spread of the step time: a second pass with an event pair around each
     # step (the events add a little queue time, so value stays the bare mean).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     for a, b in evs:
         a.record(stream)
         plans.append(step())
@@ -176,15 +266,10 @@ def main():
     # Host cost of the plan (validate, tiles, queues) and its upload, apart.
     t0 = time.perf_counter()
     for _ in range(20):
-        pl = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
-                      window=window, max_key_splits=splits)
-        pl.close()
+        new_plan().close()
     plan_host_us = (time.perf_counter() - t0) / 20 * 1e6
 
-    # The standalone K/V restore and the plan upload: events around REPS
-    # back-to-back launches, so the events' own cost is amortized.
-    plan = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False, kv_layout="rank_major",
-                    window=window, max_key_splits=splits)
+    plan = new_plan()
     plan.upload_into(ws, stream)
     reps = max(5, min(50, int(20.0 / max(ms_step, 1e-3))))
 
@@ -199,36 +284,9 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    t_restore = timed(lambda: thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g]))
     t_upload = timed(lambda: plan.upload_into(ws, stream))
-    # The same restore cold: rotate buffer sets (K, V in and out) totalling
-    # more than twice the 256 MB last-level cache, so no launch finds its
-    # rows cached by the one before.
-    set_bytes = 4 * k.numel() * k.element_size()
-    n_sets = max(3, -(-(600 << 20) // set_bytes))
-    sets = [[torch.empty_like(k_rm) for _ in range(4)] for _ in range(n_sets - 1)]
-    sets.insert(0, [k_rm, v_rm, k_g, v_g])
-    for st_ in sets[1:]:
-        st_[0].copy_(k_rm)
-        st_[1].copy_(v_rm)
-    # One untimed pass touches every destination once: the first write to a
-    # freshly allocated buffer costs extra (measured 37 us against 24 us per
-    # launch), which is allocation, not bandwidth. The timed passes stay cold:
-    # each set was last touched n_sets - 1 launches (> 512 MB) earlier.
-    for a_, b_, c_, d_ in sets:
-        thd.scatter_many([a_, b_], perm, [c_, d_])
-    torch.cuda.synchronize()
-    ec0 = torch.cuda.Event(enable_timing=True)
-    ec1 = torch.cuda.Event(enable_timing=True)
-    cold_reps = 3 * n_sets
-    ec0.record(stream)
-    for i in range(cold_reps):
-        a_, b_, c_, d_ = sets[i % n_sets]
-        thd.scatter_many([a_, b_], perm, [c_, d_])
-    ec1.record(stream)
-    torch.cuda.synchronize()
-    t_restore_cold = ec0.elapsed_time(ec1) / cold_reps
-    del sets
+    restore = restore_gather(w, k_rm, v_rm, perm, stream, reps)
+
     # Per-kernel durations inside steps: the same steps with the backward as
     # its separate launches (preprocess, dK/dV, dQ, gated zeroing -- the same
     # dK/dV launch as the composite call, whose dQ launch carries the delta
@@ -238,8 +296,7 @@ def main():
     kev = {n: [] for n in ("fwd", "dkdv", "dq")}
 
     def step_evented():
-        pl = thd.Plan(cu, cup, T, cp, r, w.strategy, H, D, upload=False,
-                      kv_layout="rank_major", window=window, max_key_splits=splits)
+        pl = new_plan()
         pl.upload_into(ws, stream)
         thd.partition_index(cup, cup_dev, T, cp, -1, w.strategy, out=perm)
         mine = perm[r * n_local:(r + 1) * n_local]
@@ -255,136 +312,218 @@ def main():
             kev[n].append(ev[n])
         return pl
 
-    for _ in range(args.steps):
+    for _ in range(steps):
         plans.append(step_evented())
     torch.cuda.synchronize()
     plans.clear()
     kms = {n: sorted(a.elapsed_time(b) for a, b in kev[n]) for n in kev}
-    t_fwd = sum(kms["fwd"]) / len(kms["fwd"])
-    t_dkdv = sum(kms["dkdv"]) / len(kms["dkdv"])
-    t_dq = sum(kms["dq"]) / len(kms["dq"])
-    t_bwd = t_dkdv + t_dq
+    t_k = {n: sum(kms[n]) / len(kms[n]) for n in kms}
 
     flop_fwd = 4.0 * D * H * pairs      # QK^T, PV
     flop_bwd = 10.0 * D * H * pairs     # S, dP, dV, dK, dQ
-    flop_dkdv = 8.0 * D * H * pairs     # S, dP, dV, dK
-    flop_dq_exec = 6.0 * D * H * pairs  # S, dP recomputed, dQ
+    # Each kernel's own algorithmic work (what an ideal fused backward computes
+    # once): the forward 4 units; dK/dV's kernel S, dP, dV, dK (8); the dQ
+    # kernel only dQ (2) -- it recomputes S and dP (4 more units it executes).
+    own = {"fwd": flop_fwd, "dkdv": 8.0 * D * H * pairs, "dq": 2.0 * D * H * pairs}
+    executed = {"fwd": flop_fwd, "dkdv": own["dkdv"], "dq": 6.0 * D * H * pairs}
+    names = {"fwd": "attn_fwd_kernel", "dkdv": "attn_bwd_dkdv_kernel", "dq": "attn_bwd_dq_kernel"}
     tflops_step = (flop_fwd + flop_bwd) / (ms_step * 1e-3) / 1e12
-    tflops_bwd = flop_bwd / (t_bwd * 1e-3) / 1e12
-    tflops_dkdv = flop_dkdv / (t_dkdv * 1e-3) / 1e12
-    tflops_dq = flop_dq_exec / (t_dq * 1e-3) / 1e12
-    tflops_fwd = flop_fwd / (t_fwd * 1e-3) / 1e12
+    t_bwd = t_k["dkdv"] + t_k["dq"]
+
+    def kroof(n):
+        a = own[n] / (t_k[n] * 1e-3) / 1e12
+        x = executed[n] / (t_k[n] * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": names[n], "achieved": round(a, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(a / PEAK_BF16_TFLOPS, 4),
+                "ms": round(t_k[n], 4), "executed_achieved": round(x, 2),
+                "executed_frac": round(x / PEAK_BF16_TFLOPS, 4)}
+
+    # The roofline object names the kernel that takes longest in the step.
+    dominant = max(t_k, key=lambda n: t_k[n])
+    roof = kroof(dominant)
+    roof["traffic"] = _traffic(w.name, names[dominant])
+    roof["note"] = ("the step's longest kernel; achieved = its own algorithmic FLOPs "
+                    "(fwd 4, dK/dV 8, dQ 2 x D x H x pairs) over its in-step duration; "
+                    "executed_* count the dQ kernel's S and dP recompute too")
     row_bytes = H * D * 2
-    restore_bytes = 2 * (2 * T * row_bytes + 4 * T)    # K and V: read + write rows, read idx
-    gbs_restore = restore_bytes / (t_restore * 1e-3) / 1e9
-    gbs_restore_cold = restore_bytes / (t_restore_cold * 1e-3) / 1e9
     # Algorithmic HBM bytes of the step (each tensor once): local Q, O, dO
     # (bf16) and dQ (fp32); K, V (bf16) and dK, dV (fp32) of the touched key
     # rows, plus zeros written to the untouched ones; LSE and delta (fp32);
     # the gather of local Q and dO (read + write).
-    touched = int(probe_touched)
     step_bytes = (3 * n_local * row_bytes + n_local * row_bytes * 2
                   + 2 * touched * row_bytes + 2 * touched * row_bytes * 2
                   + 2 * (T - touched) * row_bytes * 2 + 2 * 4 * H * n_local
                   + 2 * 2 * n_local * row_bytes)
-
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                tj = json.load(f)
-            entry = tj.get(args.workload, {}).get("attn_bwd_dkdv_kernel")
-            if entry and entry.get("source_hash") == _kernel_hash():
-                traffic = entry["bytes_per_launch"]
-        except Exception:
-            traffic = None
-
-    result = {
-        "metric": METRIC,
-        "value": round(tflops_step, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    hbm = step_bytes / (ms_step * 1e-3) / 1e9
+    block = {
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "T": T, "heads": H, "head_dim": D, "cp_size": cp,
-                   "window": list(window), "max_key_splits": splits,
-                   "rank": r, "strategy": w.strategy, "docs": w.B, "causal_pairs_per_head": pairs,
-                   "parallelism": "one simulated CP rank on one GPU"},
-        "roofline": {"bound": "mfma", "kernel": "attn_bwd_dkdv_kernel",
-                     "achieved": round(tflops_dkdv, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops_dkdv / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
-        "roofline_bwd_dq": {"bound": "mfma", "kernel": "attn_bwd_dq_kernel",
-                            "achieved": round(tflops_dq, 2), "peak": PEAK_BF16_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(tflops_dq / PEAK_BF16_TFLOPS, 4),
-                            "note": "executed FLOPs: S and dP recomputed, then dQ"},
-        "bwd_algorithmic": {"achieved": round(tflops_bwd, 2), "unit": "TFLOP/s",
-                            "frac": round(tflops_bwd / PEAK_BF16_TFLOPS, 4)},
-        "roofline_fwd": {"bound": "mfma", "kernel": "attn_fwd_kernel",
-                         "achieved": round(tflops_fwd, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops_fwd / PEAK_BF16_TFLOPS, 4)},
-        "roofline_gather": {"bound": "hbm", "kernel": "move_rows_kernel (K and V restore, one launch)",
-                            "achieved": round(gbs_restore_cold, 1), "peak": PEAK_HBM_GBS,
-                            "unit": "GB/s", "frac": round(gbs_restore_cold / PEAK_HBM_GBS, 4),
-                            "bytes": restore_bytes, "warm_achieved": round(gbs_restore, 1),
-                            "warm_frac": round(gbs_restore / PEAK_HBM_GBS, 4),
-                            "note": "achieved: buffer sets rotated through > 512 MB so every "
-                                    "launch reads and writes HBM (cold); warm: back-to-back on "
-                                    "the same buffers, served largely from the 256 MB cache"},
-        "step_hbm": {"bytes": step_bytes,
-                     "achieved": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-                     "unit": "GB/s", "frac": round(step_bytes / (ms_step * 1e-3) / 1e9
-                                                   / PEAK_HBM_GBS, 4)},
+        "tflops": round(tflops_step, 3),
+        "mfma_frac": round(tflops_step / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "roofline_fwd": kroof("fwd"),
+        "roofline_bwd_dkdv": kroof("dkdv"),
+        "roofline_bwd_dq": kroof("dq"),
+        "bwd_algorithmic": {"achieved": round(flop_bwd / (t_bwd * 1e-3) / 1e12, 2),
+                            "unit": "TFLOP/s",
+                            "frac": round(flop_bwd / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "attn_kernels": {"ms": round(t_k["fwd"] + t_bwd, 4),
+                         "tflops": round((flop_fwd + flop_bwd)
+                                         / ((t_k["fwd"] + t_bwd) * 1e-3) / 1e12, 2),
+                         "frac": round((flop_fwd + flop_bwd) / ((t_k["fwd"] + t_bwd) * 1e-3)
+                                       / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "roofline_gather": restore,
+        "step_hbm": {"bytes": step_bytes, "achieved": round(hbm, 1), "unit": "GB/s",
+                     "frac": round(hbm / PEAK_HBM_GBS, 4)},
         "times_ms": {"step": round(ms_step, 4),
                      "step_mean_evented": round(sum(per_step) / len(per_step), 4),
                      "step_median_evented": round(per_step[len(per_step) // 2], 4),
                      "step_p90_evented": round(per_step[int(0.9 * (len(per_step) - 1))], 4),
                      "plan_build_host_us": round(plan_host_us, 1),
                      "plan_upload": round(t_upload, 4),
-                     "fwd": round(t_fwd, 4),
-                     "bwd_dkdv": round(t_dkdv, 4), "bwd_dq": round(t_dq, 4),
-                     "kv_restore": round(t_restore, 4),
-                     "kv_restore_cold": round(t_restore_cold, 4),
-                     "attn_kernels_tflops": round(
-                         (flop_fwd + flop_bwd) / ((t_fwd + t_bwd) * 1e-3) / 1e12, 2),
-                     "host_wall_per_step": round(wall / args.steps * 1e3, 4),
+                     "fwd": round(t_k["fwd"], 4),
+                     "bwd_dkdv": round(t_k["dkdv"], 4), "bwd_dq": round(t_k["dq"], 4),
+                     "host_wall_per_step": round(wall / steps * 1e3, 4),
                      "kernel_reps": reps},
+        "_head": {"config": {"workload": w.name, "T": T, "heads": H, "head_dim": D,
+                             "cp_size": cp, "window": list(window), "max_key_splits": splits,
+                             "rank": r, "strategy": w.strategy, "docs": w.B,
+                             "causal_pairs_per_head": pairs,
+                             "parallelism": "one simulated CP rank on one GPU"},
+                  "flops": flop_fwd + flop_bwd, "reps": reps,
+                  "tensors": (q, k, v, do, cup_dev)},
     }
-    # Side measurements, each on a clean allocator cache: a block that frees
-    # gigabytes of buffers (mask_variants) left the P2P ring's Python loop up
-    # to 3x slower afterwards, with every kernel and phase of it unchanged.
-    def fresh():
-        import gc
-        gc.collect()
+    plan.close()
+    return block
+
+
+def restore_gather(w, k_rm, v_rm, perm, stream, reps):
+    """The K and V restore (rank-major to global order) as one standalone
+    batched gather launch, warm (back-to-back on the same buffers) and cold
+    (buffer sets rotated through more than twice the 256 MB last-level cache,
+    so no launch finds its rows cached by the one before). Under
+    NO_LOAD_BALANCE and cp_size 1 the restore is the identity; it is timed
+    all the same, as the copy it would be."""
+    import torch
+
+    import context_causal_attention_thd_amd as thd
+    T = w.T
+    row_bytes = w.H * w.D * 2
+    k_g = torch.empty_like(k_rm)
+    v_g = torch.empty_like(v_rm)
+
+    def timed(fn):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
         torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-    if cp > 1 and not args.no_p2p and window == (-1, 0):
-        fresh()
-        result["p2p_ring"] = p2p_ring(w, q, k, v, do, cup_dev, stream, args.warmup, args.steps,
-                                      reps, flop_fwd + flop_bwd, ms_step)
-    if not args.no_masks:
-        fresh()
-        result["mask_variants"] = mask_variants(stream, args.warmup)
-    if not args.no_a2a:
-        fresh()
-        result["a2a_layout"] = a2a_layout(stream)
-        if w.name == "flat_75k":
-            # the gather this workload is quoted on: the dual-chunk reorder of
-            # q, k and v that flat sharding removes (s = 75600, cp = 8)
-            row = result["a2a_layout"]["s75600"]
-            result["roofline_gather"] = {
-                "bound": "hbm", "kernel": "move_rows_kernel (q, k, v dual-chunk reorder, one launch)",
-                "achieved": row["reorder_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(row["reorder_gbs"] / PEAK_HBM_GBS, 4), "bytes": row["reorder_bytes"]}
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, t)
-    print(json.dumps(result), flush=True)
+        return e0.elapsed_time(e1) / reps
+
+    t_warm = timed(lambda: thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g]))
+    set_bytes = 4 * k_rm.numel() * k_rm.element_size()
+    n_sets = max(3, -(-(600 << 20) // set_bytes))
+    sets = [[torch.empty_like(k_rm) for _ in range(4)] for _ in range(n_sets - 1)]
+    sets.insert(0, [k_rm, v_rm, k_g, v_g])
+    for st_ in sets[1:]:
+        st_[0].copy_(k_rm)
+        st_[1].copy_(v_rm)
+    # One untimed pass touches every destination once: the first write to a
+    # freshly allocated buffer costs extra (measured 37 us against 24 us per
+    # launch), which is allocation, not bandwidth.
+    for a_, b_, c_, d_ in sets:
+        thd.scatter_many([a_, b_], perm, [c_, d_])
+    torch.cuda.synchronize()
+    ec0 = torch.cuda.Event(enable_timing=True)
+    ec1 = torch.cuda.Event(enable_timing=True)
+    cold_reps = 3 * n_sets
+    ec0.record(stream)
+    for i in range(cold_reps):
+        a_, b_, c_, d_ = sets[i % n_sets]
+        thd.scatter_many([a_, b_], perm, [c_, d_])
+    ec1.record(stream)
+    torch.cuda.synchronize()
+    t_cold = ec0.elapsed_time(ec1) / cold_reps
+    del sets
+    nbytes = 2 * (2 * T * row_bytes + 4 * T)    # K and V: read + write rows, read idx
+    cold = nbytes / (t_cold * 1e-3) / 1e9
+    warm = nbytes / (t_warm * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": "move_rows_kernel (K and V restore, one launch)",
+            "achieved": round(cold, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(cold / PEAK_HBM_GBS, 4), "bytes": nbytes, "ms": round(t_cold, 4),
+            "warm_achieved": round(warm, 1), "warm_frac": round(warm / PEAK_HBM_GBS, 4),
+            "warm_ms": round(t_warm, 4),
+            "note": "achieved: buffer sets rotated through > 512 MB so every launch reads and "
+                    "writes HBM (cold); warm: back-to-back on the same buffers, served largely "
+                    "from the 256 MB cache"}
+
+
+def gather_only(w, stream, launches):
+    """Only the workload's gathers, for a kernel trace whose per-launch figures
+    need no unpicking: the cold K and V restore of the all-gather (or, for the
+    flat share, the dual-chunk reorder of q, k and v that flat sharding
+    removes), repeated ``launches`` times over rotated buffer sets."""
+    import numpy as np
+    import torch
+
+    import context_causal_attention_thd_amd as thd
+    dev = torch.device("cuda", 0)
+    if w.name == "flat_75k":
+        cp, heads = 8, 40
+        s, hl = w.T, heads // cp
+        cup = np.array([0, s], dtype=np.int32)
+        perm = thd.partition_index(cup, torch.from_numpy(cup).to(dev), s, cp, -1,
+                                   "dual_chunk_swap")
+        n_t, row_bytes, T = 3, hl * w.D * 2, s
+        what = "q, k, v dual-chunk reorder (s = 75600, cp_size 8, 5 heads of 128 per rank)"
+    else:
+        cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+        perm = thd.partition_index(cup, torch.from_numpy(cup).to(dev), w.T, w.cp_size, -1,
+                                   w.strategy)
+        n_t, row_bytes, T = 2, w.H * w.D * 2, w.T
+        what = "K and V restore from rank-major order"
+    one = T * row_bytes // 2
+    set_bytes = 2 * n_t * T * row_bytes
+    n_sets = max(3, -(-(600 << 20) // set_bytes))
+    sets = [([torch.randn(one, device=dev).to(torch.bfloat16).view(T, -1) for _ in range(n_t)],
+             [torch.empty(T, row_bytes // 2, dtype=torch.bfloat16, device=dev)
+              for _ in range(n_t)]) for _ in range(n_sets)]
+    for a, b in sets:
+        thd.scatter_many(a, perm, b)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(launches):
+        a, b = sets[i % n_sets]
+        thd.scatter_many(a, perm, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    nbytes = n_t * (2 * T * row_bytes + 4 * T)
+    return {"gather_only": w.name, "what": what, "launches": launches, "warmup_launches": n_sets,
+            "buffer_sets": n_sets, "bytes_per_launch": nbytes, "ms_per_launch": round(ms, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def _traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` from profiles/traffic.json, when they
+    were measured on the kernel's current source (hash check); else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = {"attn_bwd_dkdv_kernel": "attn_bwd.hip", "attn_bwd_dq_kernel": "attn_bwd_dq.hip",
+           "attn_fwd_kernel": "attn_fwd.hip"}.get(kernel)
+    if not src or not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            entry = json.load(f).get(workload, {}).get(kernel)
+        if entry and entry.get("source_hash") == _source_hash(src):
+            return entry["bytes_per_launch"]
+    except Exception:
+        return None
+    return None
 
 
 def p2p_ring(w, q, k, v, do, cup_dev, stream, warmup, steps, reps, flops, ms_allgather):
@@ -635,9 +774,9 @@ def a2a_layout(stream, seqlens=(8192, 32768, 75600), cp=8, heads=40, head_dim=12
     return out
 
 
-def _kernel_hash() -> str:
+def _source_hash(name: str) -> str:
     import hashlib
-    p = os.path.join(ROOT, "context_causal_attention_thd_amd", "csrc", "attn_bwd.hip")
+    p = os.path.join(ROOT, "context_causal_attention_thd_amd", "csrc", name)
     with open(p, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 

@@ -174,3 +174,59 @@ def a2a_round_trip(cup, T, cp, H, strategy, tensors):
             (local,) = thd.a2a_unpack([recv[r]])
             assert torch.equal(local, shards[r][i]), (i, r)
     return full
+
+
+def oracle_share_chunked(w, rank, t64, heads=None, chunk_rows=512, workers=None,
+                         window=(-1, 0), idx=None, progress=None):
+    """The oracle's whole rank share (O, LSE, dQ, dK, dV over every row and
+    key), evaluated in chunks of local rows on a thread pool. Rows are
+    independent in the forward and the backward's dK/dV is a sum over rows,
+    so the chunks' results are assembled (O, LSE, dQ by row) and summed (dK,
+    dV); the oracle's arithmetic is unchanged. ``heads`` (a slice) restricts
+    the heads the oracle sees. Each chunk's key range ends at its last row,
+    which keeps the work near the causal pair count on long documents.
+    ``progress`` (callable) is told every chunk that finished."""
+    import concurrent.futures
+    import threading
+
+    cu, cup = w.cu_seqlens(), w.cu_seqlens_padded()
+    if idx is None:
+        idx = O.partition_index(cup, w.T, w.cp_size, rank, w.strategy)
+    idx = np.asarray(idx, dtype=np.int64)
+    sl = slice(None) if heads is None else heads
+    q, k, v, do = (np.ascontiguousarray(t64[x][:, sl]) for x in ("q", "k", "v", "do"))
+    ql, dol = q[idx], do[idx]
+    n, H, D = ql.shape
+    cupl = np.asarray(cup, dtype=np.int64)
+    nb = len(cupl) - 1
+    # Keys a chunk can reach lie in the documents of its rows: from the first
+    # one's start to the last one's end (rows of the buffer tail have none).
+    doc_of = np.searchsorted(cupl, idx, side="right") - 1
+    o = np.zeros((n, H, D))
+    lse = np.full((H, n), -np.inf)
+    dq = np.zeros((n, H, D))
+    dk = np.zeros((w.T, H, D))
+    dv = np.zeros((w.T, H, D))
+    lock = threading.Lock()
+
+    def one(r0):
+        rows = list(range(r0, min(n, r0 + chunk_rows)))
+        of, lf = O.attention_fwd(ql, k, v, idx, cu, cup, w.T, rows=rows, window=window)
+        gq, gk, gv = O.attention_bwd(ql, k, v, dol, idx, cu, cup, w.T, rows=rows,
+                                     window=window)
+        docs = doc_of[rows]
+        docs = docs[(docs >= 0) & (docs < nb)]
+        k0 = int(cupl[docs.min()]) if len(docs) else 0
+        k1 = int(cupl[docs.max() + 1]) if len(docs) else 0
+        with lock:
+            o[rows], lse[:, rows], dq[rows] = of[rows], lf[:, rows], gq[rows]
+            dk[k0:k1] += gk[k0:k1]
+            dv[k0:k1] += gv[k0:k1]
+        if progress is not None:
+            progress(r0)
+
+    if workers is None:
+        workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(0, n, chunk_rows)))
+    return dict(idx=idx, o=o, lse=lse, dq=dq, dk=dk, dv=dv)
