@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "thdcp_plan_upload", "thdcp_plan_destroy", "cp_attn_fwd", "cp_attn_bwd",
     "cp_attn_bwd_preprocess", "cp_attn_bwd_dkdv", "cp_attn_bwd_dq", "thdcp_zero_untouched",
     "cp_attn_fwd_step", "thdcp_lse_merge", "thdcp_lse_merge_parts", "cp_attn_bwd_step",
+    "cp_attn_bwd_noalloc",
 )
 
 
@@ -122,6 +123,8 @@ def lib() -> ctypes.CDLL:
     L.cp_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.cp_attn_bwd.restype = i32
     L.cp_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+    L.cp_attn_bwd_noalloc.restype = i32
+    L.cp_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     L.cp_attn_bwd_preprocess.restype = i32
     L.cp_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, vp, sz, vp]
     L.cp_attn_bwd_dkdv.restype = i32
@@ -472,6 +475,19 @@ def attn_bwd(plan: Plan, q_local, k, v, o, lse, d_o, dq=None, dk=None, dv=None,
                              int(bool(zero_untouched)), int(bool(accumulate_dkv)),
                              _dev_ptr(scratch, "scratch"),
                              scratch.numel() * scratch.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(plan: Plan, q_local, k, v, o, lse, d_o, dq, dk, dv,
+                     zero_untouched: bool = True, accumulate_dkv: bool = False, stream=None):
+    """cp_attn_bwd_noalloc: attn_bwd with its scratch in the library's fixed
+    device array (no scratch argument, nothing allocated). dq, dk and dv are
+    the caller's preallocated outputs."""
+    q_p, k_p, v_p, lse_p, do_p, o_p, dq_p, dk_p, dv_p = _bwd_ptrs(
+        plan, q_local, k, v, lse, d_o, o, dq, dk, dv)
+    _check(lib().cp_attn_bwd_noalloc(plan.handle, q_p, k_p, v_p, o_p, lse_p, do_p, dq_p, dk_p,
+                                     dv_p, int(bool(zero_untouched)), int(bool(accumulate_dkv)),
+                                     _stream(stream)))
     return dq, dk, dv
 
 

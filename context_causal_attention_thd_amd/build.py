@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libthdcp.so")
-SOURCES = ["capi.cpp", "rows.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]
+SOURCES = ["capi.cpp", "rows.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON = [

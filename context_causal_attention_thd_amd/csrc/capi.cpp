@@ -45,6 +45,15 @@ thdcp_status_t hip_status(hipError_t e, const char* what) {
   return fail(THDCP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+// Error reporting for the library's other translation units (not exported).
+thdcp_status_t thdcp::report_error(thdcp_status_t st, const char* msg) {
+  return fail(st, "%s", msg);
+}
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Layout rules ([AG] "Why", "Scope and constraints"; [A2A] body) and padding

@@ -5,7 +5,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "thdcp.h"
+
 namespace thdcp {
+
+// Sets the thread's thdcp_last_error() text and returns st (capi.cpp).
+thdcp_status_t report_error(thdcp_status_t st, const char* msg);
 
 // Forward work item: up to kFwdBM consecutive local rows that lie in one
 // contiguous run of global rows of one document (a DUAL_CHUNK_SWAP chunk or a

@@ -361,6 +361,29 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t plan, const void* q_local, const void* k
                            size_t scratch_bytes, void* stream);
 
 /*
+ * cp_attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same launches and results as cp_attn_bwd, with its scratch (delta, fp32
+ * [H, n_local]) in a fixed 8 MiB device array of the library instead of a
+ * caller buffer. The call allocates nothing and takes no workspace argument;
+ * the plan's own workspace (thdcp_plan_upload) is still used as by
+ * cp_attn_bwd.
+ *   Limit: n_local * H <= 2,097,152 (2^21 floats); a larger plan gets
+ *   THDCP_ERR_UNSUPPORTED before anything is enqueued.
+ *   Each GPU holds its own copy of the array until the process ends, and
+ *   every call on that GPU shares it: calls that overlap on one GPU (on two
+ *   streams, or from two threads) race. Calls enqueued on one stream are
+ *   ordered and safe. The first call on a device looks up the array's device
+ *   address (no allocation).
+ */
+THDCP_API
+thdcp_status_t cp_attn_bwd_noalloc(thdcp_plan_t plan, const void* q_local, const void* k,
+                                   const void* v, const void* o_local, const float* lse,
+                                   const void* d_o, float* dq, float* dk, float* dv,
+                                   int32_t zero_untouched, int32_t accumulate_dkv,
+                                   void* stream);
+
+/*
  * The backward as separate launches, for callers that schedule or time them
  * one by one. Calling preprocess, dkdv, dq and thdcp_zero_untouched in this
  * order on one stream computes the gradients cp_attn_bwd computes (which

@@ -409,3 +409,20 @@ def test_binding_refuses_wrong_shapes(L):
     with pytest.raises(ValueError, match="1-D"):
         thd.gather(torch.zeros(20, 8), idx.view(2, 5), out=torch.zeros(2, 8))
     plan.close()
+
+
+def test_noalloc_refuses_plans_above_its_scratch(L):
+    # n_local * H above 2^21 floats: refused on the host before any device
+    # work (the pointers are never looked at).
+    T, H = 1_100_000, 2
+    cu = np.array([0, T], np.int32)
+    plan = thd.Plan(cu, cu, T, 1, 0, "no_load_balance", H, 64, upload=False)
+    null = ctypes.c_void_p(0)
+    st = L.cp_attn_bwd_noalloc(plan.handle, null, null, null, null, null, null, null, null,
+                               null, 1, 0, null)
+    assert st == 3  # THDCP_ERR_UNSUPPORTED
+    assert b"scratch" in L.thdcp_last_error()
+    st = L.cp_attn_bwd_noalloc(None, null, null, null, null, null, null, null, null, null, 1,
+                               0, null)
+    assert st == 1  # THDCP_ERR_ARG
+    plan.close()
