@@ -256,8 +256,12 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
           const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
           const bool ok =
               !diag || (key <= my_hi && (!BAND || key >= my_lo) && key < kend);
-          const float p = ok ? fast_exp2(fmaf(s[kb][i], scale_log2, -lse2)) : 0.f;
-          dp[kb][i] = ok ? p * (dp[kb][i] - dlt) : 0.f;
+          // Branch-free: a masked key's exponent is -inf, so p = 0 exactly (dP
+          // is finite: rows past the range end load as zeros). Selecting p
+          // after the exp instead compiled to a branch around every element.
+          const float x = ok ? fmaf(s[kb][i], scale_log2, -lse2) : -INFINITY;
+          const float p = fast_exp2(x);
+          dp[kb][i] = p * (dp[kb][i] - dlt);
         }
       // dQ^T += K^T dS^T; k-step (kb, u): slot j = key kb*32 + 16u +
       // (j/4)*8 + hh*4 + j%4 (accumulator entries u*8..u*8+7 of dp[kb]).
