@@ -7,24 +7,26 @@
 // comm type" (body: the mask is the cp_size = 1 mask). Both DUAL_CHUNK_SWAP
 // chunks of a document are separate query tiles of this one launch.
 //
-// gfx950 design: a workgroup of 8 waves owns up to 128 consecutive query rows
-// of one (document piece, head); each wave owns 16 query rows (QB = 1 block;
-// the kernel is written for QB blocks per wave). Keys are walked from the
-// document start in 64-key tiles, double-buffered in LDS (row-major K and V).
-// Everything is computed in the transposed form
+// gfx950 design: a workgroup owns up to 128 consecutive query rows of one
+// (document piece, head), in waves of QB 16-row query blocks: 8 waves of 16
+// rows (QB = 1, ~115 registers, four waves per SIMD) or 4 waves of 32 rows
+// (QB = 2, ~190 registers, two per SIMD, each LDS fragment feeding two
+// MFMAs); the plan picks QB = 2 for long walks. Keys are walked from the
+// document start in 64-key tiles, double-buffered in LDS. Everything is
+// computed in the transposed form
 //   S^T = K Q^T  and  O^T = V^T P^T
 // with v_mfma_f32_16x16x32_bf16: lane l owns query column l%16 of each block
 // and keys 4*(l/16) + i of every 16-key block. K fragments are 16-byte LDS
 // reads and V^T fragments are transposing LDS reads (ds_read_b64_tr_b16) of
-// the row-major V tile; at the row pitch used both are free of bank conflicts.
-// P feeds the second product with no data movement. At ~122 registers four
-// waves share each SIMD, which is what lets one wave's softmax VALU work
-// overlap another's MFMAs.
+// the row-major V tile; the tile's chunk swizzle keeps both free of bank
+// conflicts. Each fragment is read two MFMA groups ahead of its use (held in
+// place by scheduling barriers): the loop was bound by LDS read latency. P
+// feeds the second product with no data movement.
 //
-// The next tile's K/V rows are fetched with buffer loads whose descriptor ends
-// at the last attended key: rows past it read as zero with no branch, so the
-// loads are unconditional, stay in flight during the current tile's MFMAs and
-// are only waited for when they are written to LDS. Padding never enters a
+// The next tile's K/V rows arrive by LDS DMA while the current tile is
+// computed: buffer loads that write LDS directly (no staging registers, no
+// LDS stores by the waves), whose descriptor ends at the last attended key,
+// so rows past it land as zeros with no branch. Padding never enters a
 // product.
 //
 // Online softmax in the log2 domain with lazy rescaling: the running max of a
@@ -45,14 +47,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.f;
 
+// K/V tiles in LDS: kFwdBN rows of D bf16, unpadded (LDS DMA writes each
+// wave's 1 KB block contiguously), with the 16-byte chunks of row r permuted:
+// logical chunk c sits at chunk c ^ kv_swz(r). For D = 128 the swizzle takes
+// even values on rows 0-7 and odd ones on rows 8-15 (mod 16), which keeps the
+// 16-row fragment reads (16 rows, one chunk) and the transposing V^T reads
+// (4 rows x 2 chunks per 16 lanes) on distinct banks; for D = 64 (two rows
+// per 256-byte bank line) rows of one parity take distinct values.
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  if constexpr (D == 128) return (2 * r + ((r >> 3) & 1)) & 15;
+  else return (r >> 1) & 7;
+}
+
 template <int D>
 struct FwdSmem {
-  // Row pitch (bf16) = D + 16: the 16-row fragment reads (lane = row l%16,
-  // 16-byte column l/16) and the transposing V^T reads below are free of LDS
-  // bank conflicts at this pitch (measured).
-  static constexpr int P = D + 16;
-  bf16 k[2][kFwdBN * P];
-  bf16 v[2][kFwdBN * P];
+  static constexpr int ROWB = D * 2;            // bytes per row
+  static constexpr int TILEB = kFwdBN * ROWB;   // bytes per K or V tile
+  __attribute__((aligned(1024))) char k[2][TILEB];
+  __attribute__((aligned(1024))) char v[2][TILEB];
 };
 
 // QB: 16-row query blocks per wave; the waves of a workgroup cover kFwdBM
@@ -79,10 +92,13 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
   constexpr int NB = D / 16;   // 16-wide blocks of the head dim
   constexpr int KB = BN / 16;  // 16-key blocks per tile
-  constexpr int P = FwdSmem<D>::P;
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int CH = BN * CPR / kThreads;
-  static_assert(CH * kThreads == BN * CPR, "tile chunks split evenly over the threads");
+  constexpr int kPf = 2;       // LDS fragment reads in flight ahead of their MFMAs
+  constexpr int ROWB = FwdSmem<D>::ROWB;
+  constexpr int TILEB = FwdSmem<D>::TILEB;
+  constexpr int LPR = ROWB / 16;               // lanes (16-byte chunks) per row
+  constexpr int RPI = 1024 / ROWB;             // rows per wave DMA instruction
+  constexpr int NI = TILEB / 1024 / (kThreads / 64);  // DMA instructions per wave per tensor
+  static_assert(NI * (kThreads / 64) * 1024 == TILEB, "tile splits evenly over the waves");
   __shared__ FwdSmem<D> sm;
 
   const int tile_id = blockIdx.x / H;
@@ -134,42 +150,44 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     l_part[qb] = 0.f;
   }
 
-  // Per-thread staging slots: chunk c = threadIdx + j*kThreads is row c/CPR,
-  // 16-byte column c%CPR of the tile; kThreads is a multiple of CPR, so every
-  // chunk of a thread is in the same column and its rows are RSTEP apart.
-  constexpr int RSTEP = kThreads / CPR;
-  static_assert(RSTEP * CPR == kThreads, "threads cover whole rows");
-  const int krow0 = threadIdx.x / CPR;
-  const uint32_t coff = (uint32_t)(threadIdx.x % CPR) * 16u;
-  const int soff0 = krow0 * P + (threadIdx.x % CPR) * 8;
+  // Staging by LDS DMA: DMA instruction j of wave w fills rows
+  // [(w*NI + j)*RPI, +RPI) of the tile; lane i loads row (w*NI + j)*RPI +
+  // i/LPR, physical chunk i%LPR, i.e. logical chunk (i%LPR) ^ kv_swz(row).
+  // No registers hold the tile and nothing is written to LDS by the waves;
+  // the data lands asynchronously (counted by vmcnt).
   const uint32_t row_bytes = (uint32_t)(rs * 2);
-  const uint32_t goff0 = (uint32_t)krow0 * row_bytes + coff;  // from the tile's first row
-  // Rows [k0, k0 + BN) of K or V into registers with buffer loads, for a
-  // tile of a key range ending at kend; a row at or past kend reads 0 with no
-  // branch.
+  int drow[NI];
+  uint32_t dcol[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    drow[j] = (w * NI + j) * RPI + lane / LPR;
+    dcol[j] = (uint32_t)(((lane % LPR) ^ kv_swz<D>(drow[j])) * 16);
+  }
+  // Rows [k0, k0 + BN) of K or V into LDS tile dst, for a tile of a key range
+  // ending at kend; a row at or past kend reads 0 with no branch.
   //  - Unmapped: the descriptor runs from row k0 - kv_sub to the range end,
-  //    so the constant chunk offsets land past its end for those rows.
-  //  - MAPPED: pos[] holds this thread's rows of the tile, looked up one tile
+  //    so offsets of rows past it land past its end.
+  //  - MAPPED: pos[] holds this lane's rows of the tile, looked up one tile
   //    ahead of the loads that use them so the lookup's latency stays off the
   //    prefetch path; a skipped row gets an offset past the descriptor, which
   //    spans all kv rows (below 2 GiB, checked on the host).
-  auto rows_pos = [&](int k0, int kend, int (&pos)[CH]) {
+  auto rows_pos = [&](int k0, int kend, int (&pos)[NI]) {
     if constexpr (MAPPED) {
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int key = k0 + krow0 + j * RSTEP;
+      for (int j = 0; j < NI; ++j) {
+        const int key = k0 + drow[j];
         const int r = kv_row[min(key, kend - 1)] - kv_sub;
         pos[j] = key < kend ? r : -1;
       }
     }
   };
-  auto load_rows = [&](const bf16* x, int k0, int kend, const int (&pos)[CH], u32x4* regs) {
+  auto load_rows = [&](const bf16* x, int k0, int kend, const int (&pos)[NI], char* dst) {
     if constexpr (MAPPED) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(x + head_off, kv_bytes);
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const uint32_t off = pos[j] >= 0 ? (uint32_t)pos[j] * row_bytes + coff : 0xFFFFFFF0u;
-        regs[j] = buffer_load16(r, off);
+      for (int j = 0; j < NI; ++j) {
+        const uint32_t off = pos[j] >= 0 ? (uint32_t)pos[j] * row_bytes + dcol[j] : 0xFFFFFFF0u;
+        dma16(r, off, dst + (w * NI + j) * 1024);
       }
     } else {
       const int64_t n = (int64_t)kend - k0;
@@ -177,12 +195,22 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
           n > 0 ? make_rsrc(x + (int64_t)(k0 - kv_sub) * rs + head_off, (uint32_t)(n * rs * 2))
                 : make_rsrc(x, 0u);
 #pragma unroll
-      for (int j = 0; j < CH; ++j) regs[j] = buffer_load16(r, goff0 + j * RSTEP * row_bytes);
+      for (int j = 0; j < NI; ++j)
+        dma16(r, (uint32_t)drow[j] * row_bytes + dcol[j], dst + (w * NI + j) * 1024);
     }
   };
-  auto store_rows = [&](bf16* dst, const u32x4* regs) {
-#pragma unroll
-    for (int j = 0; j < CH; ++j) *reinterpret_cast<u32x4*>(dst + soff0 + j * RSTEP * P) = regs[j];
+  // LDS byte offsets of this lane's fragment reads (lane constants): the K
+  // fragment of k-step kk and key block kb is row kb*16 + l16, logical chunk
+  // kk*4 + G; the V^T reads of head-dim block nb are rows 32ks + 4G +
+  // (l16 >> 2) (+16), logical chunk 2nb + ((l16 & 3) >> 1), half l16 & 1.
+  const int ksw = G ^ kv_swz<D>(l16);
+  const int vr = G * 4 + (l16 >> 2);
+  const int vsw = ((l16 >> 1) & 1) ^ kv_swz<D>(vr);
+  auto k_off = [&](int kb, int kk) {
+    return (kb * 16 + l16) * ROWB + (((kk * 4) ^ ksw) << 4);
+  };
+  auto v_off = [&](int ks, int half, int nb) {
+    return (32 * ks + 16 * half + vr) * ROWB + (((2 * nb) ^ vsw) << 4) + 8 * (l16 & 1);
   };
   // S^T = K Q^T for the K tile in LDS buffer kbuf: each K fragment (one
   // 16-byte LDS read) feeds the MFMAs of all QB query blocks.
@@ -193,14 +221,26 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[qb][kb][i] = 0.f;
+    // KS * KB fragment reads, each feeding QB MFMAs, read kPf ahead into a
+    // ring; the scheduling barriers keep the compiler from sinking the reads
+    // back next to their MFMAs.
+    constexpr int kN = KS * KB;
+    bf16x8 ring[kPf + 1];
+    auto fetch = [&](int n) {
+      ring[n % (kPf + 1)] =
+          load_bf16x8(reinterpret_cast<const bf16*>(&sm.k[kbuf][k_off(n % KB, n / KB)]));
+    };
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+    for (int n = 0; n < kPf; ++n) fetch(n);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = load_bf16x8(&sm.k[kbuf][(kb * 16 + l16) * P + kk * 32 + G * 8]);
+    for (int n = 0; n < kN; ++n) {
+      if (n + kPf < kN) fetch(n + kPf);
+      const int kb = n % KB, kk = n / KB;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16(a, qf[qb][kk], s[qb][kb]);
-      }
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16(ring[n % (kPf + 1)], qf[qb][kk], s[qb][kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // Band / padding mask: key j is allowed iff my_lo <= j <= my_hi and
   // j < kend (the end of the key range the tile belongs to).
@@ -273,14 +313,21 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
         l_part[qb] += ps;
         pb[qb] = pack8(s[qb][2 * ks], s[qb][2 * ks + 1]);
       }
-      const int o1 = (2 * ks * 16 + G * 4 + (l16 >> 2)) * P + 4 * (l16 & 3);
-      const int o2 = o1 + 16 * P;
+      bf16x8 ring[kPf + 1];
+      auto fetch = [&](int nb) {
+        ring[nb % (kPf + 1)] =
+            concat4(lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 0, nb)])),
+                    lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 1, nb)])));
+      };
+#pragma unroll
+      for (int nb = 0; nb < kPf; ++nb) fetch(nb);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 a = concat4(lds_read_tr4(&sm.v[vbuf][o1 + nb * 16]),
-                                 lds_read_tr4(&sm.v[vbuf][o2 + nb * 16]));
+        if (nb + kPf < NB) fetch(nb + kPf);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma16(a, pb[qb], oacc[qb][nb]);
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma16(ring[nb % (kPf + 1)], pb[qb], oacc[qb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -291,7 +338,6 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int ntiles = nt0 + nt1;
   auto tile_k0 = [&](int it) { return it < nt0 ? t.ks0 + it * BN : t.ks1 + (it - nt0) * BN; };
   auto tile_kend = [&](int it) { return it < nt0 ? t.ke0 : t.ke1; };
-  u32x4 kreg[CH], vreg[CH];
 
   // Double-buffered K/V tiles: the next tile's loads are issued before the
   // current tile's MFMAs and written to LDS after them; one barrier per tile.
@@ -310,16 +356,14 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       wave_uniform((row0 + QB * 16 - 1 < t.n) && (t.g0 + row0 + QB * 16 - 1 < t.e)) != 0;
   // The second tile's rows are looked up beside the first's, so the prologue
   // waits on one row-map round trip before the first K/V loads, not two.
-  int pos[CH], pos1[CH] = {};
+  int pos[NI], pos1[NI] = {};
   if (ntiles > 0) {
     rows_pos(tile_k0(0), tile_kend(0), pos);
     if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos1);
-    load_rows(k, tile_k0(0), tile_kend(0), pos, kreg);
-    load_rows(v, tile_k0(0), tile_kend(0), pos, vreg);
-    store_rows(sm.k[0], kreg);
-    store_rows(sm.v[0], vreg);
+    load_rows(k, tile_k0(0), tile_kend(0), pos, sm.k[0]);
+    load_rows(v, tile_k0(0), tile_kend(0), pos, sm.v[0]);
 #pragma unroll
-    for (int j = 0; j < CH; ++j) pos[j] = pos1[j];
+    for (int j = 0; j < NI; ++j) pos[j] = pos1[j];
   }
   wait_vmem();
   __syncthreads();
@@ -328,9 +372,10 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     const int kend = tile_kend(it);
     const int cur = it & 1;
     const bool has_next = it + 1 < ntiles;
-    if (has_next) {  // in flight during this tile's compute
-      load_rows(k, tile_k0(it + 1), tile_kend(it + 1), pos, kreg);
-      load_rows(v, tile_k0(it + 1), tile_kend(it + 1), pos, vreg);
+    if (has_next) {  // in flight during this tile's compute (the other buffer's
+                     // last readers passed the previous barrier)
+      load_rows(k, tile_k0(it + 1), tile_kend(it + 1), pos, sm.k[cur ^ 1]);
+      load_rows(v, tile_k0(it + 1), tile_kend(it + 1), pos, sm.v[cur ^ 1]);
       if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
     if (k0 <= wave_kmax && (!BAND || k0 + BN - 1 >= wave_kmin)) {
@@ -342,10 +387,7 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       softmax_max(s);
       softmax_pv(cur, s);
     }
-    if (has_next) {
-      store_rows(sm.k[cur ^ 1], kreg);
-      store_rows(sm.v[cur ^ 1], vreg);
-    }
+    wait_vmem();  // this wave's DMA of the next tile has landed
     __syncthreads();
   }
 
@@ -418,20 +460,20 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   }
 }
 
-// 16-row waves (QB = 1, eight waves, ~122 registers, four waves per SIMD):
-// measured against 32-row waves (QB = 2, four waves, two per SIMD) on MI355X
-// it is 4% slower on one 75600-token document and 3-10% faster on the
-// multi-document shares, whose tiles are short.
-constexpr int kFwdQB = 1;
-
-template <int D>
+// Waves of 16 query rows (QB = 1: eight waves, ~122 registers, four waves per
+// SIMD) or of 32 (QB = 2: four waves, ~220 registers, two per SIMD, every K
+// and V^T fragment read from LDS feeding two MFMAs). The plan picks QB = 2
+// for shares whose average walk is long (measured on MI355X: one 75600-token
+// document 7.7 against 8.5 ms) and QB = 1 otherwise (the multi-document
+// shares' short tiles: 10-15% faster).
+template <int D, int QB>
 hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const bf16* q,
                         const bf16* k, const bf16* v, const int32_t* kv_row, int32_t kv_sub,
                         uint32_t kv_bytes, Band band, bf16* o, float* lse, int64_t n_local,
                         float scale_log2, SplitWs split, hipStream_t stream) {
-#define THDCP_FWD(MM, BB)                                                                  \
-  hipLaunchKernelGGL((attn_fwd_kernel<D, kFwdQB, MM, BB>), dim3((unsigned)blocks),           \
-                     dim3(kFwdThreads<kFwdQB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub, \
+#define THDCP_FWD(MM, BB)                                                                \
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, MM, BB>), dim3((unsigned)blocks),             \
+                     dim3(kFwdThreads<QB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub, \
                      kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2, split)
   if (kv_row && band.causal)
     THDCP_FWD(true, false);
@@ -448,26 +490,28 @@ hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const b
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, KvRows kv, Band band,
-                           void* o, float* lse, int64_t n_local, float scale, SplitWs split,
-                           hipStream_t stream) {
+                           int32_t qb, const void* q, const void* k, const void* v, KvRows kv,
+                           Band band, void* o, float* lse, int64_t n_local, float scale,
+                           SplitWs split, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const float scale_log2 = scale * kLog2e;
-  const bf16* qb = static_cast<const bf16*>(q);
+  const bf16* qp = static_cast<const bf16*>(q);
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
   bf16* ob = static_cast<bf16*>(o);
   const int64_t kv_bytes = kv.rows * H * D * 2;
   if (kv.map && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
-  if (D == 128)
-    return launch_fwd_d<128>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, band,
-                             ob, lse, n_local, scale_log2, split, stream);
-  if (D == 64)
-    return launch_fwd_d<64>(tiles, blocks, H, qb, kb, vb, kv.map, (int32_t)kv.sub, kvb, band,
-                            ob, lse, n_local, scale_log2, split, stream);
+#define THDCP_FWD_D(DD, QQ)                                                                   \
+  return launch_fwd_d<DD, QQ>(tiles, blocks, H, qp, kb, vb, kv.map, (int32_t)kv.sub, kvb, band, \
+                              ob, lse, n_local, scale_log2, split, stream)
+  if (D == 128 && qb == 2) THDCP_FWD_D(128, 2);
+  if (D == 128 && qb == 1) THDCP_FWD_D(128, 1);
+  if (D == 64 && qb == 2) THDCP_FWD_D(64, 2);
+  if (D == 64 && qb == 1) THDCP_FWD_D(64, 1);
+#undef THDCP_FWD_D
   return hipErrorInvalidValue;
 }
 

@@ -126,6 +126,16 @@ __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
+// gfx950 LDS DMA: 16 bytes per lane from buffer r at byte offset off straight
+// into LDS, lane i at lds + 16 i (lds wave-uniform). No register holds the
+// data and the wave writes nothing to LDS itself; the write lands
+// asynchronously and is counted by vmcnt. An offset past the descriptor
+// writes zeros (as a plain buffer load reads them).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+}
+
 // s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -125,10 +125,11 @@ hipError_t launch_lse_merge_parts(int64_t n, int32_t H, int32_t D, int32_t parts
                                   float* lse_out, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
+// qb: 16-row query blocks per wave of the forward kernel (1 or 2).
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           const void* q, const void* k, const void* v, KvRows kv, Band band,
-                           void* o, float* lse, int64_t n_local, float scale, SplitWs split,
-                           hipStream_t stream);
+                           int32_t qb, const void* q, const void* k, const void* v, KvRows kv,
+                           Band band, void* o, float* lse, int64_t n_local, float scale,
+                           SplitWs split, hipStream_t stream);
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                                 const void* q, const void* k, const void* v, KvRows kv,
                                 Band band, const void* d_o, const float* lse,
