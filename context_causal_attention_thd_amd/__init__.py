@@ -73,6 +73,8 @@ class PlanInfo(ctypes.Structure):
         ("bwd_scratch_bytes", ctypes.c_size_t),
         ("n_split_tiles", ctypes.c_int32),
         ("n_fwd_parts", ctypes.c_int32),
+        ("fwd_tile_rows", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

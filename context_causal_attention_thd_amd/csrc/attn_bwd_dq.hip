@@ -5,9 +5,10 @@
 // like the forward pass: no atomics, every local row written once (padding
 // rows 0), bit-identical from run to run.
 //
-// gfx950 design (mirrors the forward kernel): a workgroup of 4 waves owns up
-// to 128 consecutive query rows of one (document piece, head), 32 per wave,
-// and walks the keys from the document start in 64-key tiles, double-buffered
+// gfx950 design (mirrors the forward kernel): a workgroup of 4 or 8 waves owns
+// up to 128 or 256 consecutive query rows of one (document piece, head), 32
+// per wave (8 waves, one workgroup per CU, for the plans with long walks:
+// each staged K/V tile serves twice the queries), and walks the keys from the document start in 64-key tiles, double-buffered
 // in LDS; the next tile arrives by LDS DMA (buffer loads that write LDS
 // directly, no registers) while the current one is computed. Per tile, with
 // v_mfma_f32_32x32x16_bf16:
@@ -26,8 +27,6 @@ namespace thdcp {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // K/V tiles in LDS: kFwdBN rows of D bf16, unpadded (LDS DMA writes each
@@ -61,8 +60,9 @@ struct DqSmem {
 // the dK/dV kernel, instead of reading it from a separate preprocess launch.
 // BAND: a general key band [g - wl, g + wr]; otherwise the causal mask
 // (wl unbounded, wr = 0, folded at compile time).
-template <int D, bool MAPPED, bool DELTA, bool BAND>
-__global__ void __launch_bounds__(kThreads, 2)
+// WAVES: 4 (128-row tiles) or 8 (256-row tiles); two waves per SIMD either way.
+template <int D, int WAVES, bool MAPPED, bool DELTA, bool BAND>
+__global__ void __launch_bounds__(WAVES * 64, 2)
 attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                    const bf16* __restrict__ k, const bf16* __restrict__ v,
                    const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
@@ -72,6 +72,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
                    float* __restrict__ dq, int64_t n_local, int32_t accumulate,
                    float scale, float scale_log2, int32_t n_attn_blocks, SplitWs split,
                    DqExtras ex) {
+  constexpr int kThreads = WAVES * 64;
   constexpr int BN = kFwdBN;
   constexpr int KSTEPS = D / 16;
   constexpr int DB = D / 32;
@@ -79,8 +80,8 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   constexpr int TILEB = DqSmem<D>::TILEB;
   constexpr int LPR = ROWB / 16;                       // lanes (16-byte chunks) per row
   constexpr int RPI = 1024 / ROWB;                     // rows per wave DMA instruction
-  constexpr int NI = TILEB / 1024 / kWaves;            // DMA instructions per wave per tensor
-  static_assert(NI * kWaves * 1024 == TILEB, "tile splits evenly over the waves");
+  constexpr int NI = TILEB / 1024 / WAVES;             // DMA instructions per wave per tensor
+  static_assert(NI * WAVES * 1024 == TILEB, "tile splits evenly over the waves");
   __shared__ DqSmem<D> sm;
 
   if ((int)blockIdx.x >= n_attn_blocks) {  // gated zeroing workgroups
@@ -338,7 +339,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
     // Split key walk: this part's accumulators go to its scratch slot in lane
     // order; the last part to finish sums all parts in part order.
     auto acc_at = [&](int x, int db, int i4) {
-      return reinterpret_cast<f32x4*>(split_slot(split.part, x, h, H, D)) +
+      return reinterpret_cast<f32x4*>(split_slot<D, WAVES * 32>(split.part, x, h, H)) +
              ((db * 4 + i4) * kThreads + threadIdx.x);
     };
 #pragma unroll
@@ -389,14 +390,15 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
 
 namespace {
 
-template <int D, bool M>
+template <int D, int WAVES, bool M>
 void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int32_t H,
                   const bf16* q, const bf16* k, const bf16* v, const int32_t* kv_row,
                   int32_t kv_sub, uint32_t kvb, Band band, const bf16* d_o, const bf16* o,
                   const float* lse, float* delta, float* dq, int64_t n_local, float scale,
                   int32_t accumulate, int32_t n_attn, SplitWs split, const DqExtras& ex) {
 #define THDCP_DQ(DL, BB)                                                                      \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, M, DL, BB>), dim3((unsigned)blocks), dim3(kThreads), \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, WAVES, M, DL, BB>), dim3((unsigned)blocks),          \
+                     dim3(WAVES * 64),                                                         \
                      0, stream, tiles, H, q, k, v, kv_row, kv_sub, kvb, band.wl, band.wr, d_o,  \
                      o, lse, delta, dq, n_local, accumulate, scale, scale * kLog2e, n_attn, split,  \
                      ex)
@@ -414,7 +416,7 @@ void launch_dq_dm(int64_t blocks, hipStream_t stream, const FwdTile* tiles, int3
 }  // namespace
 
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                              const void* q, const void* k, const void* v, KvRows kv,
+                              int32_t rows, const void* q, const void* k, const void* v, KvRows kv,
                               Band band, const void* d_o, const void* o, const float* lse,
                               float* delta, float* dq, int64_t n_local, float scale,
                               int32_t accumulate, SplitWs split, const DqExtras& ex,
@@ -434,18 +436,20 @@ hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, 
   if (kv.map && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
   const int32_t sub = (int32_t)kv.sub;
-  if (D == 128 && kv.map)
-    launch_dq_dm<128, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
-  else if (D == 128)
-    launch_dq_dm<128, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                             delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
-  else if (D == 64 && kv.map)
-    launch_dq_dm<64, true>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                           delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
-  else if (D == 64)
-    launch_dq_dm<64, false>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob, lse,
-                            delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks, split, ex);
+#define THDCP_DQ_D(DD, WW, MM)                                                                 \
+  launch_dq_dm<DD, WW, MM>(blocks, stream, tiles, H, qb, kb, vb, kv.map, sub, kvb, band, db, ob,  \
+                           lse, delta, dq, n_local, scale, accumulate, (int32_t)attn_blocks,     \
+                           split, ex)
+  const bool mm = kv.map != nullptr;
+  if (D == 128 && rows == kFwdBM)
+    mm ? THDCP_DQ_D(128, 4, true) : THDCP_DQ_D(128, 4, false);
+  else if (D == 128 && rows == kFwdBMLong)
+    mm ? THDCP_DQ_D(128, 8, true) : THDCP_DQ_D(128, 8, false);
+  else if (D == 64 && rows == kFwdBM)
+    mm ? THDCP_DQ_D(64, 4, true) : THDCP_DQ_D(64, 4, false);
+  else if (D == 64 && rows == kFwdBMLong)
+    mm ? THDCP_DQ_D(64, 8, true) : THDCP_DQ_D(64, 8, false);
+#undef THDCP_DQ_D
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

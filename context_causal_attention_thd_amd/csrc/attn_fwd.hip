@@ -7,13 +7,13 @@
 // comm type" (body: the mask is the cp_size = 1 mask). Both DUAL_CHUNK_SWAP
 // chunks of a document are separate query tiles of this one launch.
 //
-// gfx950 design: a workgroup owns up to 128 consecutive query rows of one
-// (document piece, head), in waves of QB 16-row query blocks: 8 waves of 16
-// rows (QB = 1, ~115 registers, four waves per SIMD) or 4 waves of 32 rows
-// (QB = 2, ~190 registers, two per SIMD, each LDS fragment feeding two
-// MFMAs); the plan picks QB = 2 for long walks. Keys are walked from the
-// document start in 64-key tiles, double-buffered in LDS. Everything is
-// computed in the transposed form
+// gfx950 design: a workgroup of 8 waves owns up to 128 or 256 consecutive
+// query rows of one (document piece, head), each wave QB 16-row query blocks:
+// QB = 1 (128 rows, ~120 registers, four waves per SIMD) or QB = 2 (256 rows,
+// ~200 registers, two per SIMD, each LDS fragment feeding two MFMAs and each
+// staged K/V tile serving twice the queries); the plan picks QB = 2 for long
+// walks. Keys are walked from the document start in 64-key tiles,
+// double-buffered in LDS. Everything is computed in the transposed form
 //   S^T = K Q^T  and  O^T = V^T P^T
 // with v_mfma_f32_16x16x32_bf16: lane l owns query column l%16 of each block
 // and keys 4*(l/16) + i of every 16-key block. K fragments are 16-byte LDS
@@ -68,26 +68,25 @@ struct FwdSmem {
   __attribute__((aligned(1024))) char v[2][TILEB];
 };
 
-// QB: 16-row query blocks per wave; the waves of a workgroup cover kFwdBM
-// rows.
-template <int QB>
-constexpr int kFwdThreads = kFwdBM / (16 * QB) * 64;
+// Eight waves per workgroup; QB 16-row query blocks per wave, so a tile holds
+// 128 * QB rows.
+constexpr int kFwdThreads = 512;
 
 // K/V row of key j: j - kv_sub (global order, or one rank's block of it
 // under NO_LOAD_BALANCE), or, when MAPPED, kv_row[j] - kv_sub (rank-major
 // K/V, or one rank's block of it: the restore fused into the loads).
 // BAND: a general key band [g - wl, g + wr]; otherwise the causal mask
 // (wl unbounded, wr = 0, folded at compile time).
-// The second bound is waves per SIMD: two workgroups per CU (the LDS holds
-// two), which caps the registers at 512 / that.
+// The second bound is waves per SIMD: two workgroups per CU with QB = 1, one
+// with QB = 2, which caps the registers at 512 / that.
 template <int D, int QB, bool MAPPED, bool BAND>
-__global__ void __launch_bounds__(kFwdThreads<QB>, 2 * kFwdThreads<QB> / 256)
+__global__ void __launch_bounds__(kFwdThreads, QB == 2 ? 2 : 4)
 attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                 const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
                 int32_t wl_arg, int32_t wr_arg, bf16* __restrict__ o, float* __restrict__ lse,
                 int64_t n_local, float scale_log2, SplitWs split) {
-  constexpr int kThreads = kFwdThreads<QB>;
+  constexpr int kThreads = kFwdThreads;
   constexpr int BN = kFwdBN;
   constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
   constexpr int NB = D / 16;   // 16-wide blocks of the head dim
@@ -397,13 +396,14 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     // in lane order; the last part to finish rescales every part's state to
     // the largest running max and sums them in part order, which is the
     // online softmax's own merge of two key ranges.
-    constexpr int NBLK = kFwdBM / 16;
+    constexpr int NBLK = kThreads / 64 * QB;  // 16-row query blocks per tile
     auto acc_at = [&](int x, int b, int nb) {
-      return reinterpret_cast<f32x4*>(split_slot(split.part, x, h, H, D)) +
+      return reinterpret_cast<f32x4*>(split_slot<D, NBLK * 16>(split.part, x, h, H)) +
              ((b * NB + nb) * 64 + lane);
     };
     auto st_at = [&](int x, int b) {
-      return reinterpret_cast<float2*>(split_slot(split.part, x, h, H, D) + NBLK * NB * 256) +
+      return reinterpret_cast<float2*>(split_slot<D, NBLK * 16>(split.part, x, h, H) +
+                                       NBLK * NB * 256) +
              (b * 64 + lane);
     };
 #pragma unroll
@@ -460,12 +460,13 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   }
 }
 
-// Waves of 16 query rows (QB = 1: eight waves, ~122 registers, four waves per
-// SIMD) or of 32 (QB = 2: four waves, ~220 registers, two per SIMD, every K
-// and V^T fragment read from LDS feeding two MFMAs). The plan picks QB = 2
-// for shares whose average walk is long (measured on MI355X: one 75600-token
-// document 7.7 against 8.5 ms) and QB = 1 otherwise (the multi-document
-// shares' short tiles: 10-15% faster).
+// Tiles of 128 rows (QB = 1: waves of 16 rows, four per SIMD) or 256 (QB = 2:
+// waves of 32 rows, two per SIMD, one workgroup per CU, every K and V^T
+// fragment read from LDS feeding two MFMAs and every staged K/V tile serving
+// 256 queries). The plan picks 256-row tiles for shares whose average walk is
+// long (measured on MI355X: one 75600-token document 6.9-7.0 against 7.3-7.4
+// ms with 128-row tiles of 32-row waves) and 128 otherwise (the
+// multi-document shares' short tiles: 10-15% faster).
 template <int D, int QB>
 hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const bf16* q,
                         const bf16* k, const bf16* v, const int32_t* kv_row, int32_t kv_sub,
@@ -473,7 +474,7 @@ hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const b
                         float scale_log2, SplitWs split, hipStream_t stream) {
 #define THDCP_FWD(MM, BB)                                                                \
   hipLaunchKernelGGL((attn_fwd_kernel<D, QB, MM, BB>), dim3((unsigned)blocks),             \
-                     dim3(kFwdThreads<QB>), 0, stream, tiles, H, q, k, v, kv_row, kv_sub, \
+                     dim3(kFwdThreads), 0, stream, tiles, H, q, k, v, kv_row, kv_sub, \
                      kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2, split)
   if (kv_row && band.causal)
     THDCP_FWD(true, false);
@@ -490,7 +491,7 @@ hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const b
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           int32_t qb, const void* q, const void* k, const void* v, KvRows kv,
+                           int32_t rows, const void* q, const void* k, const void* v, KvRows kv,
                            Band band, void* o, float* lse, int64_t n_local, float scale,
                            SplitWs split, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
@@ -507,10 +508,10 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
 #define THDCP_FWD_D(DD, QQ)                                                                   \
   return launch_fwd_d<DD, QQ>(tiles, blocks, H, qp, kb, vb, kv.map, (int32_t)kv.sub, kvb, band, \
                               ob, lse, n_local, scale_log2, split, stream)
-  if (D == 128 && qb == 2) THDCP_FWD_D(128, 2);
-  if (D == 128 && qb == 1) THDCP_FWD_D(128, 1);
-  if (D == 64 && qb == 2) THDCP_FWD_D(64, 2);
-  if (D == 64 && qb == 1) THDCP_FWD_D(64, 1);
+  if (D == 128 && rows == kFwdBMLong) THDCP_FWD_D(128, 2);
+  if (D == 128 && rows == kFwdBM) THDCP_FWD_D(128, 1);
+  if (D == 64 && rows == kFwdBMLong) THDCP_FWD_D(64, 2);
+  if (D == 64 && rows == kFwdBM) THDCP_FWD_D(64, 1);
 #undef THDCP_FWD_D
   return hipErrorInvalidValue;
 }

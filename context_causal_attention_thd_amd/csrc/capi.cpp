@@ -140,9 +140,9 @@ struct thdcp_plan {
   // Split key walks of the all-gather forward / dQ tiles: groups (one counter
   // per group and head) and scratch slots (one per part and head).
   int32_t split_groups = 0, split_slots = 0, split_tiles = 0;
-  // Forward wave shape (16-row query blocks per wave): 2 when the average
-  // query walks at least kLongWalk keys, else 1 (see launch_attn_fwd).
-  int32_t fwd_qb = 1;
+  // Query rows per forward / dQ tile: kFwdBMLong when the average query
+  // walks at least kLongWalk keys (all-gather plans), else kFwdBM.
+  int32_t fwd_rows = kFwdBM;
   std::vector<char> blob;  // host image of the device tables (and zeroed counters)
   size_t off_fwd = 0, off_bwd = 0, off_zero = 0, off_kvrow = 0, ws_bytes = 0;
   size_t off_sfwd = 0, off_sbwd = 0, off_szero = 0, off_cnt = 0, off_part = 0;
@@ -229,18 +229,20 @@ std::vector<Tile> lpt_order(const std::vector<Tile>& tiles, Cost cost) {
 // a prologue; hence the kSplitImbalance threshold for the automatic choice
 // (a forced max_parts >= 2 splits from the balanced load on). Returns the
 // table in LPT order.
-constexpr int64_t kConcurrentWGs = 512;  // 256 CUs x 2 forward (or dQ) workgroups
+// 256 CUs x 2 forward (or dQ) workgroups of 128-row tiles, x 1 of 256-row tiles
+constexpr int64_t kConcurrentWGs = 512;
 constexpr int64_t kMinPartTiles = 6;     // shorter parts do not repay their merge
 constexpr double kSplitImbalance = 1.75;
 constexpr int32_t kMaxParts = 8;
 
-std::vector<FwdTile> split_walks(const std::vector<FwdTile>& tiles, int32_t H, int32_t max_parts,
-                                 int32_t* n_groups, int32_t* n_slots, int32_t* n_split) {
+std::vector<FwdTile> split_walks(const std::vector<FwdTile>& tiles, int32_t H, int32_t rows,
+                                 int32_t max_parts, int32_t* n_groups, int32_t* n_slots,
+                                 int32_t* n_split) {
   int64_t total = 0;
   for (const FwdTile& t : tiles) total += fwd_cost(t);
   total *= H;
-  const int64_t target =
-      std::max<int64_t>(kMinPartTiles, (total + kConcurrentWGs - 1) / kConcurrentWGs);
+  const int64_t wgs = kConcurrentWGs * kFwdBM / rows;
+  const int64_t target = std::max<int64_t>(kMinPartTiles, (total + wgs - 1) / wgs);
   int64_t longest = 0;
   for (const FwdTile& t : tiles) longest = std::max(longest, fwd_cost(t));
   int32_t cap = max_parts == 0 ? kMaxParts : std::min(max_parts, kMaxParts);
@@ -436,14 +438,26 @@ void build_plan(thdcp_plan& p) {
     }
   }
 
+  // Query rows per forward / dQ tile. 256-row tiles (8 waves of 32 rows, one
+  // workgroup per CU) stage each K/V tile once for twice the queries and feed
+  // two MFMAs per LDS fragment, but keep one workgroup per CU instead of two,
+  // which pays only where walks are long enough to hide each workgroup's
+  // start (measured on MI355X, one 75600-token document: forward -5%, dQ even,
+  // against 128-row tiles of 32-row waves; shares of documents of a few
+  // thousand tokens: 10-15% slower). P2P steps walk one rank's keys each and
+  // keep 128.
+  constexpr int64_t kLongWalk = 4096;
+  p.fwd_rows = !d.p2p && p.pairs >= kLongWalk * std::max<int64_t>(1, p.n_local) ? kFwdBMLong
+                                                                                  : kFwdBM;
+
   // Forward tiles, longest first (LPT order over the workgroup queue).
   std::vector<FwdTile> fwd;
   std::vector<int32_t> fwd_doc;
   for (const Segment& s : segs) {
-    for (int64_t off = 0; off < s.len; off += kFwdBM) {
+    for (int64_t off = 0; off < s.len; off += p.fwd_rows) {
       FwdTile t{};
       t.m0 = (int32_t)(s.m0 + off);
-      t.n = (int32_t)std::min<int64_t>(kFwdBM, s.len - off);
+      t.n = (int32_t)std::min<int64_t>(p.fwd_rows, s.len - off);
       t.g0 = (int32_t)(s.g0 + off);
       t.e = (int32_t)s.e;
       // keys of the tile's real rows [g0, rend): from the first row's band
@@ -456,13 +470,8 @@ void build_plan(thdcp_plan& p) {
     }
   }
   p.fwd = split_walks(lpt_order(fwd, [](const FwdTile& t) { return fwd_cost(t); }), d.H,
-                      d.max_key_splits, &p.split_groups, &p.split_slots, &p.split_tiles);
-  // 32-row forward waves halve the LDS reads per MFMA but run two waves per
-  // SIMD instead of four, which pays only where walks are long enough to
-  // hide each workgroup's start (one 75600-token document: -10%; shares of
-  // documents of a few thousand tokens: +10-15%).
-  constexpr int64_t kLongWalk = 4096;
-  p.fwd_qb = p.pairs >= kLongWalk * std::max<int64_t>(1, p.n_local) ? 2 : 1;
+                      p.fwd_rows, d.max_key_splits, &p.split_groups, &p.split_slots,
+                      &p.split_tiles);
 
   // Backward tiles: per document, the keys its local real rows attend -- per
   // run of consecutive rows, from the first row's band start to the last
@@ -584,7 +593,8 @@ void build_plan(thdcp_plan& p) {
   p.off_szero = align256(p.off_sbwd + p.step_bwd.size() * sizeof(BwdTile));
   p.off_cnt = align256(p.off_szero + p.step_zero.size() * sizeof(ZeroRange));
   p.off_part = align256(p.off_cnt + (size_t)p.split_groups * d.H * sizeof(int32_t));
-  p.ws_bytes = p.off_part + (size_t)p.split_slots * d.H * kSplitFloats(d.D) * sizeof(float);
+  p.ws_bytes =
+      p.off_part + (size_t)p.split_slots * d.H * kSplitFloats(d.D, p.fwd_rows) * sizeof(float);
   if (p.ws_bytes == 0) p.ws_bytes = 256;
   // the image covers the tables and the split counters (zero), not the scratch
   p.blob.assign(std::max<size_t>(p.off_part, 256), 0);
@@ -833,6 +843,8 @@ thdcp_status_t thdcp_plan_get_info(thdcp_plan_t p, thdcp_plan_info* info) {
   info->bwd_scratch_bytes = align256((size_t)p->n_local * p->desc.H * sizeof(float));
   info->n_split_tiles = p->split_tiles;
   info->n_fwd_parts = (int32_t)p->fwd.size();
+  info->fwd_tile_rows = p->fwd_rows;
+  info->reserved = 0;
   return ok();
 }
 
@@ -986,7 +998,7 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, p->fwd_qb, q, k, v,
+                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, p->fwd_rows, q, k, v,
                       kv_map(p), p->band, o, lse, p->n_local, p->scale, split_ws(p),
                       (hipStream_t)stream),
       "cp_attn_fwd launch");
@@ -1069,7 +1081,8 @@ thdcp_status_t cp_attn_bwd_dq(thdcp_plan_t p, const void* q, const void* k, cons
   if (p->fwd.empty()) return ok();
   return hip_status(
       launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o,
+                         (int32_t)p->fwd.size(), p->desc.H, p->desc.D, p->fwd_rows, q, k, v,
+                         kv_map(p), p->band, d_o,
                          nullptr, lse, static_cast<float*>(const_cast<void*>(scratch)), dq,
                          p->n_local, p->scale, 0, split_ws(p), DqExtras{}, (hipStream_t)stream),
       "cp_attn_bwd_dq launch");
@@ -1140,8 +1153,8 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
   }
   {
     hipError_t e = launch_attn_bwd_dq(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
-                                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D, q, k, v,
-                                      kv_map(p), p->band, d_o, o, lse, delta, dq, p->n_local,
+                                      (int32_t)p->fwd.size(), p->desc.H, p->desc.D,
+                                      p->fwd_rows, q, k, v, kv_map(p), p->band, d_o, o, lse, delta, dq, p->n_local,
                                       p->scale, 0, split_ws(p), ex, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dq launch");
   }
@@ -1183,7 +1196,8 @@ thdcp_status_t cp_attn_fwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   if (sp.n_fwd == 0) return ok();
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0,
-                      sp.n_fwd, p->desc.H, p->desc.D, 1, q, k, v, kv_step(p, src), p->band, o, lse,
+                      sp.n_fwd, p->desc.H, p->desc.D, p->fwd_rows, q, k, v, kv_step(p, src),
+                      p->band, o, lse,
                       p->n_local, p->scale, SplitWs{}, (hipStream_t)stream),
       "cp_attn_fwd_step launch");
 }
@@ -1231,7 +1245,8 @@ thdcp_status_t cp_attn_bwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   if (sp.n_fwd > 0 || ex.zr) {
     hipError_t e = launch_attn_bwd_dq(
         reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0, sp.n_fwd,
-        p->desc.H, p->desc.D, q, k, v, kv, p->band, d_o, nullptr, lse, delta, dq, p->n_local,
+        p->desc.H, p->desc.D, p->fwd_rows, q, k, v, kv, p->band, d_o, nullptr, lse, delta, dq,
+        p->n_local,
         p->scale, accumulate_dq != 0, SplitWs{}, ex, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dq launch");
   }

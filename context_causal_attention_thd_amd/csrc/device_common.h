@@ -222,9 +222,11 @@ __device__ inline bool split_arrive(int32_t* cnt, int32_t nparts) {
   return s_last != 0;
 }
 
-// Scratch of one part of a split key walk (slot x, head h).
-__device__ inline float* split_slot(float* part, int32_t x, int32_t h, int32_t H, int D) {
-  return part + ((int64_t)x * H + h) * kSplitFloats(D);
+// Scratch of one part of a split key walk (slot x, head h) of a kernel whose
+// tiles hold ROWS query rows of D dims.
+template <int D, int ROWS>
+__device__ inline float* split_slot(float* part, int32_t x, int32_t h, int32_t H) {
+  return part + ((int64_t)x * H + h) * kSplitFloats(D, ROWS);
 }
 
 }  // namespace thdcp

@@ -12,8 +12,8 @@ namespace thdcp {
 // Sets the thread's thdcp_last_error() text and returns st (capi.cpp).
 thdcp_status_t report_error(thdcp_status_t st, const char* msg);
 
-// Forward work item: up to kFwdBM consecutive local rows that lie in one
-// contiguous run of global rows of one document (a DUAL_CHUNK_SWAP chunk or a
+// Forward work item: up to kFwdBM (or kFwdBMLong) consecutive local rows that
+// lie in one contiguous run of global rows of one document (a DUAL_CHUNK_SWAP chunk or a
 // NO_LOAD_BALANCE document piece), so row r of the tile is global row g0 + r.
 // The keys it attends are walked in doc-aligned blocks over [ks0, ke0), then
 // over [ks1, ke1) (either range may be empty): the whole causal range
@@ -29,7 +29,7 @@ thdcp_status_t report_error(thdcp_status_t st, const char* msg);
 // result does not depend on which part finished last.
 struct FwdTile {
   int32_t m0;        // first local row
-  int32_t n;         // rows in the tile (<= kFwdBM)
+  int32_t n;         // rows in the tile (<= the plan's tile rows)
   int32_t g0;        // global row of m0
   int32_t e;         // end of the document's real tokens (a + actual length)
   int32_t ks0, ke0;  // first key range
@@ -59,15 +59,18 @@ struct ZeroRange {
   int32_t pad0;
 };
 
-constexpr int kFwdBM = 128;  // query rows per forward / dQ workgroup
-constexpr int kFwdBN = 64;   // keys per forward K/V tile
-constexpr int kBwdBN = 128;  // keys per backward workgroup (4 waves x 32)
+constexpr int kFwdBM = 128;      // query rows per forward / dQ workgroup
+constexpr int kFwdBMLong = 256;  // the same for plans whose walks are long
+constexpr int kFwdBN = 64;       // keys per forward K/V tile
+constexpr int kBwdBN = 128;      // keys per backward workgroup (4 waves x 32)
 
-// Scratch of split key walks: per (slot, head) kSplitFloats(D) floats hold
-// one part's partial result (forward: accumulators, running max and row-sum
-// shares; dQ: accumulators), in the owning kernel's lane order; cnt[group * H
-// + head] counts the parts that have finished (0 between launches).
-constexpr int64_t kSplitFloats(int D) { return 128 * (int64_t)D + 1024; }
+// Scratch of split key walks: per (slot, head) kSplitFloats(D, rows) floats
+// hold one part's partial result for a tile of `rows` query rows (forward:
+// rows x D accumulators, then a running max and row-sum share per 16-row block
+// and lane; dQ: rows x D accumulators), in the owning kernel's lane order;
+// cnt[group * H + head] counts the parts that have finished (0 between
+// launches).
+constexpr int64_t kSplitFloats(int D, int rows) { return (int64_t)rows * (D + 8); }
 struct SplitWs {
   int32_t* cnt;
   float* part;
@@ -125,9 +128,10 @@ hipError_t launch_lse_merge_parts(int64_t n, int32_t H, int32_t D, int32_t parts
                                   float* lse_out, hipStream_t stream);
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
-// qb: 16-row query blocks per wave of the forward kernel (1 or 2).
+// rows: query rows per tile of the plan (kFwdBM or kFwdBMLong); the forward
+// and dQ launches pick their wave shape from it.
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                           int32_t qb, const void* q, const void* k, const void* v, KvRows kv,
+                           int32_t rows, const void* q, const void* k, const void* v, KvRows kv,
                            Band band, void* o, float* lse, int64_t n_local, float scale,
                            SplitWs split, hipStream_t stream);
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
@@ -150,7 +154,7 @@ struct DqExtras {
 // and written to `delta` for the dK/dV kernel; otherwise `delta` is read.
 // accumulate: add to dq (P2P steps after the first) instead of writing it.
 hipError_t launch_attn_bwd_dq(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                              const void* q, const void* k, const void* v, KvRows kv,
+                              int32_t rows, const void* q, const void* k, const void* v, KvRows kv,
                               Band band, const void* d_o, const void* o, const float* lse,
                               float* delta,
                               float* dq, int64_t n_local, float scale, int32_t accumulate,

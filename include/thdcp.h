@@ -270,6 +270,10 @@ typedef struct {
   size_t bwd_scratch_bytes;  /* device bytes cp_attn_bwd needs as scratch */
   int32_t n_split_tiles;     /* query tiles whose key walk is split */
   int32_t n_fwd_parts;       /* workgroups per head of a forward / dQ launch */
+  int32_t fwd_tile_rows;     /* query rows per forward / dQ tile: 256 where the
+                                average local query walks >= 4096 keys (not
+                                P2P plans), else 128 */
+  int32_t reserved;          /* 0 */
 } thdcp_plan_info;
 
 /* Build a plan on the host. *plan_out receives a host object the caller

@@ -316,12 +316,22 @@ def test_plan_split_walks(L):
     x = W.WORKLOADS["dcs_8k"]
     assert forced.info.workspace_bytes - never.info.workspace_bytes >= \
         2 * forced.info.n_split_tiles * x.H * (128 * x.D + 1024) * 4
-    # one 16k-token document over 4 heads: 512 workgroups whose walks run
-    # from 2 to 256 key tiles (twice the balanced load) -- split in two
+    # one 16k-token document over 4 heads: long walks, so 256-row tiles (one
+    # workgroup per CU, 256 at once): 256 workgroups whose walks run from 4 to
+    # 256 key tiles (about twice the balanced load of 130) -- the upper half
+    # split in two
     doc = thd.Plan([0, 16384], [0, 16384], 16384, 1, 0, "no_load_balance", 4, 128,
                    upload=False)
-    assert doc.info.n_fwd_tiles == 128 and doc.info.n_split_tiles == 64
-    assert doc.info.n_fwd_parts == 192
+    assert doc.info.fwd_tile_rows == 256
+    assert doc.info.n_fwd_tiles == 64 and doc.info.n_split_tiles == 32
+    assert doc.info.n_fwd_parts == 96
+    # the same document as a P2P plan keeps 128-row tiles: 512 workgroups,
+    # walks of 2 to 256 key tiles against a balanced load of 65
+    p2p = thd.Plan([0, 16384], [0, 16384], 16384, 1, 0, "no_load_balance", 4, 128,
+                   upload=False, p2p=True)
+    assert p2p.info.fwd_tile_rows == 128
+    assert p2p.info.n_fwd_tiles == 128 and p2p.info.n_split_tiles == 64
+    p2p.close()
     # the same document under DUAL_CHUNK_SWAP, cp_size 4: walks within 1.25x
     # of the balance, left whole
     dcs = thd.Plan([0, 32768], [0, 32768], 32768, 4, 3, "dual_chunk_swap", 8, 128,

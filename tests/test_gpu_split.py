@@ -154,7 +154,8 @@ def test_split_auto_long_document_full_size():
     t = W.bf16_tensors(w)
     split = run_share(w, 0, t)
     whole = run_share(w, 0, t, max_key_splits=1)
-    assert split["plan"].info.n_split_tiles == 64
+    assert split["plan"].info.fwd_tile_rows == 256
+    assert split["plan"].info.n_split_tiles == 32
     assert whole["plan"].info.n_split_tiles == 0
     rng = np.random.default_rng(11)
     rows = sorted(set(rng.choice(w.T, size=48, replace=False).tolist()) | {0, w.T - 1})
