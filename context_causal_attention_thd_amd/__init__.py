@@ -74,7 +74,7 @@ class PlanInfo(ctypes.Structure):
         ("n_split_tiles", ctypes.c_int32),
         ("n_fwd_parts", ctypes.c_int32),
         ("fwd_tile_rows", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("bwd_tile_keys", ctypes.c_int32),
     ]
 
 

@@ -6,8 +6,8 @@
 // query rows that are not real tokens are not listed, key rows past the tile
 // end are zeroed, and masked probabilities are selected to 0 (NaN-safe).
 //
-// gfx950 design: a workgroup of 4 waves owns 128 consecutive keys of one
-// document, 32 per wave (two 16-key blocks), with the K fragments in
+// gfx950 design: a workgroup of 4 or 8 waves owns 128 or 256 consecutive keys
+// of one document, 32 per wave (two 16-key blocks), with the K fragments in
 // registers and the V rows in LDS, and walks the local query rows that attend
 // them in blocks of 32. Query blocks (Q, dO, LSE, delta) are double-buffered
 // in LDS and the next block's global loads are in flight while the current
@@ -21,9 +21,11 @@
 // LDS reads of the row-major tiles. Every Q / dO fragment read from LDS feeds
 // both key blocks, so a wave reads 0.625 KB of LDS per MFMA (1 KB with 16 keys
 // per wave, which made the LDS as busy as the MFMA pipe). At <= 256 registers
-// per wave and ~75 KB of LDS per workgroup, two workgroups share a CU (two
-// waves per SIMD), and one workgroup's prologue and stores overlap the other's
-// block loop.
+// per wave and ~75 KB of LDS per workgroup, two 4-wave workgroups share a CU
+// (two waves per SIMD), and one workgroup's prologue and stores overlap the
+// other's block loop. Plans whose query walks are long use one 8-wave
+// workgroup per CU instead (~112 KB of LDS), which stages each query block
+// once for twice the keys.
 #include <atomic>
 
 #include "device_common.h"
@@ -33,12 +35,10 @@ namespace thdcp {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kBM = 32;  // query rows per block (two 16-query M-blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
+template <int D, int WAVES>
 struct BwdSmem {
   static constexpr int P = D + 16;     // Q / dO row pitch (bf16)
   bf16 q[2][kBM * P];
@@ -47,13 +47,14 @@ struct BwdSmem {
   float dlt[2][kBM];
   int32_t ghi[2][kBM];  // last key a query row attends (g + wr); -1 past the row range
   int32_t glo[2][kBM];  // first key (g - wl); read only for non-causal bands
-  bf16 v[kWaves * 32 * P];  // the tile's V rows (wave w's keys at rows 32w..), pitch P
+  bf16 v[WAVES * 32 * P];  // the tile's V rows (wave w's keys at rows 32w..), pitch P
 };
 
 // BAND: the mask is a general band [g - wl, g + wr] (a lower-bound test
-// per element); otherwise it is causal (key <= g only).
-template <int D, bool BAND>
-__global__ void __launch_bounds__(kThreads, 2)
+// per element); otherwise it is causal (key <= g only). WAVES: 4 (128-key
+// tiles) or 8 (256-key tiles); two waves per SIMD either way.
+template <int D, int WAVES, bool BAND>
+__global__ void __launch_bounds__(WAVES * 64, 2)
 attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                      const bf16* __restrict__ k, const bf16* __restrict__ v,
                      const int32_t* __restrict__ kv_row, int32_t kv_sub, int32_t wl, int32_t wr,
@@ -65,8 +66,11 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   constexpr int KS = D / 32;
   constexpr int NB = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int CH = kBM * CPR / kThreads;
-  typedef BwdSmem<D> S;
+  constexpr int kThreads = WAVES * 64;
+  constexpr int CHUNKS = kBM * CPR;                       // 16-byte chunks per block
+  constexpr int CH = (CHUNKS + kThreads - 1) / kThreads;  // staging chunks per thread
+  constexpr bool kPartial = CHUNKS % kThreads != 0;       // some threads stage nothing
+  typedef BwdSmem<D, WAVES> S;
   constexpr int P = S::P;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   S& sm = *reinterpret_cast<S*>(smem_raw);
@@ -90,6 +94,9 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   };
   // Lane l16 of key block nk holds key t.k0 + 32w + 16nk + l16: the column of
   // S / dP and the row of the dV / dK A operand.
+  // This wave's keys: [wave_kmin, wave_kmax], all below the tile end or not.
+  const int wave_kmin = t.k0 + w * 32, wave_kmax = wave_kmin + 31;
+  const bool wave_keys_ok = wave_kmax < t.k1;
   int my_key[2];
   bool key_ok[2];
   bf16x8 kf[2][KS];
@@ -125,12 +132,16 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
       }
 
   // Per-thread staging slots: chunk c = threadIdx + j*kThreads is row c/CPR,
-  // 16-byte column c%CPR of the query block.
+  // 16-byte column c%CPR of the query block. When the chunks do not fill the
+  // last round (head dim 64 over 8 waves), the waves past them stage nothing
+  // in it (a whole-wave condition: CHUNKS is a multiple of 64).
+  const bool stages_last = !kPartial || (int)threadIdx.x + (CH - 1) * kThreads < CHUNKS;
+  auto has_chunk = [&](int j) { return j < CH - 1 || stages_last; };
   uint32_t goff[CH];
   int soff[CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    const int c = threadIdx.x + j * kThreads;
+    const int c = has_chunk(j) ? threadIdx.x + j * kThreads : 0;
     const int rr = c / CPR, dc = c - rr * CPR;
     goff[j] = (uint32_t)(rr * rs * 2 + dc * 16);
     soff[j] = rr * P + dc * 8;
@@ -148,8 +159,10 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(d_o + base, bytes);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      qreg[j] = buffer_load16(rq, goff[j]);
-      dreg[j] = buffer_load16(rd, goff[j]);
+      if (has_chunk(j)) {
+        qreg[j] = buffer_load16(rq, goff[j]);
+        dreg[j] = buffer_load16(rd, goff[j]);
+      }
     }
     if (wave_uniform(w) == 0) {  // wave 0 fetches the block's per-row scalars
       const int64_t row = (int64_t)h * n_local + mb;
@@ -165,8 +178,10 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      *reinterpret_cast<u32x4*>(&sm.q[buf][soff[j]]) = qreg[j];
-      *reinterpret_cast<u32x4*>(&sm.dO[buf][soff[j]]) = dreg[j];
+      if (has_chunk(j)) {
+        *reinterpret_cast<u32x4*>(&sm.q[buf][soff[j]]) = qreg[j];
+        *reinterpret_cast<u32x4*>(&sm.dO[buf][soff[j]]) = dreg[j];
+      }
     }
     if (wave_uniform(w) == 0 && lane < kBM) {
       sm.lse2[buf][lane] = lreg * kLog2e;
@@ -218,24 +233,46 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
         }
       }
     }
+    // P = exp2(S * scale_log2 - LSE_2) and dS = P (dP - delta). A masked
+    // element takes exponent -inf, so P = 0 and dS = 0 with no branch (dP is
+    // finite: rows past the range and keys past the tile load as zeros). The
+    // per-element mask is only evaluated on blocks that need it: a block whose
+    // rows are all real and whose bands hold all of this wave's keys (rows'
+    // band ends rise with the row, and are -1 past the range) skips it.
+    const int blk_hi = min(sm.ghi[cur][0], sm.ghi[cur][kBM - 1]);
+    bool inside = wave_keys_ok && blk_hi >= wave_kmax;
+    if constexpr (BAND) inside = inside && sm.glo[cur][kBM - 1] <= wave_kmin;
+    const bool masked = wave_uniform(!inside) != 0;
 #pragma unroll
     for (int qm = 0; qm < 2; ++qm) {
       const int qr0 = qm * 16 + G * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
-      const i32x4 hi4 = *reinterpret_cast<const i32x4*>(&sm.ghi[cur][qr0]);
-      i32x4 lo4 = {0, 0, 0, 0};
-      if constexpr (BAND) lo4 = *reinterpret_cast<const i32x4*>(&sm.glo[cur][qr0]);
+      if (masked) {
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(&sm.ghi[cur][qr0]);
+        i32x4 lo4 = {0, 0, 0, 0};
+        if constexpr (BAND) lo4 = *reinterpret_cast<const i32x4*>(&sm.glo[cur][qr0]);
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bool ok = key_ok[nk] & (my_key[nk] <= hi4[i]);
+            if constexpr (BAND) ok &= my_key[nk] >= lo4[i];
+            s[qm][nk][i] = ok ? fmaf(s[qm][nk][i], scale_log2, -l4[i]) : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[qm][nk][i] = fmaf(s[qm][nk][i], scale_log2, -l4[i]);
+      }
 #pragma unroll
       for (int nk = 0; nk < 2; ++nk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          bool ok = key_ok[nk] & (my_key[nk] <= hi4[i]);
-          if constexpr (BAND) ok &= my_key[nk] >= lo4[i];
-          const float p = ok ? fast_exp2(fmaf(s[qm][nk][i], scale_log2, -l4[i])) : 0.f;
-          const float dsv = ok ? p * (dp[qm][nk][i] - d4[i]) : 0.f;
+          const float p = fast_exp2(s[qm][nk][i]);
           s[qm][nk][i] = p;
-          dp[qm][nk][i] = dsv;
+          dp[qm][nk][i] = p * (dp[qm][nk][i] - d4[i]);
         }
     }
     // dV += P^T dO, dK += dS^T Q over the block's 32 queries (one k-step):
@@ -305,7 +342,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   }
 }
 
-template <int D, bool BAND>
+template <int D, int WAVES, bool BAND>
 hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const void* q,
                         const void* k, const void* v, const int32_t* kv_row, int32_t kv_sub,
                         Band band, const void* d_o, const float* lse, const float* delta, float* dk,
@@ -314,7 +351,7 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const size_t smem = sizeof(BwdSmem<D>);
+  const size_t smem = sizeof(BwdSmem<D, WAVES>);
   // The dynamic-LDS limit is a per-device function attribute: set it once per device.
   static std::atomic<uint64_t> attr_set{0};
   int dev = 0;
@@ -322,12 +359,13 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_set.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, BAND>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, WAVES, BAND>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit);
   }
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BAND>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, WAVES, BAND>), dim3((unsigned)blocks),
+                     dim3(WAVES * 64),
                      smem, stream, tiles, H, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v), kv_row, kv_sub,
                      band.wl, band.wr, static_cast<const bf16*>(d_o),
@@ -338,18 +376,32 @@ hipError_t launch_bwd_d(const BwdTile* tiles, int32_t n_tiles, int32_t H, const 
 }  // namespace
 
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                                const void* q, const void* k, const void* v, KvRows kv,
+                                int32_t keys, const void* q, const void* k, const void* v, KvRows kv,
                                 Band band, const void* d_o, const float* lse,
                                 const float* delta, float* dk, float* dv, int64_t n_local,
                                 float scale, int32_t accumulate, hipStream_t stream) {
   const int32_t sub = (int32_t)kv.sub;
-#define THDCP_DKDV(DD, BB)                                                                   \
-  return launch_bwd_d<DD, BB>(tiles, n_tiles, H, q, k, v, kv.map, sub, band, d_o, lse, delta, \
-                              dk, dv, n_local, scale, accumulate, stream)
-  if (D == 128 && band.causal) THDCP_DKDV(128, false);
-  if (D == 128) THDCP_DKDV(128, true);
-  if (D == 64 && band.causal) THDCP_DKDV(64, false);
-  if (D == 64) THDCP_DKDV(64, true);
+#define THDCP_DKDV(DD, WW, BB)                                                                \
+  return launch_bwd_d<DD, WW, BB>(tiles, n_tiles, H, q, k, v, kv.map, sub, band, d_o, lse,     \
+                                  delta, dk, dv, n_local, scale, accumulate, stream)
+  if (keys != kBwdBN && keys != kBwdBNLong) return hipErrorInvalidValue;
+  const bool wide = keys == kBwdBNLong;
+  if (D == 128 && band.causal) {
+    if (wide) THDCP_DKDV(128, 8, false);
+    THDCP_DKDV(128, 4, false);
+  }
+  if (D == 128) {
+    if (wide) THDCP_DKDV(128, 8, true);
+    THDCP_DKDV(128, 4, true);
+  }
+  if (D == 64 && band.causal) {
+    if (wide) THDCP_DKDV(64, 8, false);
+    THDCP_DKDV(64, 4, false);
+  }
+  if (D == 64) {
+    if (wide) THDCP_DKDV(64, 8, true);
+    THDCP_DKDV(64, 4, true);
+  }
 #undef THDCP_DKDV
   return hipErrorInvalidValue;
 }

@@ -140,9 +140,11 @@ struct thdcp_plan {
   // Split key walks of the all-gather forward / dQ tiles: groups (one counter
   // per group and head) and scratch slots (one per part and head).
   int32_t split_groups = 0, split_slots = 0, split_tiles = 0;
-  // Query rows per forward / dQ tile: kFwdBMLong when the average query
-  // walks at least kLongWalk keys (all-gather plans), else kFwdBM.
+  // Query rows per forward / dQ tile and keys per dK/dV tile: kFwdBMLong and
+  // kBwdBNLong when the average query walks at least kLongWalk keys
+  // (all-gather plans), else kFwdBM and kBwdBN.
   int32_t fwd_rows = kFwdBM;
+  int32_t bwd_keys = kBwdBN;
   std::vector<char> blob;  // host image of the device tables (and zeroed counters)
   size_t off_fwd = 0, off_bwd = 0, off_zero = 0, off_kvrow = 0, ws_bytes = 0;
   size_t off_sfwd = 0, off_sbwd = 0, off_szero = 0, off_cnt = 0, off_part = 0;
@@ -335,14 +337,14 @@ std::vector<DocRows> doc_rows(const std::vector<Segment>& segs) {
   return out;
 }
 
-// Key tiles of kBwdBN keys over [lo, hi) of one document; each lists the
+// Key tiles of `keys` keys over [lo, hi) of one document; each lists the
 // contiguous local query range that can attend it: real rows with
 // g + wr >= k0 and g - wl <= k1 - 1 (causal: the rows with g >= k0). Local
 // rows of a document ascend in g, so that range is contiguous.
-void add_key_tiles(const DocRows& dr, const Band& band, int64_t lo, int64_t hi,
+void add_key_tiles(const DocRows& dr, const Band& band, int64_t keys, int64_t lo, int64_t hi,
                    std::vector<BwdTile>& out) {
-  for (int64_t k0 = lo; k0 < hi; k0 += kBwdBN) {
-    const int64_t k1 = std::min<int64_t>(k0 + kBwdBN, hi);
+  for (int64_t k0 = lo; k0 < hi; k0 += keys) {
+    const int64_t k1 = std::min<int64_t>(k0 + keys, hi);
     const int64_t gfirst = k0 - band.wr, glast = k1 - 1 + (int64_t)band.wl;
     int64_t m_lo = -1;  // first local row with g >= gfirst
     for (const DocRows::Run& rn : dr.runs) {
@@ -438,17 +440,19 @@ void build_plan(thdcp_plan& p) {
     }
   }
 
-  // Query rows per forward / dQ tile. 256-row tiles (8 waves of 32 rows, one
-  // workgroup per CU) stage each K/V tile once for twice the queries and feed
-  // two MFMAs per LDS fragment, but keep one workgroup per CU instead of two,
-  // which pays only where walks are long enough to hide each workgroup's
-  // start (measured on MI355X, one 75600-token document: forward -5%, dQ even,
-  // against 128-row tiles of 32-row waves; shares of documents of a few
-  // thousand tokens: 10-15% slower). P2P steps walk one rank's keys each and
-  // keep 128.
+  // Tile sizes. 256-row query tiles (8 waves of 32 rows, one workgroup per
+  // CU) stage each K/V tile once for twice the queries and feed two MFMAs per
+  // LDS fragment, and 256-key dK/dV tiles (8 waves, one workgroup per CU)
+  // stage each query block once for twice the keys, but both keep one
+  // workgroup per CU instead of two, which pays only where walks are long
+  // enough to hide each workgroup's start. Measured on MI355X, one
+  // 75600-token document: forward -5%, dQ even, dK/dV -5..-6%; shares of
+  // documents of a few thousand tokens: 5-15% slower. P2P steps walk one
+  // rank's keys each and keep the small tiles.
   constexpr int64_t kLongWalk = 4096;
-  p.fwd_rows = !d.p2p && p.pairs >= kLongWalk * std::max<int64_t>(1, p.n_local) ? kFwdBMLong
-                                                                                  : kFwdBM;
+  const bool long_walks = !d.p2p && p.pairs >= kLongWalk * std::max<int64_t>(1, p.n_local);
+  p.fwd_rows = long_walks ? kFwdBMLong : kFwdBM;
+  p.bwd_keys = long_walks ? kBwdBNLong : kBwdBN;
 
   // Forward tiles, longest first (LPT order over the workgroup queue).
   std::vector<FwdTile> fwd;
@@ -490,7 +494,7 @@ void build_plan(thdcp_plan& p) {
         ivs.push_back({x0, x1});
     }
     for (const auto& iv : ivs) {
-      add_key_tiles(dr, p.band, iv.first, iv.second, bwd);
+      add_key_tiles(dr, p.band, p.bwd_keys, iv.first, iv.second, bwd);
       touched.push_back(iv);
     }
   }
@@ -560,7 +564,7 @@ void build_plan(thdcp_plan& p) {
         for (int r = 0; r < nr; ++r) {
           const int64_t x0 = std::max(lo[r], dr.a), x1 = std::min(hi[r], dr.gmax + 1);
           if (x1 <= x0) continue;
-          add_key_tiles(dr, p.band, x0, x1, sb);
+          add_key_tiles(dr, p.band, p.bwd_keys, x0, x1, sb);
           st_touched.push_back({x0, x1});
         }
       }
@@ -844,7 +848,7 @@ thdcp_status_t thdcp_plan_get_info(thdcp_plan_t p, thdcp_plan_info* info) {
   info->n_split_tiles = p->split_tiles;
   info->n_fwd_parts = (int32_t)p->fwd.size();
   info->fwd_tile_rows = p->fwd_rows;
-  info->reserved = 0;
+  info->bwd_tile_keys = p->bwd_keys;
   return ok();
 }
 
@@ -1063,7 +1067,8 @@ thdcp_status_t cp_attn_bwd_dkdv(thdcp_plan_t p, const void* q, const void* k, co
   if (p->bwd.empty()) return ok();
   return hip_status(
       launch_attn_bwd_dkdv(reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd),
-                           (int32_t)p->bwd.size(), p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band,
+                           (int32_t)p->bwd.size(), p->desc.H, p->desc.D, p->bwd_keys, q, k, v,
+                           kv_map(p), p->band,
                            d_o, lse, static_cast<const float*>(scratch), dk, dv, p->n_local,
                            p->scale, accumulate_dkv, (hipStream_t)stream),
       "cp_attn_bwd_dkdv launch");
@@ -1161,7 +1166,8 @@ thdcp_status_t cp_attn_bwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (!p->bwd.empty()) {
     hipError_t e = launch_attn_bwd_dkdv(
         reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_bwd), (int32_t)p->bwd.size(),
-        p->desc.H, p->desc.D, q, k, v, kv_map(p), p->band, d_o, lse, delta, dk, dv, p->n_local,
+        p->desc.H, p->desc.D, p->bwd_keys, q, k, v, kv_map(p), p->band, d_o, lse, delta, dk, dv,
+        p->n_local,
         p->scale, accumulate_dkv, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd dkdv launch");
   }
@@ -1253,7 +1259,8 @@ thdcp_status_t cp_attn_bwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   if (sp.n_bwd > 0) {
     hipError_t e = launch_attn_bwd_dkdv(
         reinterpret_cast<const BwdTile*>(p->ws_dev + p->off_sbwd) + sp.bwd0, sp.n_bwd, p->desc.H,
-        p->desc.D, q, k, v, kv, p->band, d_o, lse, delta, dk, dv, p->n_local, p->scale, 0,
+        p->desc.D, p->bwd_keys, q, k, v, kv, p->band, d_o, lse, delta, dk, dv, p->n_local,
+        p->scale, 0,
         (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "cp_attn_bwd_step dkdv launch");
   }

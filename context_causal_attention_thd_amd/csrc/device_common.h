@@ -13,6 +13,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -32,15 +33,11 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Round two 16x16 accumulators' entries (4 each) to one bf16x8 operand.
+// Round two 16x16 accumulators' entries (4 each) to one bf16x8 operand
+// (round to nearest even, two values per conversion instruction).
 __device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r[j] = (bf16)x[j];
-    r[4 + j] = (bf16)y[j];
-  }
-  return r;
+  return __builtin_shufflevector(__builtin_convertvector(x, bf16x4),
+                                 __builtin_convertvector(y, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
@@ -64,12 +61,12 @@ __device__ __forceinline__ bf16x8 concat4(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Round-to-nearest-even float -> bf16 for 8 consecutive accumulator values.
+// Round-to-nearest-even float -> bf16 for 8 consecutive accumulator values
+// (base 0 or 8), two per conversion instruction.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& v, int base) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (bf16)v[base + j];
-  return r;
+  const f32x8 x = base == 0 ? __builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, 6, 7)
+                            : __builtin_shufflevector(v, v, 8, 9, 10, 11, 12, 13, 14, 15);
+  return __builtin_convertvector(x, bf16x8);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(bf16 lo, bf16 hi) {

@@ -63,6 +63,7 @@ constexpr int kFwdBM = 128;      // query rows per forward / dQ workgroup
 constexpr int kFwdBMLong = 256;  // the same for plans whose walks are long
 constexpr int kFwdBN = 64;       // keys per forward K/V tile
 constexpr int kBwdBN = 128;      // keys per backward workgroup (4 waves x 32)
+constexpr int kBwdBNLong = 256;  // the same for plans whose walks are long (8 x 32)
 
 // Scratch of split key walks: per (slot, head) kSplitFloats(D, rows) floats
 // hold one part's partial result for a tile of `rows` query rows (forward:
@@ -134,8 +135,9 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
                            int32_t rows, const void* q, const void* k, const void* v, KvRows kv,
                            Band band, void* o, float* lse, int64_t n_local, float scale,
                            SplitWs split, hipStream_t stream);
+// keys: keys per tile of the plan (kBwdBN or kBwdBNLong).
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
-                                const void* q, const void* k, const void* v, KvRows kv,
+                                int32_t keys, const void* q, const void* k, const void* v, KvRows kv,
                                 Band band, const void* d_o, const float* lse,
                                 const float* delta, float* dk, float* dv, int64_t n_local,
                                 float scale, int32_t accumulate, hipStream_t stream);

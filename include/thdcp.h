@@ -273,7 +273,8 @@ typedef struct {
   int32_t fwd_tile_rows;     /* query rows per forward / dQ tile: 256 where the
                                 average local query walks >= 4096 keys (not
                                 P2P plans), else 128 */
-  int32_t reserved;          /* 0 */
+  int32_t bwd_tile_keys;     /* keys per dK/dV tile: 256 where fwd_tile_rows is
+                                256, else 128 */
 } thdcp_plan_info;
 
 /* Build a plan on the host. *plan_out receives a host object the caller

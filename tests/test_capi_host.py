@@ -322,14 +322,14 @@ def test_plan_split_walks(L):
     # split in two
     doc = thd.Plan([0, 16384], [0, 16384], 16384, 1, 0, "no_load_balance", 4, 128,
                    upload=False)
-    assert doc.info.fwd_tile_rows == 256
+    assert doc.info.fwd_tile_rows == 256 and doc.info.bwd_tile_keys == 256
     assert doc.info.n_fwd_tiles == 64 and doc.info.n_split_tiles == 32
     assert doc.info.n_fwd_parts == 96
     # the same document as a P2P plan keeps 128-row tiles: 512 workgroups,
     # walks of 2 to 256 key tiles against a balanced load of 65
     p2p = thd.Plan([0, 16384], [0, 16384], 16384, 1, 0, "no_load_balance", 4, 128,
                    upload=False, p2p=True)
-    assert p2p.info.fwd_tile_rows == 128
+    assert p2p.info.fwd_tile_rows == 128 and p2p.info.bwd_tile_keys == 128
     assert p2p.info.n_fwd_tiles == 128 and p2p.info.n_split_tiles == 64
     p2p.close()
     # the same document under DUAL_CHUNK_SWAP, cp_size 4: walks within 1.25x

@@ -1,16 +1,18 @@
-"""GPU parity of the 256-row query tiles of long-walk plans.
+"""GPU parity of the large tiles of long-walk plans.
 
-A rank's forward and dQ walk, per query tile, every key its rows attend
-("[PyTorch] Add no-load-balance THD all-gather CP", "Why": the rank's
-attention steps over the gathered K/V). Where the average local query walks
-4096 keys or more (all-gather plans), the plan uses tiles of 256 query rows
-(eight waves of 32) instead of 128, so every staged K/V tile serves twice the
-queries. This checks those plans against the fp64 oracle element by element
-over the whole share: one long document with a ragged end and a buffer tail
-(head dim 128), a padded DUAL_CHUNK_SWAP pair of documents on both ranks
-(head dim 64), key bands with a right bound and the whole document, forced
-and automatic split walks against the unsplit plan, and rank-major against
-global K/V (bit-identical). Bar: max-abs 2e-2, relative-L2 5e-3.
+A rank's forward and dQ walk, per query tile, every key its rows attend, and
+its dK/dV walk, per key tile, every local query that attends it ("[PyTorch]
+Add no-load-balance THD all-gather CP", "Why": the rank's attention steps
+over the gathered K/V). Where the average local query walks 4096 keys or
+more (all-gather plans), the plan uses query tiles of 256 rows and key tiles
+of 256 keys (eight waves of 32 each) instead of 128, so every staged tile
+serves twice the rows. This checks those plans against the fp64 oracle
+element by element over the whole share: one long document with a ragged end
+and a buffer tail (head dim 128), a padded DUAL_CHUNK_SWAP pair of documents
+on both ranks (head dim 64, where half of the 8 dK/dV waves stage the query
+blocks), key bands with a right bound and the whole document, forced and
+automatic split walks against the unsplit plan, and rank-major against global
+K/V (bit-identical). Bar: max-abs 2e-2, relative-L2 5e-3.
 """
 import sys
 
@@ -51,7 +53,7 @@ def test_long_doc_whole_share():
         _say("long tiles", DOC.name, "max_key_splits", parts)
         got = run_share(DOC, 0, t, max_key_splits=parts)
         info = got["plan"].info
-        assert info.fwd_tile_rows == 256
+        assert info.fwd_tile_rows == 256 and info.bwd_tile_keys == 256
         if parts == 1:
             assert info.n_split_tiles == 0
             whole = got
@@ -70,7 +72,7 @@ def test_long_dcs_both_ranks(rank):
     t = W.bf16_tensors(DCS)
     _say("long tiles", DCS.name, "rank", rank)
     got = run_share(DCS, rank, t)
-    assert got["plan"].info.fwd_tile_rows == 256
+    assert got["plan"].info.fwd_tile_rows == 256 and got["plan"].info.bwd_tile_keys == 256
     ref = oracle_share_chunked(DCS, rank, f64(t))
     _check(got, ref, f"{DCS.name} r{rank}")
 
@@ -103,5 +105,5 @@ def test_short_walks_keep_128_row_tiles():
     w = W.custom("cut_doc", [544] * 16, [544] * 16, None, 2, 128, 1, 0, "no_load_balance")
     plan = thd.Plan(w.cu_seqlens(), w.cu_seqlens_padded(), w.T, 1, 0, w.strategy, w.H, w.D,
                     upload=False)
-    assert plan.info.fwd_tile_rows == 128
+    assert plan.info.fwd_tile_rows == 128 and plan.info.bwd_tile_keys == 128
     plan.close()
