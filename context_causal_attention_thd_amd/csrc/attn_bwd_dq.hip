@@ -288,20 +288,35 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
         dp[kb] = mfma32(vr[n % (kPf + 1)], dof[kk], dp[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const bool diag = !wave_all_valid || k0 + BN - 1 > wave_gmin + wr ||
-                        (BAND && k0 < wave_gmax - wl) || k0 + BN > kend;
+      // Exponents S * scale_log2 - LSE_2. Tiles on a band edge or past the
+      // range end (one wave-uniform test) give a masked key exponent -inf,
+      // so p = 0 exactly with no branch (dP is finite: rows past the range
+      // end load as zeros); the others skip the mask. A per-element
+      // short-circuit test, or a select after the exp, compiled to a branch
+      // around every element.
+      const bool diag = wave_uniform(!wave_all_valid || k0 + BN - 1 > wave_gmin + wr ||
+                                     (BAND && k0 < wave_gmax - wl) || k0 + BN > kend) != 0;
+      if (diag) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+            bool ok = (key <= my_hi) & (key < kend);
+            if constexpr (BAND) ok &= key >= my_lo;
+            s[kb][i] = ok ? fmaf(s[kb][i], scale_log2, -lse2) : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb][i] = fmaf(s[kb][i], scale_log2, -lse2);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          const bool ok =
-              !diag || (key <= my_hi && (!BAND || key >= my_lo) && key < kend);
-          // Branch-free: a masked key's exponent is -inf, so p = 0 exactly (dP
-          // is finite: rows past the range end load as zeros). Selecting p
-          // after the exp instead compiled to a branch around every element.
-          const float x = ok ? fmaf(s[kb][i], scale_log2, -lse2) : -INFINITY;
-          const float p = fast_exp2(x);
+          const float p = fast_exp2(s[kb][i]);
           dp[kb][i] = p * (dp[kb][i] - dlt);
         }
       // dQ^T += K^T dS^T; k-step (kb, u): slot j = key kb*32 + 16u +
