@@ -60,6 +60,22 @@ __device__ __forceinline__ int kv_swz(int r) {
   else return (r >> 1) & 7;
 }
 
+// Transposed-V mode (VT: 256-row tiles, D = 128). The transposing LDS reads
+// of a row-major V tile cost as much per instruction as a 16-byte read for
+// half the bytes (measured on MI355X), so for long walks a pre-pass writes
+// V^T (head-dim rows of all keys) and the forward stages V^T tiles: D rows
+// of 64 keys (128 bytes), whose A-operand fragments of O^T = V^T P^T are
+// plain 16-byte reads of 8 consecutive keys. P^T's k-slots must list those
+// same 8 keys, so the S^T row blocks take the K rows in a permuted order:
+// row r = 4g + i of key block kb holds key 32(kb>>1) + 8g + 4(kb&1) + i.
+// kswz_vt keeps those 16-row K reads free of bank conflicts (it maps the
+// rows read by lanes 0..15 of a group onto 16 distinct chunks); V^T tiles
+// use vt_swz (two rows per 256-byte bank line, rows of one parity distinct).
+__device__ __forceinline__ int kswz_vt(int r) {
+  return (r & 3) | (((r >> 3) & 1) << 2) | (((r >> 4) & 1) << 3);
+}
+__device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
+
 template <int D>
 struct FwdSmem {
   static constexpr int ROWB = D * 2;            // bytes per row
@@ -77,15 +93,19 @@ constexpr int kFwdThreads = 512;
 // K/V, or one rank's block of it: the restore fused into the loads).
 // BAND: a general key band [g - wl, g + wr]; otherwise the causal mask
 // (wl unbounded, wr = 0, folded at compile time).
-// The second bound is waves per SIMD: two workgroups per CU with QB = 1, one
-// with QB = 2, which caps the registers at 512 / that.
-template <int D, int QB, bool MAPPED, bool BAND>
+// VT: V is read as V^T tiles of vt (head h's D rows of vt_pitch keys, keys in
+// global order) instead of V rows. The second bound is waves per SIMD: two
+// workgroups per CU with QB = 1, one with QB = 2, which caps the registers
+// at 512 / that.
+template <int D, int QB, bool MAPPED, bool BAND, bool VT>
 __global__ void __launch_bounds__(kFwdThreads, QB == 2 ? 2 : 4)
 attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __restrict__ q,
                 const bf16* __restrict__ k, const bf16* __restrict__ v,
                 const int32_t* __restrict__ kv_row, int32_t kv_sub, uint32_t kv_bytes,
                 int32_t wl_arg, int32_t wr_arg, bf16* __restrict__ o, float* __restrict__ lse,
-                int64_t n_local, float scale_log2, SplitWs split) {
+                int64_t n_local, float scale_log2, SplitWs split, const bf16* __restrict__ vt,
+                int32_t vt_pitch) {
+  static_assert(!VT || (D == 128 && QB == 2), "transposed V: 256-row tiles of head dim 128");
   constexpr int kThreads = kFwdThreads;
   constexpr int BN = kFwdBN;
   constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
@@ -160,8 +180,28 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     drow[j] = (w * NI + j) * RPI + lane / LPR;
-    dcol[j] = (uint32_t)(((lane % LPR) ^ kv_swz<D>(drow[j])) * 16);
+    dcol[j] = (uint32_t)(((lane % LPR) ^ (VT ? kswz_vt(drow[j]) : kv_swz<D>(drow[j]))) * 16);
   }
+  // V^T staging (VT): DMA instruction j of wave w fills V^T rows (head dims)
+  // [(w*NI + j)*8, +8), 128 bytes each: lane i loads dim (w*NI + j)*8 + i/8,
+  // physical chunk i%8, i.e. keys k0 + 8*((i%8) ^ vt_swz(dim)) .. +7. The
+  // pitch leaves 64 keys past the last tile start, and keys no local query
+  // attends (padding among them) hold 0 in vt, so the keys of a tile past
+  // its range end enter P V^T as 0 * finite.
+  uint32_t vtoff[NI];
+  if constexpr (VT) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int dr = (w * NI + j) * 8 + lane / 8;
+      vtoff[j] = (uint32_t)dr * (uint32_t)vt_pitch * 2u + (uint32_t)(((lane % 8) ^ vt_swz(dr)) * 16);
+    }
+  }
+  auto load_vt = [&](int k0, char* dst) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(vt + (int64_t)h * D * vt_pitch + k0,
+                                               (uint32_t)(((int64_t)D * vt_pitch - k0) * 2));
+#pragma unroll
+    for (int j = 0; j < NI; ++j) dma16(r, vtoff[j], dst + (w * NI + j) * 1024);
+  };
   // Rows [k0, k0 + BN) of K or V into LDS tile dst, for a tile of a key range
   // ending at kend; a row at or past kend reads 0 with no branch.
   //  - Unmapped: the descriptor runs from row k0 - kv_sub to the range end,
@@ -206,6 +246,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int vr = G * 4 + (l16 >> 2);
   const int vsw = ((l16 >> 1) & 1) ^ kv_swz<D>(vr);
   auto k_off = [&](int kb, int kk) {
+    if constexpr (VT)  // row 32(kb>>1) + 8(l16>>2) + 4(kb&1) + (l16&3), whose kswz_vt is l16
+      return (32 * (kb >> 1) + 8 * (l16 >> 2) + 4 * (kb & 1) + (l16 & 3)) * ROWB +
+             (((kk * 4 + G) ^ l16) << 4);
     return (kb * 16 + l16) * ROWB + (((kk * 4) ^ ksw) << 4);
   };
   auto v_off = [&](int ks, int half, int nb) {
@@ -250,7 +293,8 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = k0 + kb * 16 + G * 4 + i;
+          const int key = VT ? k0 + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + i
+                             : k0 + kb * 16 + G * 4 + i;
           bool out = key > my_hi[qb] || key >= kend;
           if constexpr (BAND) out = out || key < my_lo[qb];
           if (out) s[qb][kb][i] = -INFINITY;
@@ -314,9 +358,13 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       }
       bf16x8 ring[kPf + 1];
       auto fetch = [&](int nb) {
-        ring[nb % (kPf + 1)] =
-            concat4(lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 0, nb)])),
-                    lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 1, nb)])));
+        if constexpr (VT)  // V^T row nb*16 + l16, keys 32ks + 8G .. +7
+          ring[nb % (kPf + 1)] = load_bf16x8(reinterpret_cast<const bf16*>(
+              &sm.v[vbuf][(nb * 16 + l16) * 128 + (((ks * 4 + G) ^ ((l16 >> 1) & 7)) << 4)]));
+        else
+          ring[nb % (kPf + 1)] =
+              concat4(lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 0, nb)])),
+                      lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 1, nb)])));
       };
 #pragma unroll
       for (int nb = 0; nb < kPf; ++nb) fetch(nb);
@@ -360,7 +408,8 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     rows_pos(tile_k0(0), tile_kend(0), pos);
     if (ntiles > 1) rows_pos(tile_k0(1), tile_kend(1), pos1);
     load_rows(k, tile_k0(0), tile_kend(0), pos, sm.k[0]);
-    load_rows(v, tile_k0(0), tile_kend(0), pos, sm.v[0]);
+    if constexpr (VT) load_vt(tile_k0(0), sm.v[0]);
+    else load_rows(v, tile_k0(0), tile_kend(0), pos, sm.v[0]);
 #pragma unroll
     for (int j = 0; j < NI; ++j) pos[j] = pos1[j];
   }
@@ -374,7 +423,8 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     if (has_next) {  // in flight during this tile's compute (the other buffer's
                      // last readers passed the previous barrier)
       load_rows(k, tile_k0(it + 1), tile_kend(it + 1), pos, sm.k[cur ^ 1]);
-      load_rows(v, tile_k0(it + 1), tile_kend(it + 1), pos, sm.v[cur ^ 1]);
+      if constexpr (VT) load_vt(tile_k0(it + 1), sm.v[cur ^ 1]);
+      else load_rows(v, tile_k0(it + 1), tile_kend(it + 1), pos, sm.v[cur ^ 1]);
       if (it + 2 < ntiles) rows_pos(tile_k0(it + 2), tile_kend(it + 2), pos);
     }
     if (k0 <= wave_kmax && (!BAND || k0 + BN - 1 >= wave_kmin)) {
@@ -467,15 +517,17 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 // long (measured on MI355X: one 75600-token document 6.9-7.0 against 7.3-7.4
 // ms with 128-row tiles of 32-row waves) and 128 otherwise (the
 // multi-document shares' short tiles: 10-15% faster).
-template <int D, int QB>
+template <int D, int QB, bool VT>
 hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const bf16* q,
                         const bf16* k, const bf16* v, const int32_t* kv_row, int32_t kv_sub,
                         uint32_t kv_bytes, Band band, bf16* o, float* lse, int64_t n_local,
-                        float scale_log2, SplitWs split, hipStream_t stream) {
-#define THDCP_FWD(MM, BB)                                                                \
-  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, MM, BB>), dim3((unsigned)blocks),             \
-                     dim3(kFwdThreads), 0, stream, tiles, H, q, k, v, kv_row, kv_sub, \
-                     kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2, split)
+                        float scale_log2, SplitWs split, const bf16* vt, int32_t vt_pitch,
+                        hipStream_t stream) {
+#define THDCP_FWD(MM, BB)                                                                   \
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB, MM, BB, VT>), dim3((unsigned)blocks),           \
+                     dim3(kFwdThreads), 0, stream, tiles, H, q, k, v, kv_row, kv_sub,        \
+                     kv_bytes, band.wl, band.wr, o, lse, n_local, scale_log2, split, vt,     \
+                     vt_pitch)
   if (kv_row && band.causal)
     THDCP_FWD(true, false);
   else if (kv_row)
@@ -488,12 +540,71 @@ hipError_t launch_fwd_d(const FwdTile* tiles, int64_t blocks, int32_t H, const b
   return hipGetLastError();
 }
 
+// V^T for the transposed-V forward: vt[(h*128 + d) * pitch + j] = V of key j
+// (K/V row j - sub, or kv_row[j] - sub), head h, dim d, for j < T; 0 for
+// j >= T and for keys in the zero ranges (keys no local query attends:
+// padding and other documents). One workgroup per 64 keys and head: the rows
+// are read as 16-byte chunks into LDS and written back as 8-key chunks of
+// one dim.
+__global__ void __launch_bounds__(256)
+v_transpose_kernel(const bf16* __restrict__ v, const int32_t* __restrict__ kv_row, int32_t sub,
+                   int32_t T, int32_t H, const ZeroRange* __restrict__ zr, int32_t n_zr,
+                   bf16* __restrict__ vt, int32_t pitch) {
+  constexpr int D = 128;
+  __shared__ bf16 tile[64][D + 8];
+  const int k0 = blockIdx.x * 64;
+  const int h = blockIdx.y;
+  const int64_t rs = (int64_t)H * D;
+  for (int c = threadIdx.x; c < 64 * (D / 8); c += 256) {
+    const int r = c / (D / 8), ch = c % (D / 8);
+    const int key = k0 + r;
+    bool live = key < T;
+    if (live && n_zr > 0) {  // last zero range starting at or before key
+      int lo = 0, hi = n_zr - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (zr[mid].r0 <= key) lo = mid; else hi = mid - 1;
+      }
+      live = !(zr[lo].r0 <= key && key < zr[lo].r1);
+    }
+    bf16x8 x = zero_bf16x8();
+    if (live) {
+      const int64_t row = (int64_t)(kv_row ? kv_row[key] : key) - sub;
+      x = load_bf16x8(v + row * rs + (int64_t)h * D + ch * 8);
+    }
+    store_bf16x8(&tile[r][ch * 8], x);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D * 8; c += 256) {
+    const int d = c / 8, kc = c % 8;
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = tile[kc * 8 + e][d];
+    store_bf16x8(vt + ((int64_t)h * D + d) * pitch + k0 + kc * 8, y);
+  }
+}
+
 }  // namespace
+
+int32_t vt_pitch_for(int64_t T) { return (int32_t)((T + 63) / 64 * 64 + 64); }
+
+hipError_t launch_v_transpose(const void* v, KvRows kv, int32_t H, int32_t D,
+                              const ZeroRange* zr, int32_t n_zr, void* vt, int32_t pitch,
+                              hipStream_t stream) {
+  if (D != 128 || pitch < vt_pitch_for(kv.rows) || pitch % 64 != 0)
+    return hipErrorInvalidValue;
+  if (H == 0 || kv.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)(pitch / 64), (unsigned)H), dim3(256), 0,
+                     stream, static_cast<const bf16*>(v), kv.map, (int32_t)kv.sub,
+                     (int32_t)kv.rows, H, zr, n_zr, static_cast<bf16*>(vt), pitch);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                            int32_t rows, const void* q, const void* k, const void* v, KvRows kv,
                            Band band, void* o, float* lse, int64_t n_local, float scale,
-                           SplitWs split, hipStream_t stream) {
+                           SplitWs split, const void* vt, int32_t vt_pitch,
+                           hipStream_t stream) {
   const int64_t blocks = (int64_t)n_tiles * H;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -501,17 +612,22 @@ hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int
   const bf16* qp = static_cast<const bf16*>(q);
   const bf16* kb = static_cast<const bf16*>(k);
   const bf16* vb = static_cast<const bf16*>(v);
+  const bf16* vtb = static_cast<const bf16*>(vt);
   bf16* ob = static_cast<bf16*>(o);
   const int64_t kv_bytes = kv.rows * H * D * 2;
   if (kv.map && kv_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const uint32_t kvb = kv.map ? (uint32_t)kv_bytes : 0u;
-#define THDCP_FWD_D(DD, QQ)                                                                   \
-  return launch_fwd_d<DD, QQ>(tiles, blocks, H, qp, kb, vb, kv.map, (int32_t)kv.sub, kvb, band, \
-                              ob, lse, n_local, scale_log2, split, stream)
-  if (D == 128 && rows == kFwdBMLong) THDCP_FWD_D(128, 2);
-  if (D == 128 && rows == kFwdBM) THDCP_FWD_D(128, 1);
-  if (D == 64 && rows == kFwdBMLong) THDCP_FWD_D(64, 2);
-  if (D == 64 && rows == kFwdBM) THDCP_FWD_D(64, 1);
+  if (vt && (D != 128 || rows != kFwdBMLong || (int64_t)D * vt_pitch * 2 >= ((int64_t)1 << 31)))
+    return hipErrorInvalidValue;
+#define THDCP_FWD_D(DD, QQ, VV)                                                              \
+  return launch_fwd_d<DD, QQ, VV>(tiles, blocks, H, qp, kb, vb, kv.map, (int32_t)kv.sub, kvb, \
+                                  band, ob, lse, n_local, scale_log2, split, vtb, vt_pitch,   \
+                                  stream)
+  if (D == 128 && rows == kFwdBMLong && vt) THDCP_FWD_D(128, 2, true);
+  if (D == 128 && rows == kFwdBMLong) THDCP_FWD_D(128, 2, false);
+  if (D == 128 && rows == kFwdBM) THDCP_FWD_D(128, 1, false);
+  if (D == 64 && rows == kFwdBMLong) THDCP_FWD_D(64, 2, false);
+  if (D == 64 && rows == kFwdBM) THDCP_FWD_D(64, 1, false);
 #undef THDCP_FWD_D
   return hipErrorInvalidValue;
 }

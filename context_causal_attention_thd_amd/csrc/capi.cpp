@@ -145,6 +145,11 @@ struct thdcp_plan {
   // (all-gather plans), else kFwdBM and kBwdBN.
   int32_t fwd_rows = kFwdBM;
   int32_t bwd_keys = kBwdBN;
+  // Transposed-V forward (256-row tiles, head dim 128): V^T of all T keys at
+  // off_vt in the workspace, key pitch vt_pitch, written by cp_attn_fwd.
+  bool fwd_vt = false;
+  int32_t vt_pitch = 0;
+  size_t off_vt = 0;
   std::vector<char> blob;  // host image of the device tables (and zeroed counters)
   size_t off_fwd = 0, off_bwd = 0, off_zero = 0, off_kvrow = 0, ws_bytes = 0;
   size_t off_sfwd = 0, off_sbwd = 0, off_szero = 0, off_cnt = 0, off_part = 0;
@@ -453,6 +458,12 @@ void build_plan(thdcp_plan& p) {
   const bool long_walks = !d.p2p && p.pairs >= kLongWalk * std::max<int64_t>(1, p.n_local);
   p.fwd_rows = long_walks ? kFwdBMLong : kFwdBM;
   p.bwd_keys = long_walks ? kBwdBNLong : kBwdBN;
+  // Their forward reads V transposed (a pre-pass writes V^T into the
+  // workspace: plain 16-byte LDS reads instead of transposing ones; -5% on
+  // one 75600-token document, the pre-pass included), for head dim 128 while
+  // one head's V^T stays below 2 GiB.
+  p.vt_pitch = vt_pitch_for(d.T);
+  p.fwd_vt = long_walks && d.D == 128 && (int64_t)d.D * p.vt_pitch * 2 < ((int64_t)1 << 31);
 
   // Forward tiles, longest first (LPT order over the workgroup queue).
   std::vector<FwdTile> fwd;
@@ -599,6 +610,10 @@ void build_plan(thdcp_plan& p) {
   p.off_part = align256(p.off_cnt + (size_t)p.split_groups * d.H * sizeof(int32_t));
   p.ws_bytes =
       p.off_part + (size_t)p.split_slots * d.H * kSplitFloats(d.D, p.fwd_rows) * sizeof(float);
+  if (p.fwd_vt) {
+    p.off_vt = align256(p.ws_bytes);
+    p.ws_bytes = p.off_vt + (size_t)d.H * d.D * p.vt_pitch * sizeof(uint16_t);
+  }
   if (p.ws_bytes == 0) p.ws_bytes = 256;
   // the image covers the tables and the split counters (zero), not the scratch
   p.blob.assign(std::max<size_t>(p.off_part, 256), 0);
@@ -1000,11 +1015,19 @@ thdcp_status_t cp_attn_fwd(thdcp_plan_t p, const void* q, const void* k, const v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(THDCP_ERR_ARG, "Q/K/V/O must be 16-byte aligned");
   if (p->fwd.empty()) return ok();
+  void* vt = nullptr;
+  if (p->fwd_vt) {
+    vt = p->ws_dev + p->off_vt;
+    hipError_t e = launch_v_transpose(v, kv_map(p), p->desc.H, p->desc.D,
+                                      reinterpret_cast<const ZeroRange*>(p->ws_dev + p->off_zero),
+                                      (int32_t)p->zero.size(), vt, p->vt_pitch, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "cp_attn_fwd transpose launch");
+  }
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_fwd),
                       (int32_t)p->fwd.size(), p->desc.H, p->desc.D, p->fwd_rows, q, k, v,
-                      kv_map(p), p->band, o, lse, p->n_local, p->scale, split_ws(p),
-                      (hipStream_t)stream),
+                      kv_map(p), p->band, o, lse, p->n_local, p->scale, split_ws(p), vt,
+                      p->vt_pitch, (hipStream_t)stream),
       "cp_attn_fwd launch");
 }
 
@@ -1203,8 +1226,8 @@ thdcp_status_t cp_attn_fwd_step(thdcp_plan_t p, int32_t src, const void* q, cons
   return hip_status(
       launch_attn_fwd(reinterpret_cast<const FwdTile*>(p->ws_dev + p->off_sfwd) + sp.fwd0,
                       sp.n_fwd, p->desc.H, p->desc.D, p->fwd_rows, q, k, v, kv_step(p, src),
-                      p->band, o, lse,
-                      p->n_local, p->scale, SplitWs{}, (hipStream_t)stream),
+                      p->band, o, lse, p->n_local, p->scale, SplitWs{}, nullptr, 0,
+                      (hipStream_t)stream),
       "cp_attn_fwd_step launch");
 }
 

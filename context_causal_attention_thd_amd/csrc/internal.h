@@ -130,11 +130,21 @@ hipError_t launch_lse_merge_parts(int64_t n, int32_t H, int32_t D, int32_t parts
 hipError_t launch_bwd_prep(const void* o, const void* d_o, const float* lse, float* delta,
                            int64_t n_local, int32_t H, int32_t D, hipStream_t stream);
 // rows: query rows per tile of the plan (kFwdBM or kFwdBMLong); the forward
-// and dQ launches pick their wave shape from it.
+// and dQ launches pick their wave shape from it. vt (optional, rows ==
+// kFwdBMLong and D == 128 only): V^T written by launch_v_transpose for the
+// same K/V, pitch vt_pitch; the forward then stages V^T tiles instead of V.
 hipError_t launch_attn_fwd(const FwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                            int32_t rows, const void* q, const void* k, const void* v, KvRows kv,
                            Band band, void* o, float* lse, int64_t n_local, float scale,
-                           SplitWs split, hipStream_t stream);
+                           SplitWs split, const void* vt, int32_t vt_pitch, hipStream_t stream);
+// Key pitch of V^T for T keys: a multiple of 64 with 64 keys to spare past
+// the last tile start.
+int32_t vt_pitch_for(int64_t T);
+// V^T [H][128][pitch] (bf16) of the kv.rows keys of V (row addressing as in
+// KvRows), 0 for keys >= kv.rows and keys inside the zero ranges zr.
+hipError_t launch_v_transpose(const void* v, KvRows kv, int32_t H, int32_t D,
+                              const ZeroRange* zr, int32_t n_zr, void* vt, int32_t pitch,
+                              hipStream_t stream);
 // keys: keys per tile of the plan (kBwdBN or kBwdBNLong).
 hipError_t launch_attn_bwd_dkdv(const BwdTile* tiles, int32_t n_tiles, int32_t H, int32_t D,
                                 int32_t keys, const void* q, const void* k, const void* v, KvRows kv,

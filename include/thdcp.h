@@ -294,10 +294,12 @@ thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
  * `stream`. The plan keeps the pointer; the workspace must stay alive and
  * unmodified while forward/backward calls using the plan are in flight.
  * Past the tables it holds the split key walks' counters (uploaded as zero,
- * left at zero by every launch) and their partial results, so the plan's
- * forward and dQ launches must not overlap: enqueue calls that use one
- * workspace on one stream (or order them). The copy covers the tables and
- * counters only.
+ * left at zero by every launch) and their partial results, and, for plans
+ * with fwd_tile_rows 256 and head dim 128, V transposed (H * 128 * pitch
+ * bf16, pitch = T rounded up to 64, plus 64), which cp_attn_fwd writes from
+ * v before its attention launch. So the plan's forward and dQ launches must
+ * not overlap: enqueue calls that use one workspace on one stream (or order
+ * them). The copy covers the tables and counters only.
  * Tables up to 1 MiB are first copied into a page-locked staging slot the
  * library keeps for the life of the process (1 MiB each, allocated 16 at a
  * time: 16 on the first upload, 16 more whenever every slot still feeds a
@@ -324,6 +326,9 @@ void thdcp_plan_destroy(thdcp_plan_t plan);
  *   o_local  bf16 [n_local, H, D]   written for every local row
  *   lse      fp32 [H, n_local]      natural log; -inf on padding rows
  * Padding rows get O = 0. Padding key rows are never read into a product.
+ * Plans with fwd_tile_rows 256 and head dim 128 first write V^T into the
+ * workspace (one pass over v; keys no local query attends, padding included,
+ * as 0) and stage V^T tiles instead of V rows.
  * A query tile whose key walk the plan split (max_key_splits) is computed by
  * several workgroups of the same launch; the last to finish merges their
  * (max, sum, accumulator) states in key order, so the output is

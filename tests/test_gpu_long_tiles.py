@@ -6,19 +6,22 @@ Add no-load-balance THD all-gather CP", "Why": the rank's attention steps
 over the gathered K/V). Where the average local query walks 4096 keys or
 more (all-gather plans), the plan uses query tiles of 256 rows and key tiles
 of 256 keys (eight waves of 32 each) instead of 128, so every staged tile
-serves twice the rows. This checks those plans against the fp64 oracle
+serves twice the rows; at head dim 128 the forward also reads V transposed
+(a pre-pass writes V^T, with the keys no local query attends set to 0). This checks those plans against the fp64 oracle
 element by element over the whole share: one long document with a ragged end
 and a buffer tail (head dim 128), a padded DUAL_CHUNK_SWAP pair of documents
 on both ranks (head dim 64, where half of the 8 dK/dV waves stage the query
 blocks), key bands with a right bound and the whole document, forced and
-automatic split walks against the unsplit plan, and rank-major against global
-K/V (bit-identical). Bar: max-abs 2e-2, relative-L2 5e-3.
+automatic split walks against the unsplit plan, rank-major against global
+K/V (bit-identical), and NaN in every padding row of Q/K/V/dO changing no
+output bit. Bar: max-abs 2e-2, relative-L2 5e-3.
 """
 import sys
 
 import numpy as np
 import pytest
 
+import oracle as O
 import workloads as W
 from _parity import assert_close, assert_lse, err, f64, oracle_share_chunked, run_share
 
@@ -36,6 +39,8 @@ def _say(*a):
 DOC = W.custom("long_doc_d128", [8700], [8704], 8800, 2, 128, 1, 0, "no_load_balance")
 DCS = W.custom("long_dcs_pad_d64", [17000, 299], [17000, 304], None, 2, 64, 2, 0,
                "dual_chunk_swap")
+DCS128 = W.custom("long_dcs_pad_d128", [12000, 299], [12000, 304], None, 2, 128, 2, 0,
+                  "dual_chunk_swap")
 
 
 def _check(got, ref, tag):
@@ -107,3 +112,35 @@ def test_short_walks_keep_128_row_tiles():
                     upload=False)
     assert plan.info.fwd_tile_rows == 128 and plan.info.bwd_tile_keys == 128
     plan.close()
+
+
+def test_long_dcs_d128_rank_major():
+    # head dim 128: the transposed-V forward, its pre-pass reading K/V through
+    # the rank-major map and zeroing the keys rank 1 does not attend
+    t = W.bf16_tensors(DCS128)
+    _say("long tiles", DCS128.name, "rank 1 rank-major")
+    m = run_share(DCS128, 1, t, kv_layout="rank_major")
+    assert m["plan"].info.fwd_tile_rows == 256 and m["plan"].info.n_zero_ranges > 0
+    ref = oracle_share_chunked(DCS128, 1, f64(t))
+    perm = m["perm"]
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    got = dict(m, dk=m["dk"][inv], dv=m["dv"][inv])
+    _check(got, ref, f"{DCS128.name} r1 rank-major")
+
+
+def test_long_padding_poison():
+    # NaN in every padding row (and the buffer tail) of Q, K, V and dO: the
+    # outputs keep every bit
+    cu, cup = DOC.cu_seqlens(), DOC.cu_seqlens_padded()
+    _, _, valid = O.token_table(cu, cup, DOC.T)
+    assert (~valid).sum() == 4 + 96
+    t = W.bf16_tensors(DOC)
+    bad = {n: x.clone() for n, x in t.items()}
+    for x in bad.values():
+        x[torch.from_numpy(~valid)] = float("nan")
+    _say("long tiles poison", DOC.name)
+    clean = run_share(DOC, 0, t)
+    dirty = run_share(DOC, 0, bad)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(clean[n], dirty[n]), n
