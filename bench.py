@@ -360,7 +360,9 @@ def measure_workload(w, t, args, dev, stream, steps, warmup, window, splits):
         "tflops": round(tflops_step, 3),
         "mfma_frac": round(tflops_step / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
-        "roofline_fwd": kroof("fwd"),
+        "roofline_fwd": dict(kroof("fwd"), **(
+            {"includes": "v_transpose_kernel (the plan's V^T pre-pass, inside the forward call)"}
+            if int(plan.info.fwd_tile_rows) == 256 and D == 128 else {})),
         "roofline_bwd_dkdv": kroof("dkdv"),
         "roofline_bwd_dq": kroof("dq"),
         "bwd_algorithmic": {"achieved": round(flop_bwd / (t_bwd * 1e-3) / 1e12, 2),
