@@ -204,17 +204,21 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     if (has_next) load_block(mb + kBM);
 
     // S and dP, [16-query M-block qm][key block nk]; element i of s[qm][nk] is
-    // query row qm*16 + 4*G + i, key my_key[nk].
+    // query row qm*16 + 4*G + i, key my_key[nk]. dP accumulates from -delta of
+    // its row, so the products leave dP - delta and dS = P (dP - delta) is one
+    // multiply.
     f32x4 s[2][2], dp[2][2];
 #pragma unroll
-    for (int qm = 0; qm < 2; ++qm)
+    for (int qm = 0; qm < 2; ++qm) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qm * 16 + G * 4]);
 #pragma unroll
       for (int nk = 0; nk < 2; ++nk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           s[qm][nk][i] = 0.f;
-          dp[qm][nk][i] = 0.f;
+          dp[qm][nk][i] = -d4[i];
         }
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       bf16x8 vb[2];
@@ -247,7 +251,6 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
     for (int qm = 0; qm < 2; ++qm) {
       const int qr0 = qm * 16 + G * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][qr0]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qr0]);
       if (masked) {
         const i32x4 hi4 = *reinterpret_cast<const i32x4*>(&sm.ghi[cur][qr0]);
         i32x4 lo4 = {0, 0, 0, 0};
@@ -272,7 +275,7 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
         for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(s[qm][nk][i]);
           s[qm][nk][i] = p;
-          dp[qm][nk][i] = p * (dp[qm][nk][i] - d4[i]);
+          dp[qm][nk][i] = p * dp[qm][nk][i];
         }
     }
     // dV += P^T dO, dK += dS^T Q over the block's 32 queries (one k-step):

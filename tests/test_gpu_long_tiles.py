@@ -13,7 +13,7 @@ and a buffer tail (head dim 128), a padded DUAL_CHUNK_SWAP pair of documents
 on both ranks (head dim 64, where half of the 8 dK/dV waves stage the query
 blocks), key bands with a right bound and the whole document, forced and
 automatic split walks against the unsplit plan, rank-major against global
-K/V (bit-identical), and NaN in every padding row of Q/K/V/dO changing no
+K/V (bit-identical but for dQ's rounding), and NaN in every padding row of Q/K/V/dO changing no
 output bit. Bar: max-abs 2e-2, relative-L2 5e-3.
 """
 import sys
@@ -92,17 +92,26 @@ def test_long_doc_bands(window):
     _check(got, ref, f"{DOC.name} {window}")
 
 
-def test_long_rank_major_bit_identical():
+def test_long_rank_major_matches_global():
+    # O, LSE, dK and dV keep every bit across the two K/V layouts. dQ differs by
+    # rounding only: over global-order K/V the 8-wave dQ kernel starts its dP
+    # accumulators at -delta, over the rank-major map it subtracts delta per
+    # element (the start at -delta spills there), so dP - delta can differ in
+    # its last fp32 bit and flip the bf16 rounding of a dS element.
     t = W.bf16_tensors(DCS)
     _say("long tiles rank-major", DCS.name)
     g = run_share(DCS, 1, t)
     m = run_share(DCS, 1, t, kv_layout="rank_major")
     assert m["plan"].info.fwd_tile_rows == 256
     perm = m["perm"]
-    for n in ("o", "lse", "dq"):
+    for n in ("o", "lse"):
         assert np.array_equal(m[n], g[n]), n
     for n in ("dk", "dv"):
         assert np.array_equal(m[n], g[n][perm]), n
+    scale = float(np.abs(g["dq"]).max())
+    assert np.abs(m["dq"] - g["dq"]).max() <= 2e-4 * scale
+    _, rel = err(m["dq"], g["dq"])
+    assert rel <= 1e-4, rel
 
 
 def test_short_walks_keep_128_row_tiles():
