@@ -398,6 +398,48 @@ def measure_workload(w, t, args, dev, stream, steps, warmup, window, splits):
     return block
 
 
+def _prepared(kind, srcs, idx, outs, stream, cp_size=0):
+    """One row-movement launch with its C arguments built once: the binding's
+    call (with its shape checks) runs first, then the returned callable repeats
+    exactly that launch through the exported entry point. Timing loops of
+    launches that last ~20-30 us then measure the kernels rather than the
+    binding's per-call argument marshalling, which takes about as long."""
+    import numpy as np
+    import torch
+
+    import context_causal_attention_thd_amd as thd
+    L = thd.lib()
+    st = thd._stream(stream)
+    src_p, out_p = thd._ptr_list(srcs, "src"), thd._ptr_list(outs, "out")
+    if kind == "scatter":
+        thd.scatter_many(srcs, idx, outs, stream=stream)
+        args = (len(srcs), src_p, srcs[0].shape[0], thd._dev_ptr(idx, "idx", torch.int32),
+                thd._row_bytes(srcs[0]), out_p, outs[0].shape[0], st)
+        fn = L.thd_scatter_batched
+    elif kind == "gather":
+        thd.gather_many(srcs, idx, outs, stream=stream)
+        args = (len(srcs), src_p, srcs[0].shape[0], thd._dev_ptr(idx, "idx", torch.int32),
+                idx.shape[0], thd._row_bytes(srcs[0]), out_p, st)
+        fn = L.thd_gather_batched
+    elif kind == "pack":
+        thd.a2a_pack(srcs, cp_size, outs=outs, stream=stream)
+        n = srcs[0].shape[0]
+        args = (len(srcs), src_p, n, cp_size, thd._row_bytes(srcs[0]) // cp_size, out_p, st)
+        fn = L.thd_a2a_pack
+    else:  # unpack
+        thd.a2a_unpack(srcs, outs=outs, stream=stream)
+        cp, n = srcs[0].shape[0], srcs[0].shape[1]
+        gb = max(1, int(np.prod(srcs[0].shape[2:])) * srcs[0].element_size())
+        args = (len(srcs), src_p, n, cp, gb, out_p, st)
+        fn = L.thd_a2a_unpack
+    keep = (srcs, idx, outs)
+
+    def call():
+        _ = keep
+        thd._check(fn(*args))
+    return call
+
+
 def restore_gather(w, k_rm, v_rm, perm, stream, reps):
     """The K and V restore (rank-major to global order) as one standalone
     batched gather launch, warm (back-to-back on the same buffers) and cold
@@ -424,7 +466,7 @@ def restore_gather(w, k_rm, v_rm, perm, stream, reps):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    t_warm = timed(lambda: thd.scatter_many([k_rm, v_rm], perm, [k_g, v_g]))
+    t_warm = timed(_prepared("scatter", [k_rm, v_rm], perm, [k_g, v_g], stream))
     set_bytes = 4 * k_rm.numel() * k_rm.element_size()
     n_sets = max(3, -(-(600 << 20) // set_bytes))
     sets = [[torch.empty_like(k_rm) for _ in range(4)] for _ in range(n_sets - 1)]
@@ -435,16 +477,14 @@ def restore_gather(w, k_rm, v_rm, perm, stream, reps):
     # One untimed pass touches every destination once: the first write to a
     # freshly allocated buffer costs extra (measured 37 us against 24 us per
     # launch), which is allocation, not bandwidth.
-    for a_, b_, c_, d_ in sets:
-        thd.scatter_many([a_, b_], perm, [c_, d_])
+    calls = [_prepared("scatter", [a_, b_], perm, [c_, d_], stream) for a_, b_, c_, d_ in sets]
     torch.cuda.synchronize()
     ec0 = torch.cuda.Event(enable_timing=True)
     ec1 = torch.cuda.Event(enable_timing=True)
     cold_reps = 3 * n_sets
     ec0.record(stream)
     for i in range(cold_reps):
-        a_, b_, c_, d_ = sets[i % n_sets]
-        thd.scatter_many([a_, b_], perm, [c_, d_])
+        calls[i % n_sets]()
     ec1.record(stream)
     torch.cuda.synchronize()
     t_cold = ec0.elapsed_time(ec1) / cold_reps
@@ -492,15 +532,13 @@ def gather_only(w, stream, launches):
     sets = [([torch.randn(one, device=dev).to(torch.bfloat16).view(T, -1) for _ in range(n_t)],
              [torch.empty(T, row_bytes // 2, dtype=torch.bfloat16, device=dev)
               for _ in range(n_t)]) for _ in range(n_sets)]
-    for a, b in sets:
-        thd.scatter_many(a, perm, b)
+    calls = [_prepared("scatter", a, perm, b, stream) for a, b in sets]
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(launches):
-        a, b = sets[i % n_sets]
-        thd.scatter_many(a, perm, b)
+        calls[i % n_sets]()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / launches
@@ -738,24 +776,23 @@ def a2a_layout(stream, seqlens=(8192, 32768, 75600), cp=8, heads=40, head_dim=12
         torch.cuda.synchronize()
         reps = max(2 * sets, 20)
 
-        def timed(fn):
-            for i in range(sets):
-                fn(bufs[i])
+        def timed(make):
+            calls = [make(b) for b in bufs]  # each runs its launch once, untimed
+            torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for i in range(reps):
-                fn(bufs[i % sets])
+                calls[i % sets]()
             e1.record(stream)
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
-        t_pack = timed(lambda b: thd.a2a_pack(b[0], cp, outs=b[1]))
-        t_reorder = timed(lambda b: thd.scatter_many(b[2], perm, b[3]))
+        t_pack = timed(lambda b: _prepared("pack", b[0], None, b[1], stream, cp_size=cp))
+        t_reorder = timed(lambda b: _prepared("scatter", b[2], perm, b[3], stream))
         # return direction, O only: rank-major gather (dual-chunk only), unpack
-        t_unorder = timed(lambda b: thd.gather_many(b[3][:1], perm, b[2][:1]))
-        t_unpack = timed(lambda b: thd.a2a_unpack(
-            [b[1][0]], outs=[b[0][0]]))
+        t_unorder = timed(lambda b: _prepared("gather", b[3][:1], perm, b[2][:1], stream))
+        t_unpack = timed(lambda b: _prepared("unpack", [b[1][0]], None, [b[0][0]], stream))
         pack_bytes = 3 * 2 * per_tensor
         reorder_bytes = 3 * (2 * per_tensor + 4 * s)
         out[f"s{s}"] = {
