@@ -8,9 +8,10 @@
 // gfx950 design (mirrors the forward kernel): a workgroup of 4 or 8 waves owns
 // up to 128 or 256 consecutive query rows of one (document piece, head), 32
 // per wave (8 waves, one workgroup per CU, for the plans with long walks:
-// each staged K/V tile serves twice the queries), and walks the keys from the document start in 64-key tiles, double-buffered
-// in LDS; the next tile arrives by LDS DMA (buffer loads that write LDS
-// directly, no registers) while the current one is computed. Per tile, with
+// each staged K/V tile serves twice the queries), and walks the keys from the
+// document start in 64-key tiles, double-buffered in LDS; the next tile
+// arrives by LDS DMA (buffer loads that write LDS directly, no registers)
+// while the current one is computed. Per tile, with
 // v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T, dP^T = V dO^T   (A = K / V rows from LDS, B = Q / dO regs)
 //   P^T = exp(S^T - LSE), dS^T = P^T (dP^T - delta)   (lane-local per query)

@@ -10,18 +10,20 @@
 // gfx950 design: a workgroup of 8 waves owns up to 128 or 256 consecutive
 // query rows of one (document piece, head), each wave QB 16-row query blocks:
 // QB = 1 (128 rows, ~120 registers, four waves per SIMD) or QB = 2 (256 rows,
-// ~200 registers, two per SIMD, each LDS fragment feeding two MFMAs and each
+// ~180 registers, two per SIMD, each LDS fragment feeding two MFMAs and each
 // staged K/V tile serving twice the queries); the plan picks QB = 2 for long
 // walks. Keys are walked from the document start in 64-key tiles,
 // double-buffered in LDS. Everything is computed in the transposed form
 //   S^T = K Q^T  and  O^T = V^T P^T
 // with v_mfma_f32_16x16x32_bf16: lane l owns query column l%16 of each block
 // and keys 4*(l/16) + i of every 16-key block. K fragments are 16-byte LDS
-// reads and V^T fragments are transposing LDS reads (ds_read_b64_tr_b16) of
-// the row-major V tile; the tile's chunk swizzle keeps both free of bank
-// conflicts. Each fragment is read two MFMA groups ahead of its use (held in
-// place by scheduling barriers): the loop was bound by LDS read latency. P
-// feeds the second product with no data movement.
+// reads. V^T fragments are transposing LDS reads (ds_read_b64_tr_b16) of the
+// row-major V tile, or, in the transposed-V mode of 256-row tiles at head dim
+// 128, 16-byte reads of V^T tiles written by a pre-pass (see kswz_vt). The
+// chunk swizzles put the 16 lanes of a group on distinct banks for each read.
+// Each fragment is read two MFMA groups ahead of its use (held in place by
+// scheduling barriers): the loop was bound by LDS read latency. P feeds the
+// second product with no data movement.
 //
 // The next tile's K/V rows arrive by LDS DMA while the current tile is
 // computed: buffer loads that write LDS directly (no staging registers, no
