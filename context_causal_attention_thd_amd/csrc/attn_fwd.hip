@@ -51,15 +51,23 @@ constexpr float kRescaleLog2 = 8.f;
 
 // K/V tiles in LDS: kFwdBN rows of D bf16, unpadded (LDS DMA writes each
 // wave's 1 KB block contiguously), with the 16-byte chunks of row r permuted:
-// logical chunk c sits at chunk c ^ kv_swz(r). For D = 128 the swizzle takes
-// even values on rows 0-7 and odd ones on rows 8-15 (mod 16), which keeps the
-// 16-row fragment reads (16 rows, one chunk) and the transposing V^T reads
-// (4 rows x 2 chunks per 16 lanes) on distinct banks; for D = 64 (two rows
-// per 256-byte bank line) rows of one parity take distinct values.
+// logical chunk c sits at chunk c ^ kv_swz(r). For D = 128 the swizzle was
+// chosen by timing both read patterns of the loop -- the 16-row fragment
+// reads (16 rows, one chunk per 16 lanes) and the transposing V^T reads
+// (4 rows x 2 chunks per 16 lanes) -- under candidate swizzles on MI355X:
+// (r ^ (r >> 2)) & 15 took 1.03 and 1.30 ms where the previous
+// (2r + ((r >> 3) & 1)) & 15, which gives 16 lanes distinct chunks as well,
+// took 1.95 and 1.57 ms. For D = 64 (two rows per 256-byte bank line) rows
+// of one parity take distinct values. Both depend on r mod 16 only: the read
+// offsets pass the row within its 16-row group, the DMA the full tile row.
 template <int D>
 __device__ __forceinline__ int kv_swz(int r) {
-  if constexpr (D == 128) return (2 * r + ((r >> 3) & 1)) & 15;
-  else return (r >> 1) & 7;
+  if constexpr (D == 128) {
+    const int s = r & 15;
+    return s ^ (s >> 2);
+  } else {
+    return (r >> 1) & 7;
+  }
 }
 
 // Transposed-V mode (VT: 256-row tiles, D = 128). The transposing LDS reads
