@@ -277,7 +277,10 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       // 16 steps (key block kb = n & 1, k-step kk = n >> 1), four independent
       // accumulator chains; each step's K and V fragments are read kPf steps
       // ahead into a ring, so an MFMA never waits on a read issued just
-      // before it.
+      // before it. The wave raises its priority over these products: on a
+      // SIMD shared with another wave, their MFMAs issue ahead of that wave's
+      // exponentials and dQ products (dQ -6.8% on one 75600-token document;
+      // raised over the dQ product as well, -4.8%).
       constexpr int kPf = 2;
       constexpr int kSteps = 2 * KSTEPS;
       bf16x8 kr[kPf + 1], vr[kPf + 1];
@@ -286,6 +289,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
         kr[n % (kPf + 1)] = load_bf16x8(reinterpret_cast<const bf16*>(&sm.k[cur][off]));
         vr[n % (kPf + 1)] = load_bf16x8(reinterpret_cast<const bf16*>(&sm.v[cur][off]));
       };
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int n = 0; n < kPf; ++n) fetch(n);
       __builtin_amdgcn_sched_barrier(0);
@@ -297,6 +301,7 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
         dp[kb] = mfma32(vr[n % (kPf + 1)], dof[kk], dp[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // Exponents S * scale_log2 - LSE_2. Tiles on a band edge or past the
       // range end (one wave-uniform test) give a masked key exponent -inf,
       // so p = 0 exactly with no branch (dP is finite: rows past the range
