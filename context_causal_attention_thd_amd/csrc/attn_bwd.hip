@@ -78,7 +78,9 @@ attn_bwd_dkdv_kernel(const BwdTile* __restrict__ tiles, int32_t H, const bf16* _
   const int tile_id = blockIdx.x / H;
   const int h = blockIdx.x - tile_id * H;
   const BwdTile t = tiles[tile_id];
-  const int w = threadIdx.x >> 6;
+  // Wave index, made wave-uniform explicitly so it and the LDS addresses
+  // derived from it live in scalar registers.
+  const int w = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
   const int G = lane >> 4;

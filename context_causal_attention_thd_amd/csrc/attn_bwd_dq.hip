@@ -93,7 +93,9 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   const int tile_id = blockIdx.x / H;
   const int h = blockIdx.x - tile_id * H;
   const FwdTile t = tiles[tile_id];
-  const int w = threadIdx.x >> 6;
+  // Wave index, made wave-uniform explicitly so it and the LDS addresses
+  // derived from it live in scalar registers.
+  const int w = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int li = lane & 31;
   const int hh = lane >> 5;

@@ -133,7 +133,9 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   const int tile_id = blockIdx.x / H;
   const int h = blockIdx.x - tile_id * H;
   const FwdTile t = tiles[tile_id];
-  const int w = threadIdx.x >> 6;
+  // Wave index, made wave-uniform explicitly so it and the LDS addresses
+  // derived from it live in scalar registers.
+  const int w = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;  // query column of this lane (and row of A operands)
   const int G = lane >> 4;    // 16-lane group
