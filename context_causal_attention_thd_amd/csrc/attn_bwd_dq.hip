@@ -213,21 +213,12 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       }
     }
   };
-  // LDS byte offsets of this lane's fragment reads (lane constants). The K /
-  // V fragment of key block kb, k-step kk is row kb*32 + li, logical chunk
-  // 2kk + hh. The K^T reads of key block kb, half u, head-dim block db are
-  // rows kb*32 + 16u + 4hh + (sl >> 2) (+8), logical chunk 4db + 2(g16 & 1) +
-  // ((sl & 3) >> 1), half sl & 1.
+  // LDS byte offsets of this lane's K / V fragment reads (lane constants):
+  // key block kb, k-step kk is row kb*32 + li, logical chunk 2kk + hh. (The
+  // K^T reads' offsets are formed in the loop.)
   const int fsw = hh ^ dq_swz<D>(li);
   auto f_off = [&](int kb, int kk) {
     return (kb * 32 + li) * ROWB + (((2 * kk) ^ fsw) << 4);
-  };
-  const int tr = hh * 4 + (sl >> 2);
-  const int tsw0 = (2 * (g16 & 1) + ((sl & 3) >> 1)) ^ dq_swz<D>(tr);
-  const int tsw1 = (2 * (g16 & 1) + ((sl & 3) >> 1)) ^ dq_swz<D>(tr + 8);
-  auto t_off = [&](int kb, int u, int half, int db) {
-    return (kb * 32 + 16 * u + 8 * half + tr) * ROWB +
-           (((4 * db) ^ (half ? tsw1 : tsw0)) << 4) + 8 * (sl & 1);
   };
 
   // Key tiles: those of [ks0, ke0), then those of [ks1, ke1).
@@ -344,12 +335,33 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
 #pragma unroll
         for (int u = 0; u < 2; ++u) dsb[kb * 2 + u] = to_bf16x8(dp[kb], u * 8);
       constexpr int kMs = 4 * DB;
+      // The transposing reads' lane offsets, recomputed per tile from a copy
+      // of the lane index the compiler cannot see through (an empty asm
+      // statement), so they are not held in registers across the whole loop:
+      // hoisted, they were spilled and reloaded inside it, and the reloads'
+      // waits also waited for the next tile's loads (dQ -0.5..1% on one 75600-token
+      // document; recomputing the K/V fragment offsets as well removed every
+      // spill but cost 8%, the address arithmetic landing among the S/dP MFMAs).
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      const int sl_o = lane_o & 15, g16_o = (lane_o >> 4) & 3, hh_o = (lane_o >> 5) & 1;
+      const int tr_o = hh_o * 4 + (sl_o >> 2);
+      const int tb_o = 2 * (g16_o & 1) + ((sl_o & 3) >> 1);
+      const int tsw0_o = tb_o ^ dq_swz<D>(tr_o), tsw1_o = tb_o ^ dq_swz<D>(tr_o + 8);
+      const int tbase_o = tr_o * ROWB + 8 * (sl_o & 1);
+      // K^T read of key block kb, half u, head-dim block db: rows kb*32 + 16u
+      // + 4hh + (sl >> 2) (+8), logical chunk 4db + 2(g16 & 1) + ((sl & 3) >>
+      // 1), half sl & 1.
+      auto t_off_o = [&](int kb, int u, int half, int db) {
+        return tbase_o + (kb * 32 + 16 * u + 8 * half) * ROWB +
+               (((4 * db) ^ (half ? tsw1_o : tsw0_o)) << 4);
+      };
       bf16x8 ar[kPf + 1];
       auto fetch_t = [&](int m) {
         const int kb = m / (2 * DB), u = (m / DB) & 1, db = m % DB;
         ar[m % (kPf + 1)] =
-            concat4(lds_read_tr4(reinterpret_cast<const bf16*>(&sm.k[cur][t_off(kb, u, 0, db)])),
-                    lds_read_tr4(reinterpret_cast<const bf16*>(&sm.k[cur][t_off(kb, u, 1, db)])));
+            concat4(lds_read_tr4(reinterpret_cast<const bf16*>(&sm.k[cur][t_off_o(kb, u, 0, db)])),
+                    lds_read_tr4(reinterpret_cast<const bf16*>(&sm.k[cur][t_off_o(kb, u, 1, db)])));
       };
 #pragma unroll
       for (int m = 0; m < kPf; ++m) fetch_t(m);
