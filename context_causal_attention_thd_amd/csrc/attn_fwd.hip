@@ -74,22 +74,24 @@ __device__ __forceinline__ int kv_swz(int r) {
 // of a row-major V tile cost as much per instruction as a 16-byte read for
 // half the bytes (measured on MI355X), so for long walks a pre-pass writes
 // V^T (head-dim rows of all keys) and the forward stages V^T tiles: D rows
-// of 64 keys (128 bytes), whose A-operand fragments of O^T = V^T P^T are
+// of 128 keys (256 bytes), whose A-operand fragments of O^T = V^T P^T are
 // plain 16-byte reads of 8 consecutive keys. P^T's k-slots must list those
 // same 8 keys, so the S^T row blocks take the K rows in a permuted order:
 // row r = 4g + i of key block kb holds key 32(kb>>1) + 8g + 4(kb&1) + i.
 // kswz_vt keeps those 16-row K reads free of bank conflicts (it maps the
 // rows read by lanes 0..15 of a group onto 16 distinct chunks); V^T tiles
-// use vt_swz (two rows per 256-byte bank line, rows of one parity distinct).
+// use kv_swz<128>, as the 16-row reads of a 256-byte-row tile. (vt_swz is
+// the swizzle of 64-key V^T tiles: two rows per 256-byte bank line, rows of
+// one parity distinct.)
 __device__ __forceinline__ int kswz_vt(int r) {
   return (r & 3) | (((r >> 3) & 1) << 2) | (((r >> 4) & 1) << 3);
 }
 __device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
 
-template <int D>
+template <int D, int BN>
 struct FwdSmem {
   static constexpr int ROWB = D * 2;            // bytes per row
-  static constexpr int TILEB = kFwdBN * ROWB;   // bytes per K or V tile
+  static constexpr int TILEB = BN * ROWB;       // bytes per K or V tile
   __attribute__((aligned(1024))) char k[2][TILEB];
   __attribute__((aligned(1024))) char v[2][TILEB];
 };
@@ -117,18 +119,20 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
                 int32_t vt_pitch) {
   static_assert(!VT || (D == 128 && QB == 2), "transposed V: 256-row tiles of head dim 128");
   constexpr int kThreads = kFwdThreads;
-  constexpr int BN = kFwdBN;
+  // Keys per tile: 128 with transposed V (one workgroup per CU, 128 KB of
+  // LDS for two K and two V^T tiles), else 64.
+  constexpr int BN = VT ? 2 * kFwdBN : kFwdBN;
   constexpr int KS = D / 32;   // 16x16x32 k-steps over the head dim
   constexpr int NB = D / 16;   // 16-wide blocks of the head dim
   constexpr int KB = BN / 16;  // 16-key blocks per tile
   constexpr int kPf = 2;       // LDS fragment reads in flight ahead of their MFMAs
-  constexpr int ROWB = FwdSmem<D>::ROWB;
-  constexpr int TILEB = FwdSmem<D>::TILEB;
+  constexpr int ROWB = FwdSmem<D, BN>::ROWB;
+  constexpr int TILEB = FwdSmem<D, BN>::TILEB;
   constexpr int LPR = ROWB / 16;               // lanes (16-byte chunks) per row
   constexpr int RPI = 1024 / ROWB;             // rows per wave DMA instruction
   constexpr int NI = TILEB / 1024 / (kThreads / 64);  // DMA instructions per wave per tensor
   static_assert(NI * (kThreads / 64) * 1024 == TILEB, "tile splits evenly over the waves");
-  __shared__ FwdSmem<D> sm;
+  __shared__ FwdSmem<D, BN> sm;
 
   const int tile_id = blockIdx.x / H;
   const int h = blockIdx.x - tile_id * H;
@@ -194,18 +198,23 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     drow[j] = (w * NI + j) * RPI + lane / LPR;
     dcol[j] = (uint32_t)(((lane % LPR) ^ (VT ? kswz_vt(drow[j]) : kv_swz<D>(drow[j]))) * 16);
   }
-  // V^T staging (VT): DMA instruction j of wave w fills V^T rows (head dims)
-  // [(w*NI + j)*8, +8), 128 bytes each: lane i loads dim (w*NI + j)*8 + i/8,
-  // physical chunk i%8, i.e. keys k0 + 8*((i%8) ^ vt_swz(dim)) .. +7. The
-  // pitch leaves 64 keys past the last tile start, and keys no local query
-  // attends (padding among them) hold 0 in vt, so the keys of a tile past
-  // its range end enter P V^T as 0 * finite.
+  // V^T staging (VT): a V^T row is BN keys (256 bytes with 128-key tiles, 16
+  // chunks). DMA instruction j of wave w fills rows (head dims)
+  // [(w*NI + j)*VRPI, +VRPI): lane i loads dim (w*NI + j)*VRPI + i/VLPR,
+  // physical chunk i%VLPR, i.e. keys k0 + 8*((i%VLPR) ^ vtswz(dim)) .. +7.
+  // The pitch leaves 128 keys past the last tile start, and keys no local
+  // query attends (padding among them) hold 0 in vt, so the keys of a tile
+  // past its range end enter P V^T as 0 * finite.
+  constexpr int VLPR = BN * 2 / 16;      // lanes (16-byte chunks) per V^T row
+  constexpr int VRPI = 64 / VLPR;        // V^T rows per DMA instruction
+  auto vtswz = [&](int r) { return BN == 128 ? kv_swz<128>(r) : vt_swz(r); };
   uint32_t vtoff[NI];
   if constexpr (VT) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int dr = (w * NI + j) * 8 + lane / 8;
-      vtoff[j] = (uint32_t)dr * (uint32_t)vt_pitch * 2u + (uint32_t)(((lane % 8) ^ vt_swz(dr)) * 16);
+      const int dr = (w * NI + j) * VRPI + lane / VLPR;
+      vtoff[j] = (uint32_t)dr * (uint32_t)vt_pitch * 2u +
+                 (uint32_t)(((lane % VLPR) ^ vtswz(dr)) * 16);
     }
   }
   auto load_vt = [&](int k0, char* dst) {
@@ -384,7 +393,7 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       auto fetch = [&](int nb) {
         if constexpr (VT)  // V^T row nb*16 + l16, keys 32ks + 8G .. +7
           ring[nb % (kPf + 1)] = load_bf16x8(reinterpret_cast<const bf16*>(
-              &sm.v[vbuf][(nb * 16 + l16) * 128 + (((ks * 4 + G) ^ ((l16 >> 1) & 7)) << 4)]));
+              &sm.v[vbuf][(nb * 16 + l16) * (BN * 2) + (((ks * 4 + G) ^ vtswz(nb * 16 + l16)) << 4)]));
         else
           ring[nb % (kPf + 1)] =
               concat4(lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 0, nb)])),
@@ -615,7 +624,7 @@ v_transpose_kernel(const bf16* __restrict__ v, const int32_t* __restrict__ kv_ro
 
 }  // namespace
 
-int32_t vt_pitch_for(int64_t T) { return (int32_t)((T + 63) / 64 * 64 + 64); }
+int32_t vt_pitch_for(int64_t T) { return (int32_t)((T + 63) / 64 * 64 + 128); }
 
 hipError_t launch_v_transpose(const void* v, KvRows kv, int32_t H, int32_t D,
                               const ZeroRange* zr, int32_t n_zr, void* vt, int32_t pitch,

@@ -296,7 +296,7 @@ thdcp_status_t thdcp_plan_local_seqlens(thdcp_plan_t plan, int32_t* out_host);
  * Past the tables it holds the split key walks' counters (uploaded as zero,
  * left at zero by every launch) and their partial results, and, for plans
  * with fwd_tile_rows 256 and head dim 128, V transposed (H * 128 * pitch
- * bf16, pitch = T rounded up to 64, plus 64), which cp_attn_fwd writes from
+ * bf16, pitch = T rounded up to 64, plus 128), which cp_attn_fwd writes from
  * v before its attention launch. So the plan's forward and dQ launches must
  * not overlap: enqueue calls that use one workspace on one stream (or order
  * them). The copy covers the tables and counters only.

@@ -440,14 +440,15 @@ def test_noalloc_refuses_plans_above_its_scratch(L):
 
 def test_plan_workspace_holds_transposed_v():
     # Long-walk plans of head dim 128 read V transposed: their workspace ends
-    # with H * 128 * pitch bf16 for V^T (pitch: T rounded up to 64, plus 64).
+    # with H * 128 * pitch bf16 for V^T (pitch: T rounded up to 64, plus 128:
+    # a 128-key tile may start at the last key).
     # Head dim 64, P2P and short-walk plans reserve nothing for it.
     def plan(D, p2p=False, lengths=(8700,), padded=(8704,)):
         cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
         cup = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
         return thd.Plan(cu, cup, 8800, 1, 0, "no_load_balance", 2, D, upload=False, p2p=p2p,
                         max_key_splits=1)
-    pitch = (8800 + 63) // 64 * 64 + 64
+    pitch = (8800 + 63) // 64 * 64 + 128
     vt_bytes = 2 * 128 * pitch * 2
     long128, long64, p2p128 = plan(128), plan(64), plan(128, p2p=True)
     short128 = plan(128, lengths=(544,) * 16, padded=(544,) * 16)
