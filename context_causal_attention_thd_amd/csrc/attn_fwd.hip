@@ -49,8 +49,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.f;
 
-// K/V tiles in LDS: kFwdBN rows of D bf16, unpadded (LDS DMA writes each
-// wave's 1 KB block contiguously), with the 16-byte chunks of row r permuted:
+// K/V tiles in LDS: BN rows of D bf16 (64 keys; 128 in the transposed-V
+// mode), unpadded (LDS DMA writes each wave's 1 KB block contiguously), with
+// the 16-byte chunks of row r permuted:
 // logical chunk c sits at chunk c ^ kv_swz(r). For D = 128 the swizzle was
 // chosen by timing both read patterns of the loop -- the 16-row fragment
 // reads (16 rows, one chunk per 16 lanes) and the transposing V^T reads
@@ -393,7 +394,8 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
       auto fetch = [&](int nb) {
         if constexpr (VT)  // V^T row nb*16 + l16, keys 32ks + 8G .. +7
           ring[nb % (kPf + 1)] = load_bf16x8(reinterpret_cast<const bf16*>(
-              &sm.v[vbuf][(nb * 16 + l16) * (BN * 2) + (((ks * 4 + G) ^ vtswz(nb * 16 + l16)) << 4)]));
+              &sm.v[vbuf][(nb * 16 + l16) * (BN * 2) +
+                          (((ks * 4 + G) ^ vtswz(nb * 16 + l16)) << 4)]));
         else
           ring[nb % (kPf + 1)] =
               concat4(lds_read_tr4(reinterpret_cast<const bf16*>(&sm.v[vbuf][v_off(ks, 0, nb)])),
