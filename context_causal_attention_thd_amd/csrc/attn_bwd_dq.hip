@@ -99,8 +99,6 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
   const int lane = threadIdx.x & 63;
   const int li = lane & 31;
   const int hh = lane >> 5;
-  const int sl = lane & 15;
-  const int g16 = lane >> 4;
   const int64_t rs = (int64_t)H * D;
   const int64_t head_off = (int64_t)h * D;
 
@@ -339,9 +337,10 @@ attn_bwd_dq_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __r
       // of the lane index the compiler cannot see through (an empty asm
       // statement), so they are not held in registers across the whole loop:
       // hoisted, they were spilled and reloaded inside it, and the reloads'
-      // waits also waited for the next tile's loads (dQ -0.5..1% on one 75600-token
-      // document; recomputing the K/V fragment offsets as well removed every
-      // spill but cost 8%, the address arithmetic landing among the S/dP MFMAs).
+      // waits also waited for the next tile's loads (dQ -0.5..1% on one
+      // 75600-token document; recomputing the K/V fragment offsets as well
+      // removed every spill but cost 8%, the address arithmetic landing among
+      // the S/dP MFMAs).
       int lane_o = lane;
       asm volatile("" : "+v"(lane_o));
       const int sl_o = lane_o & 15, g16_o = (lane_o >> 4) & 3, hh_o = (lane_o >> 5) & 1;
