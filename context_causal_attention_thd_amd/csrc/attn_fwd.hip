@@ -36,10 +36,10 @@
 // so probabilities stay below 2^kRescaleLog2 (exact in fp32, representable in
 // bf16) and the accumulator rescale, with its cross-lane max, runs only on the
 // rare tiles where some lane of the wave crosses that bound (a wave vote). The
-// row sum comes from the matrix core, not from per-element adds: one more MFMA
-// per k-step multiplies the same bf16 P by a block of ones, so the sum that
-// normalises O is that of the P the P V^T product used (one VALU add per
-// score element less; the loop carries more VALU work than its MFMAs hide).
+// row sum (head dim 128) comes from the matrix core, not from per-element adds:
+// one more MFMA per k-step multiplies the same bf16 P by a block of ones, so the
+// sum that normalises O is that of the P the P V^T product used (one VALU add
+// per score element less; the loop carries more VALU work than its MFMAs hide).
 // Only tiles on the causal diagonal apply a per-element mask.
 #include "device_common.h"
 #include "internal.h"
@@ -183,9 +183,12 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[qb][nb][i] = 0.f;
   float m_run[QB], l_part[QB];  // running max (log2 units); this lane's share of the row sum
-  // Row sums on the matrix core: lsum[qb] += 1 P^T per k-step (all four entries
-  // hold the sum of the lane's query; measured on one 75600-token document:
-  // forward -2.4..-3.9% against per-element fp32 adds).
+  // Head dim 128: row sums on the matrix core, lsum[qb] += 1 P^T per k-step
+  // (all four entries hold the sum of the lane's query; measured on one
+  // 75600-token document: forward -2.4..-3.9% against per-element fp32 adds).
+  // Head dim 64 keeps the per-lane fp32 adds: there the eight more registers
+  // cost the 128-row instance a workgroup per CU (nlb_32k at head dim 64: +10%).
+  constexpr bool kMfmaRowSum = D == 128;
   f32x4 lsum[QB];
   bf16x8 ones;
 #pragma unroll
@@ -357,8 +360,12 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
         const float m_new = rm > m_run[qb] + kRescaleLog2 ? rm : m_run[qb];
         const float alpha = m_new == m_run[qb] ? 1.f : fast_exp2(m_run[qb] - m_new);
         m_run[qb] = m_new;
+        if constexpr (kMfmaRowSum) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lsum[qb][i] *= alpha;
+          for (int i = 0; i < 4; ++i) lsum[qb][i] *= alpha;
+        } else {
+          l_part[qb] *= alpha;
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -375,15 +382,19 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
   // (the scheduling barriers keep the compiler from moving them there on its
   // own): forward -1.3% on one 75600-token document, bit-identical.
   auto softmax_pv = [&](int vbuf, f32x4 (&s)[QB][KB]) {
-    float m_use[QB];
+    float m_use[QB], ps[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+    for (int qb = 0; qb < QB; ++qb) {
+      m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      ps[qb] = 0.f;
+    }
     // Exponential e of k-step ks: query block e / 8, key block 2ks + (e % 8) / 4,
     // entry e % 4 (each block's sum in the order of a plain loop).
     auto expo = [&](int ks, int e) {
       const int qb = e / 8, kb = 2 * ks + (e % 8) / 4, i = e % 4;
       const float p = fast_exp2(fmaf(s[qb][kb][i], scale_log2, -m_use[qb]));
       s[qb][kb][i] = p;
+      if constexpr (!kMfmaRowSum) ps[qb] += p;
     };
     constexpr int kE = QB * 8;       // exponentials per k-step
     constexpr int kEPer = kE / NB;   // of the next k-step per P V^T step
@@ -394,7 +405,13 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
     for (int ks = 0; ks < KB / 2; ++ks) {
       bf16x8 pb[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) pb[qb] = pack8(s[qb][2 * ks], s[qb][2 * ks + 1]);
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (!kMfmaRowSum) {
+          l_part[qb] += ps[qb];
+          ps[qb] = 0.f;
+        }
+        pb[qb] = pack8(s[qb][2 * ks], s[qb][2 * ks + 1]);
+      }
       bf16x8 ring[kPf + 1];
       auto fetch = [&](int nb) {
         if constexpr (VT)  // V^T row nb*16 + l16, keys 32ks + 8G .. +7
@@ -415,7 +432,7 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
         if (nb + kPf < NB) fetch(nb + kPf);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma16(ring[nb % (kPf + 1)], pb[qb], oacc[qb][nb]);
-        if (nb == 0) {
+        if (kMfmaRowSum && nb == 0) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) lsum[qb] = mfma16(ones, pb[qb], lsum[qb]);
         }
@@ -491,8 +508,10 @@ attn_fwd_kernel(const FwdTile* __restrict__ tiles, int32_t H, const bf16* __rest
 
   // The row sum as four shares, one per lane group, as the merge and the
   // epilogue take it.
+  if constexpr (kMfmaRowSum) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) l_part[qb] = G == 0 ? lsum[qb][0] : 0.f;
+    for (int qb = 0; qb < QB; ++qb) l_part[qb] = G == 0 ? lsum[qb][0] : 0.f;
+  }
 
   if (t.nparts > 1) {
     // Split key walk: this part's state (accumulators, then per query block
