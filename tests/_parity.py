@@ -24,19 +24,22 @@ def err(got, ref):
     return max_abs, rel
 
 
-def _log(name, a, r):
-    """Append measured errors to $THDCP_PARITY_LOG (JSON lines) when set."""
+def _log(name, a, r, bar):
+    """Append measured errors and the bars they were held to to
+    $THDCP_PARITY_LOG (JSON lines) when set."""
     path = os.environ.get("THDCP_PARITY_LOG")
     if path:
         with open(path, "a") as f:
-            f.write(json.dumps({"check": name, "max_abs": a, "rel_l2": r}) + "\n")
+            f.write(json.dumps({"check": name, "max_abs": a, "rel_l2": r,
+                                "bar": [bar[0], bar[1] if np.isfinite(bar[1]) else None]})
+                    + "\n")
 
 
 def assert_close(got, ref, name, max_abs=MAX_ABS, rel_l2=REL_L2):
     got = np.asarray(got, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     a, r = err(got, ref)
-    _log(name, a, r)
+    _log(name, a, r, (max_abs, rel_l2))
     assert a <= max_abs and r <= rel_l2, f"{name}: max_abs={a:.3e} rel_l2={r:.3e}"
     return a, r
 

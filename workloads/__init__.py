@@ -162,3 +162,31 @@ def dense_bf16(layout: str, B: int, S: int, H: int, D: int, seed: int,
         out[n] = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(
             torch.bfloat16)
     return out
+
+
+def stair_bf16(w: Workload, step_keys: int = 256, jump_log2: float = 10.0, q_mag: float = 2.0,
+               noise: float = 0.05):
+    """Dict of torch.bfloat16 CPU tensors [T, H, D] whose attention scores
+    climb in steps along each document: every ``step_keys`` keys the score of
+    a key rises by about ``jump_log2`` in log2 units at the usual 1/sqrt(D)
+    scale. Q = q_mag (1 + noise n), K = c(pos) (1 + noise n) with
+    c(pos) = step * (pos // step_keys), pos the key's offset in its padded
+    document and step = jump_log2 / (q_mag sqrt(D) log2(e)); V ~ N(0, 1),
+    dO ~ N(0, 1) / 4 (n: i.i.d. N(0, 1) float32 from default_rng(1000 *
+    number + tensor id + 50), all rounded to bf16). It only builds inputs;
+    the scores are named to say what the layout is for."""
+    import torch
+    cup = w.cu_seqlens_padded()
+    pos = np.zeros(w.T, dtype=np.int64)
+    for d in range(len(cup) - 1):
+        pos[cup[d]:cup[d + 1]] = np.arange(cup[d + 1] - cup[d])
+    step = jump_log2 / (q_mag * np.sqrt(w.D) * np.log2(np.e))
+    c = (step * (pos // step_keys)).astype(np.float32)[:, None, None]
+    n = {x: normal_f32(w, x, seed_offset=50) for x in ("q", "k", "v", "do")}
+    arrs = {
+        "q": q_mag * (1.0 + noise * n["q"]),
+        "k": c * (1.0 + noise * n["k"]),
+        "v": n["v"],
+        "do": 0.25 * n["do"],
+    }
+    return {x: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16) for x, a in arrs.items()}
